@@ -1,0 +1,139 @@
+"""Planted mistakes in the oracle must be caught by its pins.
+
+Each case swaps one oracle function for a copy with a plausible mistake (a
+dropped term, a wrong sign, an off-by-one, a transposed index, a wrong
+base, a wrong tile, a missing renormalisation) and checks that at least one
+of the pins in test_oracle_pins / test_oracle_fp8 then fails.  Everything
+runs on the CPU.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.mla_oracle as om
+from tests import test_oracle_fp8 as fp8pins
+from tests import test_oracle_pins as pins
+
+
+def _pin_suite():
+    checks = [
+        lambda: pins.test_decode_matches_torch_sdpa(16),
+        lambda: pins.test_decode_matches_torch_sdpa(1),
+        lambda: pins.test_prefill_matches_torch_sdpa(True),
+        lambda: pins.test_single_key_returns_its_row(),
+        lambda: pins.test_zero_scale_gives_mean_and_log_count(),
+        lambda: pins.test_split_merge_equals_unsplit([64, 128, 129]),
+        lambda: pins.test_causal_visibility_boundary(),
+        lambda: fp8pins.test_hand_built_record_decodes_as_the_layout_says(),
+        lambda: fp8pins.test_record_encoder_layout_and_scales(),
+        lambda: fp8pins.test_all_codes_match_torch_float8_e4m3fn(),
+    ]
+    failed = 0
+    for c in checks:
+        try:
+            c()
+        except (AssertionError, ValueError, IndexError):
+            failed += 1
+    return failed
+
+
+def _attend_variant(mistake):
+    def attend(qn, qp, ckv, kpe, sm_scale, n_visible):
+        qn = np.asarray(qn, dtype=np.float64)
+        qp = np.asarray(qp, dtype=np.float64)
+        R, L = qn.shape[0], ckv.shape[0]
+        n_visible = np.broadcast_to(np.asarray(n_visible, dtype=np.int64), (R,))
+        if L == 0:
+            return np.zeros((R, 512)), np.full(R, -np.inf)
+        if mistake == "drop_rope":
+            s = sm_scale * (qn @ ckv.T)
+        elif mistake == "scale_one_term":
+            s = sm_scale * (qn @ ckv.T) + qp @ kpe.T
+        elif mistake == "sign":
+            s = -sm_scale * (qn @ ckv.T + qp @ kpe.T)
+        else:
+            s = sm_scale * (qn @ ckv.T + qp @ kpe.T)
+        vis_n = n_visible - 1 if mistake == "off_by_one" else n_visible
+        visible = np.arange(L)[None, :] < vis_n[:, None]
+        s = np.where(visible, s, -np.inf)
+        m = s.max(axis=1, initial=-np.inf)
+        m = np.where(np.isfinite(m), m, 0.0)
+        z = np.exp(s - m[:, None]).sum(axis=1)
+        lse = m + np.log(np.maximum(z, 1e-300))
+        if mistake == "base2_lse":
+            lse = lse / math.log(2.0)
+        w = np.where(visible, np.exp(s - (m if mistake == "unnormalised" else lse)[:, None]), 0.0)
+        return w @ ckv, lse
+    return attend
+
+
+@pytest.mark.parametrize("mistake", ["drop_rope", "scale_one_term", "sign", "off_by_one",
+                                     "base2_lse", "unnormalised"])
+def test_attend_mistakes_are_caught(monkeypatch, mistake):
+    assert _pin_suite() == 0  # the real oracle passes
+    bad = _attend_variant(mistake)
+    monkeypatch.setattr(om, "attend", bad)
+    monkeypatch.setattr(oracle, "attend", bad)
+    assert _pin_suite() > 0
+
+
+def test_transposed_slot_mapping_is_caught(monkeypatch):
+    def slots(kv_indptr, kv_indices, b, kv_len, page_size):
+        pages = kv_indices[kv_indptr[b]:kv_indptr[b + 1]]
+        j = np.arange(kv_len)
+        return pages[np.minimum(j % page_size, len(pages) - 1)], np.minimum(j // page_size, page_size - 1)
+    monkeypatch.setattr(om, "_token_slots", slots)
+    assert _pin_suite() > 0
+
+
+def test_causal_alignment_mistake_is_caught(monkeypatch):
+    # top-left instead of bottom-right alignment
+    monkeypatch.setattr(om, "prefill_visible", lambda L, n, causal: np.arange(n) + 1 if causal else np.full(n, L))
+    assert _pin_suite() > 0
+
+
+@pytest.mark.parametrize("mistake", ["tile64", "inverse_scale", "rope_big_endian"])
+def test_fp8_record_mistakes_are_caught(monkeypatch, mistake):
+    real = om.fp8_record_decode
+
+    def decode(records):
+        r = om._as_u8(records)
+        flat = r.reshape(-1, 656)
+        codes = flat[:, :512]
+        scales = np.ascontiguousarray(flat[:, 512:528]).view("<f4").astype(np.float64)
+        rope_bits = np.ascontiguousarray(flat[:, 528:]).view(">u2" if mistake == "rope_big_endian" else "<u2")
+        vals = om.e4m3_decode(codes)
+        d = np.arange(512)
+        tile = (d // 64) % 4 if mistake == "tile64" else d // 128
+        sc = scales[:, tile]
+        nope = vals / sc if mistake == "inverse_scale" else vals * sc
+        rope = om.bf16_bits_to_f64(rope_bits.astype(np.uint16))
+        return nope.reshape(*r.shape[:-1], 512), rope.reshape(*r.shape[:-1], 64)
+
+    assert real is not decode
+    monkeypatch.setattr(om, "fp8_record_decode", decode)
+    monkeypatch.setattr(oracle, "fp8_record_decode", decode)
+    with np.errstate(all="ignore"):
+        assert _pin_suite() > 0
+
+
+def test_merge_without_renormalisation_is_caught(monkeypatch):
+    def merge(outs, lses):
+        outs = np.asarray(outs)
+        lses = np.asarray(lses)
+        M = lses.max(axis=0)
+        w = np.exp(lses - M[None])
+        return (w[:, :, None] * outs).sum(axis=0), M + np.log(w.sum(axis=0))
+    monkeypatch.setattr(om, "merge_partials", merge)
+    monkeypatch.setattr(oracle, "merge_partials", merge)
+    assert _pin_suite() > 0
+
+
+def test_e4m3_exponent_bias_mistake_is_caught(monkeypatch):
+    real = om.e4m3_decode
+    monkeypatch.setattr(om, "e4m3_decode", lambda c: real(c) * 2.0)
+    monkeypatch.setattr(oracle, "e4m3_decode", lambda c: real(c) * 2.0)
+    assert _pin_suite() > 0
