@@ -1,0 +1,195 @@
+/*
+ * mla.h — C ABI of the paged absorbed-MLA attention library (libmla.so),
+ * built for AMD Instinct MI355X (gfx950) with hand-written HIP kernels.
+ *
+ * The operation ("MLA Paged", FlashInfer bench docs, sections "decode" and
+ * "prefill"): for each query row r and head h,
+ *     s_j  = sm_scale * (q_nope[r,h,:] . ckv_j + q_pe[r,h,:] . kpe_j)
+ *     lse  = ln sum_j exp(s_j)                     (natural log, fp32)
+ *     out  = sum_j exp(s_j - lse) * ckv_j          (V = first 512 latent dims,
+ *                                                   "mla_decoding_single_batch")
+ * over the keys j the row may see, gathered through the page table
+ * kv_indptr / kv_indices from [num_pages, page_size, dim] caches.  The
+ * log-sum-exp / exp(P - lse) form is the one written in FlashMLA's "Sparse
+ * MLA Prefill Kernel" passage (there in base 2; here natural log).
+ *
+ * Conventions for every call below
+ *   - Pointers named *_host are host memory; every other array pointer is
+ *     device memory on the current HIP device.  All tensors are dense,
+ *     row-major and contiguous with the shapes given.
+ *   - bf16 means IEEE-754 binary32 truncated to its upper 16 bits
+ *     (bfloat16), little-endian; int32 arrays are little-endian.
+ *   - The caller owns every device buffer (inputs, out, lse, workspace) and
+ *     the stream.  The library owns only the host-side plan object.
+ *   - No call throws.  Every call returns an mla_status; on error nothing is
+ *     launched and no output is written.
+ *   - Run calls (mla_decode, mla_prefill, mla_decode_fp8) allocate nothing,
+ *     never synchronise and never copy to or from the host: they only enqueue
+ *     kernels on `stream`, so they can be captured into a HIP graph.  Calls
+ *     that overlap in time must use different workspaces.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mla_status {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARGUMENT = -1, /* null pointer, bad size, inconsistent host arrays */
+  MLA_ERR_UNSUPPORTED = -2,      /* a shape or mode this build does not implement     */
+  MLA_ERR_WORKSPACE = -3,        /* workspace missing, misaligned or too small        */
+  MLA_ERR_PLAN_MISMATCH = -4,    /* run call does not match the plan's kind / format  */
+  MLA_ERR_DEVICE = -5            /* a HIP runtime call or kernel launch failed        */
+} mla_status;
+
+typedef enum mla_dtype { MLA_DTYPE_BF16 = 0, MLA_DTYPE_FP32 = 1 } mla_dtype;
+
+/* Latent-cache formats.
+ *   MLA_KV_BF16: two caches, ckv [num_pages, page_size, 512] bf16 and
+ *     kpe [num_pages, page_size, 64] bf16 ("MLA Paged", Inputs).
+ *   MLA_KV_FP8_E4M3_T128: one cache [num_pages, page_size, 656] uint8, one
+ *     656-byte record per token (FlashMLA digest, "FP8 KV Cache Quantization
+ *     and Dequantization", V32_FP8Sparse): bytes 0..511 = 512 OCP e4m3
+ *     codes of the latent dims, bytes 512..527 = four little-endian fp32
+ *     scales (scale t applies to dims 128t..128t+127), bytes 528..655 = the
+ *     64 rope dims as bf16.  Key value = code * scale; rope as stored.   */
+typedef enum mla_kv_format { MLA_KV_BF16 = 0, MLA_KV_FP8_E4M3_T128 = 1 } mla_kv_format;
+
+typedef enum mla_kind { MLA_KIND_DECODE = 0, MLA_KIND_PREFILL = 1 } mla_kind;
+
+/* Tile modes of the attention kernel (0 lets the planner choose).
+ *   MLA_TILE_WIDE:   a workgroup holds up to 128 query rows, 32 per wave, and
+ *                    all four waves share each key tile (rows >= 64).
+ *   MLA_TILE_NARROW: a workgroup holds up to 16 query rows and its four waves
+ *                    split every key tile between them (few rows).          */
+typedef enum mla_tile_mode { MLA_TILE_AUTO = 0, MLA_TILE_WIDE = 1, MLA_TILE_NARROW = 2 } mla_tile_mode;
+
+typedef struct mla_plan_desc {
+  int32_t kind;          /* mla_kind                                                */
+  int32_t batch;         /* number of requests, >= 0                                */
+  int32_t num_qo_heads;  /* query heads H, >= 1 (the latent cache has one KV head) */
+  int32_t head_dim_ckv;  /* must be 512                                             */
+  int32_t head_dim_kpe;  /* must be 64                                              */
+  int32_t page_size;     /* tokens per page, a power of two in [1, 4096]            */
+  int32_t num_pages;     /* pages in the cache pool, >= 1                           */
+  int32_t kv_format;     /* mla_kv_format                                           */
+  int32_t causal;        /* prefill only: 1 = causal, bottom-right aligned; 0 = none */
+  int32_t num_cus;       /* compute units to balance for; 0 = ask the current device */
+  int32_t max_splits;    /* upper bound on key chunks per request; 0 = automatic    */
+  int32_t force_splits;  /* > 0: cut every request into this many chunks (testing)  */
+  int32_t tile_mode;     /* mla_tile_mode                                           */
+} mla_plan_desc;
+
+typedef struct mla_plan mla_plan; /* opaque, immutable after creation */
+
+/* Host-side plan: the split-KV schedule for one set of request lengths.
+ * Follows the planning step the pages describe: FlashMLA's
+ * "get_mla_metadata" (computed once before the decode loop, reusable across
+ * layers while cache_seqlens are unchanged) and FlashInfer's
+ * "batch_mla_decode_with_paged_kv_cache" (the host reads seq_lens and
+ * qo_indptr to derive plan bounds; run outside graph capture).
+ *
+ *   kv_len_host    [batch]   int32: keys of each request (the pages'
+ *                  seq_lens / cache_seqlens).  NULL means every page of the
+ *                  request is full: kv_len = pages * page_size.
+ *   kv_indptr_host [batch+1] int32: the same CSR offsets that will be passed
+ *                  to the run call; kv_indptr[b+1]-kv_indptr[b] must equal
+ *                  ceil(kv_len[b] / page_size) and kv_indptr[0] must be 0.
+ *   qo_indptr_host [batch+1] int32, prefill only (else NULL): query row
+ *                  offsets, qo_indptr[0] = 0, non-decreasing; with causal=1
+ *                  each request needs q_len <= kv_len.
+ * The plan is valid for any call with the same lengths and descriptor.
+ * Errors: MLA_ERR_INVALID_ARGUMENT (null pointers, inconsistent arrays),
+ * MLA_ERR_UNSUPPORTED (head dims other than 512/64, page_size not a power of
+ * two in range, fp8 prefill), MLA_ERR_DEVICE (num_cus = 0 and the device
+ * query failed).  Makes no device allocation and launches nothing.       */
+mla_status mla_plan_create(mla_plan** plan, const mla_plan_desc* desc,
+                           const int32_t* kv_len_host, const int32_t* kv_indptr_host,
+                           const int32_t* qo_indptr_host);
+
+void mla_plan_destroy(mla_plan* plan);
+
+/* Bytes of device workspace the run calls need with this plan (work list,
+ * split partial outputs and their lse), and the number of work items and of
+ * split groups (diagnostics).                                             */
+size_t mla_plan_workspace_bytes(const mla_plan* plan);
+int32_t mla_plan_num_work_items(const mla_plan* plan);
+int32_t mla_plan_num_split_groups(const mla_plan* plan);
+
+/* Copy the plan's work list [num_work_items][8] int32 to host memory
+ * `items_host` (test and diagnostic use): per item
+ *   {request, first_row, num_rows, key_begin, key_end, kv_len, q_len, slot}
+ * where rows count (query token, head) pairs of the request as
+ * token * H + head and slot is -1 for an item that writes the final output
+ * or the index of its partial-result slot.                               */
+mla_status mla_plan_get_work_items(const mla_plan* plan, int32_t* items_host, size_t capacity);
+
+/* Grid of the attention kernel: workgroup w processes work items
+ * wg_ptr[w] .. wg_ptr[w+1]-1 in order.  mla_plan_get_workgroup_ptr copies
+ * the [num_workgroups + 1] int32 offsets to host memory (diagnostics).    */
+int32_t mla_plan_num_workgroups(const mla_plan* plan);
+mla_status mla_plan_get_workgroup_ptr(const mla_plan* plan, int32_t* wg_ptr_host, size_t capacity);
+
+/* One asynchronous host-to-device copy of the plan's work list into the
+ * head of `workspace` (device memory of at least mla_plan_workspace_bytes,
+ * 256-byte aligned) on `stream`.  Must be called (outside graph capture)
+ * before the first run call that uses this workspace with this plan.      */
+mla_status mla_plan_upload(const mla_plan* plan, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/* Decode ("MLA Paged", section "decode"): one query row per request.
+ *   q_nope [batch, H, 512] bf16; q_pe [batch, H, 64] bf16
+ *   ckv_cache [num_pages, page_size, 512] bf16; kpe_cache [num_pages, page_size, 64] bf16
+ *   kv_indptr [batch+1] int32 (device copy of the plan's), kv_indices
+ *   [kv_indptr[batch]] int32 page ids in [0, num_pages)
+ *   sm_scale: scale applied to q.k ("softmax scale", finite)
+ *   out [batch, H, 512] of out_dtype (bf16 or fp32); lse [batch, H] fp32,
+ *   natural log; a request with kv_len 0 gets out = 0 and lse = -inf.
+ * Slots past kv_len in a request's last page and pages no request lists
+ * are never read into the result (they may hold any bits, NaN included).
+ * Errors: MLA_ERR_INVALID_ARGUMENT (null pointer, non-finite sm_scale, bad
+ * out_dtype), MLA_ERR_PLAN_MISMATCH (plan is not a bf16 decode plan),
+ * MLA_ERR_WORKSPACE, MLA_ERR_DEVICE (launch failed).                     */
+mla_status mla_decode(const mla_plan* plan, const void* q_nope, const void* q_pe,
+                      const void* ckv_cache, const void* kpe_cache, const int32_t* kv_indptr,
+                      const int32_t* kv_indices, float sm_scale, void* out, int32_t out_dtype,
+                      float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Prefill ("MLA Paged", section "prefill"): packed query rows, request b
+ * owning rows qo_indptr[b] .. qo_indptr[b+1]-1, total_q = qo_indptr[batch].
+ *   q_nope [total_q, H, 512] bf16; q_pe [total_q, H, 64] bf16
+ *   qo_indptr [batch+1] int32 (device copy of the plan's)
+ *   out [total_q, H, 512]; lse [total_q, H] fp32.
+ * With causal=1 (the default mask_type of "batch_mla_decode_with_paged_kv_cache"),
+ * query i of a request with n queries and L keys sees keys 0..L-n+i.
+ * Everything else as for mla_decode; the plan must be a bf16 prefill plan. */
+mla_status mla_prefill(const mla_plan* plan, const void* q_nope, const void* q_pe,
+                       const void* ckv_cache, const void* kpe_cache, const int32_t* qo_indptr,
+                       const int32_t* kv_indptr, const int32_t* kv_indices, float sm_scale,
+                       void* out, int32_t out_dtype, float* lse, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream);
+
+/* Decode over the fp8 record cache (MLA_KV_FP8_E4M3_T128 above):
+ *   kv_cache [num_pages, page_size, 656] uint8; q_nope / q_pe bf16 as in
+ *   mla_decode.  Keys are dequantised in the kernel (code * scale, rounded to
+ *   bf16); everything else as for mla_decode.  Plan: fp8 decode plan.     */
+mla_status mla_decode_fp8(const mla_plan* plan, const void* q_nope, const void* q_pe,
+                          const void* kv_cache, const int32_t* kv_indptr,
+                          const int32_t* kv_indices, float sm_scale, void* out,
+                          int32_t out_dtype, float* lse, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
+/* Static description of a status code. */
+const char* mla_status_str(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

@@ -239,7 +239,9 @@ def _take_rows(cache, page, slot):
         import torch
 
         if isinstance(cache, torch.Tensor):
-            return cache.detach().cpu()[torch.from_numpy(page), torch.from_numpy(slot)]
+            dev = cache.device
+            rows = cache.detach()[torch.from_numpy(page).to(dev), torch.from_numpy(slot).to(dev)]
+            return rows.cpu()
     except ImportError:  # pragma: no cover
         pass
     return np.asarray(cache)[page, slot]

@@ -1,0 +1,29 @@
+"""Paged absorbed-MLA attention for AMD Instinct MI355X (gfx950).
+
+A thin Python binding over the C ABI of ``libmla.so`` (declared in
+``include/mla.h``).  It only marshals arguments: allocation of outputs and
+workspace goes through torch, every step of the computation runs in the
+library's HIP kernels.  If the library is missing or cannot be loaded, every
+call raises; there is no fallback.
+
+Names follow the C ABI: :func:`mla_plan_create`, :func:`mla_decode`,
+:func:`mla_prefill`, :func:`mla_decode_fp8`.
+"""
+
+from ._binding import (  # noqa: F401
+    MLAError,
+    Plan,
+    lib_path,
+    load_library,
+    mla_decode,
+    mla_decode_fp8,
+    mla_plan_create,
+    mla_prefill,
+    MLA_KIND_DECODE,
+    MLA_KIND_PREFILL,
+    MLA_KV_BF16,
+    MLA_KV_FP8_E4M3_T128,
+    MLA_TILE_AUTO,
+    MLA_TILE_WIDE,
+    MLA_TILE_NARROW,
+)

@@ -1,0 +1,292 @@
+"""ctypes binding of libmla.so (argument marshalling only)."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+MLA_OK = 0
+MLA_KIND_DECODE = 0
+MLA_KIND_PREFILL = 1
+MLA_KV_BF16 = 0
+MLA_KV_FP8_E4M3_T128 = 1
+MLA_DTYPE_BF16 = 0
+MLA_DTYPE_FP32 = 1
+MLA_TILE_AUTO = 0
+MLA_TILE_WIDE = 1
+MLA_TILE_NARROW = 2
+
+_DIM_CKV = 512
+_DIM_KPE = 64
+_FP8_RECORD = 656
+
+
+class MLAError(RuntimeError):
+    """A status other than MLA_OK from the library (or a missing library)."""
+
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: status {status}")
+
+
+class _Desc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "kind", "batch", "num_qo_heads", "head_dim_ckv", "head_dim_kpe", "page_size", "num_pages",
+        "kv_format", "causal", "num_cus", "max_splits", "force_splits", "tile_mode")]
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def lib_path() -> str:
+    return os.environ.get("MLA_LIBRARY", os.path.join(_HERE, "libmla.so"))
+
+
+def load_library():
+    """Load libmla.so once; raise MLAError if it is not there."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        path = lib_path()
+        if not os.path.exists(path):
+            raise MLAError(-5, f"libmla.so not built ({path}); run __graft_entry__.build()")
+        L = ctypes.CDLL(path)
+        vp, i32, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+        pi32 = ctypes.POINTER(ctypes.c_int32)
+        L.mla_plan_create.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(_Desc), pi32, pi32, pi32]
+        L.mla_plan_create.restype = i32
+        L.mla_plan_destroy.argtypes = [vp]
+        L.mla_plan_destroy.restype = None
+        L.mla_plan_workspace_bytes.argtypes = [vp]
+        L.mla_plan_workspace_bytes.restype = sz
+        L.mla_plan_num_work_items.argtypes = [vp]
+        L.mla_plan_num_work_items.restype = i32
+        L.mla_plan_num_split_groups.argtypes = [vp]
+        L.mla_plan_num_split_groups.restype = i32
+        L.mla_plan_get_work_items.argtypes = [vp, pi32, sz]
+        L.mla_plan_get_work_items.restype = i32
+        L.mla_plan_num_workgroups.argtypes = [vp]
+        L.mla_plan_num_workgroups.restype = i32
+        L.mla_plan_get_workgroup_ptr.argtypes = [vp, pi32, sz]
+        L.mla_plan_get_workgroup_ptr.restype = i32
+        L.mla_plan_upload.argtypes = [vp, vp, sz, vp]
+        L.mla_plan_upload.restype = i32
+        L.mla_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32, vp, i32, vp, vp, sz, vp]
+        L.mla_decode.restype = i32
+        L.mla_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, i32, vp, vp, sz, vp]
+        L.mla_prefill.restype = i32
+        L.mla_decode_fp8.argtypes = [vp, vp, vp, vp, vp, vp, f32, vp, i32, vp, vp, sz, vp]
+        L.mla_decode_fp8.restype = i32
+        L.mla_status_str.argtypes = [i32]
+        L.mla_status_str.restype = ctypes.c_char_p
+        _lib = L
+        return L
+
+
+def _check(status: int, what: str):
+    if status != MLA_OK:
+        msg = load_library().mla_status_str(status).decode()
+        raise MLAError(status, f"{what} failed ({msg})")
+
+
+def _host_i32(x, n: Optional[int] = None):
+    if x is None:
+        return None, None
+    t = torch.as_tensor(x).detach().to("cpu", torch.int32).contiguous()
+    if n is not None and t.numel() != n:
+        raise ValueError(f"expected {n} int32 values, got {t.numel()}")
+    return t, t.data_ptr()
+
+
+class Plan:
+    """A host plan (split-KV schedule) plus its device workspace."""
+
+    def __init__(self, handle, desc: _Desc, kv_len, kv_indptr, qo_indptr):
+        self._h = handle
+        self.desc = desc
+        self.kv_len = kv_len
+        self.kv_indptr = kv_indptr
+        self.qo_indptr = qo_indptr
+        self._ws = {}
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h and _lib is not None:
+            _lib.mla_plan_destroy(h)
+            self._h = None
+
+    @property
+    def handle(self):
+        return self._h
+
+    @property
+    def kind(self) -> int:
+        return self.desc.kind
+
+    @property
+    def num_heads(self) -> int:
+        return self.desc.num_qo_heads
+
+    @property
+    def workspace_bytes(self) -> int:
+        return int(load_library().mla_plan_workspace_bytes(self._h))
+
+    @property
+    def num_work_items(self) -> int:
+        return int(load_library().mla_plan_num_work_items(self._h))
+
+    @property
+    def num_split_groups(self) -> int:
+        return int(load_library().mla_plan_num_split_groups(self._h))
+
+    def work_items(self) -> torch.Tensor:
+        n = self.num_work_items
+        buf = torch.zeros((max(n, 1), 8), dtype=torch.int32)
+        _check(load_library().mla_plan_get_work_items(
+            self._h, ctypes.cast(buf.data_ptr(), ctypes.POINTER(ctypes.c_int32)), n), "mla_plan_get_work_items")
+        return buf[:n]
+
+    def workgroup_ptr(self) -> torch.Tensor:
+        n = int(load_library().mla_plan_num_workgroups(self._h))
+        buf = torch.zeros(n + 1, dtype=torch.int32)
+        _check(load_library().mla_plan_get_workgroup_ptr(
+            self._h, ctypes.cast(buf.data_ptr(), ctypes.POINTER(ctypes.c_int32)), n + 1),
+            "mla_plan_get_workgroup_ptr")
+        return buf
+
+    def workspace(self, device: torch.device) -> torch.Tensor:
+        """The device workspace of this plan, allocated and uploaded once per device."""
+        device = torch.device(device)
+        key = (device.type, device.index if device.index is not None else torch.cuda.current_device())
+        ws = self._ws.get(key)
+        if ws is None:
+            nbytes = max(self.workspace_bytes, 256)
+            ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+            off = (-ws.data_ptr()) % 256
+            ws = ws[off:off + nbytes]
+            stream = torch.cuda.current_stream(device)
+            _check(load_library().mla_plan_upload(self._h, ws.data_ptr(), nbytes, stream.cuda_stream),
+                   "mla_plan_upload")
+            self._ws[key] = ws
+        return ws
+
+
+def mla_plan_create(kind: int, batch: int, num_heads: int, page_size: int, num_pages: int, kv_len,
+                    kv_indptr, qo_indptr=None, kv_format: int = MLA_KV_BF16, causal: bool = True,
+                    num_cus: int = 0, max_splits: int = 0, force_splits: int = 0,
+                    tile_mode: int = MLA_TILE_AUTO) -> Plan:
+    """Host plan for one set of request lengths (see include/mla.h)."""
+    L = load_library()
+    d = _Desc(kind=kind, batch=batch, num_qo_heads=num_heads, head_dim_ckv=_DIM_CKV,
+              head_dim_kpe=_DIM_KPE, page_size=page_size, num_pages=num_pages, kv_format=kv_format,
+              causal=int(bool(causal)), num_cus=num_cus, max_splits=max_splits,
+              force_splits=force_splits, tile_mode=tile_mode)
+    kl, kl_p = _host_i32(kv_len, batch)
+    ki, ki_p = _host_i32(kv_indptr, batch + 1)
+    qo, qo_p = _host_i32(qo_indptr, batch + 1) if qo_indptr is not None else (None, None)
+    h = ctypes.c_void_p()
+    P = ctypes.POINTER(ctypes.c_int32)
+    cast = lambda p: ctypes.cast(p, P) if p is not None else None
+    _check(L.mla_plan_create(ctypes.byref(h), ctypes.byref(d), cast(kl_p), cast(ki_p), cast(qo_p)),
+           "mla_plan_create")
+    return Plan(h, d, kl, ki, qo)
+
+
+def _dev(t: torch.Tensor, name: str, dtype, shape=None):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr()
+
+
+def _outputs(q_nope: torch.Tensor, out, lse, out_dtype):
+    rows, H = q_nope.shape[0], q_nope.shape[1]
+    if out is None:
+        out = torch.empty((rows, H, _DIM_CKV), dtype=out_dtype, device=q_nope.device)
+    if lse is None:
+        lse = torch.empty((rows, H), dtype=torch.float32, device=q_nope.device)
+    if out.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("out must be bf16 or fp32")
+    _dev(out, "out", out.dtype, (rows, H, _DIM_CKV))
+    _dev(lse, "lse", torch.float32, (rows, H))
+    code = MLA_DTYPE_BF16 if out.dtype == torch.bfloat16 else MLA_DTYPE_FP32
+    return out, lse, code
+
+
+def _q(plan: Plan, q_nope, q_pe, rows: int):
+    H = plan.num_heads
+    return (_dev(q_nope, "q_nope", torch.bfloat16, (rows, H, _DIM_CKV)),
+            _dev(q_pe, "q_pe", torch.bfloat16, (rows, H, _DIM_KPE)))
+
+
+def _paging(plan: Plan, kv_indptr, kv_indices):
+    a = _dev(kv_indptr, "kv_indptr", torch.int32, (plan.desc.batch + 1,))
+    b = _dev(kv_indices, "kv_indices", torch.int32)
+    if plan.desc.batch > 0 and kv_indices.numel() < int(plan.kv_indptr[-1]):
+        raise ValueError("kv_indices is shorter than kv_indptr[-1]")
+    return a, b
+
+
+def mla_decode(plan: Plan, q_nope, q_pe, ckv_cache, kpe_cache, kv_indptr, kv_indices, sm_scale: float,
+               out=None, lse=None, out_dtype=torch.bfloat16, workspace=None):
+    """Paged MLA decode; returns (out [B, H, 512], lse [B, H] fp32, natural log)."""
+    L = load_library()
+    B, P, ps = plan.desc.batch, plan.desc.num_pages, plan.desc.page_size
+    qn, qp = _q(plan, q_nope, q_pe, B)
+    c = _dev(ckv_cache, "ckv_cache", torch.bfloat16, (P, ps, _DIM_CKV))
+    k = _dev(kpe_cache, "kpe_cache", torch.bfloat16, (P, ps, _DIM_KPE))
+    ip, ix = _paging(plan, kv_indptr, kv_indices)
+    out, lse, code = _outputs(q_nope, out, lse, out_dtype)
+    ws = plan.workspace(q_nope.device) if workspace is None else workspace
+    stream = torch.cuda.current_stream(q_nope.device).cuda_stream
+    _check(L.mla_decode(plan.handle, qn, qp, c, k, ip, ix, float(sm_scale), out.data_ptr(), code,
+                        lse.data_ptr(), ws.data_ptr(), ws.numel(), stream), "mla_decode")
+    return out, lse
+
+
+def mla_prefill(plan: Plan, q_nope, q_pe, ckv_cache, kpe_cache, qo_indptr, kv_indptr, kv_indices,
+                sm_scale: float, out=None, lse=None, out_dtype=torch.bfloat16, workspace=None):
+    """Paged MLA prefill over packed queries; returns (out [total_q, H, 512], lse [total_q, H])."""
+    L = load_library()
+    B, P, ps = plan.desc.batch, plan.desc.num_pages, plan.desc.page_size
+    total_q = int(plan.qo_indptr[-1]) if plan.qo_indptr is not None else 0
+    qn, qp = _q(plan, q_nope, q_pe, total_q)
+    c = _dev(ckv_cache, "ckv_cache", torch.bfloat16, (P, ps, _DIM_CKV))
+    k = _dev(kpe_cache, "kpe_cache", torch.bfloat16, (P, ps, _DIM_KPE))
+    qo = _dev(qo_indptr, "qo_indptr", torch.int32, (B + 1,))
+    ip, ix = _paging(plan, kv_indptr, kv_indices)
+    out, lse, code = _outputs(q_nope, out, lse, out_dtype)
+    ws = plan.workspace(q_nope.device) if workspace is None else workspace
+    stream = torch.cuda.current_stream(q_nope.device).cuda_stream
+    _check(L.mla_prefill(plan.handle, qn, qp, c, k, qo, ip, ix, float(sm_scale), out.data_ptr(), code,
+                         lse.data_ptr(), ws.data_ptr(), ws.numel(), stream), "mla_prefill")
+    return out, lse
+
+
+def mla_decode_fp8(plan: Plan, q_nope, q_pe, kv_cache, kv_indptr, kv_indices, sm_scale: float,
+                   out=None, lse=None, out_dtype=torch.bfloat16, workspace=None):
+    """Paged MLA decode over 656-byte fp8 token records."""
+    L = load_library()
+    B, P, ps = plan.desc.batch, plan.desc.num_pages, plan.desc.page_size
+    qn, qp = _q(plan, q_nope, q_pe, B)
+    kv = _dev(kv_cache, "kv_cache", torch.uint8, (P, ps, _FP8_RECORD))
+    ip, ix = _paging(plan, kv_indptr, kv_indices)
+    out, lse, code = _outputs(q_nope, out, lse, out_dtype)
+    ws = plan.workspace(q_nope.device) if workspace is None else workspace
+    stream = torch.cuda.current_stream(q_nope.device).cuda_stream
+    _check(L.mla_decode_fp8(plan.handle, qn, qp, kv, ip, ix, float(sm_scale), out.data_ptr(), code,
+                            lse.data_ptr(), ws.data_ptr(), ws.numel(), stream), "mla_decode_fp8")
+    return out, lse

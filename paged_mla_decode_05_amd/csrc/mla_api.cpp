@@ -1,0 +1,364 @@
+// C ABI of libmla.so: argument validation, the host split-KV planner, and
+// the launch sequence (attention kernel, then the split combine kernel).
+//
+// The planner is the counterpart of the host planning step the pages
+// describe: FlashMLA's "get_mla_metadata" (tile-scheduler metadata derived
+// from cache_seqlens once before the decode loop, reused across layers) and
+// FlashInfer's "batch_mla_decode_with_paged_kv_cache" (host reads seq_lens /
+// qo_indptr to derive plan bounds; capture-safe callers pre-plan).  Its
+// contents are our own: a static per-workgroup list of work items that
+// balances key tokens across compute units, cutting requests into key
+// chunks where needed.  Partial results of cut requests are merged by the
+// log-sum-exp identity ("mla_decoding_single_batch": exp_sum / qk_max
+// statistics used for split-K reduction).
+#include "../../include/mla.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "mla_internal.h"
+
+using mla::SplitGroup;
+using mla::WorkItem;
+
+struct mla_plan {
+  mla_plan_desc d;
+  int32_t tile_mode = 0;       // resolved: MLA_TILE_WIDE or MLA_TILE_NARROW
+  int32_t rows_per_block = 0;  // rows one workgroup holds
+  int32_t num_wgs = 0;         // grid size of the attention kernel
+  int32_t num_slots = 0;       // partial-result slots
+  std::vector<int32_t> wg_ptr;  // [num_wgs + 1] item range of each workgroup
+  std::vector<WorkItem> items;
+  std::vector<SplitGroup> groups;
+  std::vector<int32_t> blob;    // uploaded image: wg_ptr | items | groups
+  size_t off_items = 0, off_groups = 0, off_part_lse = 0, off_part_o = 0, ws_bytes = 0;
+};
+
+namespace {
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool is_pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int32_t ilog2(int32_t x) {
+  int32_t s = 0;
+  while ((1 << s) < x) ++s;
+  return s;
+}
+
+// Fixed per-item cost in key-token units: loading Q, the epilogue, and the
+// pipeline fill.  Used only to balance the schedule.
+constexpr int64_t kItemOverhead = 64;
+// Smallest key chunk worth a separate work item (unless it is a remainder).
+constexpr int64_t kMinChunk = 128;
+
+struct Unit {
+  int32_t b, row0, nrows, vis, kv_len, q_len;
+};
+
+// Greedy packing of units into workgroups with `budget` key-token units
+// each: a unit is cut into pieces (multiples of the stage size) where a
+// workgroup's budget runs out; a cut unit becomes a split group whose
+// pieces own consecutive partial-result slots.
+void pack_units(mla_plan* p, const std::vector<Unit>& units, int64_t budget) {
+  const mla_plan_desc& d = p->d;
+  const int64_t stage = mla::kStageTokens;
+  p->items.clear();
+  p->groups.clear();
+  p->wg_ptr.assign(1, 0);
+  p->num_slots = 0;
+  auto close_wg = [&]() { p->wg_ptr.push_back((int32_t)p->items.size()); };
+  auto wg_open = [&]() { return p->items.size() > (size_t)p->wg_ptr.back(); };
+  int64_t left = budget;  // budget left on the current workgroup
+  for (const Unit& u : units) {
+    size_t first = p->items.size();
+    if (d.force_splits > 0) {
+      // exactly min(force_splits, stages) pieces, stages spread evenly
+      const int64_t nchunks = std::max<int64_t>(1, (u.vis + stage - 1) / stage);
+      const int64_t s = std::min<int64_t>(d.force_splits, nchunks);
+      int64_t t = 0;
+      for (int64_t k = 0; k < s; ++k) {
+        const int64_t n = nchunks / s + (k < nchunks % s ? 1 : 0);
+        const int64_t e = std::min<int64_t>(u.vis, t + n * stage);
+        if (left < kItemOverhead + kMinChunk && wg_open()) {
+          close_wg();
+          left = budget;
+        }
+        p->items.push_back({u.b, u.row0, u.nrows, (int32_t)t, (int32_t)e, u.kv_len, u.q_len, -1});
+        left -= (e - t) + kItemOverhead;
+        t = e;
+      }
+    } else {
+      int64_t t = 0;
+      int32_t npieces = 0;
+      do {
+        const int64_t rest = u.vis - t;
+        if (left < kItemOverhead + std::min<int64_t>(kMinChunk, rest) && wg_open()) {
+          close_wg();
+          left = budget;
+        }
+        int64_t take = std::max<int64_t>(left - kItemOverhead, stage) / stage * stage;
+        // never leave a remainder smaller than a minimum chunk behind
+        if (rest - take < kMinChunk) take = rest;
+        if (d.max_splits > 0 && npieces + 1 >= d.max_splits) take = rest;
+        take = std::min<int64_t>(take, rest);
+        p->items.push_back({u.b, u.row0, u.nrows, (int32_t)t, (int32_t)(t + take), u.kv_len, u.q_len, -1});
+        ++npieces;
+        left -= take + kItemOverhead;
+        t += take;
+      } while (t < u.vis);
+    }
+    const int32_t n = (int32_t)(p->items.size() - first);
+    if (n > 1) {
+      SplitGroup g{u.b, u.row0, u.nrows, n, p->num_slots, {0, 0, 0}};
+      for (int32_t k = 0; k < n; ++k) p->items[first + k].slot = p->num_slots + k;
+      p->num_slots += n;
+      p->groups.push_back(g);
+    }
+  }
+  if (wg_open()) close_wg();
+  p->num_wgs = (int32_t)p->wg_ptr.size() - 1;
+}
+
+mla_status build_schedule(mla_plan* p, const std::vector<int32_t>& kv_len,
+                          const std::vector<int32_t>& q_len, int32_t num_cus) {
+  const mla_plan_desc& d = p->d;
+  const int32_t H = d.num_qo_heads;
+  int64_t max_rows = 0;
+  for (int32_t b = 0; b < d.batch; ++b) max_rows = std::max<int64_t>(max_rows, (int64_t)q_len[b] * H);
+  int32_t mode = d.tile_mode;
+  if (mode == MLA_TILE_AUTO) mode = (max_rows >= 64) ? MLA_TILE_WIDE : MLA_TILE_NARROW;
+  p->tile_mode = mode;
+  const int32_t RB = (mode == MLA_TILE_WIDE) ? mla::kWideRows : mla::kNarrowRows;
+  p->rows_per_block = RB;
+
+  // Units: (request, row block) with the keys the block can see.
+  std::vector<Unit> units;
+  for (int32_t b = 0; b < d.batch; ++b) {
+    const int64_t rows = (int64_t)q_len[b] * H;
+    for (int64_t r0 = 0; r0 < rows; r0 += RB) {
+      const int32_t nr = (int32_t)std::min<int64_t>(RB, rows - r0);
+      int32_t vis = kv_len[b];
+      if (d.kind == MLA_KIND_PREFILL && d.causal) {
+        const int32_t last_q = (int32_t)((r0 + nr - 1) / H);  // query token of the block's last row
+        vis = kv_len[b] - q_len[b] + last_q + 1;
+      }
+      units.push_back({b, (int32_t)r0, nr, vis, kv_len[b], q_len[b]});
+    }
+  }
+
+  int64_t total = 0;
+  for (const Unit& u : units) total += u.vis + kItemOverhead;
+  const int64_t cus = std::max<int32_t>(1, num_cus);
+  // Smallest per-workgroup budget whose packing needs at most `cus`
+  // workgroups: one persistent workgroup per compute unit.
+  int64_t budget = std::max<int64_t>((total + cus - 1) / cus, kItemOverhead + kMinChunk);
+  for (int iter = 0; iter < 400; ++iter) {
+    pack_units(p, units, budget);
+    if (p->num_wgs <= cus) break;
+    budget += std::max<int64_t>(16, budget / 256);
+  }
+
+  // Workspace layout: [wg_ptr | items | groups] [part_lse] [part_o]
+  const size_t n_ptr = align_up((size_t)(p->num_wgs + 1) * 4, 32);
+  p->off_items = n_ptr;
+  p->off_groups = p->off_items + p->items.size() * sizeof(WorkItem);
+  const size_t blob_bytes = p->off_groups + p->groups.size() * sizeof(SplitGroup);
+  p->off_part_lse = align_up(blob_bytes, mla::kWsAlign);
+  p->off_part_o = align_up(p->off_part_lse + (size_t)p->num_slots * RB * 4, mla::kWsAlign);
+  p->ws_bytes = align_up(p->off_part_o + (size_t)p->num_slots * RB * mla::kDimCkv * 4, mla::kWsAlign);
+  p->blob.assign(blob_bytes / 4, 0);
+  std::memcpy(p->blob.data(), p->wg_ptr.data(), p->wg_ptr.size() * 4);
+  std::memcpy((char*)p->blob.data() + p->off_items, p->items.data(), p->items.size() * sizeof(WorkItem));
+  std::memcpy((char*)p->blob.data() + p->off_groups, p->groups.data(), p->groups.size() * sizeof(SplitGroup));
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_str(int32_t s) {
+  switch (s) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "unsupported";
+    case MLA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case MLA_ERR_PLAN_MISMATCH: return "plan does not match this call";
+    case MLA_ERR_DEVICE: return "HIP device error";
+    default: return "unknown status";
+  }
+}
+
+mla_status mla_plan_create(mla_plan** out, const mla_plan_desc* d, const int32_t* kv_len_host,
+                           const int32_t* kv_indptr_host, const int32_t* qo_indptr_host) {
+  if (!out || !d) return MLA_ERR_INVALID_ARGUMENT;
+  *out = nullptr;
+  if (d->kind != MLA_KIND_DECODE && d->kind != MLA_KIND_PREFILL) return MLA_ERR_INVALID_ARGUMENT;
+  if (d->batch < 0 || d->num_qo_heads < 1 || d->num_pages < 1) return MLA_ERR_INVALID_ARGUMENT;
+  if (d->head_dim_ckv != mla::kDimCkv || d->head_dim_kpe != mla::kDimKpe) return MLA_ERR_UNSUPPORTED;
+  if (!is_pow2(d->page_size) || d->page_size > 4096) return MLA_ERR_UNSUPPORTED;
+  if (d->kv_format != MLA_KV_BF16 && d->kv_format != MLA_KV_FP8_E4M3_T128) return MLA_ERR_UNSUPPORTED;
+  if (d->kv_format == MLA_KV_FP8_E4M3_T128 && d->kind != MLA_KIND_DECODE) return MLA_ERR_UNSUPPORTED;
+  if (d->tile_mode < MLA_TILE_AUTO || d->tile_mode > MLA_TILE_NARROW) return MLA_ERR_INVALID_ARGUMENT;
+  if (d->max_splits < 0 || d->force_splits < 0 || d->num_cus < 0) return MLA_ERR_INVALID_ARGUMENT;
+  if (d->batch > 0 && !kv_indptr_host) return MLA_ERR_INVALID_ARGUMENT;
+  if (d->kind == MLA_KIND_PREFILL && d->batch > 0 && !qo_indptr_host) return MLA_ERR_INVALID_ARGUMENT;
+  if (d->kind == MLA_KIND_DECODE && qo_indptr_host) return MLA_ERR_INVALID_ARGUMENT;
+
+  std::vector<int32_t> kv_len(d->batch), q_len(d->batch, 1);
+  if (d->batch > 0 && kv_indptr_host[0] != 0) return MLA_ERR_INVALID_ARGUMENT;
+  for (int32_t b = 0; b < d->batch; ++b) {
+    const int64_t np = (int64_t)kv_indptr_host[b + 1] - kv_indptr_host[b];
+    if (np < 0) return MLA_ERR_INVALID_ARGUMENT;
+    const int64_t L = kv_len_host ? kv_len_host[b] : np * d->page_size;
+    if (L < 0 || L > (int64_t)1 << 30) return MLA_ERR_INVALID_ARGUMENT;
+    if ((L + d->page_size - 1) / d->page_size != np) return MLA_ERR_INVALID_ARGUMENT;
+    kv_len[b] = (int32_t)L;
+    if (d->kind == MLA_KIND_PREFILL) {
+      if (b == 0 && qo_indptr_host[0] != 0) return MLA_ERR_INVALID_ARGUMENT;
+      const int64_t n = (int64_t)qo_indptr_host[b + 1] - qo_indptr_host[b];
+      if (n < 0) return MLA_ERR_INVALID_ARGUMENT;
+      if (d->causal && n > L) return MLA_ERR_INVALID_ARGUMENT;
+      q_len[b] = (int32_t)n;
+    }
+  }
+
+  int32_t num_cus = d->num_cus;
+  if (num_cus == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_DEVICE;
+    if (hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return MLA_ERR_DEVICE;
+  }
+
+  mla_plan* p = new (std::nothrow) mla_plan();
+  if (!p) return MLA_ERR_INVALID_ARGUMENT;
+  p->d = *d;
+  mla_status st = build_schedule(p, kv_len, q_len, num_cus);
+  if (st != MLA_OK) {
+    delete p;
+    return st;
+  }
+  *out = p;
+  return MLA_OK;
+}
+
+void mla_plan_destroy(mla_plan* p) { delete p; }
+
+size_t mla_plan_workspace_bytes(const mla_plan* p) { return p ? p->ws_bytes : 0; }
+int32_t mla_plan_num_work_items(const mla_plan* p) { return p ? (int32_t)p->items.size() : -1; }
+int32_t mla_plan_num_split_groups(const mla_plan* p) { return p ? (int32_t)p->groups.size() : -1; }
+
+int32_t mla_plan_num_workgroups(const mla_plan* p) { return p ? p->num_wgs : -1; }
+
+mla_status mla_plan_get_workgroup_ptr(const mla_plan* p, int32_t* out, size_t capacity) {
+  if (!p || !out || capacity < p->wg_ptr.size()) return MLA_ERR_INVALID_ARGUMENT;
+  std::memcpy(out, p->wg_ptr.data(), p->wg_ptr.size() * 4);
+  return MLA_OK;
+}
+
+mla_status mla_plan_get_work_items(const mla_plan* p, int32_t* items_host, size_t capacity) {
+  if (!p || (!items_host && !p->items.empty())) return MLA_ERR_INVALID_ARGUMENT;
+  if (capacity < p->items.size()) return MLA_ERR_INVALID_ARGUMENT;
+  if (!p->items.empty()) std::memcpy(items_host, p->items.data(), p->items.size() * sizeof(WorkItem));
+  return MLA_OK;
+}
+
+mla_status mla_plan_upload(const mla_plan* p, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!p) return MLA_ERR_INVALID_ARGUMENT;
+  if (p->blob.empty()) return MLA_OK;
+  if (!ws || ws_bytes < p->ws_bytes || ((uintptr_t)ws % mla::kWsAlign) != 0) return MLA_ERR_WORKSPACE;
+  if (hipMemcpyAsync(ws, p->blob.data(), p->blob.size() * 4, hipMemcpyHostToDevice, stream) != hipSuccess)
+    return MLA_ERR_DEVICE;
+  return MLA_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+mla_status run(const mla_plan* p, int32_t want_kind, int32_t want_format, const void* q_nope,
+               const void* q_pe, const void* ckv, const void* kpe, const void* kv_fp8,
+               const int32_t* qo_indptr, const int32_t* kv_indptr, const int32_t* kv_indices,
+               float sm_scale, void* out, int32_t out_dtype, float* lse, void* ws, size_t ws_bytes,
+               hipStream_t stream) {
+  if (!p) return MLA_ERR_INVALID_ARGUMENT;
+  if (p->d.kind != want_kind || p->d.kv_format != want_format) return MLA_ERR_PLAN_MISMATCH;
+  if (out_dtype != MLA_DTYPE_BF16 && out_dtype != MLA_DTYPE_FP32) return MLA_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(sm_scale)) return MLA_ERR_INVALID_ARGUMENT;
+  if (p->items.empty()) return MLA_OK;  // nothing to compute (batch 0 or no rows)
+  if (!q_nope || !q_pe || !kv_indptr || !kv_indices || !out || !lse) return MLA_ERR_INVALID_ARGUMENT;
+  if (want_format == MLA_KV_BF16 && (!ckv || !kpe)) return MLA_ERR_INVALID_ARGUMENT;
+  if (want_format == MLA_KV_FP8_E4M3_T128 && !kv_fp8) return MLA_ERR_INVALID_ARGUMENT;
+  if (want_kind == MLA_KIND_PREFILL && !qo_indptr) return MLA_ERR_INVALID_ARGUMENT;
+  if (!ws || ws_bytes < p->ws_bytes || ((uintptr_t)ws % mla::kWsAlign) != 0) return MLA_ERR_WORKSPACE;
+
+  mla::AttnArgs a{};
+  a.q_nope = q_nope;
+  a.q_pe = q_pe;
+  a.ckv = ckv;
+  a.kpe = kpe;
+  a.kv_fp8 = kv_fp8;
+  a.kv_indptr = kv_indptr;
+  a.kv_indices = kv_indices;
+  a.qo_indptr = (want_kind == MLA_KIND_PREFILL) ? qo_indptr : nullptr;
+  char* w = (char*)ws;
+  a.wg_ptr = (const int32_t*)w;
+  a.items = (const WorkItem*)(w + p->off_items);
+  a.groups = (const SplitGroup*)(w + p->off_groups);
+  a.out = out;
+  a.lse = lse;
+  a.part_o = (float*)(w + p->off_part_o);
+  a.part_lse = (float*)(w + p->off_part_lse);
+  a.scale_log2 = sm_scale * 1.4426950408889634f;
+  a.num_heads = p->d.num_qo_heads;
+  a.page_shift = ilog2(p->d.page_size);
+  a.out_bf16 = out_dtype == MLA_DTYPE_BF16;
+  a.causal = (want_kind == MLA_KIND_PREFILL) ? p->d.causal : 0;
+  a.rows_per_block = p->rows_per_block;
+  a.num_wgs = p->num_wgs;
+  a.num_items = (int32_t)p->items.size();
+  a.num_groups = (int32_t)p->groups.size();
+  hipError_t e = mla::launch_attention(a, p->tile_mode, want_format == MLA_KV_FP8_E4M3_T128, stream);
+  if (e != hipSuccess) return MLA_ERR_DEVICE;
+  if (!p->groups.empty()) {
+    e = mla::launch_combine(a, stream);
+    if (e != hipSuccess) return MLA_ERR_DEVICE;
+  }
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_decode(const mla_plan* p, const void* q_nope, const void* q_pe, const void* ckv,
+                      const void* kpe, const int32_t* kv_indptr, const int32_t* kv_indices,
+                      float sm_scale, void* out, int32_t out_dtype, float* lse, void* ws,
+                      size_t ws_bytes, hipStream_t stream) {
+  return run(p, MLA_KIND_DECODE, MLA_KV_BF16, q_nope, q_pe, ckv, kpe, nullptr, nullptr, kv_indptr,
+             kv_indices, sm_scale, out, out_dtype, lse, ws, ws_bytes, stream);
+}
+
+mla_status mla_prefill(const mla_plan* p, const void* q_nope, const void* q_pe, const void* ckv,
+                       const void* kpe, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                       const int32_t* kv_indices, float sm_scale, void* out, int32_t out_dtype,
+                       float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return run(p, MLA_KIND_PREFILL, MLA_KV_BF16, q_nope, q_pe, ckv, kpe, nullptr, qo_indptr, kv_indptr,
+             kv_indices, sm_scale, out, out_dtype, lse, ws, ws_bytes, stream);
+}
+
+mla_status mla_decode_fp8(const mla_plan* p, const void* q_nope, const void* q_pe, const void* kv,
+                          const int32_t* kv_indptr, const int32_t* kv_indices, float sm_scale,
+                          void* out, int32_t out_dtype, float* lse, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
+  return run(p, MLA_KIND_DECODE, MLA_KV_FP8_E4M3_T128, q_nope, q_pe, nullptr, nullptr, kv, nullptr,
+             kv_indptr, kv_indices, sm_scale, out, out_dtype, lse, ws, ws_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,696 @@
+// Paged absorbed-MLA attention kernels for gfx950 (MI355X).
+//
+// What is computed ("MLA Paged", sections "decode"/"prefill"; FlashMLA
+// "Sparse MLA Prefill Kernel" for the lse / exp(P - lse) form; V = the
+// first 512 latent dims per "mla_decoding_single_batch"): for every query
+// row, logits s_j = sm_scale * (q_nope . ckv_j + q_pe . kpe_j) over the
+// keys the row may see, out = softmax(s) @ ckv, lse = ln sum exp(s).
+//
+// How (our design, for CDNA4):
+//  * A persistent grid: workgroup w walks its static list of work items
+//    (request, row block, key chunk) made by the host planner.
+//  * Gather loader: each 64-key stage is copied HBM -> LDS with 16-byte
+//    direct-to-LDS loads (global_load_lds_dwordx4); one wave instruction
+//    moves one 1 KB ckv row, or the 128-byte kpe rows of 8 keys.  The page of
+//    key T is kv_indices[kv_indptr[b] + (T >> log2 page_size)], slot
+//    T & (page_size-1) (FlashMLA's block/offset mapping); keys past the
+//    chunk read a zero row, so stale or NaN tail slots never reach the math.
+//    Two stages are in flight (double-buffered, 2 x 72 KB of LDS).
+//  * QK^T is computed transposed, S^T = K . Q^T, on bf16 MFMA with the
+//    query fragments held in registers; each lane then owns one query row
+//    (head), so the online-softmax state (running max m, sum l) is per lane.
+//  * P.V is computed as O^T = V^T . P^T: P^T comes straight from the S^T
+//    accumulator (no shuffle), V^T from LDS with ds_read_b64_tr_b16.
+//  * Online softmax in base 2 on logits pre-scaled by sm_scale*log2(e)
+//    (the base-2 trick of FlashMLA's sparse-prefill passage), with a lazy
+//    rescale: the running max is only raised when a tile beats it by more
+//    than kRescaleSlack, which keeps every P value <= 2^kRescaleSlack.
+//  * Tile modes.  WIDE: 4 waves x 32 rows share every key tile
+//    (mfma_f32_32x32x16_bf16).  NARROW: one block of 16 rows; the 4 waves
+//    split every key tile 16 keys each (mfma_f32_16x16x32_bf16 for S,
+//    mfma_f32_16x16x16_bf16 for P.V) and merge their partial results
+//    through LDS at the end of the item.
+//  * A work item that covers only part of a request's keys writes a
+//    normalised partial output and its lse; mla_combine merges them by the
+//    log-sum-exp identity (the split-K statistics of
+//    "mla_decoding_single_batch").
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr int kCkvRowBytes = kDimCkv * 2;                      // 1024
+constexpr int kKpeRowBytes = kDimKpe * 2;                      // 128
+constexpr int kStageCkvBytes = kStageTokens * kCkvRowBytes;    // 65536
+constexpr int kStageBytes = kStageCkvBytes + kStageTokens * kKpeRowBytes;  // 73728
+constexpr int kLdsBytes = 2 * kStageBytes;                      // 147456
+constexpr float kRescaleSlack = 8.0f;                           // log2 units
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kLn2 = 0.69314718055994531f;
+
+// 1 KB of zeros: the source of every key row outside the current chunk.
+__device__ __attribute__((aligned(16))) uint32_t g_zero_row[256];
+
+// ---------------------------------------------------------------------------
+// LDS layout of one stage: ckv rows [64][1024 B] then kpe rows [64][128 B].
+// 16-byte chunks are XOR-swizzled per row so that the MFMA operand reads
+// (16 consecutive keys at one chunk; 4 keys x 4 chunks for the transposed
+// reads) hit distinct LDS banks.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int ckv_swz(int t) {
+  const int q = (t >> 2) & 3;
+  return ((t & 3) << 2) | (((q & 1) << 1) | (q >> 1));
+}
+__device__ __forceinline__ int kpe_swz(int t) { return (t >> 1) & 7; }
+__device__ __forceinline__ int ckv_off(int t, int c) { return t * kCkvRowBytes + ((c ^ ckv_swz(t)) << 4); }
+__device__ __forceinline__ int kpe_off(int t, int c) {
+  return kStageCkvBytes + t * kKpeRowBytes + ((c ^ kpe_swz(t)) << 4);
+}
+
+__device__ __forceinline__ bf16x8 lds_read_b128(const LDS_AS char* base, int off) {
+  return *(const LDS_AS bf16x8*)(base + off);
+}
+
+__device__ __forceinline__ i16x4 lds_read_tr(const LDS_AS char* base, int off) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(base + off));
+}
+
+// {x_l, x_(l^32)} for every lane l, through v_permlane32_swap.  The two
+// results pass through an empty asm statement: without it the compiler
+// treats them as one value (fmaxf(r0, r1) was folded to r0).
+__device__ __forceinline__ void xor32_pair(float x, float& a, float& b) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  uint32_t ra = r[0], rb = r[1];
+  asm volatile("" : "+v"(ra), "+v"(rb));
+  a = __builtin_bit_cast(float, ra);
+  b = __builtin_bit_cast(float, rb);
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  float a, b;
+  xor32_pair(x, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  float a, b;
+  xor32_pair(x, a, b);
+  return a + b;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Waits until at most `n` vector-memory loads of this wave are outstanding
+// (n <= 63); the other counters are left alone.
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Read-only tables (page indices, work list) are read through the constant
+// address space, so uniform reads become scalar loads that do not wait on
+// the in-flight direct-to-LDS loads.
+#define CONST_AS __attribute__((address_space(4)))
+__device__ __forceinline__ int ld_const(const int32_t* p, int i) {
+  return ((const CONST_AS int32_t*)p)[i];
+}
+
+// Page-size classes of the gather loader (a template parameter, so each
+// kernel instantiation has a single addressing path):
+//   kPageBig:   page_size >= 64, a 64-key stage lies inside one page;
+//   kPageMid:   8 <= page_size < 64, the 8 keys of one kpe load share a page;
+//   kPageSmall: page_size < 8.
+constexpr int kPageBig = 0, kPageMid = 1, kPageSmall = 2;
+
+// ---------------------------------------------------------------------------
+// Gather loader (bf16 caches): stage of keys [s_tok0, s_tok0 + 64) of a
+// request whose page list starts at kv_indices[page_base], into LDS stage
+// `st`.  18 direct-to-LDS loads per wave; keys >= tok_end read zeros.
+// ---------------------------------------------------------------------------
+template <int kPageClass>
+__device__ __forceinline__ void issue_stage_bf16(const AttnArgs& a, LDS_AS char* st, int page_base,
+                                                 int s_tok0, int tok_end, int wave, int lane) {
+  const int sh = a.page_shift;
+  const int mask = (1 << sh) - 1;
+  const char* ckv = (const char*)a.ckv;
+  const char* kpe = (const char*)a.kpe;
+  size_t row0 = 0;
+  if (kPageClass == kPageBig) {
+    const int page = (s_tok0 < tok_end) ? ld_const(a.kv_indices, page_base + (s_tok0 >> sh)) : 0;
+    row0 = ((size_t)page << sh) + (s_tok0 & mask);
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int t = wave * 16 + i;
+    const int T = s_tok0 + t;
+    size_t row;
+    if (kPageClass == kPageBig) {
+      row = row0 + t;
+    } else {
+      const int page = (T < tok_end) ? ld_const(a.kv_indices, page_base + (T >> sh)) : 0;
+      row = ((size_t)page << sh) + (T & mask);
+    }
+    const char* src = (T < tok_end) ? ckv + row * kCkvRowBytes + ((lane ^ ckv_swz(t)) << 4)
+                                    : (const char*)g_zero_row + (lane << 4);
+    __builtin_amdgcn_global_load_lds(src, st + t * kCkvRowBytes, 16, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int grp = wave * 2 + i;
+    const int t = grp * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ kpe_swz(t);
+    const int T = s_tok0 + t;
+    const int T0 = s_tok0 + grp * 8;
+    size_t row;
+    if (kPageClass == kPageBig) {
+      row = row0 + t;
+    } else if (kPageClass == kPageMid) {
+      const int page = (T0 < tok_end) ? ld_const(a.kv_indices, page_base + (T0 >> sh)) : 0;
+      row = ((size_t)page << sh) + (T & mask);
+    } else {
+      // one scalar page lookup per key, then each lane picks its key's page
+      int page = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int pj = (T0 + j < tok_end) ? ld_const(a.kv_indices, page_base + ((T0 + j) >> sh)) : 0;
+        page = ((lane >> 3) == j) ? pj : page;
+      }
+      row = ((size_t)page << sh) + (T & mask);
+    }
+    const char* src = (T < tok_end) ? kpe + row * kKpeRowBytes + (c << 4)
+                                    : (const char*)g_zero_row + ((lane & 7) << 4);
+    __builtin_amdgcn_global_load_lds(src, st + kStageCkvBytes + grp * 1024, 16, 0, 0);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Item bookkeeping shared by both modes
+// ---------------------------------------------------------------------------
+struct RowInfo {
+  size_t qrow;  // flattened [total_q * H] index of the row
+  int qi;       // query token of the row within its request
+  bool ok;      // row exists in this block
+};
+
+__device__ __forceinline__ RowInfo row_info(const AttnArgs& a, const WorkItem& it, int r_in_block) {
+  RowInfo ri;
+  const int H = a.num_heads;
+  const int r = it.row0 + r_in_block;
+  ri.ok = r_in_block < it.nrows;
+  const int rr = ri.ok ? r : it.row0;
+  ri.qi = rr / H;
+  const int head = rr - ri.qi * H;
+  const int q_start = a.qo_indptr ? ld_const(a.qo_indptr, it.b) : it.b;
+  ri.qrow = (size_t)(q_start + ri.qi) * H + head;
+  return ri;
+}
+
+__device__ __forceinline__ int row_key_bound(const AttnArgs& a, const WorkItem& it, const RowInfo& ri) {
+  int vis = it.kv_len;
+  if (a.causal) vis = it.kv_len - it.q_len + ri.qi + 1;
+  if (!ri.ok) vis = 0;
+  return min(vis, it.tok1);
+}
+
+// Final or partial write of one row's 4 consecutive output dims.
+__device__ __forceinline__ void store4(const AttnArgs& a, const WorkItem& it, const RowInfo& ri,
+                                       int r_in_block, int dim, f32x4 v) {
+  if (it.slot < 0) {
+    if (a.out_bf16) {
+      bf16x4 h;
+      h[0] = (__bf16)v[0];
+      h[1] = (__bf16)v[1];
+      h[2] = (__bf16)v[2];
+      h[3] = (__bf16)v[3];
+      *(bf16x4*)((__bf16*)a.out + ri.qrow * kDimCkv + dim) = h;
+    } else {
+      *(f32x4*)((float*)a.out + ri.qrow * kDimCkv + dim) = v;
+    }
+  } else {
+    float* dst = a.part_o + ((size_t)it.slot * a.rows_per_block + r_in_block) * kDimCkv + dim;
+    *(f32x4*)dst = v;
+  }
+}
+
+__device__ __forceinline__ void store_lse(const AttnArgs& a, const WorkItem& it, const RowInfo& ri,
+                                          int r_in_block, float lse_nat) {
+  if (it.slot < 0) {
+    a.lse[ri.qrow] = lse_nat;
+  } else {
+    a.part_lse[(size_t)it.slot * a.rows_per_block + r_in_block] = lse_nat;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// WIDE mode: 4 waves x 32 rows; every wave reads every key of each stage.
+//
+// LDS addresses are a handful of per-lane base offsets plus compile-time
+// immediates: with t = key row and c = 16-byte chunk, the swizzle only
+// depends on t mod 16 and only flips the low four bits of c, so stepping c
+// by a multiple of 16 (or t by a multiple of 16) is a constant offset.
+// ---------------------------------------------------------------------------
+struct WideState {
+  f32x16 o[16];   // O^T: lane holds row n, dims 32cb + 8(r/4) + 4g + r%4
+  float m_run;    // running max (log2 units), per row
+  float l_run;    // running sum of this lane's keys
+};
+
+__device__ __forceinline__ void wide_stage(const AttnArgs& a, const bf16x8 (&qf)[36], WideState& st,
+                                           const LDS_AS char* __restrict__ cur, int stage_tok, int bound,
+                                           const int (&kb)[8], const int (&pb)[4], const int (&vb)[8],
+                                           int g) {
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub) {
+    const int tb = sub * 32;
+    // S^T[32 keys x 32 rows] = K . Q^T over 576 dims
+    f32x16 sacc = {};
+#pragma unroll
+    for (int ks = 0; ks < 32; ++ks) {
+      const bf16x8 kf = lds_read_b128(cur, kb[ks & 7] + 256 * (ks >> 3) + tb * kCkvRowBytes);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 kf = lds_read_b128(cur, pb[ks] + tb * kKpeRowBytes);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[32 + ks], sacc, 0, 0, 0);
+    }
+    // online softmax (base 2); lane holds keys 8(r/4) + 4g + r%4 of the sub-tile
+    float sv[16];
+    float mx = kNegInf;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int tok = stage_tok + tb + 8 * (r >> 2) + 4 * g + (r & 3);
+      const float x = sacc[r] * a.scale_log2;
+      sv[r] = tok < bound ? x : kNegInf;
+      mx = fmaxf(mx, sv[r]);
+    }
+    mx = max_xor32(mx);
+    const bool need = mx > st.m_run + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      const float m_new = fmaxf(st.m_run, mx);
+      const float alpha = (st.m_run == kNegInf) ? 0.f : fast_exp2(st.m_run - m_new);
+      st.l_run *= alpha;
+      // one column block at a time keeps the rescale's register peak small
+#pragma unroll
+      for (int cb = 0; cb < 16; ++cb) {
+        st.o[cb] *= alpha;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      st.m_run = m_new;
+    }
+    const float mref = (st.m_run == kNegInf) ? 0.f : st.m_run;
+    bf16x8 pt[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = fast_exp2(sv[r] - mref);
+      st.l_run += p;
+      pt[r >> 3][r & 7] = (__bf16)p;
+    }
+    // O^T[32 dims x 32 rows] += V^T[32 dims x 16 keys] . P^T[16 keys x 32 rows]
+#pragma unroll
+    for (int cb = 0; cb < 16; ++cb) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int imm = (tb + 16 * kk) * kCkvRowBytes + 256 * (cb >> 2);
+        const i16x4 v0 = lds_read_tr(cur, vb[cb & 3] + imm);
+        const i16x4 v1 = lds_read_tr(cur, vb[4 + (cb & 3)] + imm);
+        const i16x8 v = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        st.o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v), pt[kk], st.o[cb], 0, 0, 0);
+      }
+    }
+  }
+}
+
+template <int kPC>
+__device__ __forceinline__ void wide_body(const AttnArgs& a, const bf16x8 (&qf)[36], WideState& st,
+                                          const LDS_AS char* __restrict__ cur, LDS_AS char* __restrict__ nxt,
+                                          bool prefetch, int page_base, int next_tok, int tok_end,
+                                          int stage_tok, int bound, const int (&kb)[8], const int (&pb)[4],
+                                          const int (&vb)[8], int wave, int lane) {
+  if (prefetch) issue_stage_bf16<kPC>(a, nxt, page_base, next_tok, tok_end, wave, lane);
+  wide_stage(a, qf, st, cur, stage_tok, bound, kb, pb, vb, lane >> 5);
+}
+
+template <int kPC, bool kFp8>
+__device__ void wide_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* smem, int wave, int lane) {
+  const int g = lane >> 5;   // lane half
+  const int n = lane & 31;   // row within the wave (S^T / O^T column)
+  const int rib = wave * 32 + n;
+  const RowInfo ri = row_info(a, it, rib);
+  const int bound = row_key_bound(a, it, ri);
+
+  // Query fragments, B operand of S^T = K . Q^T: lane holds row n, dims 8g..8g+7 of each k-step.
+  bf16x8 qf[36];
+  {
+    const bf16x8 z = {};
+    const __bf16* qn = (const __bf16*)a.q_nope + ri.qrow * kDimCkv + 8 * g;
+    const __bf16* qp = (const __bf16*)a.q_pe + ri.qrow * kDimKpe + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 32; ++ks) qf[ks] = ri.ok ? *(const bf16x8*)(qn + 16 * ks) : z;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qf[32 + ks] = ri.ok ? *(const bf16x8*)(qp + 16 * ks) : z;
+  }
+  // LDS base offsets (see the comment above WideState)
+  int kb[8], pb[4], vb[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) kb[k] = ckv_off(n, 2 * k + g);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) pb[k] = kpe_off(n, 2 * k + g);
+  {
+    const int t0 = 4 * g + ((lane & 15) >> 2);
+    const int cl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    const int w8 = (lane & 1) ? 8 : 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      vb[k] = ckv_off(t0, 4 * k + cl) + w8;
+      vb[4 + k] = ckv_off(t0 + 8, 4 * k + cl) + w8;
+    }
+  }
+
+  WideState st;
+#pragma unroll
+  for (int cb = 0; cb < 16; ++cb) st.o[cb] = f32x16{};
+  st.m_run = kNegInf;
+  st.l_run = 0.f;
+
+  const int page_base = ld_const(a.kv_indptr, it.b);
+  const int nstage = (it.tok1 - it.tok0 + kStageTokens - 1) / kStageTokens;
+  if (nstage > 0) issue_stage_bf16<kPC>(a, smem, page_base, it.tok0, it.tok1, wave, lane);
+  for (int s = 0; s < nstage; ++s) {
+    wait_vmcnt<0>();
+    __syncthreads();
+    wide_body<kPC>(a, qf, st, smem + (s & 1) * kStageBytes, smem + ((s + 1) & 1) * kStageBytes, s + 1 < nstage,
+              page_base, it.tok0 + (s + 1) * kStageTokens, it.tok1, it.tok0 + s * kStageTokens, bound, kb, pb,
+              vb, wave, lane);
+    __syncthreads();  // every wave is done with this stage before it is refilled
+  }
+
+  // epilogue: lane owns row n; the partner lane (n, 1-g) holds the other dims
+  const float l_tot = sum_xor32(st.l_run);
+  const bool empty = !(l_tot > 0.f);
+  const float inv = empty ? 0.f : 1.f / l_tot;
+  if (ri.ok) {
+#pragma unroll
+    for (int cb = 0; cb < 16; ++cb) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 v = {st.o[cb][4 * q] * inv, st.o[cb][4 * q + 1] * inv, st.o[cb][4 * q + 2] * inv,
+                         st.o[cb][4 * q + 3] * inv};
+        store4(a, it, ri, rib, 32 * cb + 8 * q + 4 * g, v);
+      }
+    }
+    if (g == 0) store_lse(a, it, ri, rib, empty ? kNegInf : (st.m_run + __log2f(l_tot)) * kLn2);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// NARROW mode: one block of <= 16 rows; wave w takes keys [16w, 16w+16) of
+// each stage; the four partial results are merged through LDS.
+// ---------------------------------------------------------------------------
+constexpr int kMergeRowFloats = kDimCkv + 4;  // padded row of the merge buffer
+
+struct NarrowState {
+  f32x4 o[32];    // O^T: lane holds row n, dims 16cb + 4g4 + r
+  float m_run;
+  float l_run;
+};
+
+template <int kPC>
+__device__ __forceinline__ void narrow_body(const AttnArgs& a, const bf16x8 (&qf)[18], NarrowState& st,
+                                            const LDS_AS char* __restrict__ cur, LDS_AS char* __restrict__ nxt,
+                                            bool prefetch, int page_base, int next_tok, int tok_end,
+                                            int stage_tok, int bound, const int (&kb)[4], const int (&pb)[2],
+                                            const int (&vb)[8], int wave, int lane) {
+  if (prefetch) issue_stage_bf16<kPC>(a, nxt, page_base, next_tok, tok_end, wave, lane);
+  const int g4 = lane >> 4;
+  const int tb = wave * 16;
+  // S^T[16 keys x 16 rows]
+  f32x4 sacc = {};
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks) {
+    const bf16x8 kf = lds_read_b128(cur, kb[ks & 3] + 256 * (ks >> 2));
+    sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], sacc, 0, 0, 0);
+  }
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const bf16x8 kf = lds_read_b128(cur, pb[ks]);
+    sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[16 + ks], sacc, 0, 0, 0);
+  }
+  float sv[4];
+  float mx = kNegInf;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int tok = stage_tok + tb + 4 * g4 + r;
+    const float x = sacc[r] * a.scale_log2;
+    sv[r] = tok < bound ? x : kNegInf;
+    mx = fmaxf(mx, sv[r]);
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const bool need = mx > st.m_run + kRescaleSlack;
+  if (__builtin_amdgcn_ballot_w64(need) != 0) {
+    const float m_new = fmaxf(st.m_run, mx);
+    const float alpha = (st.m_run == kNegInf) ? 0.f : fast_exp2(st.m_run - m_new);
+    st.l_run *= alpha;
+#pragma unroll
+    for (int cb = 0; cb < 32; ++cb) {
+      st.o[cb] *= alpha;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    st.m_run = m_new;
+  }
+  const float mref = (st.m_run == kNegInf) ? 0.f : st.m_run;
+  i16x4 pt;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float p = fast_exp2(sv[r] - mref);
+    st.l_run += p;
+    pt[r] = __builtin_bit_cast(short, (__bf16)p);
+  }
+  // O^T[16 dims x 16 rows] += V^T[16 dims x 16 keys] . P^T[16 keys x 16 rows]
+#pragma unroll
+  for (int cb = 0; cb < 32; ++cb) {
+    const i16x4 v = lds_read_tr(cur, vb[cb & 7] + 256 * (cb >> 3));
+    st.o[cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v, pt, st.o[cb], 0, 0, 0);
+  }
+}
+
+template <int kPC, bool kFp8>
+__device__ void narrow_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* smem, int wave, int lane) {
+  const int g4 = lane >> 4;  // lane quarter
+  const int n = lane & 15;   // row within the block
+  const RowInfo ri = row_info(a, it, n);
+  const int bound = row_key_bound(a, it, ri);
+
+  bf16x8 qf[18];
+  {
+    const bf16x8 z = {};
+    const __bf16* qn = (const __bf16*)a.q_nope + ri.qrow * kDimCkv + 8 * g4;
+    const __bf16* qp = (const __bf16*)a.q_pe + ri.qrow * kDimKpe + 8 * g4;
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) qf[ks] = ri.ok ? *(const bf16x8*)(qn + 32 * ks) : z;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) qf[16 + ks] = ri.ok ? *(const bf16x8*)(qp + 32 * ks) : z;
+  }
+  int kb[4], pb[2], vb[8];
+  {
+    const int t = wave * 16 + n;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) kb[k] = ckv_off(t, 4 * k + g4);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) pb[k] = kpe_off(t, 4 * k + g4);
+    const int t0 = wave * 16 + 4 * g4 + ((lane & 15) >> 2);
+    const int x = (lane & 3) >> 1;
+    const int w8 = (lane & 1) ? 8 : 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) vb[k] = ckv_off(t0, 2 * k + x) + w8;
+  }
+
+  NarrowState st;
+#pragma unroll
+  for (int cb = 0; cb < 32; ++cb) st.o[cb] = f32x4{};
+  st.m_run = kNegInf;
+  st.l_run = 0.f;
+
+  const int page_base = ld_const(a.kv_indptr, it.b);
+  const int nstage = (it.tok1 - it.tok0 + kStageTokens - 1) / kStageTokens;
+  if (nstage > 0) issue_stage_bf16<kPC>(a, smem, page_base, it.tok0, it.tok1, wave, lane);
+  for (int s = 0; s < nstage; ++s) {
+    wait_vmcnt<0>();
+    __syncthreads();
+    narrow_body<kPC>(a, qf, st, smem + (s & 1) * kStageBytes, smem + ((s + 1) & 1) * kStageBytes, s + 1 < nstage,
+                page_base, it.tok0 + (s + 1) * kStageTokens, it.tok1, it.tok0 + s * kStageTokens, bound, kb, pb,
+                vb, wave, lane);
+    __syncthreads();
+  }
+
+  // ---- merge the four waves' partial results through LDS ----
+  float l_run = st.l_run;
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  LDS_AS float* mbuf = (LDS_AS float*)smem;                       // [4][16][kMergeRowFloats]
+  LDS_AS float* stats = mbuf + 4 * 16 * kMergeRowFloats;         // [4][16][2]
+  if (g4 == 0) {
+    stats[(wave * 16 + n) * 2 + 0] = st.m_run;
+    stats[(wave * 16 + n) * 2 + 1] = l_run;
+  }
+  __syncthreads();
+  float m_all = kNegInf;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) m_all = fmaxf(m_all, stats[(w * 16 + n) * 2]);
+  float l_all = 0.f;
+  float my_f = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float mw = stats[(w * 16 + n) * 2];
+    const float f = (mw == kNegInf) ? 0.f : fast_exp2(mw - m_all);
+    l_all += stats[(w * 16 + n) * 2 + 1] * f;
+    if (w == wave) my_f = f;
+  }
+  const bool empty = !(l_all > 0.f);
+  const float sc = empty ? 0.f : my_f / l_all;
+#pragma unroll
+  for (int cb = 0; cb < 32; ++cb) {
+    const int dim = 16 * cb + 4 * g4;
+    *(LDS_AS f32x4*)(mbuf + (wave * 16 + n) * kMergeRowFloats + dim) = st.o[cb] * sc;
+  }
+  __syncthreads();
+  // wave w finalises dims [128w, 128w+128): lane -> row lane/4, 32 dims
+  {
+    const int row = lane >> 2;
+    const int d0 = 128 * wave + 32 * (lane & 3);
+    const RowInfo rj = row_info(a, it, row);
+    if (rj.ok) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        f32x4 acc = {};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) acc += *(LDS_AS f32x4*)(mbuf + (w * 16 + row) * kMergeRowFloats + d0 + 4 * q);
+        store4(a, it, rj, row, d0 + 4 * q, acc);
+      }
+    }
+  }
+  if (wave == 0 && g4 == 0 && ri.ok) store_lse(a, it, ri, n, empty ? kNegInf : (m_all + __log2f(l_all)) * kLn2);
+  __syncthreads();  // merge buffer overlaps stage 0 of the next item
+}
+
+template <int kMode, int kPC, bool kFp8>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mla_attn_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem_raw[kLdsBytes];
+  LDS_AS char* smem = (LDS_AS char*)smem_raw;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int i0 = ld_const(a.wg_ptr, blockIdx.x);
+  const int i1 = ld_const(a.wg_ptr, blockIdx.x + 1);
+  for (int i = i0; i < i1; ++i) {
+    const int32_t* ip = (const int32_t*)(a.items + i);
+    WorkItem it;
+    it.b = ld_const(ip, 0);
+    it.row0 = ld_const(ip, 1);
+    it.nrows = ld_const(ip, 2);
+    it.tok0 = ld_const(ip, 3);
+    it.tok1 = ld_const(ip, 4);
+    it.kv_len = ld_const(ip, 5);
+    it.q_len = ld_const(ip, 6);
+    it.slot = ld_const(ip, 7);
+    if (kMode == 1) {
+      wide_item<kPC, kFp8>(a, it, smem, wave, lane);
+    } else {
+      narrow_item<kPC, kFp8>(a, it, smem, wave, lane);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Combine: merge the partial results of each split (request, row block).
+// out = sum_s w_s o_s / sum_s w_s with w_s = exp(lse_s - max lse), and
+// lse = max lse + ln sum w (the log-sum-exp identity).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void mla_combine_kernel(AttnArgs a) {
+  const SplitGroup grp = a.groups[blockIdx.x];
+  const int sub = threadIdx.x >> 6;
+  const int d0 = (threadIdx.x & 63) * 8;
+  const int H = a.num_heads;
+  const int q_start = a.qo_indptr ? a.qo_indptr[grp.b] : grp.b;
+  for (int r = sub; r < grp.nrows; r += 4) {
+    float M = kNegInf;
+    for (int s = 0; s < grp.nsplit; ++s)
+      M = fmaxf(M, a.part_lse[(size_t)(grp.slot0 + s) * a.rows_per_block + r]);
+    float W = 0.f;
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (M != kNegInf) {
+      for (int s = 0; s < grp.nsplit; ++s) {
+        const size_t slot_row = (size_t)(grp.slot0 + s) * a.rows_per_block + r;
+        const float ls = a.part_lse[slot_row];
+        const float w = (ls == kNegInf) ? 0.f : __expf(ls - M);
+        W += w;
+        const f32x4* src = (const f32x4*)(a.part_o + slot_row * kDimCkv + d0);
+        const f32x4 v0 = src[0], v1 = src[1];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[j] += w * v0[j];
+          acc[4 + j] += w * v1[j];
+        }
+      }
+    }
+    const float inv = (W > 0.f) ? 1.f / W : 0.f;
+    const int rr = grp.row0 + r;
+    const int qi = rr / H;
+    const size_t qrow = (size_t)(q_start + qi) * H + (rr - qi * H);
+    if (a.out_bf16) {
+      bf16x8 h;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) h[j] = (__bf16)(acc[j] * inv);
+      *(bf16x8*)((__bf16*)a.out + qrow * kDimCkv + d0) = h;
+    } else {
+      f32x4* dst = (f32x4*)((float*)a.out + qrow * kDimCkv + d0);
+      dst[0] = f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+      dst[1] = f32x4{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
+    }
+    if ((threadIdx.x & 63) == 0) a.lse[qrow] = (W > 0.f) ? M + __logf(W) : kNegInf;
+  }
+}
+
+}  // namespace
+
+template <int kMode, int kPC>
+hipError_t launch_mode(const AttnArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((mla_attn_kernel<kMode, kPC, false>), dim3(a.num_wgs), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention(const AttnArgs& a, int tile_mode, int kv_fp8, hipStream_t stream) {
+  if (a.num_wgs <= 0) return hipSuccess;
+  if (kv_fp8) return hipErrorNotSupported;
+  const int pc = a.page_shift >= 6 ? kPageBig : (a.page_shift >= 3 ? kPageMid : kPageSmall);
+  if (tile_mode == 1) {
+    if (pc == kPageBig) return launch_mode<1, kPageBig>(a, stream);
+    if (pc == kPageMid) return launch_mode<1, kPageMid>(a, stream);
+    return launch_mode<1, kPageSmall>(a, stream);
+  }
+  if (pc == kPageBig) return launch_mode<2, kPageBig>(a, stream);
+  if (pc == kPageMid) return launch_mode<2, kPageMid>(a, stream);
+  return launch_mode<2, kPageSmall>(a, stream);
+}
+
+hipError_t launch_combine(const AttnArgs& a, hipStream_t stream) {
+  if (a.num_groups <= 0) return hipSuccess;
+  hipLaunchKernelGGL(mla_combine_kernel, dim3(a.num_groups), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,74 @@
+// Internal types shared by the host planner / C ABI and the HIP kernels.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+namespace mla {
+
+constexpr int kDimCkv = 512;
+constexpr int kDimKpe = 64;
+constexpr int kFp8RecordBytes = 656;
+constexpr int kStageTokens = 64;      // keys per LDS stage; chunk boundaries are multiples
+constexpr int kWideRows = 128;        // rows per workgroup in the wide tile mode (4 waves x 32)
+constexpr int kNarrowRows = 16;       // rows per workgroup in the narrow tile mode
+constexpr size_t kWsAlign = 256;
+
+// One workgroup's work: rows [row0, row0+nrows) of request b against keys
+// [tok0, tok1).  Rows count (query token, head) pairs of the request as
+// token*H + head.  slot < 0: write the final output; else partial slot.
+struct WorkItem {
+  int32_t b;
+  int32_t row0;
+  int32_t nrows;
+  int32_t tok0;
+  int32_t tok1;
+  int32_t kv_len;
+  int32_t q_len;
+  int32_t slot;
+};
+static_assert(sizeof(WorkItem) == 32, "work item is 8 int32");
+
+// One split (request, row block): its nsplit partial slots are consecutive.
+struct SplitGroup {
+  int32_t b;
+  int32_t row0;
+  int32_t nrows;
+  int32_t nsplit;
+  int32_t slot0;
+  int32_t pad[3];
+};
+static_assert(sizeof(SplitGroup) == 32, "split group is 8 int32");
+
+struct AttnArgs {
+  const void* q_nope;      // bf16 [rows_total, H, 512]
+  const void* q_pe;        // bf16 [rows_total, H, 64]
+  const void* ckv;         // bf16 [P, ps, 512]   (bf16 format)
+  const void* kpe;         // bf16 [P, ps, 64]    (bf16 format)
+  const void* kv_fp8;      // u8   [P, ps, 656]   (fp8 format)
+  const int32_t* kv_indptr;
+  const int32_t* kv_indices;
+  const int32_t* qo_indptr;  // prefill; nullptr for decode (q row of request b is b)
+  const int32_t* wg_ptr;   // [grid+1] item range of each workgroup
+  const WorkItem* items;
+  const SplitGroup* groups;
+  void* out;
+  float* lse;
+  float* part_o;           // [slots][rows_per_block][512] fp32, normalised partial outputs
+  float* part_lse;         // [slots][rows_per_block] fp32 (natural log)
+  float scale_log2;        // sm_scale * log2(e)
+  int32_t num_heads;
+  int32_t page_shift;      // log2(page_size)
+  int32_t out_bf16;        // 1: bf16 out, 0: fp32 out
+  int32_t causal;          // prefill causal mask
+  int32_t rows_per_block;  // partial slot stride in rows
+  int32_t num_wgs;
+  int32_t num_items;
+  int32_t num_groups;
+};
+
+// Launchers (mla_attn.hip).  They only enqueue on `stream`; return hipError_t.
+hipError_t launch_attention(const AttnArgs& a, int tile_mode, int kv_fp8, hipStream_t stream);
+hipError_t launch_combine(const AttnArgs& a, hipStream_t stream);
+
+}  // namespace mla

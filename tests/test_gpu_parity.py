@@ -1,0 +1,246 @@
+"""GPU parity: the HIP library (through its C ABI) against the float64 oracle
+on the same seeded inputs.
+
+Tolerances (floating point): output max |err| <= 2e-2 and relative L2
+<= 1e-2 for bf16 caches (6e-2 / 3e-2 for the fp8 cache, against the oracle on
+the dequantised records), lse max |err| <= 1e-3.  Page indexing is checked
+bit-exactly: moving pages around in the pool must not change a single bit.
+Unused pool pages and tail slots hold NaN in every case here.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import make_workload
+
+pytestmark = pytest.mark.gpu
+
+TOL_BF16 = dict(max_abs=2e-2, rel_l2=1e-2, lse=1e-3)
+TOL_FP8 = dict(max_abs=6e-2, rel_l2=3e-2, lse=1e-3)
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def mla():
+    import paged_mla_decode_05_amd as m
+
+    m.load_library()
+    assert torch.cuda.is_available()
+    return m
+
+
+def compare(out, lse, ref_o, ref_l, tol, rows=None):
+    o = out.double().cpu().numpy()
+    l = lse.double().cpu().numpy()
+    if rows is not None:
+        o, l, ref_o, ref_l = o[rows], l[rows], ref_o[rows], ref_l[rows]
+    assert np.all(np.isfinite(o)), "non-finite output"
+    empty = np.isneginf(ref_l)
+    assert np.array_equal(np.isneginf(l), empty), "lse = -inf must mark exactly the rows with no keys"
+    assert np.all(o[empty] == 0)
+    err = np.abs(o - ref_o).max() if o.size else 0.0
+    den = np.linalg.norm(ref_o)
+    rel = np.linalg.norm(o - ref_o) / den if den > 0 else 0.0
+    lerr = np.abs(l[~empty] - ref_l[~empty]).max() if (~empty).any() else 0.0
+    say(f"    max|dout|={err:.3e} relL2={rel:.3e} max|dlse|={lerr:.3e}")
+    assert err <= tol["max_abs"] and rel <= tol["rel_l2"] and lerr <= tol["lse"]
+
+
+def run_decode(mla, w, dev, **plan_kw):
+    fmt = mla.MLA_KV_FP8_E4M3_T128 if w.kv_format == "fp8" else mla.MLA_KV_BF16
+    plan = mla.mla_plan_create(mla.MLA_KIND_DECODE, w.batch, w.num_heads, w.page_size, w.num_pages,
+                               w.kv_len, w.kv_indptr, kv_format=fmt, **plan_kw)
+    if w.kv_format == "fp8":
+        out, lse = mla.mla_decode_fp8(plan, w.q_nope.to(dev), w.q_pe.to(dev), w.kv_fp8.to(dev),
+                                      w.kv_indptr.to(dev), w.kv_indices.to(dev), w.sm_scale,
+                                      out_dtype=w.out_dtype)
+    else:
+        out, lse = mla.mla_decode(plan, w.q_nope.to(dev), w.q_pe.to(dev), w.ckv.to(dev), w.kpe.to(dev),
+                                  w.kv_indptr.to(dev), w.kv_indices.to(dev), w.sm_scale, out_dtype=w.out_dtype)
+    torch.cuda.synchronize()
+    return out, lse, plan
+
+
+def ref_decode(w, requests=None):
+    if w.kv_format == "fp8":
+        return oracle.mla_decode_fp8_ref(w.q_nope, w.q_pe, w.kv_fp8, w.kv_indptr, w.kv_indices, w.kv_len,
+                                         w.sm_scale, requests=requests)
+    return oracle.mla_decode_ref(w.q_nope, w.q_pe, w.ckv, w.kpe, w.kv_indptr, w.kv_indices, w.kv_len,
+                                 w.sm_scale, requests=requests)
+
+
+def run_prefill(mla, w, dev, **plan_kw):
+    plan = mla.mla_plan_create(mla.MLA_KIND_PREFILL, w.batch, w.num_heads, w.page_size, w.num_pages,
+                               w.kv_len, w.kv_indptr, qo_indptr=w.qo_indptr, causal=w.causal, **plan_kw)
+    out, lse = mla.mla_prefill(plan, w.q_nope.to(dev), w.q_pe.to(dev), w.ckv.to(dev), w.kpe.to(dev),
+                               w.qo_indptr.to(dev), w.kv_indptr.to(dev), w.kv_indices.to(dev), w.sm_scale,
+                               out_dtype=w.out_dtype)
+    torch.cuda.synchronize()
+    return out, lse, plan
+
+
+def ref_prefill(w, requests=None):
+    return oracle.mla_prefill_ref(w.q_nope, w.q_pe, w.ckv, w.kpe, w.qo_indptr, w.kv_indptr, w.kv_indices,
+                                  w.kv_len, w.sm_scale, causal=w.causal, requests=requests)
+
+
+DEV = "cuda:0"
+
+
+# ---------------------------------------------------------------------------
+# small cases, every row checked
+# ---------------------------------------------------------------------------
+
+def test_tiny_decode_config(mla):
+    w = make_workload("tiny_decode")
+    say("tiny_decode B=4 H=16 lens [1,37,64,200] fp32 out")
+    out, lse, _ = run_decode(mla, w, DEV)
+    compare(out, lse, *ref_decode(w), TOL_BF16)
+
+
+CASES = [
+    # (heads, page_size, kv_lens, tile_mode, force_splits, out fp32)
+    (16, 64, [1, 37, 64, 200], 2, 0, False),
+    (16, 16, [5, 300, 64, 1], 2, 3, False),
+    (16, 1, [3, 70, 129], 2, 2, True),
+    (128, 64, [1, 37, 64, 200], 1, 0, False),
+    (128, 16, [700, 3, 65], 1, 3, True),
+    (128, 1, [2, 130], 1, 2, False),
+    (128, 128, [1000, 1, 257], 1, 4, False),
+    (40, 64, [100, 400, 0, 33], 1, 2, False),
+    (40, 8, [100, 400, 0, 33], 2, 0, False),
+    (1, 64, [200, 77], 2, 0, False),
+    (24, 4, [90, 31], 0, 0, True),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"H{c[0]}-ps{c[1]}-m{c[3]}-s{c[4]}" for c in CASES])
+def test_decode_small_cases(mla, case):
+    H, ps, lens, mode, fs, f32 = case
+    say(f"decode H={H} page_size={ps} lens={lens} tile_mode={mode} force_splits={fs}")
+    w = make_workload(kv_lens=lens, heads=H, page_size=ps, seed=100 + H + ps,
+                      out_dtype=torch.float32 if f32 else torch.bfloat16)
+    out, lse, _ = run_decode(mla, w, DEV, tile_mode=mode, force_splits=fs, num_cus=0)
+    compare(out, lse, *ref_decode(w), TOL_BF16)
+
+
+PREFILL_CASES = [
+    (128, 64, [3, 1, 8, 5], [64, 100, 700, 5], True, 1, 0),
+    (128, 16, [2, 4], [300, 17], True, 1, 3),
+    (16, 64, [8, 1, 3], [500, 9, 64], True, 0, 0),
+    (16, 1, [4, 2], [50, 3], False, 2, 2),
+    (128, 64, [1, 7], [1000, 1500], False, 1, 2),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=[f"H{c[0]}-ps{c[1]}-c{int(c[4])}-m{c[5]}" for c in PREFILL_CASES])
+def test_prefill_small_cases(mla, case):
+    H, ps, qlens, lens, causal, mode, fs = case
+    say(f"prefill H={H} page_size={ps} q={qlens} kv={lens} causal={causal} mode={mode} splits={fs}")
+    w = make_workload(kind="prefill", kv_lens=lens, q_lens=qlens, heads=H, page_size=ps, causal=causal,
+                      seed=7 + H)
+    out, lse, _ = run_prefill(mla, w, DEV, tile_mode=mode, force_splits=fs)
+    compare(out, lse, *ref_prefill(w), TOL_BF16)
+
+
+def test_empty_batch_is_a_no_op(mla):
+    plan = mla.mla_plan_create(mla.MLA_KIND_DECODE, 0, 16, 64, 1, [], [0])
+    z = torch.zeros((0, 16, 512), dtype=torch.bfloat16, device=DEV)
+    zp = torch.zeros((0, 16, 64), dtype=torch.bfloat16, device=DEV)
+    ckv = torch.zeros((1, 64, 512), dtype=torch.bfloat16, device=DEV)
+    kpe = torch.zeros((1, 64, 64), dtype=torch.bfloat16, device=DEV)
+    out, lse = mla.mla_decode(plan, z, zp, ckv, kpe, torch.zeros(1, dtype=torch.int32, device=DEV),
+                              torch.zeros(1, dtype=torch.int32, device=DEV), 0.1)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 16, 512)
+
+
+# ---------------------------------------------------------------------------
+# bit-exact properties of the paged gather
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("H,mode", [(16, 2), (128, 1)])
+def test_page_permutation_is_bitwise_invariant(mla, H, mode):
+    say(f"page permutation H={H} mode={mode}")
+    w = make_workload(kv_lens=[130, 64, 1, 900], heads=H, page_size=16, seed=55)
+    out1, lse1, _ = run_decode(mla, w, DEV, tile_mode=mode, force_splits=2)
+    perm = torch.randperm(w.num_pages, generator=torch.Generator().manual_seed(9))
+    ckv2 = torch.empty_like(w.ckv)
+    kpe2 = torch.empty_like(w.kpe)
+    ckv2[perm] = w.ckv
+    kpe2[perm] = w.kpe
+    w.ckv, w.kpe, w.kv_indices = ckv2, kpe2, perm.to(torch.int32)[w.kv_indices.long()]
+    out2, lse2, _ = run_decode(mla, w, DEV, tile_mode=mode, force_splits=2)
+    assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+
+
+def test_repeat_runs_are_bitwise_identical(mla):
+    w = make_workload(kv_lens=[3000, 20, 700], heads=128, page_size=64, seed=56)
+    out1, lse1, _ = run_decode(mla, w, DEV)
+    out2, lse2, _ = run_decode(mla, w, DEV)
+    assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+
+
+def test_prefill_single_query_equals_decode(mla):
+    w = make_workload(kv_lens=[300, 77], heads=128, page_size=64, seed=57)
+    outd, lsed, _ = run_decode(mla, w, DEV)
+    wp = make_workload(kind="prefill", kv_lens=[300, 77], q_lens=[1, 1], heads=128, page_size=64, seed=57)
+    # same inputs as the decode call: one query per request
+    wp.q_nope, wp.q_pe, wp.ckv, wp.kpe, wp.kv_indices = w.q_nope, w.q_pe, w.ckv, w.kpe, w.kv_indices
+    outp, lsep, _ = run_prefill(mla, wp, DEV)
+    assert torch.equal(outd, outp) and torch.equal(lsed, lsep)
+
+
+def test_forced_split_matches_unsplit(mla):
+    w = make_workload(kv_lens=[2000, 1500], heads=128, page_size=64, seed=58)
+    o1, l1, _ = run_decode(mla, w, DEV, force_splits=1)
+    o5, l5, p5 = run_decode(mla, w, DEV, force_splits=5)
+    assert p5.num_split_groups == 2
+    ref = ref_decode(w)
+    compare(o1, l1, *ref, TOL_BF16)
+    compare(o5, l5, *ref, TOL_BF16)
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, sampled requests checked against the oracle
+# ---------------------------------------------------------------------------
+
+def _sample(n, k, seed):
+    return sorted(np.random.default_rng(seed).choice(n, size=min(k, n), replace=False).tolist())
+
+
+def test_decode_b64_h128_full_size(mla):
+    say("decode_b64_h128 full size, 12 sampled requests")
+    w = make_workload("decode_b64_h128", device=DEV)
+    out, lse, _ = run_decode(mla, w, DEV)
+    req = _sample(w.batch, 12, 1)
+    ro, rl = ref_decode(w, requests=req)
+    compare(out, lse, ro, rl, TOL_BF16, rows=req)
+
+
+def test_decode_b128_h16_skew_full_size(mla):
+    w = make_workload("decode_b128_h16_skew", device=DEV)
+    long_req = [b for b in range(w.batch) if int(w.kv_len[b]) == 32768][:3]
+    req = sorted(set(long_req + _sample(w.batch, 5, 2)))
+    say(f"decode_b128_h16_skew full size, requests {req}")
+    out, lse, _ = run_decode(mla, w, DEV)
+    ro, rl = ref_decode(w, requests=req)
+    compare(out, lse, ro, rl, TOL_BF16, rows=req)
+
+
+def test_prefill_causal_h128_full_size(mla):
+    w = make_workload("prefill_causal_h128", device=DEV)
+    req = _sample(w.batch, 8, 3)
+    say(f"prefill_causal_h128 full size, requests {req}")
+    out, lse, _ = run_prefill(mla, w, DEV)
+    ro, rl = ref_prefill(w, requests=req)
+    qo = w.qo_indptr.numpy()
+    rows = np.concatenate([np.arange(qo[b], qo[b + 1]) for b in req])
+    compare(out, lse, ro, rl, TOL_BF16, rows=rows)
