@@ -1,0 +1,320 @@
+#!/usr/bin/env python3
+"""Paged MLA decode benchmark on one MI355X; prints one JSON line.
+
+A step is one mla_decode (or mla_prefill / mla_decode_fp8) call over the
+whole workload: the attention kernel plus the split combine.  Inputs are
+resident in HBM before the timed region.  To keep repeated steps from being
+served by the 256 MB Infinity Cache, the key/value pool is replicated and
+consecutive steps read different replicas (at least ~1 GB apart).
+
+value        = algorithmic FLOP/s of the step (TFLOP/s): 2*(512+64) + 2*512
+               flops per visible (row, key), masked keys excluded
+kv_gb_per_s  = live latent-cache bytes / step time (each live key once)
+roofline     = the attention kernel alone, timed with HIP events recorded
+               around it inside the timed region, against MI355X's
+               published peaks (HBM 8 TB/s, dense bf16 MFMA 2.5 PFLOP/s)
+cpu_baseline = the float64 oracle on this host's cores, timed on repeated
+               passes over the same workload (bounded to ~10-30 s)
+"""
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode TFLOP/s + KV GB/s (% of roofline), B=64 H=128 d=512+64"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+FLOPS_PER_ROW_KEY = 2 * (512 + 64) + 2 * 512
+KV_BYTES = {"bf16": (512 + 64) * 2, "fp8": 656}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def workload_counts(w):
+    """Exact algorithmic flops and bytes of a workload."""
+    import numpy as np
+
+    H = w.num_heads
+    L = w.kv_len.numpy().astype(np.int64)
+    n = w.q_lens().numpy().astype(np.int64)
+    rows_keys = 0
+    for b in range(w.batch):
+        if w.kind == "prefill" and w.causal:
+            vis = L[b] - n[b] + np.arange(n[b]) + 1
+            rows_keys += int(vis.sum()) * H
+        else:
+            rows_keys += int(n[b] * L[b]) * H
+    flops = rows_keys * FLOPS_PER_ROW_KEY
+    live_kv = int(L.sum()) * KV_BYTES[w.kv_format]
+    rows = int(n.sum())
+    out_bytes = 4 if str(w.out_dtype).endswith("float32") else 2
+    bytes_alg = (live_kv + rows * H * (512 + 64) * 2 + rows * H * 512 * out_bytes + rows * H * 4
+                 + int(w.kv_indices.numel()) * 4)
+    return flops, live_kv, bytes_alg
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime (for the per-kernel timing)."""
+
+    def __init__(self):
+        import paged_mla_decode_05_amd as mla
+
+        mla.load_library()
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        e = ctypes.c_void_p()
+        assert self.hip.hipEventCreate(ctypes.byref(e)) == 0
+        return e
+
+    def elapsed_ms(self, a, b):
+        self.hip.hipEventSynchronize(b)
+        ms = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+
+def read_counters(config_name, kernel_sha):
+    """HBM traffic per attention launch from committed rocprofv3 counter runs,
+    if they were taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"attention_{config_name}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != kernel_sha:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def kernel_sha():
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in ("mla_attn.hip", "mla_internal.h"):
+        h.update(open(os.path.join(ROOT, "paged_mla_decode_05_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
+def cpu_baseline(w, flops_total, min_seconds):
+    """Time the oracle on repeated passes over the workload's requests."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    # host copies once, outside the timed region
+    if w.kind == "prefill":
+        args = (w.q_nope.cpu(), w.q_pe.cpu(), w.ckv.cpu(), w.kpe.cpu(), w.qo_indptr, w.kv_indptr,
+                w.kv_indices, w.kv_len, w.sm_scale)
+        fn = lambda reqs: oracle.mla_prefill_ref(*args, causal=w.causal, requests=reqs)
+    elif w.kv_format == "fp8":
+        args = (w.q_nope.cpu(), w.q_pe.cpu(), w.kv_fp8.cpu(), w.kv_indptr, w.kv_indices, w.kv_len, w.sm_scale)
+        fn = lambda reqs: oracle.mla_decode_fp8_ref(*args, requests=reqs)
+    else:
+        args = (w.q_nope.cpu(), w.q_pe.cpu(), w.ckv.cpu(), w.kpe.cpu(), w.kv_indptr, w.kv_indices, w.kv_len,
+                w.sm_scale)
+        fn = lambda reqs: oracle.mla_decode_ref(*args, requests=reqs)
+    import numpy as np
+
+    L = w.kv_len.numpy().astype(np.int64)
+    n = w.q_lens().numpy().astype(np.int64)
+    per_req = []
+    for b in range(w.batch):
+        if w.kind == "prefill" and w.causal:
+            keys = int((L[b] - n[b] + np.arange(n[b]) + 1).sum())
+        else:
+            keys = int(n[b] * L[b])
+        per_req.append(keys * w.num_heads * FLOPS_PER_ROW_KEY)
+    done_flops = 0.0
+    reqs_done = 0
+    t0 = time.perf_counter()
+    stop = False
+    while not stop:
+        for b in range(w.batch):
+            fn([b])
+            reqs_done += 1
+            done_flops += per_req[b]
+            if time.perf_counter() - t0 >= 30.0:
+                stop = True
+                break
+        if time.perf_counter() - t0 >= min_seconds:
+            stop = True
+    dt = time.perf_counter() - t0
+    return {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{reqs_done} request evaluations ({reqs_done / w.batch:.2f} passes over all "
+                      f"{w.batch} requests of {w.name}), {dt:.1f} s wall, float64 NumPy"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="decode_b64_h128")
+    ap.add_argument("--rotate-bytes", type=float, default=1.5e9,
+                    help="replicate the cache pool until consecutive steps are this many bytes apart")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(one MI355X share of the workload is what it measures).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_mla_decode_05_amd as mla
+    from workloads import make_workload
+
+    if not os.path.exists(mla.lib_path()):
+        import __graft_entry__
+
+        __graft_entry__.build()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"bench: generating {args.config} on {dev}")
+    w = make_workload(args.config, device=dev, poison=False)
+    flops, live_kv, bytes_alg = workload_counts(w)
+    fmt = mla.MLA_KV_FP8_E4M3_T128 if w.kv_format == "fp8" else mla.MLA_KV_BF16
+    kind = mla.MLA_KIND_PREFILL if w.kind == "prefill" else mla.MLA_KIND_DECODE
+    t_plan = time.perf_counter()
+    plan = mla.mla_plan_create(kind, w.batch, w.num_heads, w.page_size, w.num_pages, w.kv_len, w.kv_indptr,
+                               qo_indptr=w.qo_indptr if w.kind == "prefill" else None, kv_format=fmt,
+                               causal=w.causal)
+    plan_ms = (time.perf_counter() - t_plan) * 1e3
+    kv_indptr = w.kv_indptr.to(dev)
+    kv_indices = w.kv_indices.to(dev)
+    qo_indptr = w.qo_indptr.to(dev) if w.qo_indptr is not None else None
+    pool_bytes = (w.kv_fp8.numel() if fmt else (w.ckv.numel() + w.kpe.numel()) * 2)
+    reps = max(1, min(16, math.ceil(args.rotate_bytes / max(live_kv, 1))))
+    pools = [(w.ckv, w.kpe, w.kv_fp8)]
+    for _ in range(reps - 1):
+        pools.append((w.ckv.clone() if w.ckv is not None else None, w.kpe.clone() if w.kpe is not None else None,
+                      w.kv_fp8.clone() if w.kv_fp8 is not None else None))
+    out = torch.empty((w.rows, w.num_heads, 512), dtype=w.out_dtype, device=dev)
+    lse = torch.empty((w.rows, w.num_heads), dtype=torch.float32, device=dev)
+    ws = plan.workspace(dev)
+    log(f"bench: {plan.num_work_items} work items on {plan.workgroup_ptr().numel() - 1} workgroups, "
+        f"{plan.num_split_groups} split groups, workspace {plan.workspace_bytes / 1e6:.1f} MB, "
+        f"{reps} pool replicas of {pool_bytes / 1e6:.0f} MB")
+
+    def step(i):
+        ckv, kpe, kv8 = pools[i % reps]
+        if fmt:
+            mla.mla_decode_fp8(plan, w.q_nope, w.q_pe, kv8, kv_indptr, kv_indices, w.sm_scale, out=out, lse=lse,
+                               workspace=ws)
+        elif kind == mla.MLA_KIND_PREFILL:
+            mla.mla_prefill(plan, w.q_nope, w.q_pe, ckv, kpe, qo_indptr, kv_indptr, kv_indices, w.sm_scale,
+                            out=out, lse=lse, workspace=ws)
+        else:
+            mla.mla_decode(plan, w.q_nope, w.q_pe, ckv, kpe, kv_indptr, kv_indices, w.sm_scale, out=out,
+                           lse=lse, workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"bench: warmup {args.warmup} done; timing {args.steps} steps")
+
+    ev = HipEvents()
+    kb = [ev.create() for _ in range(args.steps)]
+    ke = [ev.create() for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(args.steps):
+        mla.mla_record_attention_events(kb[i], ke[i])
+        step(args.warmup + i)
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    attn_ms = sorted(ev.elapsed_ms(kb[i], ke[i]) for i in range(args.steps))
+    attn_avg = sum(attn_ms) / len(attn_ms)
+    log(f"bench: {ms_step * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us), attention kernel avg "
+        f"{attn_avg * 1e3:.1f} us (p10 {attn_ms[len(attn_ms) // 10] * 1e3:.1f}, "
+        f"p90 {attn_ms[(9 * len(attn_ms)) // 10] * 1e3:.1f})")
+
+    ai = flops / bytes_alg
+    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    hbm_bound = ai < ridge
+    t_s = ms_step * 1e-3
+    ta_s = attn_avg * 1e-3
+    tflops = flops / t_s / 1e12
+    kv_gbs = live_kv / t_s / 1e9
+    pct = 100.0 * max((bytes_alg / (HBM_PEAK_GBS * 1e9)), flops / (BF16_PEAK_TFLOPS * 1e12)) / t_s
+    sha = kernel_sha()
+    traffic = read_counters(args.config, sha)
+    if hbm_bound:
+        achieved = bytes_alg / ta_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": (round(traffic / ta_s / 1e9, 1) if traffic is not None else None)}
+    else:
+        achieved = flops / ta_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                "traffic": (round(traffic / ta_s / 1e9, 1) if traffic is not None else None)}
+    roof["kernel"] = "mla_attn_kernel"
+    roof["kernel_avg_us"] = round(attn_avg * 1e3, 2)
+    roof["algorithmic_bytes_per_launch"] = bytes_alg
+    roof["algorithmic_flops_per_launch"] = flops
+    if traffic is not None:
+        roof["traffic_note"] = "GB/s of HBM traffic per launch from rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-kernel scaled"
+
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.kv_format == "bf16" else "fp8-e4m3 cache, bf16 math",
+        "data": "synthetic (seeded N(0,1) bf16 inputs shaped like the workload)",
+        "config": {"workload": w.name, "batch": w.batch, "num_qo_heads": w.num_heads, "head_dim_ckv": 512,
+                   "head_dim_kpe": 64, "page_size": w.page_size, "kv_format": w.kv_format,
+                   "kv_len_total": int(w.kv_len.sum()), "rows": w.rows, "parallelism": "single GPU"},
+        "kv_gb_per_s": round(kv_gbs, 1),
+        "pct_of_roofline": round(pct, 2),
+        "plan_ms": round(plan_ms, 3),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle")
+        result["cpu_baseline"] = cpu_baseline(w, flops, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

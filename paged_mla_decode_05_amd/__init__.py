@@ -19,6 +19,7 @@ from ._binding import (  # noqa: F401
     mla_decode_fp8,
     mla_plan_create,
     mla_prefill,
+    mla_record_attention_events,
     MLA_KIND_DECODE,
     MLA_KIND_PREFILL,
     MLA_KV_BF16,

@@ -85,6 +85,8 @@ def load_library():
         L.mla_prefill.restype = i32
         L.mla_decode_fp8.argtypes = [vp, vp, vp, vp, vp, vp, f32, vp, i32, vp, vp, sz, vp]
         L.mla_decode_fp8.restype = i32
+        L.mla_record_attention_events.argtypes = [vp, vp]
+        L.mla_record_attention_events.restype = i32
         L.mla_status_str.argtypes = [i32]
         L.mla_status_str.restype = ctypes.c_char_p
         _lib = L
@@ -198,6 +200,12 @@ def mla_plan_create(kind: int, batch: int, num_heads: int, page_size: int, num_p
     _check(L.mla_plan_create(ctypes.byref(h), ctypes.byref(d), cast(kl_p), cast(ki_p), cast(qo_p)),
            "mla_plan_create")
     return Plan(h, d, kl, ki, qo)
+
+
+def mla_record_attention_events(before, after):
+    """Record two caller-owned hipEvent_t handles around the attention kernel
+    of the next run call on this thread (timing diagnostics)."""
+    _check(load_library().mla_record_attention_events(before, after), "mla_record_attention_events")
 
 
 def _dev(t: torch.Tensor, name: str, dtype, shape=None):

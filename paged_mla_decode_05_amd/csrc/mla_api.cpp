@@ -282,6 +282,9 @@ mla_status mla_plan_upload(const mla_plan* p, void* ws, size_t ws_bytes, hipStre
 
 namespace {
 
+thread_local hipEvent_t t_ev_before = nullptr;
+thread_local hipEvent_t t_ev_after = nullptr;
+
 mla_status run(const mla_plan* p, int32_t want_kind, int32_t want_format, const void* q_nope,
                const void* q_pe, const void* ckv, const void* kpe, const void* kv_fp8,
                const int32_t* qo_indptr, const int32_t* kv_indptr, const int32_t* kv_indices,
@@ -324,8 +327,12 @@ mla_status run(const mla_plan* p, int32_t want_kind, int32_t want_format, const 
   a.num_wgs = p->num_wgs;
   a.num_items = (int32_t)p->items.size();
   a.num_groups = (int32_t)p->groups.size();
+  hipEvent_t ev0 = t_ev_before, ev1 = t_ev_after;
+  t_ev_before = t_ev_after = nullptr;
+  if (ev0 && hipEventRecord(ev0, stream) != hipSuccess) return MLA_ERR_DEVICE;
   hipError_t e = mla::launch_attention(a, p->tile_mode, want_format == MLA_KV_FP8_E4M3_T128, stream);
   if (e != hipSuccess) return MLA_ERR_DEVICE;
+  if (ev1 && hipEventRecord(ev1, stream) != hipSuccess) return MLA_ERR_DEVICE;
   if (!p->groups.empty()) {
     e = mla::launch_combine(a, stream);
     if (e != hipSuccess) return MLA_ERR_DEVICE;
@@ -336,6 +343,13 @@ mla_status run(const mla_plan* p, int32_t want_kind, int32_t want_format, const 
 }  // namespace
 
 extern "C" {
+
+mla_status mla_record_attention_events(hipEvent_t before, hipEvent_t after) {
+  if ((before == nullptr) != (after == nullptr)) return MLA_ERR_INVALID_ARGUMENT;
+  t_ev_before = before;
+  t_ev_after = after;
+  return MLA_OK;
+}
 
 mla_status mla_decode(const mla_plan* p, const void* q_nope, const void* q_pe, const void* ckv,
                       const void* kpe, const int32_t* kv_indptr, const int32_t* kv_indices,
