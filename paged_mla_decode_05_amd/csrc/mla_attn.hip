@@ -61,9 +61,6 @@ constexpr float kRescaleSlack = 8.0f;                           // log2 units
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kLn2 = 0.69314718055994531f;
 
-// 1 KB of zeros: the source of every key row outside the current chunk.
-__device__ __attribute__((aligned(16))) uint32_t g_zero_row[256];
-
 // ---------------------------------------------------------------------------
 // LDS layout of one stage: ckv rows [64][1024 B] then kpe rows [64][128 B].
 // 16-byte chunks are XOR-swizzled per row so that the MFMA operand reads
@@ -110,6 +107,23 @@ __device__ __forceinline__ float sum_xor32(float x) {
   return a + b;
 }
 
+// Multiplies an accumulator tile held in AGPRs by alpha through one
+// temporary VGPR per element.  Written as asm so that the accumulator keeps
+// its AGPR home: a plain C++ multiply makes the register allocator move the
+// whole accumulator to VGPRs and spill.
+template <int N>
+__device__ __forceinline__ void scale_acc(float __attribute__((ext_vector_type(N)))& v, float alpha) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    float x = v[i];
+    float tmp;
+    asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                 : "+a"(x), "=&v"(tmp)
+                 : "v"(alpha));
+    v[i] = x;
+  }
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Waits until at most `n` vector-memory loads of this wave are outstanding
@@ -119,6 +133,49 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(n >= 0 && n < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
+
+// One 16-byte-per-lane direct-to-LDS load: lane l reads 16 bytes at
+// sbase + voff and writes them to LDS bytes [lds + 16 l, lds + 16 l + 16).
+// The scalar base / 32-bit lane offset form keeps the address in one VGPR.
+// Issued through asm so the compiler neither hoists 64-bit per-lane
+// addresses nor inserts waits for it: the caller waits with vmcnt and a
+// barrier before any wave reads the destination.  M0 (the LDS address) is
+// saved and restored around the load.
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "v"(voff), "s"(sbase), "s"(lds));
+}
+
+// The same with a full 64-bit per-lane address (lanes reading unrelated pages).
+__device__ __forceinline__ void dma16_v(const void* vaddr, uint32_t lds) {
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "v"(vaddr), "s"(lds));
+}
+
+// The lane id, re-materialised where it is used: values derived from it are
+// cheap to recompute, and keeping them live across the stage loop only
+// adds register pressure.
+__device__ __forceinline__ int lane_here() {
+  int l = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  asm volatile("" : "+v"(l));
+  return l;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const LDS_AS char* p) { return (uint32_t)(uintptr_t)p; }
 
 // Read-only tables (page indices, work list) are read through the constant
 // address space, so uniform reads become scalar loads that do not wait on
@@ -138,61 +195,78 @@ constexpr int kPageBig = 0, kPageMid = 1, kPageSmall = 2;
 // ---------------------------------------------------------------------------
 // Gather loader (bf16 caches): stage of keys [s_tok0, s_tok0 + 64) of a
 // request whose page list starts at kv_indices[page_base], into LDS stage
-// `st`.  18 direct-to-LDS loads per wave; keys >= tok_end read zeros.
+// `st`.  18 direct-to-LDS loads per wave (the two per-lane kpe loads first).
+// Each load's address is a uniform
+// (scalar) base plus a 32-bit per-lane offset.  Keys at or past tok_end
+// re-read the chunk's last key (finite data; the softmax masks them out), so
+// nothing outside the request's live keys is ever read.
 // ---------------------------------------------------------------------------
 template <int kPageClass>
 __device__ __forceinline__ void issue_stage_bf16(const AttnArgs& a, LDS_AS char* st, int page_base,
-                                                 int s_tok0, int tok_end, int wave, int lane) {
+                                                 int s_tok0, int tok_end, int wave, int) {
+  const int lane = lane_here();
   const int sh = a.page_shift;
   const int mask = (1 << sh) - 1;
   const char* ckv = (const char*)a.ckv;
   const char* kpe = (const char*)a.kpe;
-  size_t row0 = 0;
+  const int last = tok_end - 1 - s_tok0;  // >= 0: the stage holds at least one live key
   if (kPageClass == kPageBig) {
-    const int page = (s_tok0 < tok_end) ? ld_const(a.kv_indices, page_base + (s_tok0 >> sh)) : 0;
-    row0 = ((size_t)page << sh) + (s_tok0 & mask);
-  }
+    // the stage lies in one page; one scalar page lookup
+    const int page = ld_const(a.kv_indices, page_base + (s_tok0 >> sh));
+    const size_t row0 = ((size_t)page << sh) + (s_tok0 & mask);
+    const char* cbase = ckv + row0 * kCkvRowBytes;
+    const char* pbase = kpe + row0 * kKpeRowBytes;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int t = wave * 16 + i;
-    const int T = s_tok0 + t;
-    size_t row;
-    if (kPageClass == kPageBig) {
-      row = row0 + t;
-    } else {
-      const int page = (T < tok_end) ? ld_const(a.kv_indices, page_base + (T >> sh)) : 0;
-      row = ((size_t)page << sh) + (T & mask);
+    for (int i = 0; i < 2; ++i) {
+      const int grp = wave * 2 + i;
+      const int t = grp * 8 + (lane >> 3);
+      const int tc = min(t, last);
+      const uint32_t off = (uint32_t)(tc * kKpeRowBytes) + (uint32_t)(((lane & 7) ^ kpe_swz(t)) << 4);
+      dma16(pbase, off, lds_addr(st + kStageCkvBytes + grp * 1024));
     }
-    const char* src = (T < tok_end) ? ckv + row * kCkvRowBytes + ((lane ^ ckv_swz(t)) << 4)
-                                    : (const char*)g_zero_row + (lane << 4);
-    __builtin_amdgcn_global_load_lds(src, st + t * kCkvRowBytes, 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int t = wave * 16 + i;
+      const int tc = min(t, last);
+      const uint32_t off = (uint32_t)(tc * kCkvRowBytes) + (uint32_t)((lane ^ ckv_swz(t)) << 4);
+      dma16(cbase, off, lds_addr(st + t * kCkvRowBytes));
+    }
+    return;
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int grp = wave * 2 + i;
     const int t = grp * 8 + (lane >> 3);
     const int c = (lane & 7) ^ kpe_swz(t);
-    const int T = s_tok0 + t;
-    const int T0 = s_tok0 + grp * 8;
-    size_t row;
-    if (kPageClass == kPageBig) {
-      row = row0 + t;
-    } else if (kPageClass == kPageMid) {
-      const int page = (T0 < tok_end) ? ld_const(a.kv_indices, page_base + (T0 >> sh)) : 0;
-      row = ((size_t)page << sh) + (T & mask);
+    const int T = s_tok0 + min(t, last);
+    if (kPageClass == kPageMid) {
+      // the 8 keys of this load share one page (clamped keys included)
+      const int T0 = s_tok0 + min(grp * 8, last);
+      const int page = ld_const(a.kv_indices, page_base + (T0 >> sh));
+      const char* base = kpe + (((size_t)page << sh) + (T0 & mask)) * kKpeRowBytes;
+      const uint32_t off = (uint32_t)((T - T0) * kKpeRowBytes + (c << 4));
+      dma16(base, off, lds_addr(st + kStageCkvBytes + grp * 1024));
     } else {
       // one scalar page lookup per key, then each lane picks its key's page
       int page = 0;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int pj = (T0 + j < tok_end) ? ld_const(a.kv_indices, page_base + ((T0 + j) >> sh)) : 0;
+        const int Tj = s_tok0 + min(grp * 8 + j, last);
+        const int pj = ld_const(a.kv_indices, page_base + (Tj >> sh));
         page = ((lane >> 3) == j) ? pj : page;
       }
-      row = ((size_t)page << sh) + (T & mask);
+      // per-lane pages: a full per-lane address
+      const char* src = kpe + (((size_t)page << sh) + (T & mask)) * kKpeRowBytes + (c << 4);
+      dma16_v(src, lds_addr(st + kStageCkvBytes + grp * 1024));
     }
-    const char* src = (T < tok_end) ? kpe + row * kKpeRowBytes + (c << 4)
-                                    : (const char*)g_zero_row + ((lane & 7) << 4);
-    __builtin_amdgcn_global_load_lds(src, st + kStageCkvBytes + grp * 1024, 16, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int t = wave * 16 + i;
+    const int T = s_tok0 + min(t, last);
+    const int page = ld_const(a.kv_indices, page_base + (T >> sh));
+    const char* base = ckv + (((size_t)page << sh) + (T & mask)) * kCkvRowBytes;
+    dma16(base, (uint32_t)((lane ^ ckv_swz(t)) << 4), lds_addr(st + t * kCkvRowBytes));
   }
 }
 
@@ -277,15 +351,17 @@ __device__ __forceinline__ void wide_stage(const AttnArgs& a, const bf16x8 (&qf)
     const int tb = sub * 32;
     // S^T[32 keys x 32 rows] = K . Q^T over 576 dims
     f32x16 sacc = {};
+    auto kread = [&](int ks) -> bf16x8 {
+      return ks < 32 ? lds_read_b128(cur, kb[ks & 7] + 256 * (ks >> 3) + tb * kCkvRowBytes)
+                     : lds_read_b128(cur, pb[ks - 32] + tb * kKpeRowBytes);
+    };
+    bf16x8 k0 = kread(0), k1 = kread(1);
 #pragma unroll
-    for (int ks = 0; ks < 32; ++ks) {
-      const bf16x8 kf = lds_read_b128(cur, kb[ks & 7] + 256 * (ks >> 3) + tb * kCkvRowBytes);
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc, 0, 0, 0);
-    }
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8 kf = lds_read_b128(cur, pb[ks] + tb * kKpeRowBytes);
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[32 + ks], sacc, 0, 0, 0);
+    for (int ks = 0; ks < 36; ++ks) {
+      const bf16x8 k2 = (ks + 2 < 36) ? kread(ks + 2) : k1;
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[ks], sacc, 0, 0, 0);
+      k0 = k1;
+      k1 = k2;
     }
     // online softmax (base 2); lane holds keys 8(r/4) + 4g + r%4 of the sub-tile
     float sv[16];
@@ -303,12 +379,8 @@ __device__ __forceinline__ void wide_stage(const AttnArgs& a, const bf16x8 (&qf)
       const float m_new = fmaxf(st.m_run, mx);
       const float alpha = (st.m_run == kNegInf) ? 0.f : fast_exp2(st.m_run - m_new);
       st.l_run *= alpha;
-      // one column block at a time keeps the rescale's register peak small
 #pragma unroll
-      for (int cb = 0; cb < 16; ++cb) {
-        st.o[cb] *= alpha;
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      for (int cb = 0; cb < 16; ++cb) scale_acc<16>(st.o[cb], alpha);
       st.m_run = m_new;
     }
     const float mref = (st.m_run == kNegInf) ? 0.f : st.m_run;
@@ -320,16 +392,21 @@ __device__ __forceinline__ void wide_stage(const AttnArgs& a, const bf16x8 (&qf)
       pt[r >> 3][r & 7] = (__bf16)p;
     }
     // O^T[32 dims x 32 rows] += V^T[32 dims x 16 keys] . P^T[16 keys x 32 rows]
+    auto vread = [&](int j) -> bf16x8 {  // j = 2*cb + kk
+      const int cb = j >> 1, kk = j & 1;
+      const int imm = (tb + 16 * kk) * kCkvRowBytes + 256 * (cb >> 2);
+      const i16x4 v0 = lds_read_tr(cur, vb[cb & 3] + imm);
+      const i16x4 v1 = lds_read_tr(cur, vb[4 + (cb & 3)] + imm);
+      const i16x8 v = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      return __builtin_bit_cast(bf16x8, v);
+    };
+    bf16x8 v0 = vread(0), v1 = vread(1);
 #pragma unroll
-    for (int cb = 0; cb < 16; ++cb) {
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int imm = (tb + 16 * kk) * kCkvRowBytes + 256 * (cb >> 2);
-        const i16x4 v0 = lds_read_tr(cur, vb[cb & 3] + imm);
-        const i16x4 v1 = lds_read_tr(cur, vb[4 + (cb & 3)] + imm);
-        const i16x8 v = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-        st.o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v), pt[kk], st.o[cb], 0, 0, 0);
-      }
+    for (int j = 0; j < 32; ++j) {
+      const bf16x8 v2 = (j + 2 < 32) ? vread(j + 2) : v1;
+      st.o[j >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, pt[j & 1], st.o[j >> 1], 0, 0, 0);
+      v0 = v1;
+      v1 = v2;
     }
   }
 }
@@ -620,13 +697,18 @@ void mla_attn_kernel(AttnArgs a) {
 // out = sum_s w_s o_s / sum_s w_s with w_s = exp(lse_s - max lse), and
 // lse = max lse + ln sum w (the log-sum-exp identity).
 // ---------------------------------------------------------------------------
+constexpr int kCombineRows = 16;  // rows per combine workgroup (4 per wave)
+
 __global__ __launch_bounds__(256) void mla_combine_kernel(AttnArgs a) {
-  const SplitGroup grp = a.groups[blockIdx.x];
-  const int sub = threadIdx.x >> 6;
+  // blockIdx.x -> (group, 16-row chunk): chunks of a group are consecutive
+  const int chunks_per_group = a.rows_per_block / kCombineRows;
+  const int gi = blockIdx.x / chunks_per_group;
+  const int r0 = (blockIdx.x - gi * chunks_per_group) * kCombineRows;
+  const SplitGroup grp = a.groups[gi];
   const int d0 = (threadIdx.x & 63) * 8;
   const int H = a.num_heads;
   const int q_start = a.qo_indptr ? a.qo_indptr[grp.b] : grp.b;
-  for (int r = sub; r < grp.nrows; r += 4) {
+  for (int r = r0 + (threadIdx.x >> 6); r < min(grp.nrows, r0 + kCombineRows); r += 4) {
     float M = kNegInf;
     for (int s = 0; s < grp.nsplit; ++s)
       M = fmaxf(M, a.part_lse[(size_t)(grp.slot0 + s) * a.rows_per_block + r]);
@@ -689,7 +771,8 @@ hipError_t launch_attention(const AttnArgs& a, int tile_mode, int kv_fp8, hipStr
 
 hipError_t launch_combine(const AttnArgs& a, hipStream_t stream) {
   if (a.num_groups <= 0) return hipSuccess;
-  hipLaunchKernelGGL(mla_combine_kernel, dim3(a.num_groups), dim3(256), 0, stream, a);
+  const int chunks = a.rows_per_block / kCombineRows;
+  hipLaunchKernelGGL(mla_combine_kernel, dim3(a.num_groups * chunks), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
