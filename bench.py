@@ -178,6 +178,7 @@ def main():
                     help="replicate the cache pool until consecutive steps are this many bytes apart")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--tile-mode", type=int, default=0, help="0 = planner's choice; 1 wide, 2 narrow, 3 quad")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -204,7 +205,7 @@ def main():
     t_plan = time.perf_counter()
     plan = mla.mla_plan_create(kind, w.batch, w.num_heads, w.page_size, w.num_pages, w.kv_len, w.kv_indptr,
                                qo_indptr=w.qo_indptr if w.kind == "prefill" else None, kv_format=fmt,
-                               causal=w.causal)
+                               causal=w.causal, tile_mode=args.tile_mode)
     plan_ms = (time.perf_counter() - t_plan) * 1e3
     kv_indptr = w.kv_indptr.to(dev)
     kv_indices = w.kv_indices.to(dev)

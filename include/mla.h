@@ -63,12 +63,23 @@ typedef enum mla_kv_format { MLA_KV_BF16 = 0, MLA_KV_FP8_E4M3_T128 = 1 } mla_kv_
 
 typedef enum mla_kind { MLA_KIND_DECODE = 0, MLA_KIND_PREFILL = 1 } mla_kind;
 
-/* Tile modes of the attention kernel (0 lets the planner choose).
+/* Tile modes of the attention kernel (0 lets the planner choose: WIDE when
+ * some request holds at least 64 query rows (heads x query tokens), NARROW
+ * otherwise).
  *   MLA_TILE_WIDE:   a workgroup holds up to 128 query rows, 32 per wave, and
- *                    all four waves share each key tile (rows >= 64).
+ *                    all four waves share each key tile.
  *   MLA_TILE_NARROW: a workgroup holds up to 16 query rows and its four waves
- *                    split every key tile between them (few rows).          */
-typedef enum mla_tile_mode { MLA_TILE_AUTO = 0, MLA_TILE_WIDE = 1, MLA_TILE_NARROW = 2 } mla_tile_mode;
+ *                    split every key tile between them.
+ *   MLA_TILE_QUAD:   a workgroup holds 32 rows; its waves split each key tile
+ *                    for Q.K^T and the 512 output columns for P.V; up to four
+ *                    sibling workgroups on one XCD hold the other 32-row
+ *                    slices of the same rows and walk the same keys.       */
+typedef enum mla_tile_mode {
+  MLA_TILE_AUTO = 0,
+  MLA_TILE_WIDE = 1,
+  MLA_TILE_NARROW = 2,
+  MLA_TILE_QUAD = 3
+} mla_tile_mode;
 
 typedef struct mla_plan_desc {
   int32_t kind;          /* mla_kind                                                */
@@ -130,10 +141,13 @@ int32_t mla_plan_num_split_groups(const mla_plan* plan);
  * or the index of its partial-result slot.                               */
 mla_status mla_plan_get_work_items(const mla_plan* plan, int32_t* items_host, size_t capacity);
 
-/* Grid of the attention kernel: workgroup w processes work items
- * wg_ptr[w] .. wg_ptr[w+1]-1 in order.  mla_plan_get_workgroup_ptr copies
+/* Work lists of the attention kernel: list w holds work items
+ * wg_ptr[w] .. wg_ptr[w+1]-1, processed in order by one workgroup (by each
+ * of mla_plan_group_size sibling workgroups in the quad tile mode, sibling r
+ * taking rows 32r..32r+31 of every item).  mla_plan_get_workgroup_ptr copies
  * the [num_workgroups + 1] int32 offsets to host memory (diagnostics).    */
 int32_t mla_plan_num_workgroups(const mla_plan* plan);
+int32_t mla_plan_group_size(const mla_plan* plan);
 mla_status mla_plan_get_workgroup_ptr(const mla_plan* plan, int32_t* wg_ptr_host, size_t capacity);
 
 /* One asynchronous host-to-device copy of the plan's work list into the

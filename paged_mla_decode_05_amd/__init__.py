@@ -27,4 +27,5 @@ from ._binding import (  # noqa: F401
     MLA_TILE_AUTO,
     MLA_TILE_WIDE,
     MLA_TILE_NARROW,
+    MLA_TILE_QUAD,
 )

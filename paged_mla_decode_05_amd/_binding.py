@@ -21,6 +21,7 @@ MLA_DTYPE_FP32 = 1
 MLA_TILE_AUTO = 0
 MLA_TILE_WIDE = 1
 MLA_TILE_NARROW = 2
+MLA_TILE_QUAD = 3
 
 _DIM_CKV = 512
 _DIM_KPE = 64
@@ -75,6 +76,8 @@ def load_library():
         L.mla_plan_get_work_items.restype = i32
         L.mla_plan_num_workgroups.argtypes = [vp]
         L.mla_plan_num_workgroups.restype = i32
+        L.mla_plan_group_size.argtypes = [vp]
+        L.mla_plan_group_size.restype = i32
         L.mla_plan_get_workgroup_ptr.argtypes = [vp, pi32, sz]
         L.mla_plan_get_workgroup_ptr.restype = i32
         L.mla_plan_upload.argtypes = [vp, vp, sz, vp]
@@ -155,6 +158,10 @@ class Plan:
         _check(load_library().mla_plan_get_work_items(
             self._h, ctypes.cast(buf.data_ptr(), ctypes.POINTER(ctypes.c_int32)), n), "mla_plan_get_work_items")
         return buf[:n]
+
+    @property
+    def group_size(self) -> int:
+        return int(load_library().mla_plan_group_size(self._h))
 
     def workgroup_ptr(self) -> torch.Tensor:
         n = int(load_library().mla_plan_num_workgroups(self._h))

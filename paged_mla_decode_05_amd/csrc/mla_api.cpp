@@ -27,9 +27,12 @@ using mla::WorkItem;
 
 struct mla_plan {
   mla_plan_desc d;
-  int32_t tile_mode = 0;       // resolved: MLA_TILE_WIDE or MLA_TILE_NARROW
+  int32_t tile_mode = 0;       // resolved: MLA_TILE_WIDE, _NARROW or _QUAD
   int32_t rows_per_block = 0;  // rows one workgroup holds
-  int32_t num_wgs = 0;         // grid size of the attention kernel
+  int32_t num_wgs = 0;         // work lists (per workgroup; per sibling group in quad mode)
+  int32_t grid = 0;            // workgroups launched
+  int32_t group_size = 1;      // quad mode: sibling workgroups per work list
+  int32_t xcd_map = 0;         // quad mode: siblings share blockIdx.x mod 8
   int32_t num_slots = 0;       // partial-result slots
   std::vector<int32_t> wg_ptr;  // [num_wgs + 1] item range of each workgroup
   std::vector<WorkItem> items;
@@ -122,6 +125,7 @@ void pack_units(mla_plan* p, const std::vector<Unit>& units, int64_t budget) {
   }
   if (wg_open()) close_wg();
   p->num_wgs = (int32_t)p->wg_ptr.size() - 1;
+  p->grid = p->num_wgs;
 }
 
 mla_status build_schedule(mla_plan* p, const std::vector<int32_t>& kv_len,
@@ -131,9 +135,28 @@ mla_status build_schedule(mla_plan* p, const std::vector<int32_t>& kv_len,
   int64_t max_rows = 0;
   for (int32_t b = 0; b < d.batch; ++b) max_rows = std::max<int64_t>(max_rows, (int64_t)q_len[b] * H);
   int32_t mode = d.tile_mode;
-  if (mode == MLA_TILE_AUTO) mode = (max_rows >= 64) ? MLA_TILE_WIDE : MLA_TILE_NARROW;
+  // Automatic choice: the 128-row tile once a request holds at least half
+  // of one (its key stream then feeds 4 waves' MFMAs from one LDS copy),
+  // otherwise the 16-row tile, which splits keys across waves.
+  if (mode == MLA_TILE_AUTO) mode = (max_rows >= mla::kWideRows / 2) ? MLA_TILE_WIDE : MLA_TILE_NARROW;
   p->tile_mode = mode;
-  const int32_t RB = (mode == MLA_TILE_WIDE) ? mla::kWideRows : mla::kNarrowRows;
+  int32_t RB = (mode == MLA_TILE_WIDE) ? mla::kWideRows : mla::kNarrowRows;
+  int64_t lists = std::max<int32_t>(1, num_cus);
+  p->group_size = 1;
+  p->xcd_map = 0;
+  if (mode == MLA_TILE_QUAD) {
+    // G sibling workgroups (one 32-row slice each) per row group; siblings
+    // share an XCD when the grid is a multiple of 8 G.
+    const int32_t G = std::min<int32_t>(4, std::max<int32_t>(1, (H + mla::kQuadRowsPerWg - 1) / mla::kQuadRowsPerWg));
+    p->group_size = G;
+    RB = G * mla::kQuadRowsPerWg;
+    if (num_cus >= 8 * G) {
+      lists = (num_cus / (8 * G)) * 8;
+      p->xcd_map = 1;
+    } else {
+      lists = std::max<int32_t>(1, num_cus / G);
+    }
+  }
   p->rows_per_block = RB;
 
   // Units: (request, row block) with the keys the block can see.
@@ -153,7 +176,7 @@ mla_status build_schedule(mla_plan* p, const std::vector<int32_t>& kv_len,
 
   int64_t total = 0;
   for (const Unit& u : units) total += u.vis + kItemOverhead;
-  const int64_t cus = std::max<int32_t>(1, num_cus);
+  const int64_t cus = lists;
   // Smallest per-workgroup budget whose packing needs at most `cus`
   // workgroups: one persistent workgroup per compute unit.
   int64_t budget = std::max<int64_t>((total + cus - 1) / cus, kItemOverhead + kMinChunk);
@@ -161,6 +184,9 @@ mla_status build_schedule(mla_plan* p, const std::vector<int32_t>& kv_len,
     pack_units(p, units, budget);
     if (p->num_wgs <= cus) break;
     budget += std::max<int64_t>(16, budget / 256);
+  }
+  if (p->tile_mode == MLA_TILE_QUAD) {
+    p->grid = p->xcd_map ? (int32_t)cus * p->group_size : p->num_wgs * p->group_size;
   }
 
   // Workspace layout: [wg_ptr | items | groups] [part_lse] [part_o]
@@ -204,7 +230,7 @@ mla_status mla_plan_create(mla_plan** out, const mla_plan_desc* d, const int32_t
   if (!is_pow2(d->page_size) || d->page_size > 4096) return MLA_ERR_UNSUPPORTED;
   if (d->kv_format != MLA_KV_BF16 && d->kv_format != MLA_KV_FP8_E4M3_T128) return MLA_ERR_UNSUPPORTED;
   if (d->kv_format == MLA_KV_FP8_E4M3_T128 && d->kind != MLA_KIND_DECODE) return MLA_ERR_UNSUPPORTED;
-  if (d->tile_mode < MLA_TILE_AUTO || d->tile_mode > MLA_TILE_NARROW) return MLA_ERR_INVALID_ARGUMENT;
+  if (d->tile_mode < MLA_TILE_AUTO || d->tile_mode > MLA_TILE_QUAD) return MLA_ERR_INVALID_ARGUMENT;
   if (d->max_splits < 0 || d->force_splits < 0 || d->num_cus < 0) return MLA_ERR_INVALID_ARGUMENT;
   if (d->batch > 0 && !kv_indptr_host) return MLA_ERR_INVALID_ARGUMENT;
   if (d->kind == MLA_KIND_PREFILL && d->batch > 0 && !qo_indptr_host) return MLA_ERR_INVALID_ARGUMENT;
@@ -255,6 +281,7 @@ int32_t mla_plan_num_work_items(const mla_plan* p) { return p ? (int32_t)p->item
 int32_t mla_plan_num_split_groups(const mla_plan* p) { return p ? (int32_t)p->groups.size() : -1; }
 
 int32_t mla_plan_num_workgroups(const mla_plan* p) { return p ? p->num_wgs : -1; }
+int32_t mla_plan_group_size(const mla_plan* p) { return p ? p->group_size : -1; }
 
 mla_status mla_plan_get_workgroup_ptr(const mla_plan* p, int32_t* out, size_t capacity) {
   if (!p || !out || capacity < p->wg_ptr.size()) return MLA_ERR_INVALID_ARGUMENT;
@@ -325,6 +352,9 @@ mla_status run(const mla_plan* p, int32_t want_kind, int32_t want_format, const 
   a.causal = (want_kind == MLA_KIND_PREFILL) ? p->d.causal : 0;
   a.rows_per_block = p->rows_per_block;
   a.num_wgs = p->num_wgs;
+  a.grid = p->grid;
+  a.group_size = p->group_size;
+  a.xcd_map = p->xcd_map;
   a.num_items = (int32_t)p->items.size();
   a.num_groups = (int32_t)p->groups.size();
   hipEvent_t ev0 = t_ev_before, ev1 = t_ev_after;

@@ -193,81 +193,115 @@ __device__ __forceinline__ int ld_const(const int32_t* p, int i) {
 constexpr int kPageBig = 0, kPageMid = 1, kPageSmall = 2;
 
 // ---------------------------------------------------------------------------
-// Gather loader (bf16 caches): stage of keys [s_tok0, s_tok0 + 64) of a
-// request whose page list starts at kv_indices[page_base], into LDS stage
-// `st`.  18 direct-to-LDS loads per wave (the two per-lane kpe loads first).
-// Each load's address is a uniform
-// (scalar) base plus a 32-bit per-lane offset.  Keys at or past tok_end
-// re-read the chunk's last key (finite data; the softmax masks them out), so
-// nothing outside the request's live keys is ever read.
+// Gather loader (bf16 caches).  A stage is keys [s_tok0, s_tok0 + 64) of a
+// request whose page list starts at kv_indices[page_base]; each wave moves
+// 18 slices of it into LDS with 16-byte-per-lane direct loads: slices 0..15
+// are the 1 KB ckv rows 16w..16w+15, slices 16..17 the kpe rows of 8 keys
+// each.  begin() does the page lookups (scalar loads) and issue(i) one
+// slice, so the callers can spread the 18 loads through their MFMA work:
+// issued back to back they stall the wave at the address unit.  Every
+// address is a uniform (scalar) base plus a 32-bit lane offset.  Keys at or
+// past tok_end re-read the chunk's last key (finite data; the softmax masks
+// them), so nothing outside the request's live keys is ever read.
 // ---------------------------------------------------------------------------
+constexpr int kDmaPerWave = 18;
+
 template <int kPageClass>
-__device__ __forceinline__ void issue_stage_bf16(const AttnArgs& a, LDS_AS char* st, int page_base,
-                                                 int s_tok0, int tok_end, int wave, int) {
-  const int lane = lane_here();
-  const int sh = a.page_shift;
-  const int mask = (1 << sh) - 1;
-  const char* ckv = (const char*)a.ckv;
-  const char* kpe = (const char*)a.kpe;
-  const int last = tok_end - 1 - s_tok0;  // >= 0: the stage holds at least one live key
-  if (kPageClass == kPageBig) {
-    // the stage lies in one page; one scalar page lookup
-    const int page = ld_const(a.kv_indices, page_base + (s_tok0 >> sh));
-    const size_t row0 = ((size_t)page << sh) + (s_tok0 & mask);
-    const char* cbase = ckv + row0 * kCkvRowBytes;
-    const char* pbase = kpe + row0 * kKpeRowBytes;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int grp = wave * 2 + i;
-      const int t = grp * 8 + (lane >> 3);
-      const int tc = min(t, last);
-      const uint32_t off = (uint32_t)(tc * kKpeRowBytes) + (uint32_t)(((lane & 7) ^ kpe_swz(t)) << 4);
-      dma16(pbase, off, lds_addr(st + kStageCkvBytes + grp * 1024));
+struct StageLoader {
+  const char* ckv_row[16];  // kPageBig: [0] is the stage's first row; else one per ckv slice
+  const char* kpe_base[2];
+  int kpe_t0[2];            // kPageMid: first (clamped) key of the kpe slice, relative to the stage
+  int kpe_page[2];          // kPageSmall: this lane's page
+  int last;                 // last live key of the stage, relative to s_tok0
+  int s_tok0;
+  LDS_AS char* st;
+
+  __device__ __forceinline__ void begin(const AttnArgs& a, LDS_AS char* stage, int page_base, int tok0,
+                                        int tok_end, int wave) {
+    const int sh = a.page_shift;
+    const int mask = (1 << sh) - 1;
+    const char* ckv = (const char*)a.ckv;
+    const char* kpe = (const char*)a.kpe;
+    st = stage;
+    s_tok0 = tok0;
+    last = tok_end - 1 - tok0;
+    if (kPageClass == kPageBig) {
+      const int page = ld_const(a.kv_indices, page_base + (tok0 >> sh));
+      const size_t row0 = ((size_t)page << sh) + (tok0 & mask);
+      ckv_row[0] = ckv + row0 * kCkvRowBytes;
+      kpe_base[0] = kpe + row0 * kKpeRowBytes;
+      return;
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int t = wave * 16 + i;
-      const int tc = min(t, last);
-      const uint32_t off = (uint32_t)(tc * kCkvRowBytes) + (uint32_t)((lane ^ ckv_swz(t)) << 4);
-      dma16(cbase, off, lds_addr(st + t * kCkvRowBytes));
+      const int T = tok0 + min(wave * 16 + i, last);
+      const int page = ld_const(a.kv_indices, page_base + (T >> sh));
+      ckv_row[i] = ckv + (((size_t)page << sh) + (T & mask)) * kCkvRowBytes;
     }
-    return;
-  }
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int grp = wave * 2 + i;
-    const int t = grp * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ kpe_swz(t);
-    const int T = s_tok0 + min(t, last);
-    if (kPageClass == kPageMid) {
-      // the 8 keys of this load share one page (clamped keys included)
-      const int T0 = s_tok0 + min(grp * 8, last);
-      const int page = ld_const(a.kv_indices, page_base + (T0 >> sh));
-      const char* base = kpe + (((size_t)page << sh) + (T0 & mask)) * kKpeRowBytes;
-      const uint32_t off = (uint32_t)((T - T0) * kKpeRowBytes + (c << 4));
-      dma16(base, off, lds_addr(st + kStageCkvBytes + grp * 1024));
-    } else {
-      // one scalar page lookup per key, then each lane picks its key's page
-      int page = 0;
+    for (int i = 0; i < 2; ++i) {
+      const int grp = wave * 2 + i;
+      if (kPageClass == kPageMid) {
+        // the 8 keys of this slice share one page (clamped keys included)
+        const int T0 = tok0 + min(grp * 8, last);
+        const int page = ld_const(a.kv_indices, page_base + (T0 >> sh));
+        kpe_base[i] = kpe + (((size_t)page << sh) + (T0 & mask)) * kKpeRowBytes;
+        kpe_t0[i] = T0 - tok0;
+      } else {
+        // one scalar page lookup per key, then each lane keeps its key's page
+        const int lane = lane_here();
+        int page = 0;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int Tj = s_tok0 + min(grp * 8 + j, last);
-        const int pj = ld_const(a.kv_indices, page_base + (Tj >> sh));
-        page = ((lane >> 3) == j) ? pj : page;
+        for (int j = 0; j < 8; ++j) {
+          const int Tj = tok0 + min(grp * 8 + j, last);
+          const int pj = ld_const(a.kv_indices, page_base + (Tj >> sh));
+          page = ((lane >> 3) == j) ? pj : page;
+        }
+        kpe_page[i] = page;
       }
-      // per-lane pages: a full per-lane address
-      const char* src = kpe + (((size_t)page << sh) + (T & mask)) * kKpeRowBytes + (c << 4);
-      dma16_v(src, lds_addr(st + kStageCkvBytes + grp * 1024));
     }
   }
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int t = wave * 16 + i;
-    const int T = s_tok0 + min(t, last);
-    const int page = ld_const(a.kv_indices, page_base + (T >> sh));
-    const char* base = ckv + (((size_t)page << sh) + (T & mask)) * kCkvRowBytes;
-    dma16(base, (uint32_t)((lane ^ ckv_swz(t)) << 4), lds_addr(st + t * kCkvRowBytes));
+
+  __device__ __forceinline__ void issue(const AttnArgs& a, int i, int wave) {
+    const int lane = lane_here();
+    if (i < 16) {
+      const int t = wave * 16 + i;
+      const uint32_t swz_off = (uint32_t)((lane ^ ckv_swz(t)) << 4);
+      if (kPageClass == kPageBig) {
+        dma16(ckv_row[0], (uint32_t)(min(t, last) * kCkvRowBytes) + swz_off, lds_addr(st + t * kCkvRowBytes));
+      } else {
+        dma16(ckv_row[i], swz_off, lds_addr(st + t * kCkvRowBytes));
+      }
+      return;
+    }
+    const int k = i - 16;
+    const int grp = wave * 2 + k;
+    const int t = grp * 8 + (lane >> 3);
+    const int tc = min(t, last);
+    const int c = (lane & 7) ^ kpe_swz(t);
+    LDS_AS char* dst = st + kStageCkvBytes + grp * 1024;
+    if (kPageClass == kPageBig) {
+      dma16(kpe_base[0], (uint32_t)(tc * kKpeRowBytes + (c << 4)), lds_addr(dst));
+    } else if (kPageClass == kPageMid) {
+      dma16(kpe_base[k], (uint32_t)((tc - kpe_t0[k]) * kKpeRowBytes + (c << 4)), lds_addr(dst));
+    } else {
+      const int sh = a.page_shift;
+      const int T = s_tok0 + tc;
+      const char* src = (const char*)a.kpe + (((size_t)kpe_page[k] << sh) + (T & ((1 << sh) - 1))) * kKpeRowBytes +
+                        (c << 4);
+      dma16_v(src, lds_addr(dst));
+    }
   }
+};
+
+// The whole stage at once (used where nothing else is in flight).
+template <int kPageClass>
+__device__ __forceinline__ void issue_stage_bf16(const AttnArgs& a, LDS_AS char* st, int page_base,
+                                                 int s_tok0, int tok_end, int wave, int) {
+  StageLoader<kPageClass> ld;
+  ld.begin(a, st, page_base, s_tok0, tok_end, wave);
+#pragma unroll
+  for (int i = 0; i < kDmaPerWave; ++i) ld.issue(a, i, wave);
 }
 
 // ---------------------------------------------------------------------------
@@ -342,10 +376,11 @@ struct WideState {
   float l_run;    // running sum of this lane's keys
 };
 
+template <int kPC>
 __device__ __forceinline__ void wide_stage(const AttnArgs& a, const bf16x8 (&qf)[36], WideState& st,
                                            const LDS_AS char* __restrict__ cur, int stage_tok, int bound,
                                            const int (&kb)[8], const int (&pb)[4], const int (&vb)[8],
-                                           int g) {
+                                           int g, StageLoader<kPC>& ld, bool prefetch, int wave) {
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub) {
     const int tb = sub * 32;
@@ -358,6 +393,7 @@ __device__ __forceinline__ void wide_stage(const AttnArgs& a, const bf16x8 (&qf)
     bf16x8 k0 = kread(0), k1 = kread(1);
 #pragma unroll
     for (int ks = 0; ks < 36; ++ks) {
+      if (prefetch && (ks & 3) == 0) ld.issue(a, sub * 9 + (ks >> 2), wave);  // 9 slices per sub-tile
       const bf16x8 k2 = (ks + 2 < 36) ? kread(ks + 2) : k1;
       sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[ks], sacc, 0, 0, 0);
       k0 = k1;
@@ -417,8 +453,9 @@ __device__ __forceinline__ void wide_body(const AttnArgs& a, const bf16x8 (&qf)[
                                           bool prefetch, int page_base, int next_tok, int tok_end,
                                           int stage_tok, int bound, const int (&kb)[8], const int (&pb)[4],
                                           const int (&vb)[8], int wave, int lane) {
-  if (prefetch) issue_stage_bf16<kPC>(a, nxt, page_base, next_tok, tok_end, wave, lane);
-  wide_stage(a, qf, st, cur, stage_tok, bound, kb, pb, vb, lane >> 5);
+  StageLoader<kPC> ld;
+  if (prefetch) ld.begin(a, nxt, page_base, next_tok, tok_end, wave);
+  wide_stage<kPC>(a, qf, st, cur, stage_tok, bound, kb, pb, vb, lane >> 5, ld, prefetch, wave);
 }
 
 template <int kPC, bool kFp8>
@@ -511,20 +548,17 @@ __device__ __forceinline__ void narrow_body(const AttnArgs& a, const bf16x8 (&qf
                                             bool prefetch, int page_base, int next_tok, int tok_end,
                                             int stage_tok, int bound, const int (&kb)[4], const int (&pb)[2],
                                             const int (&vb)[8], int wave, int lane) {
-  if (prefetch) issue_stage_bf16<kPC>(a, nxt, page_base, next_tok, tok_end, wave, lane);
+  StageLoader<kPC> ld;
+  if (prefetch) ld.begin(a, nxt, page_base, next_tok, tok_end, wave);
   const int g4 = lane >> 4;
   const int tb = wave * 16;
   // S^T[16 keys x 16 rows]
   f32x4 sacc = {};
 #pragma unroll
-  for (int ks = 0; ks < 16; ++ks) {
-    const bf16x8 kf = lds_read_b128(cur, kb[ks & 3] + 256 * (ks >> 2));
+  for (int ks = 0; ks < 18; ++ks) {
+    if (prefetch) ld.issue(a, ks, wave);  // one prefetch slice per k-step
+    const bf16x8 kf = ks < 16 ? lds_read_b128(cur, kb[ks & 3] + 256 * (ks >> 2)) : lds_read_b128(cur, pb[ks - 16]);
     sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], sacc, 0, 0, 0);
-  }
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    const bf16x8 kf = lds_read_b128(cur, pb[ks]);
-    sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[16 + ks], sacc, 0, 0, 0);
   }
   float sv[4];
   float mx = kNegInf;
@@ -664,6 +698,287 @@ __device__ void narrow_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* 
   __syncthreads();  // merge buffer overlaps stage 0 of the next item
 }
 
+// ---------------------------------------------------------------------------
+// QUAD mode: a workgroup owns 32 rows.  Up to four sibling workgroups (same
+// XCD, identical key ranges) hold the four 32-row slices of a row group, so
+// the key stream is fetched once and re-served from L2.  Inside a workgroup
+// the four waves split each 64-key stage for S = Q.K^T (wave w: keys
+// [16w, 16w+16), all 32 rows) and split the 512 output columns for P.V
+// (wave w: dims [128w, 128w+128), all 32 rows, all 64 keys); P goes through
+// LDS.  All MFMAs are mfma_f32_16x16x32_bf16.
+//
+// The row max is shared: every wave computes P against the same running
+// reference m, raised only when some wave's tile max passes m + kQuadSlack
+// (log2 units).  Until then P <= 2^kQuadSlack, far inside bf16/fp32 range,
+// and the exact softmax is unchanged.  The check reads all waves' tile
+// maxima after the barrier that publishes P, so every wave takes the same
+// branch; the raise path rescales O and l, recomputes P and re-publishes.
+// ---------------------------------------------------------------------------
+constexpr int kQuadRows = 32;
+constexpr int kPRowBytes = 64 * 2 + 16;                       // P row: 64 keys bf16 + pad
+constexpr int kPBufOff = 2 * kStageBytes;                      // after the two stages
+constexpr int kTmaxOff = kPBufOff + kQuadRows * kPRowBytes;    // [4 waves][32 rows] float
+constexpr int kQuadLdsBytes = kTmaxOff + 4 * kQuadRows * 4;
+static_assert(kQuadLdsBytes <= 160 * 1024, "quad-mode LDS budget");
+constexpr float kQuadSlack = 64.0f;
+
+struct QuadState {
+  f32x4 o[8][2];  // O^T tiles [col tile][row tile]: lane holds row 16t+n, dims 128w+16c+4g4+r
+  float m[2];     // running reference max of rows n and 16+n (log2 units)
+  float l[2];     // sum of P over this lane's keys, rows n and 16+n
+};
+
+__device__ __forceinline__ float max_xor16_32(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+
+// P for this lane's 2 x 4 (row, key) values against reference m; writes them
+// (bf16) to the P buffer and returns the fp32 values.
+__device__ __forceinline__ void quad_write_p(LDS_AS char* __restrict__ pbuf, const float (&sv)[2][4],
+                                             const float (&m)[2], float (&p)[2][4], int wave, int lane) {
+  const int g4 = lane >> 4, n = lane & 15;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const float mref = (m[t] == kNegInf) ? 0.f : m[t];
+    i16x4 h;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      p[t][r] = fast_exp2(sv[t][r] - mref);
+      h[r] = __builtin_bit_cast(short, (__bf16)p[t][r]);
+    }
+    *(LDS_AS i16x4*)(pbuf + (16 * t + n) * kPRowBytes + (16 * wave + 4 * g4) * 2) = h;
+  }
+}
+
+template <int kPC>
+__device__ __forceinline__ void quad_body(const AttnArgs& a, const bf16x8 (&qf)[2][18], QuadState& st,
+                                          const LDS_AS char* __restrict__ cur, LDS_AS char* __restrict__ nxt,
+                                          LDS_AS char* __restrict__ scr, bool prefetch, int page_base,
+                                          int next_tok, int tok_end, int stage_tok, const int (&bound)[2],
+                                          const int (&kb)[4], const int (&pb)[2], const int (&vb)[2],
+                                          const int (&vx)[2], int wave, int lane) {
+  StageLoader<kPC> ld;
+  if (prefetch) ld.begin(a, nxt, page_base, next_tok, tok_end, wave);
+  const int g4 = lane >> 4, n = lane & 15;
+  LDS_AS char* pbuf = scr;
+  LDS_AS float* tmax = (LDS_AS float*)(scr + (kTmaxOff - kPBufOff));
+
+  // S^T tiles [16 keys x 16 rows] for row tiles 0 and 1; the K fragment is shared
+  f32x4 sacc[2] = {f32x4{}, f32x4{}};
+  auto kread = [&](int ks) -> bf16x8 {
+    return ks < 16 ? lds_read_b128(cur, kb[ks & 3] + 256 * (ks >> 2)) : lds_read_b128(cur, pb[ks - 16]);
+  };
+  bf16x8 k0 = kread(0), k1 = kread(1);
+#pragma unroll
+  for (int ks = 0; ks < 18; ++ks) {
+    if (prefetch) ld.issue(a, ks, wave);  // one prefetch slice per k-step
+    const bf16x8 k2 = (ks + 2 < 18) ? kread(ks + 2) : k1;
+    sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[0][ks], sacc[0], 0, 0, 0);
+    sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[1][ks], sacc[1], 0, 0, 0);
+    k0 = k1;
+    k1 = k2;
+  }
+  // scale, mask, tile max over this wave's 16 keys
+  float sv[2][4], tm[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    tm[t] = kNegInf;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tok = stage_tok + 16 * wave + 4 * g4 + r;
+      const float x = sacc[t][r] * a.scale_log2;
+      sv[t][r] = tok < bound[t] ? x : kNegInf;
+      tm[t] = fmaxf(tm[t], sv[t][r]);
+    }
+    tm[t] = max_xor16_32(tm[t]);
+  }
+  float p[2][4];
+  quad_write_p(pbuf, sv, st.m, p, wave, lane);
+  if (g4 == 0) {
+    tmax[wave * kQuadRows + n] = tm[0];
+    tmax[wave * kQuadRows + 16 + n] = tm[1];
+  }
+  __syncthreads();  // P and the tile maxima of all waves are published
+  float smax[2];
+  bool need = false;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    smax[t] = fmaxf(fmaxf(tmax[16 * t + n], tmax[kQuadRows + 16 * t + n]),
+                    fmaxf(tmax[2 * kQuadRows + 16 * t + n], tmax[3 * kQuadRows + 16 * t + n]));
+    need |= smax[t] > st.m[t] + kQuadSlack;
+  }
+  if (__builtin_amdgcn_ballot_w64(need) != 0) {  // same decision in every wave
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const float m_new = fmaxf(st.m[t], smax[t]);
+      const float alpha = (st.m[t] == kNegInf) ? 0.f : fast_exp2(st.m[t] - m_new);
+      st.l[t] *= alpha;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) scale_acc<4>(st.o[c][t], alpha);
+      st.m[t] = m_new;
+    }
+    // nobody has read P yet (only the tile maxima): rewrite it, publish again
+    quad_write_p(pbuf, sv, st.m, p, wave, lane);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int t = 0; t < 2; ++t) st.l[t] += (p[t][0] + p[t][1]) + (p[t][2] + p[t][3]);
+
+  // O^T[128 dims x 32 rows] += V^T[128 dims x 64 keys] . P^T[64 keys x 32 rows]
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    bf16x8 pt[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      pt[t] = lds_read_b128(pbuf, (16 * t + n) * kPRowBytes + (32 * kk + 8 * g4) * 2);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      // keys 32kk + 8g4 + 0..3 and +4..7 of dims 128w + 16c + (lane & 15)
+      const int cx0 = (32 * c) ^ vx[0];
+      const int cx1 = (32 * c) ^ vx[1];
+      const i16x4 v0 = lds_read_tr(cur, vb[0] + cx0 + 32 * kk * kCkvRowBytes);
+      const i16x4 v1 = lds_read_tr(cur, vb[1] + cx1 + 32 * kk * kCkvRowBytes);
+      const i16x8 v = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      const bf16x8 vf = __builtin_bit_cast(bf16x8, v);
+      st.o[c][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pt[0], st.o[c][0], 0, 0, 0);
+      st.o[c][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pt[1], st.o[c][1], 0, 0, 0);
+    }
+  }
+}
+
+template <int kPC, bool kFp8>
+__device__ void quad_item(const AttnArgs& a, const WorkItem& it, int role, LDS_AS char* smem, int wave,
+                          int lane) {
+  const int g4 = lane >> 4, n = lane & 15;
+  const int rbase = kQuadRows * role;  // this workgroup's rows within the item's row group
+  RowInfo ri[2];
+  int bound[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    ri[t] = row_info(a, it, rbase + 16 * t + n);
+    bound[t] = row_key_bound(a, it, ri[t]);
+  }
+  bf16x8 qf[2][18];
+  {
+    const bf16x8 z = {};
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const __bf16* qn = (const __bf16*)a.q_nope + ri[t].qrow * kDimCkv + 8 * g4;
+      const __bf16* qp = (const __bf16*)a.q_pe + ri[t].qrow * kDimKpe + 8 * g4;
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) qf[t][ks] = ri[t].ok ? *(const bf16x8*)(qn + 32 * ks) : z;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) qf[t][16 + ks] = ri[t].ok ? *(const bf16x8*)(qp + 32 * ks) : z;
+    }
+  }
+  // LDS base offsets: K reads (as in the narrow mode), V^T reads
+  int kb[4], pb[2], vb[2], vx[2];
+  {
+    const int t = wave * 16 + n;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) kb[k] = ckv_off(t, 4 * k + g4);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) pb[k] = kpe_off(t, 4 * k + g4);
+    const int q = (lane & 15) >> 2;
+    const int x = (lane & 3) >> 1;
+    const int w8 = (lane & 1) ? 8 : 0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = 8 * g4 + q + 4 * h;    // key row within a 32-key half (mod 16 fixes the swizzle)
+      const int sw = ckv_swz(row);
+      vb[h] = row * kCkvRowBytes + 256 * wave + ((x ^ (sw & 1)) << 4) + w8;
+      vx[h] = (sw & 14) << 4;                 // chunk 2c of column tile c lands at (2c ^ (sw & 14))
+    }
+  }
+
+  QuadState st;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    st.o[c][0] = f32x4{};
+    st.o[c][1] = f32x4{};
+  }
+  st.m[0] = st.m[1] = kNegInf;
+  st.l[0] = st.l[1] = 0.f;
+
+  LDS_AS char* scr = smem + kPBufOff;
+  const int page_base = ld_const(a.kv_indptr, it.b);
+  const int nstage = (it.tok1 - it.tok0 + kStageTokens - 1) / kStageTokens;
+  if (nstage > 0) issue_stage_bf16<kPC>(a, smem, page_base, it.tok0, it.tok1, wave, lane);
+  for (int s = 0; s < nstage; ++s) {
+    wait_vmcnt<0>();
+    __syncthreads();  // stage s landed; every wave is done with stage s-1
+    quad_body<kPC>(a, qf, st, smem + (s & 1) * kStageBytes, smem + ((s + 1) & 1) * kStageBytes, scr,
+                   s + 1 < nstage, page_base, it.tok0 + (s + 1) * kStageTokens, it.tok1,
+                   it.tok0 + s * kStageTokens, bound, kb, pb, vb, vx, wave, lane);
+  }
+
+  // row sums: this lane's keys -> this wave's keys -> all waves
+  LDS_AS float* lsum = (LDS_AS float*)(smem + kTmaxOff);
+  float lw[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    lw[t] = st.l[t] + __shfl_xor(st.l[t], 16);
+    lw[t] += __shfl_xor(lw[t], 32);
+  }
+  __syncthreads();  // the last stage's tile maxima have been read
+  if (g4 == 0) {
+    lsum[wave * kQuadRows + n] = lw[0];
+    lsum[wave * kQuadRows + 16 + n] = lw[1];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int r = 16 * t + n;
+    const float L = (lsum[r] + lsum[kQuadRows + r]) + (lsum[2 * kQuadRows + r] + lsum[3 * kQuadRows + r]);
+    const bool empty = !(L > 0.f);
+    const float inv = empty ? 0.f : 1.f / L;
+    if (ri[t].ok) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) store4(a, it, ri[t], rbase + r, 128 * wave + 16 * c + 4 * g4, st.o[c][t] * inv);
+      if (wave == 0 && g4 == 0) store_lse(a, it, ri[t], rbase + r, empty ? kNegInf : (st.m[t] + __log2f(L)) * kLn2);
+    }
+  }
+  __syncthreads();  // LDS is reused by the next item
+}
+
+template <int kPC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mla_attn_quad_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem_raw[kQuadLdsBytes];
+  LDS_AS char* smem = (LDS_AS char*)smem_raw;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  // workgroup -> (virtual unit, role); siblings of a unit share blockIdx.x mod 8 (one XCD)
+  const int G = a.group_size;
+  int vcu, role;
+  if (a.xcd_map) {
+    const int x = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    vcu = x + 8 * (slot / G);
+    role = slot - (slot / G) * G;
+  } else {
+    vcu = blockIdx.x / G;
+    role = blockIdx.x - vcu * G;
+  }
+  if (vcu >= a.num_wgs) return;
+  const int i0 = ld_const(a.wg_ptr, vcu);
+  const int i1 = ld_const(a.wg_ptr, vcu + 1);
+  for (int i = i0; i < i1; ++i) {
+    const int32_t* ip = (const int32_t*)(a.items + i);
+    WorkItem it;
+    it.b = ld_const(ip, 0);
+    it.row0 = ld_const(ip, 1);
+    it.nrows = ld_const(ip, 2);
+    it.tok0 = ld_const(ip, 3);
+    it.tok1 = ld_const(ip, 4);
+    it.kv_len = ld_const(ip, 5);
+    it.q_len = ld_const(ip, 6);
+    it.slot = ld_const(ip, 7);
+    if (kQuadRows * role >= it.nrows) continue;  // this slice of the row group is empty
+    quad_item<kPC, false>(a, it, role, smem, wave, lane);
+  }
+}
+
 template <int kMode, int kPC, bool kFp8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_attn_kernel(AttnArgs a) {
@@ -755,10 +1070,21 @@ hipError_t launch_mode(const AttnArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int kPC>
+hipError_t launch_quad(const AttnArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((mla_attn_quad_kernel<kPC>), dim3(a.grid), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_attention(const AttnArgs& a, int tile_mode, int kv_fp8, hipStream_t stream) {
   if (a.num_wgs <= 0) return hipSuccess;
   if (kv_fp8) return hipErrorNotSupported;
   const int pc = a.page_shift >= 6 ? kPageBig : (a.page_shift >= 3 ? kPageMid : kPageSmall);
+  if (tile_mode == 3) {
+    if (pc == kPageBig) return launch_quad<kPageBig>(a, stream);
+    if (pc == kPageMid) return launch_quad<kPageMid>(a, stream);
+    return launch_quad<kPageSmall>(a, stream);
+  }
   if (tile_mode == 1) {
     if (pc == kPageBig) return launch_mode<1, kPageBig>(a, stream);
     if (pc == kPageMid) return launch_mode<1, kPageMid>(a, stream);

@@ -12,6 +12,7 @@ constexpr int kFp8RecordBytes = 656;
 constexpr int kStageTokens = 64;      // keys per LDS stage; chunk boundaries are multiples
 constexpr int kWideRows = 128;        // rows per workgroup in the wide tile mode (4 waves x 32)
 constexpr int kNarrowRows = 16;       // rows per workgroup in the narrow tile mode
+constexpr int kQuadRowsPerWg = 32;    // rows per workgroup in the quad tile mode
 constexpr size_t kWsAlign = 256;
 
 // One workgroup's work: rows [row0, row0+nrows) of request b against keys
@@ -62,7 +63,10 @@ struct AttnArgs {
   int32_t out_bf16;        // 1: bf16 out, 0: fp32 out
   int32_t causal;          // prefill causal mask
   int32_t rows_per_block;  // partial slot stride in rows
-  int32_t num_wgs;
+  int32_t num_wgs;         // work lists (one per workgroup, or per sibling group in quad mode)
+  int32_t grid;            // workgroups launched
+  int32_t group_size;      // quad mode: sibling workgroups per work list
+  int32_t xcd_map;         // quad mode: siblings share blockIdx.x mod 8
   int32_t num_items;
   int32_t num_groups;
 };

@@ -79,7 +79,7 @@ def _check_cover(plan, kv_len, q_len, H, causal=False, prefill=False):
     return items, ptr
 
 
-@pytest.mark.parametrize("tile_mode", [0, 1, 2])
+@pytest.mark.parametrize("tile_mode", [0, 1, 2, 3])
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_decode_schedule_covers_every_key_once(mla, tile_mode, seed):
     rng = np.random.default_rng(seed)
@@ -171,6 +171,7 @@ def test_plan_argument_errors(mla):
     assert _status(mla, **{**pre, "qo_indptr": [0, 3, 2]}) == -1        # decreasing
     assert _status(mla, **{**pre, "kv_format": 1}) == -2                # fp8 prefill
     assert _status(mla, **{**ok, "batch": 0, "kv_len": [], "kv_indptr": [0]}) == 0
+    assert _status(mla, **{**ok, "tile_mode": 4}) == -1
 
 
 def test_header_dims_are_enforced(mla):
@@ -215,3 +216,31 @@ def test_workspace_grows_with_splits(mla):
     assert p1.num_split_groups == 0
     assert p8.num_split_groups == 4
     assert p8.workspace_bytes >= 4 * 8 * 128 * 513 * 4
+
+
+def test_auto_mode_choice(mla):
+    # automatic tile: 128-row tile from 64 rows per request, else 16-row tile
+    lens = np.array([300, 700])
+    indptr = np.concatenate([[0], np.cumsum(-(-lens // 64))])
+    for heads, group in ((128, 1), (64, 1), (16, 1)):
+        plan = mla.mla_plan_create(0, 2, heads, 64, int(indptr[-1]), lens, indptr, num_cus=8)
+        assert plan.group_size == group
+        items, _ = _check_cover(plan, lens, [1, 1], heads)
+        want = 128 if heads >= 64 else 16
+        assert max(it["nrows"] for it in items) == min(want, heads)
+
+
+def test_quad_mode_groups_siblings(mla):
+    # 128 heads -> four 32-row sibling workgroups per row group, work lists
+    # are a multiple of 8 so that siblings share blockIdx.x mod 8
+    rng = np.random.default_rng(2)
+    lens = rng.integers(512, 4097, 64)
+    indptr = np.concatenate([[0], np.cumsum(-(-lens // 64))])
+    plan = mla.mla_plan_create(0, 64, 128, 64, int(indptr[-1]), lens, indptr, num_cus=256,
+                               tile_mode=mla.MLA_TILE_QUAD)
+    assert plan.group_size == 4
+    items, ptr = _check_cover(plan, lens, [1] * 64, 128)
+    assert len(ptr) - 1 <= 64
+    assert all(it["nrows"] == 128 for it in items)
+    # a request mostly fits one work list: few split groups
+    assert plan.num_split_groups <= 48

@@ -118,6 +118,13 @@ CASES = [
     (40, 8, [100, 400, 0, 33], 2, 0, False),
     (1, 64, [200, 77], 2, 0, False),
     (24, 4, [90, 31], 0, 0, True),
+    (128, 64, [1, 37, 64, 200], 3, 0, False),
+    (128, 16, [700, 3, 65], 3, 3, True),
+    (128, 1, [2, 130], 3, 2, False),
+    (128, 128, [1000, 1, 257], 3, 4, False),
+    (64, 64, [300, 5000], 3, 0, False),
+    (40, 8, [100, 400, 0, 33], 3, 2, False),
+    (256, 64, [150, 90], 3, 2, False),
 ]
 
 
@@ -137,6 +144,9 @@ PREFILL_CASES = [
     (16, 64, [8, 1, 3], [500, 9, 64], True, 0, 0),
     (16, 1, [4, 2], [50, 3], False, 2, 2),
     (128, 64, [1, 7], [1000, 1500], False, 1, 2),
+    (128, 64, [3, 1, 8, 5], [64, 100, 700, 5], True, 3, 0),
+    (128, 16, [2, 4], [300, 17], True, 3, 3),
+    (32, 64, [8, 1, 3], [500, 9, 64], True, 3, 2),
 ]
 
 
@@ -166,7 +176,7 @@ def test_empty_batch_is_a_no_op(mla):
 # bit-exact properties of the paged gather
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("H,mode", [(16, 2), (128, 1)])
+@pytest.mark.parametrize("H,mode", [(16, 2), (128, 1), (128, 3)])
 def test_page_permutation_is_bitwise_invariant(mla, H, mode):
     say(f"page permutation H={H} mode={mode}")
     w = make_workload(kv_lens=[130, 64, 1, 900], heads=H, page_size=16, seed=55)
