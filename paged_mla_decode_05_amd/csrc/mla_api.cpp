@@ -231,6 +231,7 @@ mla_status mla_plan_create(mla_plan** out, const mla_plan_desc* d, const int32_t
   if (d->kv_format != MLA_KV_BF16 && d->kv_format != MLA_KV_FP8_E4M3_T128) return MLA_ERR_UNSUPPORTED;
   if (d->kv_format == MLA_KV_FP8_E4M3_T128 && d->kind != MLA_KIND_DECODE) return MLA_ERR_UNSUPPORTED;
   if (d->tile_mode < MLA_TILE_AUTO || d->tile_mode > MLA_TILE_QUAD) return MLA_ERR_INVALID_ARGUMENT;
+  if (d->kv_format == MLA_KV_FP8_E4M3_T128 && d->tile_mode == MLA_TILE_QUAD) return MLA_ERR_UNSUPPORTED;
   if (d->max_splits < 0 || d->force_splits < 0 || d->num_cus < 0) return MLA_ERR_INVALID_ARGUMENT;
   if (d->batch > 0 && !kv_indptr_host) return MLA_ERR_INVALID_ARGUMENT;
   if (d->kind == MLA_KIND_PREFILL && d->batch > 0 && !qo_indptr_host) return MLA_ERR_INVALID_ARGUMENT;

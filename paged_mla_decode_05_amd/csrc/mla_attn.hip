@@ -305,6 +305,128 @@ __device__ __forceinline__ void issue_stage_bf16(const AttnArgs& a, LDS_AS char*
 }
 
 // ---------------------------------------------------------------------------
+// fp8 record caches (FlashMLA, "Quantization and Dequantization": per token
+// 512 e4m3 codes, four fp32 scales of 128 dims each, the 64 rope dims as
+// bf16; 656 bytes).  A stage's records move raw into LDS with 16-byte direct
+// loads; the workgroup then dequantises them into the bf16 stage layout the
+// attention bodies read, so the compute path is the one of the bf16 cache.
+// Wave w moves the 16 records of keys [16w, 16w+16): 16 x 41 chunks of 16
+// bytes, lane l of issue i taking chunk 64i + l, so the raw stage is the 64
+// records back to back.  Keys past tok_end re-read the chunk's last key.
+// ---------------------------------------------------------------------------
+constexpr int kRecChunks = kFp8RecordBytes / 16;                 // 41
+constexpr int kFp8RawBytes = kStageTokens * kFp8RecordBytes;     // 41984
+constexpr int kFp8DmaPerWave = (16 * kRecChunks + 63) / 64;      // 11
+constexpr int kFp8RawOff = kStageBytes;                          // [bf16 stage][raw 0][raw 1][scales]
+constexpr int kFp8ScaleOff = kStageBytes + 2 * kFp8RawBytes;     // float [4 tiles][64 keys]
+constexpr int kFp8LdsBytes = kFp8ScaleOff + 4 * kStageTokens * 4;  // 158720
+static_assert(kFp8LdsBytes <= 160 * 1024, "fp8 LDS budget");
+
+template <int kPageClass>
+struct RecordLoader {
+  const char* base;  // kPageBig: record of the stage's first key
+  int page;          // other classes: lane j < 16 holds the page of key 16w + j (clamped)
+  int last;          // last live key of the stage, relative to s_tok0
+  int s_tok0;
+  LDS_AS char* raw;
+
+  __device__ __forceinline__ void begin(const AttnArgs& a, LDS_AS char* raw_stage, int page_base, int tok0,
+                                        int tok_end, int wave) {
+    const int sh = a.page_shift;
+    const int mask = (1 << sh) - 1;
+    raw = raw_stage;
+    s_tok0 = tok0;
+    last = tok_end - 1 - tok0;
+    if (kPageClass == kPageBig) {
+      const int pg = ld_const(a.kv_indices, page_base + (tok0 >> sh));
+      base = (const char*)a.kv_fp8 + (((size_t)pg << sh) + (tok0 & mask)) * kFp8RecordBytes;
+      return;
+    }
+    const int lane = lane_here();
+    int p = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int T = tok0 + min(wave * 16 + j, last);
+      const int pj = ld_const(a.kv_indices, page_base + (T >> sh));
+      p = (lane == j) ? pj : p;
+    }
+    page = p;
+  }
+
+  __device__ __forceinline__ void issue(const AttnArgs& a, int i, int wave) {
+    const int lane = lane_here();
+    const int c = 64 * i + lane;
+    const int cc = min(c, 16 * kRecChunks - 1);
+    const int tr = (cc * 200) >> 13;  // cc / 41 for cc < 704
+    const int k = cc - kRecChunks * tr;
+    const int tc = min(wave * 16 + tr, last);
+    LDS_AS char* dst = raw + (wave * 16 * kRecChunks + 64 * i) * 16;
+    if (kPageClass == kPageBig) {
+      if (c < 16 * kRecChunks) dma16(base, (uint32_t)(tc * kFp8RecordBytes + 16 * k), lds_addr(dst));
+    } else {
+      const int p = __shfl(page, tr);
+      const int sh = a.page_shift;
+      const int T = s_tok0 + tc;
+      const char* src = (const char*)a.kv_fp8 + (((size_t)p << sh) + (T & ((1 << sh) - 1))) * kFp8RecordBytes +
+                        16 * k;
+      if (c < 16 * kRecChunks) dma16_v(src, lds_addr(dst));
+    }
+  }
+};
+
+template <int kPageClass>
+__device__ __forceinline__ void issue_stage_fp8(const AttnArgs& a, LDS_AS char* raw, int page_base, int s_tok0,
+                                                int tok_end, int wave) {
+  RecordLoader<kPageClass> ld;
+  ld.begin(a, raw, page_base, s_tok0, tok_end, wave);
+#pragma unroll
+  for (int i = 0; i < kFp8DmaPerWave; ++i) ld.issue(a, i, wave);
+}
+
+// Four e4m3 codes (one per byte of x) as bf16, exactly: the OCP e4m3 decode
+// is the hardware conversion of gfx950, and every e4m3 value (3 mantissa
+// bits, exponents 2^-9 .. 2^8) is a bf16 value.
+__device__ __forceinline__ void codes_to_bf16(uint32_t x, bf16x8& h, int at) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(x, false);
+  const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(x, true);
+  h[at + 0] = (__bf16)lo[0];
+  h[at + 1] = (__bf16)lo[1];
+  h[at + 2] = (__bf16)hi[0];
+  h[at + 3] = (__bf16)hi[1];
+}
+
+// Wave w unpacks the records of keys [16w, 16w+16) from the raw stage: the
+// ckv codes go to the bf16 stage as exact bf16 values (code, not code *
+// scale), the rope dims are copied, and the four tile scales go to the
+// scale table sct[tile][key].  The scale is applied in fp32 by the consumer:
+// to each tile's partial dot product in Q.K^T, and to P for the tile's
+// output dims in P.V, so no dequantised key is ever rounded.  Lane l
+// handles ckv chunk l (dims 8l..8l+7) of every key, then two rope chunks.
+__device__ __forceinline__ void dequant_stage(const LDS_AS char* __restrict__ raw, LDS_AS char* __restrict__ st,
+                                              LDS_AS float* __restrict__ sct, int wave, int lane) {
+#pragma unroll 4
+  for (int i = 0; i < 16; ++i) {
+    const int t = wave * 16 + i;
+    const LDS_AS char* rec = raw + t * kFp8RecordBytes;
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 codes = *(const LDS_AS u32x2*)(rec + 8 * lane);
+    bf16x8 h;
+    codes_to_bf16(codes[0], h, 0);
+    codes_to_bf16(codes[1], h, 4);
+    *(LDS_AS bf16x8*)(st + ckv_off(t, lane)) = h;
+    if ((lane & 15) == 0) sct[(lane >> 4) * kStageTokens + t] = *(const LDS_AS float*)(rec + kDimCkv + (lane >> 2));
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int t = wave * 16 + 8 * i + (lane >> 3);
+    const int c = lane & 7;
+    const u32x4 r = *(const LDS_AS u32x4*)(raw + t * kFp8RecordBytes + kDimCkv + 16 + 16 * c);
+    *(LDS_AS u32x4*)(st + kpe_off(t, c)) = r;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Item bookkeeping shared by both modes
 // ---------------------------------------------------------------------------
 struct RowInfo {
@@ -376,16 +498,22 @@ struct WideState {
   float l_run;    // running sum of this lane's keys
 };
 
-template <int kPC>
+template <int kPC, bool kFp8>
 __device__ __forceinline__ void wide_stage(const AttnArgs& a, const bf16x8 (&qf)[36], WideState& st,
                                            const LDS_AS char* __restrict__ cur, int stage_tok, int bound,
                                            const int (&kb)[8], const int (&pb)[4], const int (&vb)[8],
-                                           int g, StageLoader<kPC>& ld, bool prefetch, int wave) {
+                                           int g, StageLoader<kPC>& ld, bool prefetch, int wave,
+                                           const LDS_AS float* __restrict__ sct) {
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub) {
     const int tb = sub * 32;
+    // fp8 cache: scales of this lane's keys tb + 8q + 4g + (0..3) in tile t
+    auto scales = [&](int t, int q) -> f32x4 {
+      return *(const LDS_AS f32x4*)(sct + t * kStageTokens + tb + 8 * q + 4 * g);
+    };
     // S^T[32 keys x 32 rows] = K . Q^T over 576 dims
     f32x16 sacc = {};
+    f32x16 part = {};  // fp8: one 128-dim tile of the codes' dot products
     auto kread = [&](int ks) -> bf16x8 {
       return ks < 32 ? lds_read_b128(cur, kb[ks & 7] + 256 * (ks >> 3) + tb * kCkvRowBytes)
                      : lds_read_b128(cur, pb[ks - 32] + tb * kKpeRowBytes);
@@ -395,7 +523,20 @@ __device__ __forceinline__ void wide_stage(const AttnArgs& a, const bf16x8 (&qf)
     for (int ks = 0; ks < 36; ++ks) {
       if (prefetch && (ks & 3) == 0) ld.issue(a, sub * 9 + (ks >> 2), wave);  // 9 slices per sub-tile
       const bf16x8 k2 = (ks + 2 < 36) ? kread(ks + 2) : k1;
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[ks], sacc, 0, 0, 0);
+      if (kFp8 && ks < 32) {
+        part = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[ks], part, 0, 0, 0);
+        if ((ks & 7) == 7) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x4 sc = scales(ks >> 3, q);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sacc[4 * q + r] += part[4 * q + r] * sc[r];
+          }
+          part = f32x16{};
+        }
+      } else {
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[ks], sacc, 0, 0, 0);
+      }
       k0 = k1;
       k1 = k2;
     }
@@ -421,10 +562,12 @@ __device__ __forceinline__ void wide_stage(const AttnArgs& a, const bf16x8 (&qf)
     }
     const float mref = (st.m_run == kNegInf) ? 0.f : st.m_run;
     bf16x8 pt[2];
+    float pf[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const float p = fast_exp2(sv[r] - mref);
       st.l_run += p;
+      pf[r] = p;
       pt[r >> 3][r & 7] = (__bf16)p;
     }
     // O^T[32 dims x 32 rows] += V^T[32 dims x 16 keys] . P^T[16 keys x 32 rows]
@@ -439,6 +582,15 @@ __device__ __forceinline__ void wide_stage(const AttnArgs& a, const bf16x8 (&qf)
     bf16x8 v0 = vread(0), v1 = vread(1);
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
+      if (kFp8 && (j & 7) == 0) {
+        // output dims of tile j/8: P scaled by each key's tile scale
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 sc = scales(j >> 3, q);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) pt[q >> 1][4 * (q & 1) + r] = (__bf16)(pf[4 * q + r] * sc[r]);
+        }
+      }
       const bf16x8 v2 = (j + 2 < 32) ? vread(j + 2) : v1;
       st.o[j >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, pt[j & 1], st.o[j >> 1], 0, 0, 0);
       v0 = v1;
@@ -455,7 +607,7 @@ __device__ __forceinline__ void wide_body(const AttnArgs& a, const bf16x8 (&qf)[
                                           const int (&vb)[8], int wave, int lane) {
   StageLoader<kPC> ld;
   if (prefetch) ld.begin(a, nxt, page_base, next_tok, tok_end, wave);
-  wide_stage<kPC>(a, qf, st, cur, stage_tok, bound, kb, pb, vb, lane >> 5, ld, prefetch, wave);
+  wide_stage<kPC, false>(a, qf, st, cur, stage_tok, bound, kb, pb, vb, lane >> 5, ld, prefetch, wave, nullptr);
 }
 
 template <int kPC, bool kFp8>
@@ -502,14 +654,39 @@ __device__ void wide_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* sm
 
   const int page_base = ld_const(a.kv_indptr, it.b);
   const int nstage = (it.tok1 - it.tok0 + kStageTokens - 1) / kStageTokens;
-  if (nstage > 0) issue_stage_bf16<kPC>(a, smem, page_base, it.tok0, it.tok1, wave, lane);
-  for (int s = 0; s < nstage; ++s) {
-    wait_vmcnt<0>();
-    __syncthreads();
-    wide_body<kPC>(a, qf, st, smem + (s & 1) * kStageBytes, smem + ((s + 1) & 1) * kStageBytes, s + 1 < nstage,
-              page_base, it.tok0 + (s + 1) * kStageTokens, it.tok1, it.tok0 + s * kStageTokens, bound, kb, pb,
-              vb, wave, lane);
-    __syncthreads();  // every wave is done with this stage before it is refilled
+  if (kFp8) {
+    // raw records two stages ahead; one stage unpacked per step
+    LDS_AS char* raw = smem + kFp8RawOff;
+    LDS_AS float* sct = (LDS_AS float*)(smem + kFp8ScaleOff);
+    if (nstage > 0) issue_stage_fp8<kPC>(a, raw, page_base, it.tok0, it.tok1, wave);
+    if (nstage > 1) issue_stage_fp8<kPC>(a, raw + kFp8RawBytes, page_base, it.tok0 + kStageTokens, it.tok1, wave);
+    for (int s = 0; s < nstage; ++s) {
+      if (s + 1 < nstage) {
+        wait_vmcnt<kFp8DmaPerWave>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      __syncthreads();  // raw stage s landed; every wave is done with the bf16 stage
+      dequant_stage(raw + (s & 1) * kFp8RawBytes, smem, sct, wave, lane);
+      __syncthreads();  // bf16 stage complete; raw stage s consumed
+      if (s + 2 < nstage)
+        issue_stage_fp8<kPC>(a, raw + (s & 1) * kFp8RawBytes, page_base, it.tok0 + (s + 2) * kStageTokens, it.tok1,
+                             wave);
+      StageLoader<kPC> none;
+      wide_stage<kPC, true>(a, qf, st, smem, it.tok0 + s * kStageTokens, bound, kb, pb, vb, g, none, false, wave,
+                            sct);
+    }
+    __syncthreads();  // the bf16 stage is free for the next item
+  } else {
+    if (nstage > 0) issue_stage_bf16<kPC>(a, smem, page_base, it.tok0, it.tok1, wave, lane);
+    for (int s = 0; s < nstage; ++s) {
+      wait_vmcnt<0>();
+      __syncthreads();
+      wide_body<kPC>(a, qf, st, smem + (s & 1) * kStageBytes, smem + ((s + 1) & 1) * kStageBytes,
+                     s + 1 < nstage, page_base, it.tok0 + (s + 1) * kStageTokens, it.tok1,
+                     it.tok0 + s * kStageTokens, bound, kb, pb, vb, wave, lane);
+      __syncthreads();  // every wave is done with this stage before it is refilled
+    }
   }
 
   // epilogue: lane owns row n; the partner lane (n, 1-g) holds the other dims
@@ -542,23 +719,35 @@ struct NarrowState {
   float l_run;
 };
 
-template <int kPC>
+template <int kPC, bool kFp8>
 __device__ __forceinline__ void narrow_body(const AttnArgs& a, const bf16x8 (&qf)[18], NarrowState& st,
                                             const LDS_AS char* __restrict__ cur, LDS_AS char* __restrict__ nxt,
                                             bool prefetch, int page_base, int next_tok, int tok_end,
                                             int stage_tok, int bound, const int (&kb)[4], const int (&pb)[2],
-                                            const int (&vb)[8], int wave, int lane) {
+                                            const int (&vb)[8], int wave, int lane,
+                                            const LDS_AS float* __restrict__ sct) {
   StageLoader<kPC> ld;
   if (prefetch) ld.begin(a, nxt, page_base, next_tok, tok_end, wave);
   const int g4 = lane >> 4;
   const int tb = wave * 16;
+  // fp8 cache: scales of this lane's keys tb + 4 g4 + (0..3) in tile t
+  auto scales = [&](int t) -> f32x4 { return *(const LDS_AS f32x4*)(sct + t * kStageTokens + tb + 4 * g4); };
   // S^T[16 keys x 16 rows]
   f32x4 sacc = {};
+  f32x4 part = {};
 #pragma unroll
   for (int ks = 0; ks < 18; ++ks) {
     if (prefetch) ld.issue(a, ks, wave);  // one prefetch slice per k-step
     const bf16x8 kf = ks < 16 ? lds_read_b128(cur, kb[ks & 3] + 256 * (ks >> 2)) : lds_read_b128(cur, pb[ks - 16]);
-    sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], sacc, 0, 0, 0);
+    if (kFp8 && ks < 16) {
+      part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], part, 0, 0, 0);
+      if ((ks & 3) == 3) {
+        sacc += part * scales(ks >> 2);
+        part = f32x4{};
+      }
+    } else {
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], sacc, 0, 0, 0);
+    }
   }
   float sv[4];
   float mx = kNegInf;
@@ -585,15 +774,23 @@ __device__ __forceinline__ void narrow_body(const AttnArgs& a, const bf16x8 (&qf
   }
   const float mref = (st.m_run == kNegInf) ? 0.f : st.m_run;
   i16x4 pt;
+  f32x4 pf;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const float p = fast_exp2(sv[r] - mref);
     st.l_run += p;
+    pf[r] = p;
     pt[r] = __builtin_bit_cast(short, (__bf16)p);
   }
   // O^T[16 dims x 16 rows] += V^T[16 dims x 16 keys] . P^T[16 keys x 16 rows]
 #pragma unroll
   for (int cb = 0; cb < 32; ++cb) {
+    if (kFp8 && (cb & 7) == 0) {
+      // output dims of tile cb/8: P scaled by each key's tile scale
+      const f32x4 ps = pf * scales(cb >> 3);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pt[r] = __builtin_bit_cast(short, (__bf16)ps[r]);
+    }
     const i16x4 v = lds_read_tr(cur, vb[cb & 7] + 256 * (cb >> 3));
     st.o[cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v, pt, st.o[cb], 0, 0, 0);
   }
@@ -638,14 +835,37 @@ __device__ void narrow_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* 
 
   const int page_base = ld_const(a.kv_indptr, it.b);
   const int nstage = (it.tok1 - it.tok0 + kStageTokens - 1) / kStageTokens;
-  if (nstage > 0) issue_stage_bf16<kPC>(a, smem, page_base, it.tok0, it.tok1, wave, lane);
-  for (int s = 0; s < nstage; ++s) {
-    wait_vmcnt<0>();
+  if (kFp8) {
+    LDS_AS char* raw = smem + kFp8RawOff;
+    LDS_AS float* sct = (LDS_AS float*)(smem + kFp8ScaleOff);
+    if (nstage > 0) issue_stage_fp8<kPC>(a, raw, page_base, it.tok0, it.tok1, wave);
+    if (nstage > 1) issue_stage_fp8<kPC>(a, raw + kFp8RawBytes, page_base, it.tok0 + kStageTokens, it.tok1, wave);
+    for (int s = 0; s < nstage; ++s) {
+      if (s + 1 < nstage) {
+        wait_vmcnt<kFp8DmaPerWave>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      __syncthreads();
+      dequant_stage(raw + (s & 1) * kFp8RawBytes, smem, sct, wave, lane);
+      __syncthreads();
+      if (s + 2 < nstage)
+        issue_stage_fp8<kPC>(a, raw + (s & 1) * kFp8RawBytes, page_base, it.tok0 + (s + 2) * kStageTokens, it.tok1,
+                             wave);
+      narrow_body<kPC, true>(a, qf, st, smem, smem, false, page_base, 0, it.tok1, it.tok0 + s * kStageTokens, bound,
+                             kb, pb, vb, wave, lane, sct);
+    }
     __syncthreads();
-    narrow_body<kPC>(a, qf, st, smem + (s & 1) * kStageBytes, smem + ((s + 1) & 1) * kStageBytes, s + 1 < nstage,
-                page_base, it.tok0 + (s + 1) * kStageTokens, it.tok1, it.tok0 + s * kStageTokens, bound, kb, pb,
-                vb, wave, lane);
-    __syncthreads();
+  } else {
+    if (nstage > 0) issue_stage_bf16<kPC>(a, smem, page_base, it.tok0, it.tok1, wave, lane);
+    for (int s = 0; s < nstage; ++s) {
+      wait_vmcnt<0>();
+      __syncthreads();
+      narrow_body<kPC, false>(a, qf, st, smem + (s & 1) * kStageBytes, smem + ((s + 1) & 1) * kStageBytes,
+                       s + 1 < nstage, page_base, it.tok0 + (s + 1) * kStageTokens, it.tok1,
+                       it.tok0 + s * kStageTokens, bound, kb, pb, vb, wave, lane, nullptr);
+      __syncthreads();
+    }
   }
 
   // ---- merge the four waves' partial results through LDS ----
@@ -982,7 +1202,7 @@ void mla_attn_quad_kernel(AttnArgs a) {
 template <int kMode, int kPC, bool kFp8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_attn_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem_raw[kLdsBytes];
+  __shared__ __attribute__((aligned(1024))) char smem_raw[kFp8 ? kFp8LdsBytes : kLdsBytes];
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -1065,8 +1285,12 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(AttnArgs a) {
 }  // namespace
 
 template <int kMode, int kPC>
-hipError_t launch_mode(const AttnArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((mla_attn_kernel<kMode, kPC, false>), dim3(a.num_wgs), dim3(256), 0, stream, a);
+hipError_t launch_mode(const AttnArgs& a, int kv_fp8, hipStream_t stream) {
+  if (kv_fp8) {
+    hipLaunchKernelGGL((mla_attn_kernel<kMode, kPC, true>), dim3(a.num_wgs), dim3(256), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((mla_attn_kernel<kMode, kPC, false>), dim3(a.num_wgs), dim3(256), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
@@ -1078,21 +1302,21 @@ hipError_t launch_quad(const AttnArgs& a, hipStream_t stream) {
 
 hipError_t launch_attention(const AttnArgs& a, int tile_mode, int kv_fp8, hipStream_t stream) {
   if (a.num_wgs <= 0) return hipSuccess;
-  if (kv_fp8) return hipErrorNotSupported;
   const int pc = a.page_shift >= 6 ? kPageBig : (a.page_shift >= 3 ? kPageMid : kPageSmall);
   if (tile_mode == 3) {
+    if (kv_fp8) return hipErrorNotSupported;  // rejected when the plan is made
     if (pc == kPageBig) return launch_quad<kPageBig>(a, stream);
     if (pc == kPageMid) return launch_quad<kPageMid>(a, stream);
     return launch_quad<kPageSmall>(a, stream);
   }
   if (tile_mode == 1) {
-    if (pc == kPageBig) return launch_mode<1, kPageBig>(a, stream);
-    if (pc == kPageMid) return launch_mode<1, kPageMid>(a, stream);
-    return launch_mode<1, kPageSmall>(a, stream);
+    if (pc == kPageBig) return launch_mode<1, kPageBig>(a, kv_fp8, stream);
+    if (pc == kPageMid) return launch_mode<1, kPageMid>(a, kv_fp8, stream);
+    return launch_mode<1, kPageSmall>(a, kv_fp8, stream);
   }
-  if (pc == kPageBig) return launch_mode<2, kPageBig>(a, stream);
-  if (pc == kPageMid) return launch_mode<2, kPageMid>(a, stream);
-  return launch_mode<2, kPageSmall>(a, stream);
+  if (pc == kPageBig) return launch_mode<2, kPageBig>(a, kv_fp8, stream);
+  if (pc == kPageMid) return launch_mode<2, kPageMid>(a, kv_fp8, stream);
+  return launch_mode<2, kPageSmall>(a, kv_fp8, stream);
 }
 
 hipError_t launch_combine(const AttnArgs& a, hipStream_t stream) {

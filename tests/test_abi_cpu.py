@@ -172,6 +172,8 @@ def test_plan_argument_errors(mla):
     assert _status(mla, **{**pre, "kv_format": 1}) == -2                # fp8 prefill
     assert _status(mla, **{**ok, "batch": 0, "kv_len": [], "kv_indptr": [0]}) == 0
     assert _status(mla, **{**ok, "tile_mode": 4}) == -1
+    assert _status(mla, **{**ok, "kv_format": 1}) == 0                  # fp8 decode
+    assert _status(mla, **{**ok, "kv_format": 1, "tile_mode": 3}) == -2  # fp8 has no quad tile
 
 
 def test_header_dims_are_enforced(mla):

@@ -138,6 +138,28 @@ def test_decode_small_cases(mla, case):
     compare(out, lse, *ref_decode(w), TOL_BF16)
 
 
+FP8_CASES = [
+    # (heads, page_size, kv_lens, tile_mode, force_splits, out fp32)
+    (128, 64, [1, 37, 64, 200], 1, 0, False),
+    (128, 16, [700, 3, 65], 1, 3, True),
+    (128, 1, [2, 130], 1, 2, False),
+    (128, 128, [1000, 1, 257], 0, 4, False),
+    (16, 64, [1, 37, 64, 200], 2, 0, True),
+    (16, 8, [5, 300, 64, 1], 2, 3, False),
+    (40, 4, [100, 400, 0, 33], 0, 2, False),
+]
+
+
+@pytest.mark.parametrize("case", FP8_CASES, ids=[f"H{c[0]}-ps{c[1]}-m{c[3]}-s{c[4]}" for c in FP8_CASES])
+def test_decode_fp8_small_cases(mla, case):
+    H, ps, lens, mode, fs, f32 = case
+    say(f"decode fp8 H={H} page_size={ps} lens={lens} tile_mode={mode} force_splits={fs}")
+    w = make_workload(kv_lens=lens, heads=H, page_size=ps, seed=300 + H + ps, kv_format="fp8",
+                      out_dtype=torch.float32 if f32 else torch.bfloat16)
+    out, lse, _ = run_decode(mla, w, DEV, tile_mode=mode, force_splits=fs, num_cus=0)
+    compare(out, lse, *ref_decode(w), TOL_FP8)
+
+
 PREFILL_CASES = [
     (128, 64, [3, 1, 8, 5], [64, 100, 700, 5], True, 1, 0),
     (128, 16, [2, 4], [300, 17], True, 1, 3),
@@ -187,6 +209,19 @@ def test_page_permutation_is_bitwise_invariant(mla, H, mode):
     ckv2[perm] = w.ckv
     kpe2[perm] = w.kpe
     w.ckv, w.kpe, w.kv_indices = ckv2, kpe2, perm.to(torch.int32)[w.kv_indices.long()]
+    out2, lse2, _ = run_decode(mla, w, DEV, tile_mode=mode, force_splits=2)
+    assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+
+
+@pytest.mark.parametrize("H,mode", [(16, 2), (128, 1)])
+def test_fp8_page_permutation_is_bitwise_invariant(mla, H, mode):
+    say(f"fp8 page permutation H={H} mode={mode}")
+    w = make_workload(kv_lens=[130, 64, 1, 900], heads=H, page_size=16, seed=59, kv_format="fp8")
+    out1, lse1, _ = run_decode(mla, w, DEV, tile_mode=mode, force_splits=2)
+    perm = torch.randperm(w.num_pages, generator=torch.Generator().manual_seed(10))
+    kv2 = torch.empty_like(w.kv_fp8)
+    kv2[perm] = w.kv_fp8
+    w.kv_fp8, w.kv_indices = kv2, perm.to(torch.int32)[w.kv_indices.long()]
     out2, lse2, _ = run_decode(mla, w, DEV, tile_mode=mode, force_splits=2)
     assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
 
@@ -254,3 +289,12 @@ def test_prefill_causal_h128_full_size(mla):
     qo = w.qo_indptr.numpy()
     rows = np.concatenate([np.arange(qo[b], qo[b + 1]) for b in req])
     compare(out, lse, ro, rl, TOL_BF16, rows=rows)
+
+
+def test_decode_fp8_b128_h128_full_size(mla):
+    w = make_workload("decode_fp8_b128_h128", device=DEV)
+    req = _sample(w.batch, 6, 4)
+    say(f"decode_fp8_b128_h128 full size, requests {req}")
+    out, lse, _ = run_decode(mla, w, DEV)
+    ro, rl = ref_decode(w, requests=req)
+    compare(out, lse, ro, rl, TOL_FP8, rows=req)
