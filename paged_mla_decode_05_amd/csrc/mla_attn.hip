@@ -14,8 +14,8 @@
 //    moves one 1 KB ckv row, or the 128-byte kpe rows of 8 keys.  The page of
 //    key T is kv_indices[kv_indptr[b] + (T >> log2 page_size)], slot
 //    T & (page_size-1) (FlashMLA's block/offset mapping); keys past the
-//    chunk read a zero row, so stale or NaN tail slots never reach the math.
-//    Two stages are in flight (double-buffered, 2 x 72 KB of LDS).
+//    chunk re-read its last live key and are masked, so stale or NaN tail
+//    slots are never read.  Two stages are in flight (2 x 72 KB of LDS).
 //  * QK^T is computed transposed, S^T = K . Q^T, on bf16 MFMA with the
 //    query fragments held in registers; each lane then owns one query row
 //    (head), so the online-softmax state (running max m, sum l) is per lane.
@@ -30,6 +30,11 @@
 //    split every key tile 16 keys each (mfma_f32_16x16x32_bf16 for S,
 //    mfma_f32_16x16x16_bf16 for P.V) and merge their partial results
 //    through LDS at the end of the item.
+//  * QUAD (selectable): 32 rows per workgroup, waves split keys for S and
+//    output dims for P.V; sibling workgroups on one XCD share the key stream
+//    through L2.
+//  * fp8 656-byte records: raw records to LDS, codes unpacked to exact bf16
+//    values, per-tile scales applied in fp32 to the partial logits and to P.
 //  * A work item that covers only part of a request's keys writes a
 //    normalised partial output and its lse; mla_combine merges them by the
 //    log-sum-exp identity (the split-K statistics of
