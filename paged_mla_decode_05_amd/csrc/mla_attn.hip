@@ -131,6 +131,27 @@ __device__ __forceinline__ void scale_acc(float __attribute__((ext_vector_type(N
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// S^T chains on mfma_f32_32x32x16_bf16 with the accumulator in VGPRs.  The
+// compiler gives every builtin MFMA of these kernels an AGPR accumulator,
+// and the 256 AGPRs are O's; S must live in VGPRs, so its MFMAs are written
+// here.  mfma32_first starts a chain (inline-zero C operand), mfma32_acc
+// continues it (C = D exactly: the hardware's back-to-back accumulation,
+// no wait states), and mfma32_drain puts 24 wait states between the last
+// MFMA and the first other reader or writer of the accumulator (the XDL
+// write -> VALU read / SrcC read -> VALU write distance of gfx950 is less).
+__device__ __forceinline__ void mfma32_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma32_acc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma32_drain(f32x16& x) { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x)); }
+__device__ __forceinline__ void mfma32_drain(f32x16& x, f32x16& y) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x), "+v"(y));
+}
+
+
+
 // Waits until at most `n` vector-memory loads of this wave are outstanding
 // (n <= 63); the other counters are left alone.
 template <int n>
@@ -475,8 +496,12 @@ __device__ __forceinline__ void store4(const AttnArgs& a, const WorkItem& it, co
       *(f32x4*)((float*)a.out + ri.qrow * kDimCkv + dim) = v;
     }
   } else {
-    float* dst = a.part_o + ((size_t)it.slot * a.rows_per_block + r_in_block) * kDimCkv + dim;
-    *(f32x4*)dst = v;
+    bf16x4 h;
+    h[0] = (__bf16)v[0];
+    h[1] = (__bf16)v[1];
+    h[2] = (__bf16)v[2];
+    h[3] = (__bf16)v[3];
+    *(bf16x4*)(a.part_o + ((size_t)it.slot * a.rows_per_block + r_in_block) * kDimCkv + dim) = h;
   }
 }
 
@@ -517,8 +542,8 @@ __device__ __forceinline__ void wide_stage(const AttnArgs& a, const bf16x8 (&qf)
       return *(const LDS_AS f32x4*)(sct + t * kStageTokens + tb + 8 * q + 4 * g);
     };
     // S^T[32 keys x 32 rows] = K . Q^T over 576 dims
-    f32x16 sacc = {};
-    f32x16 part = {};  // fp8: one 128-dim tile of the codes' dot products
+    f32x16 sacc;
+    f32x16 part;  // fp8: one 128-dim tile of the codes' dot products
     auto kread = [&](int ks) -> bf16x8 {
       return ks < 32 ? lds_read_b128(cur, kb[ks & 7] + 256 * (ks >> 3) + tb * kCkvRowBytes)
                      : lds_read_b128(cur, pb[ks - 32] + tb * kKpeRowBytes);
@@ -529,22 +554,32 @@ __device__ __forceinline__ void wide_stage(const AttnArgs& a, const bf16x8 (&qf)
       if (prefetch && (ks & 3) == 0) ld.issue(a, sub * 9 + (ks >> 2), wave);  // 9 slices per sub-tile
       const bf16x8 k2 = (ks + 2 < 36) ? kread(ks + 2) : k1;
       if (kFp8 && ks < 32) {
-        part = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[ks], part, 0, 0, 0);
+        if ((ks & 7) == 0) {
+          mfma32_first(part, k0, qf[ks]);
+        } else {
+          mfma32_acc(part, k0, qf[ks]);
+        }
         if ((ks & 7) == 7) {
+          mfma32_drain(part);
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const f32x4 sc = scales(ks >> 3, q);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sacc[4 * q + r] += part[4 * q + r] * sc[r];
+            for (int r = 0; r < 4; ++r) {
+              const float t = part[4 * q + r] * sc[r];
+              sacc[4 * q + r] = (ks == 7) ? t : sacc[4 * q + r] + t;
+            }
           }
-          part = f32x16{};
         }
+      } else if (ks == 0) {
+        mfma32_first(sacc, k0, qf[0]);
       } else {
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[ks], sacc, 0, 0, 0);
+        mfma32_acc(sacc, k0, qf[ks]);
       }
       k0 = k1;
       k1 = k2;
     }
+    mfma32_drain(sacc);
     // online softmax (base 2); lane holds keys 8(r/4) + 4g + r%4 of the sub-tile
     float sv[16];
     float mx = kNegInf;
@@ -710,6 +745,259 @@ __device__ void wide_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* sm
     }
     if (g == 0) store_lse(a, it, ri, rib, empty ? kNegInf : (st.m_run + __log2f(l_tot)) * kLn2);
   }
+}
+
+// ---------------------------------------------------------------------------
+// SPLIT mode: 128 rows per workgroup like WIDE, but P.V is split by output
+// columns.  Wave w computes S^T = K . Q^T for its own rows [32w, 32w+32)
+// (Q stays in its registers) and owns their softmax state; P goes through
+// LDS, and wave w then computes O^T for output dims [128w, 128w+128) of all
+// 128 rows.  Each wave reads a quarter of V instead of all of it, which
+// quarters the transposed LDS reads, the costliest LDS traffic of WIDE.
+//
+// A stage's P is exchanged in two 32-key halves: keys 0..31 through a
+// dedicated 8 KB buffer (written before barrier A), keys 32..63 through the
+// stage's kpe region (free once every wave is past Q.K^T, i.e. after A;
+// visible after barrier B).  When an owner raises a row's running max it
+// publishes the row's factor alpha and a flag; after A every wave applies
+// the factors to its O columns (rare: lazy rescale as in WIDE).
+// ---------------------------------------------------------------------------
+constexpr int kSplitP0Off = 2 * kStageBytes;                   // P keys 0..31: [128 rows][64 B]
+constexpr int kSplitXOff = kSplitP0Off + kWideRows * 64;       // alpha / l [128] f32, flags [4] i32
+constexpr int kSplitLdsBytes = kSplitXOff + kWideRows * 4 + 16;
+static_assert(kSplitLdsBytes <= 160 * 1024, "split-mode LDS budget");
+
+// P row layout: 32 keys of bf16 = four 16-byte chunks, XOR-swizzled by row
+// so that 8 consecutive rows reading one chunk hit distinct banks.
+__device__ __forceinline__ int p_off(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 1) & 3)) << 4); }
+
+struct SplitState {
+  f32x16 o[4][4];  // O^T tiles [ct][rt]: lane holds row 32rt + n, dims 128w + 32ct + 8(r/4) + 4g + r%4
+  float m_run;     // owner: running max (log2 units) of row 32w + n
+  float l_run;     // owner: running sum of this lane's keys
+};
+
+template <int kPC, bool kPrefetch>
+__device__ __forceinline__ void split_stage(const AttnArgs& a, const bf16x8 (&qf)[36], SplitState& st,
+                                            LDS_AS char* __restrict__ cur, LDS_AS char* __restrict__ p0,
+                                            LDS_AS char* __restrict__ xch, int stage_tok, int bound,
+                                            const int (&kb)[8], const int (&pb)[4], const int (&vb)[4][2],
+                                            const int (&pr)[2], const int (&pw)[4], int g, int n,
+                                            StageLoader<kPC>& ld, int wave) {
+  // ---- S^T[64 keys x 32 rows] = K . Q^T: two 32-key chains sharing each Q fragment
+  f32x16 s0, s1;
+  auto kread = [&](int ks, int tb) -> bf16x8 {
+    return ks < 32 ? lds_read_b128(cur, kb[ks & 7] + 256 * (ks >> 3) + tb * kCkvRowBytes)
+                   : lds_read_b128(cur, pb[ks - 32] + tb * kKpeRowBytes);
+  };
+  constexpr int D = 3;  // k-steps of K fragments in flight
+  bf16x8 kr0[D], kr1[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) {
+    kr0[i] = kread(i, 0);
+    kr1[i] = kread(i, 32);
+  }
+#pragma unroll
+  for (int ks = 0; ks < 36; ++ks) {
+    if (kPrefetch && (ks & 1) == 0) ld.issue(a, ks >> 1, wave);  // 18 slices over 36 k-steps
+    const bf16x8 a0 = kr0[ks % D], a1 = kr1[ks % D];
+    if (ks + D < 36) {
+      kr0[ks % D] = kread(ks + D, 0);
+      kr1[ks % D] = kread(ks + D, 32);
+    }
+    if (ks == 0) {
+      mfma32_first(s0, a0, qf[0]);
+      mfma32_first(s1, a1, qf[0]);
+    } else {
+      mfma32_acc(s0, a0, qf[ks]);
+      mfma32_acc(s1, a1, qf[ks]);
+    }
+  }
+  mfma32_drain(s0, s1);
+
+  // ---- owner softmax over the 64 keys of row 32w + n
+  // lane holds keys 8(r/4) + 4g + r%4 of each 32-key half
+  float mx = kNegInf;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int k0 = stage_tok + 8 * (r >> 2) + 4 * g + (r & 3);
+    s0[r] = k0 < bound ? s0[r] * a.scale_log2 : kNegInf;
+    s1[r] = k0 + 32 < bound ? s1[r] * a.scale_log2 : kNegInf;
+    mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+  }
+  mx = max_xor32(mx);
+  const bool raise = __builtin_amdgcn_ballot_w64(mx > st.m_run + kRescaleSlack) != 0;
+  float alpha = 1.f;
+  if (raise) {
+    const float m_new = fmaxf(st.m_run, mx);
+    alpha = (st.m_run == kNegInf) ? 0.f : fast_exp2(st.m_run - m_new);
+    st.l_run *= alpha;
+    st.m_run = m_new;
+  }
+  const float mref = (st.m_run == kNegInf) ? 0.f : st.m_run;
+  bf16x4 h0[4], h1[4];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const float p0v = fast_exp2(s0[r] - mref);
+    const float p1v = fast_exp2(s1[r] - mref);
+    st.l_run += p0v + p1v;
+    h0[r >> 2][r & 3] = (__bf16)p0v;
+    h1[r >> 2][r & 3] = (__bf16)p1v;
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) *(LDS_AS bf16x4*)(p0 + pw[q]) = h0[q];
+  LDS_AS float* xa = (LDS_AS float*)xch;
+  if (raise && g == 0) xa[32 * wave + n] = alpha;
+  if (lane_here() == 0) ((LDS_AS int*)(xch + kWideRows * 4))[wave] = raise ? 1 : 0;
+  __syncthreads();  // A: P keys 0..31, factors and flags published; every wave is past Q.K^T
+
+  LDS_AS char* p1 = cur + kStageCkvBytes;  // the stage's kpe region now holds P keys 32..63
+#pragma unroll
+  for (int q = 0; q < 4; ++q) *(LDS_AS bf16x4*)(p1 + pw[q]) = h1[q];
+  {
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+    const i32x4 fl = *(const LDS_AS i32x4*)(xch + kWideRows * 4);
+    if ((fl[0] | fl[1] | fl[2] | fl[3]) != 0) {
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const float f = fl[rt] ? xa[32 * rt + n] : 1.f;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) scale_acc<16>(st.o[ct][rt], f);
+      }
+    }
+  }
+
+  // ---- O^T[128 dims x 128 rows] += V^T . P^T, 16 keys per k-step
+  auto vread = [&](int ct, int kk) -> bf16x8 {  // kk = 16-key step within the stage
+    const i16x4 v0 = lds_read_tr(cur, vb[ct][0] + kk * 16 * kCkvRowBytes);
+    const i16x4 v1 = lds_read_tr(cur, vb[ct][1] + kk * 16 * kCkvRowBytes);
+    const i16x8 v = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    return __builtin_bit_cast(bf16x8, v);
+  };
+  auto pv_half = [&](const LDS_AS char* __restrict__ pbuf, int kk0) {
+    // per 16-key step: the 4 P^T fragments (one per row tile) stay in
+    // registers; V^T fragments (one per dim tile) stream two ahead
+    bf16x8 pf[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pf[r] = lds_read_b128(pbuf, pr[0] + r * 32 * 64);
+    bf16x8 v0 = vread(0, kk0), v1 = vread(1, kk0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {  // j = 4 kk + ct
+      const int kk = j >> 2, c = j & 3;
+      const bf16x8 v2 = (j + 2 < 8) ? vread((j + 2) & 3, kk0 + ((j + 2) >> 2)) : v1;
+      if (j == 4) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pf[r] = lds_read_b128(pbuf, pr[1] + r * 32 * 64);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        st.o[c][r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, pf[r], st.o[c][r], 0, 0, 0);
+      (void)kk;
+      v0 = v1;
+      v1 = v2;
+    }
+  };
+  pv_half(p0, 0);
+  __syncthreads();  // B: P keys 32..63 visible
+  pv_half(p1, 2);
+}
+
+template <int kPC>
+__device__ void split_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* smem, int wave, int lane) {
+  const int g = lane >> 5;
+  const int n = lane & 31;
+  const int rib = wave * 32 + n;  // the row this lane owns for Q.K^T and the softmax
+  const RowInfo ri = row_info(a, it, rib);
+  const int bound = row_key_bound(a, it, ri);
+
+  bf16x8 qf[36];
+  {
+    const bf16x8 z = {};
+    const __bf16* qn = (const __bf16*)a.q_nope + ri.qrow * kDimCkv + 8 * g;
+    const __bf16* qp = (const __bf16*)a.q_pe + ri.qrow * kDimKpe + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 32; ++ks) qf[ks] = ri.ok ? *(const bf16x8*)(qn + 16 * ks) : z;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qf[32 + ks] = ri.ok ? *(const bf16x8*)(qp + 16 * ks) : z;
+  }
+  int kb[8], pb[4], vb[4][2], pr[2], pw[4];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) kb[k] = ckv_off(n, 2 * k + g);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) pb[k] = kpe_off(n, 2 * k + g);
+  {
+    // V^T operand (32 dims x 16 keys): lane l reads key 8(l/32) + (l%16)/4 (+4),
+    // dims 128w + 32ct + 16((l/16)%2) + 4(l%4) .. +3
+    const int t = 8 * g + ((lane & 15) >> 2);
+    const int cl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    const int w8 = (lane & 1) ? 8 : 0;
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      vb[ct][0] = ckv_off(t, 4 * ct + cl) + w8 + 256 * wave;
+      vb[ct][1] = ckv_off(t + 4, 4 * ct + cl) + w8 + 256 * wave;
+    }
+  }
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) pr[kk] = p_off(n, 2 * kk + g);       // P^T operand: row n, keys 16kk + 8g ..
+#pragma unroll
+  for (int q = 0; q < 4; ++q) pw[q] = p_off(rib, q) + 8 * g;         // P writer: keys 8q + 4g .. +3
+
+  SplitState st;
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) st.o[ct][rt] = f32x16{};
+  st.m_run = kNegInf;
+  st.l_run = 0.f;
+
+  LDS_AS char* p0 = smem + kSplitP0Off;
+  LDS_AS char* xch = smem + kSplitXOff;
+  const int page_base = ld_const(a.kv_indptr, it.b);
+  const int nstage = (it.tok1 - it.tok0 + kStageTokens - 1) / kStageTokens;
+  if (nstage > 0) issue_stage_bf16<kPC>(a, smem, page_base, it.tok0, it.tok1, wave, lane);
+  for (int s = 0; s < nstage; ++s) {
+    wait_vmcnt<0>();
+    __syncthreads();  // stage s landed; every wave is done with stage s-1 (its buffer, P, factors)
+    LDS_AS char* cur = smem + (s & 1) * kStageBytes;
+    StageLoader<kPC> ld;
+    if (s + 1 < nstage) {
+      ld.begin(a, smem + ((s + 1) & 1) * kStageBytes, page_base, it.tok0 + (s + 1) * kStageTokens, it.tok1, wave);
+      split_stage<kPC, true>(a, qf, st, cur, p0, xch, it.tok0 + s * kStageTokens, bound, kb, pb, vb, pr, pw, g, n,
+                             ld, wave);
+    } else {
+      split_stage<kPC, false>(a, qf, st, cur, p0, xch, it.tok0 + s * kStageTokens, bound, kb, pb, vb, pr, pw, g,
+                              n, ld, wave);
+    }
+  }
+
+  // ---- epilogue: owners publish l; every wave normalises its dims of all 128 rows
+  const float l_tot = sum_xor32(st.l_run);
+  __syncthreads();  // every wave is done reading the factors of the last stage
+  if (g == 0) ((LDS_AS float*)xch)[rib] = l_tot;
+  if (ri.ok && g == 0) {
+    const bool empty = !(l_tot > 0.f);
+    store_lse(a, it, ri, rib, empty ? kNegInf : (st.m_run + __log2f(l_tot)) * kLn2);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    const int row = 32 * rt + n;
+    const RowInfo rj = row_info(a, it, row);
+    const float l = ((const LDS_AS float*)xch)[row];
+    const float inv = (l > 0.f) ? 1.f / l : 0.f;
+    if (rj.ok) {
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 v = {st.o[ct][rt][4 * q] * inv, st.o[ct][rt][4 * q + 1] * inv, st.o[ct][rt][4 * q + 2] * inv,
+                           st.o[ct][rt][4 * q + 3] * inv};
+          store4(a, it, rj, row, 128 * wave + 32 * ct + 8 * q + 4 * g, v);
+        }
+      }
+    }
+  }
+  __syncthreads();  // the exchange area is reused by the next item
 }
 
 // ---------------------------------------------------------------------------
@@ -1207,7 +1495,7 @@ void mla_attn_quad_kernel(AttnArgs a) {
 template <int kMode, int kPC, bool kFp8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_attn_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem_raw[kFp8 ? kFp8LdsBytes : kLdsBytes];
+  __shared__ __attribute__((aligned(1024))) char smem_raw[kFp8 ? kFp8LdsBytes : (kMode == 4 ? kSplitLdsBytes : kLdsBytes)];
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -1226,6 +1514,8 @@ void mla_attn_kernel(AttnArgs a) {
     it.slot = ld_const(ip, 7);
     if (kMode == 1) {
       wide_item<kPC, kFp8>(a, it, smem, wave, lane);
+    } else if (kMode == 4) {
+      split_item<kPC>(a, it, smem, wave, lane);
     } else {
       narrow_item<kPC, kFp8>(a, it, smem, wave, lane);
     }
@@ -1235,66 +1525,95 @@ void mla_attn_kernel(AttnArgs a) {
 // ---------------------------------------------------------------------------
 // Combine: merge the partial results of each split (request, row block).
 // out = sum_s w_s o_s / sum_s w_s with w_s = exp(lse_s - max lse), and
-// lse = max lse + ln sum w (the log-sum-exp identity).
+// lse = max lse + ln sum w (the log-sum-exp identity).  One wave per row:
+// lane s < nsplit reads lse_s, lane l then owns dims 8l..8l+7 and issues
+// the loads of up to 8 splits before it uses any, so the row's reads are in
+// flight together.
 // ---------------------------------------------------------------------------
-constexpr int kCombineRows = 16;  // rows per combine workgroup (4 per wave)
+constexpr int kCombineRows = 4;  // rows per combine workgroup (one per wave)
 
 __global__ __launch_bounds__(256) void mla_combine_kernel(AttnArgs a) {
-  // blockIdx.x -> (group, 16-row chunk): chunks of a group are consecutive
   const int chunks_per_group = a.rows_per_block / kCombineRows;
   const int gi = blockIdx.x / chunks_per_group;
-  const int r0 = (blockIdx.x - gi * chunks_per_group) * kCombineRows;
-  const SplitGroup grp = a.groups[gi];
-  const int d0 = (threadIdx.x & 63) * 8;
-  const int H = a.num_heads;
-  const int q_start = a.qo_indptr ? a.qo_indptr[grp.b] : grp.b;
-  for (int r = r0 + (threadIdx.x >> 6); r < min(grp.nrows, r0 + kCombineRows); r += 4) {
-    float M = kNegInf;
-    for (int s = 0; s < grp.nsplit; ++s)
-      M = fmaxf(M, a.part_lse[(size_t)(grp.slot0 + s) * a.rows_per_block + r]);
-    float W = 0.f;
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (M != kNegInf) {
-      for (int s = 0; s < grp.nsplit; ++s) {
-        const size_t slot_row = (size_t)(grp.slot0 + s) * a.rows_per_block + r;
-        const float ls = a.part_lse[slot_row];
-        const float w = (ls == kNegInf) ? 0.f : __expf(ls - M);
-        W += w;
-        const f32x4* src = (const f32x4*)(a.part_o + slot_row * kDimCkv + d0);
-        const f32x4 v0 = src[0], v1 = src[1];
+  const int r = (blockIdx.x - gi * chunks_per_group) * kCombineRows + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int32_t* gp = (const int32_t*)(a.groups + gi);
+  const int g_b = ld_const(gp, 0), g_row0 = ld_const(gp, 1), g_nrows = ld_const(gp, 2);
+  const int nsplit = ld_const(gp, 3), slot0 = ld_const(gp, 4);
+  if (r >= g_nrows) return;
+  const size_t row0 = (size_t)slot0 * a.rows_per_block + r;  // row r of the group's first slot
+  const size_t stride = (size_t)a.rows_per_block;             // rows between consecutive slots
+  // max and weight sum over the splits, 64 splits per pass (lane s + 64k)
+  float M = kNegInf;
+  for (int sp = lane; sp < nsplit; sp += 64) M = fmaxf(M, a.part_lse[row0 + sp * stride]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          acc[j] += w * v0[j];
-          acc[4 + j] += w * v1[j];
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  float W = 0.f;
+  for (int sp = lane; sp < nsplit; sp += 64) {
+    const float ls = a.part_lse[row0 + sp * stride];
+    W += (ls == kNegInf) ? 0.f : __expf(ls - M);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) W += __shfl_xor(W, o);
+  const int d0 = lane * 8;
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (M != kNegInf) {
+    for (int c = 0; c < nsplit; c += 64) {
+      // weight of split c + lane in lane `lane`
+      float wl = 0.f;
+      if (c + lane < nsplit) {
+        const float ls = a.part_lse[row0 + (c + lane) * stride];
+        wl = (ls == kNegInf) ? 0.f : __expf(ls - M);
+      }
+      const int n_here = min(64, nsplit - c);
+      for (int s0 = 0; s0 < n_here; s0 += 8) {
+        bf16x8 v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (s0 + j < n_here)
+            v[j] = *(const bf16x8*)(a.part_o + (row0 + (size_t)(c + s0 + j) * stride) * kDimCkv + d0);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float w = __shfl(wl, s0 + j);
+          if (s0 + j < n_here) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] += w * (float)v[j][e];
+          }
         }
       }
     }
-    const float inv = (W > 0.f) ? 1.f / W : 0.f;
-    const int rr = grp.row0 + r;
-    const int qi = rr / H;
-    const size_t qrow = (size_t)(q_start + qi) * H + (rr - qi * H);
-    if (a.out_bf16) {
-      bf16x8 h;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) h[j] = (__bf16)(acc[j] * inv);
-      *(bf16x8*)((__bf16*)a.out + qrow * kDimCkv + d0) = h;
-    } else {
-      f32x4* dst = (f32x4*)((float*)a.out + qrow * kDimCkv + d0);
-      dst[0] = f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
-      dst[1] = f32x4{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
-    }
-    if ((threadIdx.x & 63) == 0) a.lse[qrow] = (W > 0.f) ? M + __logf(W) : kNegInf;
   }
+  const float inv = (W > 0.f) ? 1.f / W : 0.f;
+  const int H = a.num_heads;
+  const int q_start = a.qo_indptr ? ld_const(a.qo_indptr, g_b) : g_b;
+  const int rr = g_row0 + r;
+  const int qi = rr / H;
+  const size_t qrow = (size_t)(q_start + qi) * H + (rr - qi * H);
+  if (a.out_bf16) {
+    bf16x8 h;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) h[j] = (__bf16)(acc[j] * inv);
+    *(bf16x8*)((__bf16*)a.out + qrow * kDimCkv + d0) = h;
+  } else {
+    f32x4* dst = (f32x4*)((float*)a.out + qrow * kDimCkv + d0);
+    dst[0] = f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+    dst[1] = f32x4{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
+  }
+  if (lane == 0) a.lse[qrow] = (W > 0.f) ? M + __logf(W) : kNegInf;
 }
 
 }  // namespace
 
 template <int kMode, int kPC>
 hipError_t launch_mode(const AttnArgs& a, int kv_fp8, hipStream_t stream) {
-  if (kv_fp8) {
-    hipLaunchKernelGGL((mla_attn_kernel<kMode, kPC, true>), dim3(a.num_wgs), dim3(256), 0, stream, a);
-  } else {
+  if constexpr (kMode == 4) {
     hipLaunchKernelGGL((mla_attn_kernel<kMode, kPC, false>), dim3(a.num_wgs), dim3(256), 0, stream, a);
+  } else {
+    if (kv_fp8) {
+      hipLaunchKernelGGL((mla_attn_kernel<kMode, kPC, true>), dim3(a.num_wgs), dim3(256), 0, stream, a);
+    } else {
+      hipLaunchKernelGGL((mla_attn_kernel<kMode, kPC, false>), dim3(a.num_wgs), dim3(256), 0, stream, a);
+    }
   }
   return hipGetLastError();
 }
@@ -1313,6 +1632,12 @@ hipError_t launch_attention(const AttnArgs& a, int tile_mode, int kv_fp8, hipStr
     if (pc == kPageBig) return launch_quad<kPageBig>(a, stream);
     if (pc == kPageMid) return launch_quad<kPageMid>(a, stream);
     return launch_quad<kPageSmall>(a, stream);
+  }
+  if (tile_mode == 4) {
+    if (kv_fp8) return hipErrorNotSupported;  // rejected when the plan is made
+    if (pc == kPageBig) return launch_mode<4, kPageBig>(a, 0, stream);
+    if (pc == kPageMid) return launch_mode<4, kPageMid>(a, 0, stream);
+    return launch_mode<4, kPageSmall>(a, 0, stream);
   }
   if (tile_mode == 1) {
     if (pc == kPageBig) return launch_mode<1, kPageBig>(a, kv_fp8, stream);

@@ -55,7 +55,7 @@ struct AttnArgs {
   const SplitGroup* groups;
   void* out;
   float* lse;
-  float* part_o;           // [slots][rows_per_block][512] fp32, normalised partial outputs
+  __bf16* part_o;          // [slots][rows_per_block][512] bf16, normalised partial outputs
   float* part_lse;         // [slots][rows_per_block] fp32 (natural log)
   float scale_log2;        // sm_scale * log2(e)
   int32_t num_heads;

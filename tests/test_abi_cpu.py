@@ -79,7 +79,7 @@ def _check_cover(plan, kv_len, q_len, H, causal=False, prefill=False):
     return items, ptr
 
 
-@pytest.mark.parametrize("tile_mode", [0, 1, 2, 3])
+@pytest.mark.parametrize("tile_mode", [0, 1, 2, 3, 4])
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_decode_schedule_covers_every_key_once(mla, tile_mode, seed):
     rng = np.random.default_rng(seed)
@@ -171,7 +171,8 @@ def test_plan_argument_errors(mla):
     assert _status(mla, **{**pre, "qo_indptr": [0, 3, 2]}) == -1        # decreasing
     assert _status(mla, **{**pre, "kv_format": 1}) == -2                # fp8 prefill
     assert _status(mla, **{**ok, "batch": 0, "kv_len": [], "kv_indptr": [0]}) == 0
-    assert _status(mla, **{**ok, "tile_mode": 4}) == -1
+    assert _status(mla, **{**ok, "tile_mode": 5}) == -1
+    assert _status(mla, **{**ok, "kv_format": 1, "tile_mode": 4}) == -2  # fp8 has no split tile
     assert _status(mla, **{**ok, "kv_format": 1}) == 0                  # fp8 decode
     assert _status(mla, **{**ok, "kv_format": 1, "tile_mode": 3}) == -2  # fp8 has no quad tile
 
@@ -217,7 +218,7 @@ def test_workspace_grows_with_splits(mla):
     p8 = mla.mla_plan_create(0, 4, 128, 64, int(indptr[-1]), lens, indptr, num_cus=4, force_splits=8)
     assert p1.num_split_groups == 0
     assert p8.num_split_groups == 4
-    assert p8.workspace_bytes >= 4 * 8 * 128 * 513 * 4
+    assert p8.workspace_bytes >= 4 * 8 * 128 * (512 * 2 + 4)  # bf16 partial rows + fp32 lse
 
 
 def test_auto_mode_choice(mla):
