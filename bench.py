@@ -106,6 +106,68 @@ def read_counters(config_name, kernel_sha):
         return None
 
 
+def _pmc_values(csv_dir, name_filter):
+    """Per-dispatch values of the one counter in a rocprofv3 --pmc csv run,
+    for dispatches whose kernel name contains name_filter."""
+    import csv
+    import glob
+
+    vals = []
+    for f in glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if name_filter in r.get("Kernel_Name", ""):
+                vals.append(float(r["Counter_Value"]))
+    return vals
+
+
+def write_counters(config_name, pmc_dir, copy_bytes, commands):
+    """Summarise FETCH_SIZE / WRITE_SIZE runs of the attention kernel into
+    profiles/attention_<config>_counters.txt, scaled by the same counters
+    read on a plain copy kernel of known size (copy_bytes read + written).
+
+    Layout under pmc_dir: fetch/, write/ (bench runs of the workload) and
+    copy_fetch/, copy_write/ (bench --copy-calibration runs)."""
+    import statistics
+
+    cf = statistics.median(_pmc_values(os.path.join(pmc_dir, "copy_fetch"), "copy"))
+    cw = statistics.median(_pmc_values(os.path.join(pmc_dir, "copy_write"), "copy"))
+    kib = copy_bytes / 1024.0
+    f_fetch, f_write = kib / cf, kib / cw
+    fv = _pmc_values(os.path.join(pmc_dir, "fetch"), "mla_attn")
+    wv = _pmc_values(os.path.join(pmc_dir, "write"), "mla_attn")
+    fetch_b = statistics.median(fv) * 1024 * f_fetch
+    write_b = statistics.median(wv) * 1024 * f_write
+    path = os.path.join(ROOT, "profiles", f"attention_{config_name}_counters.txt")
+    with open(path, "w") as fo:
+        fo.write(f"# HBM traffic of the attention kernel, workload {config_name}\n")
+        fo.write("# rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (KiB per dispatch), median over dispatches,\n")
+        fo.write(f"# scaled by the same counters on a plain copy kernel of {copy_bytes} bytes read + written\n")
+        for c in commands:
+            fo.write(f"# command: {c}\n")
+        fo.write(f"kernel_source_sha256: {kernel_sha()}\n")
+        fo.write(f"copy_fetch_kib: {cf:.1f}\ncopy_write_kib: {cw:.1f}\n")
+        fo.write(f"fetch_scale: {f_fetch:.4f}\nwrite_scale: {f_write:.4f}\n")
+        fo.write(f"attention_fetch_kib_median: {statistics.median(fv):.1f}  (n={len(fv)})\n")
+        fo.write(f"attention_write_kib_median: {statistics.median(wv):.1f}  (n={len(wv)})\n")
+        fo.write(f"hbm_fetch_bytes_per_launch: {fetch_b:.0f}\n")
+        fo.write(f"hbm_write_bytes_per_launch: {write_b:.0f}\n")
+        fo.write(f"hbm_bytes_per_launch: {fetch_b + write_b:.0f}\n")
+    return path
+
+
+def copy_calibration(nbytes):
+    """A plain device copy of nbytes (read nbytes, write nbytes), five times."""
+    import torch
+
+    n = nbytes // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n * 4, "repeats": 5}), flush=True)
+
+
 def kernel_sha():
     import hashlib
 
@@ -178,8 +240,22 @@ def main():
                     help="replicate the cache pool until consecutive steps are this many bytes apart")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--tile-mode", type=int, default=0, help="0 = planner's choice; 1 wide, 2 narrow, 3 quad")
+    ap.add_argument("--tile-mode", type=int, default=0,
+                    help="0 = planner's choice; 1 wide, 2 narrow, 3 quad, 4 split")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain copy of BYTES (counter calibration) and exit")
+    ap.add_argument("--write-counters", metavar="PMC_DIR",
+                    help="summarise rocprofv3 FETCH_SIZE/WRITE_SIZE runs under PMC_DIR into profiles/ and exit")
+    ap.add_argument("--copy-bytes", type=int, default=1 << 30)
+    ap.add_argument("--command", action="append", default=[], help="command lines recorded with --write-counters")
     args = ap.parse_args()
+
+    if args.write_counters:
+        print(write_counters(args.config, args.write_counters, args.copy_bytes, args.command))
+        return
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -271,6 +347,9 @@ def main():
     pct = 100.0 * max((bytes_alg / (HBM_PEAK_GBS * 1e9)), flops / (BF16_PEAK_TFLOPS * 1e12)) / t_s
     sha = kernel_sha()
     traffic = read_counters(args.config, sha)
+    if traffic is not None:
+        log(f"bench: HBM traffic per attention launch {traffic / 1e6:.1f} MB "
+            f"({traffic / bytes_alg:.2f}x the algorithmic {bytes_alg / 1e6:.1f} MB)")
     if hbm_bound:
         achieved = bytes_alg / ta_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -286,7 +365,13 @@ def main():
     roof["algorithmic_bytes_per_launch"] = bytes_alg
     roof["algorithmic_flops_per_launch"] = flops
     if traffic is not None:
-        roof["traffic_note"] = "GB/s of HBM traffic per launch from rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-kernel scaled"
+        roof["traffic_bytes_per_launch"] = round(traffic)
+        roof["traffic_note"] = ("GB/s: HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-kernel "
+                                "scaled) / average launch time")
+    result_steps = {"p10_us": round(attn_ms[len(attn_ms) // 10] * 1e3, 2),
+                    "p90_us": round(attn_ms[(9 * len(attn_ms)) // 10] * 1e3, 2),
+                    "median_us": round(attn_ms[len(attn_ms) // 2] * 1e3, 2)}
+    roof["kernel_time"] = result_steps
 
     result = {
         "metric": METRIC,

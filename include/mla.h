@@ -203,11 +203,12 @@ mla_status mla_decode_fp8(const mla_plan* plan, const void* q_nope, const void* 
                           int32_t out_dtype, float* lse, void* workspace,
                           size_t workspace_bytes, hipStream_t stream);
 
-/* Diagnostics for timing: the next run call made on this host thread
- * records `before` on its stream right before the attention kernel and
- * `after` right after it (before the split combine), then forgets both.
- * Pass NULL, NULL to cancel.  The events are created and owned by the
- * caller; the computation is unchanged.                                   */
+/* Diagnostics for timing: the next run call made on this host thread has
+ * the attention kernel's own dispatch record `before` when the kernel
+ * starts and `after` when it ends (hipExtLaunchKernel's start / stop
+ * events; the split combine is not included), then forgets both.  Pass
+ * NULL, NULL to cancel.  The events are created and owned by the caller;
+ * the computation is unchanged.                                           */
 mla_status mla_record_attention_events(hipEvent_t before, hipEvent_t after);
 
 /* Static description of a status code. */

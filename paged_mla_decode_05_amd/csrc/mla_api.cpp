@@ -361,10 +361,8 @@ mla_status run(const mla_plan* p, int32_t want_kind, int32_t want_format, const 
   a.num_groups = (int32_t)p->groups.size();
   hipEvent_t ev0 = t_ev_before, ev1 = t_ev_after;
   t_ev_before = t_ev_after = nullptr;
-  if (ev0 && hipEventRecord(ev0, stream) != hipSuccess) return MLA_ERR_DEVICE;
-  hipError_t e = mla::launch_attention(a, p->tile_mode, want_format == MLA_KV_FP8_E4M3_T128, stream);
+  hipError_t e = mla::launch_attention(a, p->tile_mode, want_format == MLA_KV_FP8_E4M3_T128, stream, ev0, ev1);
   if (e != hipSuccess) return MLA_ERR_DEVICE;
-  if (ev1 && hipEventRecord(ev1, stream) != hipSuccess) return MLA_ERR_DEVICE;
   if (!p->groups.empty()) {
     e = mla::launch_combine(a, stream);
     if (e != hipSuccess) return MLA_ERR_DEVICE;

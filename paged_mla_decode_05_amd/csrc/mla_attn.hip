@@ -39,6 +39,7 @@
 //    normalised partial output and its lse; mla_combine merges them by the
 //    log-sum-exp identity (the split-K statistics of
 //    "mla_decoding_single_batch").
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -131,6 +132,13 @@ __device__ __forceinline__ void scale_acc(float __attribute__((ext_vector_type(N
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// A compiler memory barrier: LDS reads written after it are not hoisted
+// above it, nor those before it sunk below it.  The MFMA loops place one per
+// step so that each operand read is issued a fixed number of MFMAs ahead of
+// its use (the scheduler would otherwise sink it next to the use); the
+// compiler still inserts the lgkmcnt wait before the use.
+__device__ __forceinline__ void pin_loads() { asm volatile("" ::: "memory"); }
+
 // S^T chains on mfma_f32_32x32x16_bf16 with the accumulator in VGPRs.  The
 // compiler gives every builtin MFMA of these kernels an AGPR accumulator,
 // and the 256 AGPRs are O's; S must live in VGPRs, so its MFMAs are written
@@ -140,10 +148,10 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // MFMA and the first other reader or writer of the accumulator (the XDL
 // write -> VALU read / SrcC read -> VALU write distance of gfx950 is less).
 __device__ __forceinline__ void mfma32_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void mfma32_acc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void mfma32_drain(f32x16& x) { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x)); }
 __device__ __forceinline__ void mfma32_drain(f32x16& x, f32x16& y) {
@@ -179,6 +187,26 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t
       : "v"(voff), "s"(sbase), "s"(lds));
 }
 
+// dma16 gated by `on` (all ones or zero, an SGPR; every lane active at the
+// call): with zero the load executes with an empty EXEC mask and moves
+// nothing.  Lets a loop issue its prefetch slices without a branch.
+__device__ __forceinline__ void dma16_on(const void* sbase, uint32_t voff, uint32_t lds, uint32_t on) {
+  uint32_t save;
+  uint64_t save_exec;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b64 %1, exec\n\t"
+      "s_mov_b32 exec_lo, %5\n\t"
+      "s_mov_b32 exec_hi, %5\n\t"
+      "s_mov_b32 m0, %4\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b64 exec, %1\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save), "=&s"(save_exec)
+      : "v"(voff), "s"(sbase), "s"(lds), "s"(on));
+}
+
 // The same with a full 64-bit per-lane address (lanes reading unrelated pages).
 __device__ __forceinline__ void dma16_v(const void* vaddr, uint32_t lds) {
   uint32_t save;
@@ -190,6 +218,23 @@ __device__ __forceinline__ void dma16_v(const void* vaddr, uint32_t lds) {
       "s_mov_b32 m0, %0"
       : "=&s"(save)
       : "v"(vaddr), "s"(lds));
+}
+
+__device__ __forceinline__ void dma16_v_on(const void* vaddr, uint32_t lds, uint32_t on) {
+  uint32_t save;
+  uint64_t save_exec;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b64 %1, exec\n\t"
+      "s_mov_b32 exec_lo, %4\n\t"
+      "s_mov_b32 exec_hi, %4\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b64 exec, %1\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save), "=&s"(save_exec)
+      : "v"(vaddr), "s"(lds), "s"(on));
 }
 
 // The lane id, re-materialised where it is used: values derived from it are
@@ -241,6 +286,7 @@ struct StageLoader {
   int last;                 // last live key of the stage, relative to s_tok0
   int s_tok0;
   LDS_AS char* st;
+  uint32_t on = ~0u;        // EXEC mask (both halves) of the slices: zero turns issue() into no-ops
 
   __device__ __forceinline__ void begin(const AttnArgs& a, LDS_AS char* stage, int page_base, int tok0,
                                         int tok_end, int wave) {
@@ -294,9 +340,9 @@ struct StageLoader {
       const int t = wave * 16 + i;
       const uint32_t swz_off = (uint32_t)((lane ^ ckv_swz(t)) << 4);
       if (kPageClass == kPageBig) {
-        dma16(ckv_row[0], (uint32_t)(min(t, last) * kCkvRowBytes) + swz_off, lds_addr(st + t * kCkvRowBytes));
+        dma16_on(ckv_row[0], (uint32_t)(min(t, last) * kCkvRowBytes) + swz_off, lds_addr(st + t * kCkvRowBytes), on);
       } else {
-        dma16(ckv_row[i], swz_off, lds_addr(st + t * kCkvRowBytes));
+        dma16_on(ckv_row[i], swz_off, lds_addr(st + t * kCkvRowBytes), on);
       }
       return;
     }
@@ -307,15 +353,15 @@ struct StageLoader {
     const int c = (lane & 7) ^ kpe_swz(t);
     LDS_AS char* dst = st + kStageCkvBytes + grp * 1024;
     if (kPageClass == kPageBig) {
-      dma16(kpe_base[0], (uint32_t)(tc * kKpeRowBytes + (c << 4)), lds_addr(dst));
+      dma16_on(kpe_base[0], (uint32_t)(tc * kKpeRowBytes + (c << 4)), lds_addr(dst), on);
     } else if (kPageClass == kPageMid) {
-      dma16(kpe_base[k], (uint32_t)((tc - kpe_t0[k]) * kKpeRowBytes + (c << 4)), lds_addr(dst));
+      dma16_on(kpe_base[k], (uint32_t)((tc - kpe_t0[k]) * kKpeRowBytes + (c << 4)), lds_addr(dst), on);
     } else {
       const int sh = a.page_shift;
       const int T = s_tok0 + tc;
       const char* src = (const char*)a.kpe + (((size_t)kpe_page[k] << sh) + (T & ((1 << sh) - 1))) * kKpeRowBytes +
                         (c << 4);
-      dma16_v(src, lds_addr(dst));
+      dma16_v_on(src, lds_addr(dst), on);
     }
   }
 };
@@ -528,31 +574,94 @@ struct WideState {
   float l_run;    // running sum of this lane's keys
 };
 
-template <int kPC, bool kFp8>
+// Value fences for hand-interleaving VALU work into an MFMA stream: code
+// that uses x runs after hold(x), and x is computed before done(x).  Both
+// are empty volatile asm, ordered with the (volatile) MFMA and barrier asm,
+// so work placed between them stays in that slot of the instruction stream.
+__device__ __forceinline__ void hold(float& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void done(float x) { asm volatile("" ::"v"(x)); }
+
+// Online-softmax pieces of one 32-key sub-tile S^T (lane: row n, keys
+// 8(r/4) + 4g + r%4), split so that they can ride along an MFMA stream.
+struct WideSoftmax {
+  float mx = kNegInf;
+  bool raise = false;
+  float alpha = 1.f;
+  float mref = 0.f;
+};
+
+template <int kPC, bool kFp8, bool kPrefetch>
 __device__ __forceinline__ void wide_stage(const AttnArgs& a, const bf16x8 (&qf)[36], WideState& st,
                                            const LDS_AS char* __restrict__ cur, int stage_tok, int bound,
                                            const int (&kb)[8], const int (&pb)[4], const int (&vb)[8],
-                                           int g, StageLoader<kPC>& ld, bool prefetch, int wave,
+                                           int g, StageLoader<kPC>& ld, int wave,
                                            const LDS_AS float* __restrict__ sct) {
+  // fp8 cache: scales of this lane's keys tb + 8q + 4g + (0..3) in tile t
+  auto scales = [&](int tb, int t, int q) -> f32x4 {
+    return *(const LDS_AS f32x4*)(sct + t * kStageTokens + tb + 8 * q + 4 * g);
+  };
+  auto kread = [&](int tb, int ks) -> bf16x8 {
+    return ks < 32 ? lds_read_b128(cur, kb[ks & 7] + 256 * (ks >> 3) + tb * kCkvRowBytes)
+                   : lds_read_b128(cur, pb[ks - 32] + tb * kKpeRowBytes);
+  };
+  auto vread = [&](int tb, int j) -> bf16x8 {  // j = 2*cb + kk
+    const int cb = j >> 1, kk = j & 1;
+    const int imm = (tb + 16 * kk) * kCkvRowBytes + 256 * (cb >> 2);
+    const i16x4 v0 = lds_read_tr(cur, vb[cb & 3] + imm);
+    const i16x4 v1 = lds_read_tr(cur, vb[4 + (cb & 3)] + imm);
+    const i16x8 v = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    return __builtin_bit_cast(bf16x8, v);
+  };
+
+  // ---- softmax pieces on S^T of sub-tile tb (values scaled to log2 units in place)
+  auto sm_scale_mask = [&](float (&sv)[16], WideSoftmax& sm, int tb, int r) {
+    float x = sv[r];
+    hold(x);
+    const int tok = stage_tok + tb + 8 * (r >> 2) + 4 * g + (r & 3);
+    x = tok < bound ? x * a.scale_log2 : kNegInf;
+    sv[r] = x;
+    sm.mx = fmaxf(sm.mx, x);
+    done(sm.mx);
+  };
+  auto sm_decide = [&](WideSoftmax& sm) {  // row max over the sub-tile; raise the running max if needed
+    sm.mx = max_xor32(sm.mx);
+    sm.raise = __builtin_amdgcn_ballot_w64(sm.mx > st.m_run + kRescaleSlack) != 0;
+    if (sm.raise) {
+      const float m_new = fmaxf(st.m_run, sm.mx);
+      sm.alpha = (st.m_run == kNegInf) ? 0.f : fast_exp2(st.m_run - m_new);
+      st.l_run *= sm.alpha;
+      st.m_run = m_new;
+    }
+    sm.mref = (st.m_run == kNegInf) ? 0.f : st.m_run;
+    done(sm.mref);
+  };
+  auto sm_exp = [&](const float (&sv)[16], const WideSoftmax& sm, bf16x8 (&pt)[2], float (&pf)[16], int r) {
+    float x = sv[r];
+    hold(x);
+    const float p = fast_exp2(x - sm.mref);
+    st.l_run += p;
+    pf[r] = p;
+    pt[r >> 3][r & 7] = (__bf16)p;
+    done(st.l_run);
+  };
+  auto rescale_o = [&](float alpha) {
 #pragma unroll
-  for (int sub = 0; sub < 2; ++sub) {
-    const int tb = sub * 32;
-    // fp8 cache: scales of this lane's keys tb + 8q + 4g + (0..3) in tile t
-    auto scales = [&](int t, int q) -> f32x4 {
-      return *(const LDS_AS f32x4*)(sct + t * kStageTokens + tb + 8 * q + 4 * g);
-    };
-    // S^T[32 keys x 32 rows] = K . Q^T over 576 dims
-    f32x16 sacc;
+    for (int cb = 0; cb < 16; ++cb) scale_acc<16>(st.o[cb], alpha);
+  };
+
+  // ---- S^T[32 keys x 32 rows] = K . Q^T over 576 dims for sub-tile tb, with
+  // `side(ks)` run after MFMA ks (interleaved VALU work of another phase)
+  auto qk = [&](f32x16& sacc, int tb, int dma0, auto&& side) {
     f32x16 part;  // fp8: one 128-dim tile of the codes' dot products
-    auto kread = [&](int ks) -> bf16x8 {
-      return ks < 32 ? lds_read_b128(cur, kb[ks & 7] + 256 * (ks >> 3) + tb * kCkvRowBytes)
-                     : lds_read_b128(cur, pb[ks - 32] + tb * kKpeRowBytes);
-    };
-    bf16x8 k0 = kread(0), k1 = kread(1);
+    constexpr int KD = 4;  // K fragments in flight
+    bf16x8 kr[KD];
+#pragma unroll
+    for (int i = 0; i < KD; ++i) kr[i] = kread(tb, i);
 #pragma unroll
     for (int ks = 0; ks < 36; ++ks) {
-      if (prefetch && (ks & 3) == 0) ld.issue(a, sub * 9 + (ks >> 2), wave);  // 9 slices per sub-tile
-      const bf16x8 k2 = (ks + 2 < 36) ? kread(ks + 2) : k1;
+      pin_loads();
+      if (kPrefetch && (ks & 3) == 0) ld.issue(a, dma0 + (ks >> 2), wave);  // 9 slices per sub-tile
+      const bf16x8 k0 = kr[ks % KD];
       if (kFp8 && ks < 32) {
         if ((ks & 7) == 0) {
           mfma32_first(part, k0, qf[ks]);
@@ -563,7 +672,7 @@ __device__ __forceinline__ void wide_stage(const AttnArgs& a, const bf16x8 (&qf)
           mfma32_drain(part);
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const f32x4 sc = scales(ks >> 3, q);
+            const f32x4 sc = scales(tb, ks >> 3, q);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const float t = part[4 * q + r] * sc[r];
@@ -576,66 +685,94 @@ __device__ __forceinline__ void wide_stage(const AttnArgs& a, const bf16x8 (&qf)
       } else {
         mfma32_acc(sacc, k0, qf[ks]);
       }
-      k0 = k1;
-      k1 = k2;
+      if (ks + KD < 36) kr[ks % KD] = kread(tb, ks + KD);
+      side(ks);
     }
+    pin_loads();
     mfma32_drain(sacc);
-    // online softmax (base 2); lane holds keys 8(r/4) + 4g + r%4 of the sub-tile
-    float sv[16];
-    float mx = kNegInf;
+  };
+
+  // ---- O^T[32 dims x 32 rows] += V^T[32 dims x 16 keys] . P^T[16 keys x 32 rows] for sub-tile tb
+  auto pv = [&](int tb, bf16x8 (&pt)[2], const float (&pf)[16], auto&& side) {
+    constexpr int VD = 3;  // V^T fragments in flight
+    bf16x8 vr[VD];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int tok = stage_tok + tb + 8 * (r >> 2) + 4 * g + (r & 3);
-      const float x = sacc[r] * a.scale_log2;
-      sv[r] = tok < bound ? x : kNegInf;
-      mx = fmaxf(mx, sv[r]);
-    }
-    mx = max_xor32(mx);
-    const bool need = mx > st.m_run + kRescaleSlack;
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
-      const float m_new = fmaxf(st.m_run, mx);
-      const float alpha = (st.m_run == kNegInf) ? 0.f : fast_exp2(st.m_run - m_new);
-      st.l_run *= alpha;
-#pragma unroll
-      for (int cb = 0; cb < 16; ++cb) scale_acc<16>(st.o[cb], alpha);
-      st.m_run = m_new;
-    }
-    const float mref = (st.m_run == kNegInf) ? 0.f : st.m_run;
-    bf16x8 pt[2];
-    float pf[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = fast_exp2(sv[r] - mref);
-      st.l_run += p;
-      pf[r] = p;
-      pt[r >> 3][r & 7] = (__bf16)p;
-    }
-    // O^T[32 dims x 32 rows] += V^T[32 dims x 16 keys] . P^T[16 keys x 32 rows]
-    auto vread = [&](int j) -> bf16x8 {  // j = 2*cb + kk
-      const int cb = j >> 1, kk = j & 1;
-      const int imm = (tb + 16 * kk) * kCkvRowBytes + 256 * (cb >> 2);
-      const i16x4 v0 = lds_read_tr(cur, vb[cb & 3] + imm);
-      const i16x4 v1 = lds_read_tr(cur, vb[4 + (cb & 3)] + imm);
-      const i16x8 v = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-      return __builtin_bit_cast(bf16x8, v);
-    };
-    bf16x8 v0 = vread(0), v1 = vread(1);
+    for (int i = 0; i < VD; ++i) vr[i] = vread(tb, i);
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
+      pin_loads();
       if (kFp8 && (j & 7) == 0) {
         // output dims of tile j/8: P scaled by each key's tile scale
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const f32x4 sc = scales(j >> 3, q);
+          const f32x4 sc = scales(tb, j >> 3, q);
 #pragma unroll
           for (int r = 0; r < 4; ++r) pt[q >> 1][4 * (q & 1) + r] = (__bf16)(pf[4 * q + r] * sc[r]);
         }
       }
-      const bf16x8 v2 = (j + 2 < 32) ? vread(j + 2) : v1;
-      st.o[j >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, pt[j & 1], st.o[j >> 1], 0, 0, 0);
-      v0 = v1;
-      v1 = v2;
+      st.o[j >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[j % VD], pt[j & 1], st.o[j >> 1], 0, 0, 0);
+      if (j + VD < 32) vr[j % VD] = vread(tb, j + VD);
+      side(j);
     }
+    pin_loads();
+  };
+
+  // Software pipeline over the two sub-tiles:
+  //   QK(0);  QK(1) + softmax(0);  PV(0) + softmax(1);  PV(1)
+  // The softmax VALU work issues between MFMAs of the other phase.  A raise
+  // of the running max found in softmax(1) rescales O only after PV(0) has
+  // accumulated (its P was computed against the old reference).
+  f32x16 sa0, sa1;
+  float s0[16], s1[16];
+  WideSoftmax sm0, sm1;
+  bf16x8 pt0[2], pt1[2];
+  float pf0[16], pf1[16];
+  if constexpr (kFp8) {
+    // fp8: the per-tile scale work already rides along both products, and
+    // its registers leave no room for a second sub-tile in flight
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      qk(sa0, 32 * sub, 9 * sub, [&](int) {});
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s0[r] = sa0[r];
+      WideSoftmax sm;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sm_scale_mask(s0, sm, 32 * sub, r);
+      sm_decide(sm);
+      if (sm.raise) rescale_o(sm.alpha);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sm_exp(s0, sm, pt0, pf0, r);
+      pv(32 * sub, pt0, pf0, [&](int) {});
+    }
+  } else {
+    // Software pipeline over the two sub-tiles:
+    //   QK(0);  QK(1) + softmax(0);  PV(0) + softmax(1);  PV(1)
+    // The softmax VALU work issues between MFMAs of the other phase.  A
+    // raise of the running max found in softmax(1) rescales O only after
+    // PV(0) has accumulated (its P was computed against the old reference).
+    qk(sa0, 0, 0, [&](int) {});
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s0[r] = sa0[r];
+    qk(sa1, 32, 9, [&](int ks) {
+      if (ks < 16) sm_scale_mask(s0, sm0, 0, ks);
+      if (ks == 16) sm_decide(sm0);
+      if (ks >= 17 && ks < 33) sm_exp(s0, sm0, pt0, pf0, ks - 17);
+    });
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s1[r] = sa1[r];
+    if (sm0.raise) rescale_o(sm0.alpha);  // no P.V is in flight here
+    pv(0, pt0, pf0, [&](int j) {
+      if (j < 16) sm_scale_mask(s1, sm1, 32, j);
+      if (j == 16) sm_decide(sm1);
+      if (j >= 17) sm_exp(s1, sm1, pt1, pf1, j - 17);
+    });
+    sm_exp(s1, sm1, pt1, pf1, 15);
+    if (sm1.raise) {
+      // the last P.V MFMAs write O: let them retire before the AGPRs are read
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+      rescale_o(sm1.alpha);
+    }
+    pv(32, pt1, pf1, [&](int) {});
   }
 }
 
@@ -645,9 +782,14 @@ __device__ __forceinline__ void wide_body(const AttnArgs& a, const bf16x8 (&qf)[
                                           bool prefetch, int page_base, int next_tok, int tok_end,
                                           int stage_tok, int bound, const int (&kb)[8], const int (&pb)[4],
                                           const int (&vb)[8], int wave, int lane) {
+  // The slices of the next stage ride along this stage's Q.K^T.  For the
+  // last stage they are issued with an empty EXEC mask (and addresses of
+  // this stage, so every page lookup stays inside the request): one
+  // instruction stream, no branch in the MFMA loop.
   StageLoader<kPC> ld;
-  if (prefetch) ld.begin(a, nxt, page_base, next_tok, tok_end, wave);
-  wide_stage<kPC, false>(a, qf, st, cur, stage_tok, bound, kb, pb, vb, lane >> 5, ld, prefetch, wave, nullptr);
+  ld.begin(a, nxt, page_base, prefetch ? next_tok : stage_tok, tok_end, wave);
+  ld.on = __builtin_amdgcn_readfirstlane(prefetch ? ~0u : 0u);
+  wide_stage<kPC, false, true>(a, qf, st, cur, stage_tok, bound, kb, pb, vb, lane >> 5, ld, wave, nullptr);
 }
 
 template <int kPC, bool kFp8>
@@ -713,8 +855,8 @@ __device__ void wide_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* sm
         issue_stage_fp8<kPC>(a, raw + (s & 1) * kFp8RawBytes, page_base, it.tok0 + (s + 2) * kStageTokens, it.tok1,
                              wave);
       StageLoader<kPC> none;
-      wide_stage<kPC, true>(a, qf, st, smem, it.tok0 + s * kStageTokens, bound, kb, pb, vb, g, none, false, wave,
-                            sct);
+      wide_stage<kPC, true, false>(a, qf, st, smem, it.tok0 + s * kStageTokens, bound, kb, pb, vb, g, none, wave,
+                                   sct);
     }
     __syncthreads();  // the bf16 stage is free for the next item
   } else {
@@ -1604,49 +1746,54 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(AttnArgs a) {
 
 }  // namespace
 
+// Attention launches go through hipExtLaunchKernelGGL so that optional
+// timing events are recorded by the kernel's own dispatch (start and end of
+// its execution, no queue gaps); with null events it is a plain launch.
 template <int kMode, int kPC>
-hipError_t launch_mode(const AttnArgs& a, int kv_fp8, hipStream_t stream) {
+hipError_t launch_mode(const AttnArgs& a, int kv_fp8, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
   if constexpr (kMode == 4) {
-    hipLaunchKernelGGL((mla_attn_kernel<kMode, kPC, false>), dim3(a.num_wgs), dim3(256), 0, stream, a);
+    hipExtLaunchKernelGGL((mla_attn_kernel<kMode, kPC, false>), dim3(a.num_wgs), dim3(256), 0, stream, t0, t1, 0, a);
   } else {
     if (kv_fp8) {
-      hipLaunchKernelGGL((mla_attn_kernel<kMode, kPC, true>), dim3(a.num_wgs), dim3(256), 0, stream, a);
+      hipExtLaunchKernelGGL((mla_attn_kernel<kMode, kPC, true>), dim3(a.num_wgs), dim3(256), 0, stream, t0, t1, 0, a);
     } else {
-      hipLaunchKernelGGL((mla_attn_kernel<kMode, kPC, false>), dim3(a.num_wgs), dim3(256), 0, stream, a);
+      hipExtLaunchKernelGGL((mla_attn_kernel<kMode, kPC, false>), dim3(a.num_wgs), dim3(256), 0, stream, t0, t1, 0,
+                            a);
     }
   }
   return hipGetLastError();
 }
 
 template <int kPC>
-hipError_t launch_quad(const AttnArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((mla_attn_quad_kernel<kPC>), dim3(a.grid), dim3(256), 0, stream, a);
+hipError_t launch_quad(const AttnArgs& a, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
+  hipExtLaunchKernelGGL((mla_attn_quad_kernel<kPC>), dim3(a.grid), dim3(256), 0, stream, t0, t1, 0, a);
   return hipGetLastError();
 }
 
-hipError_t launch_attention(const AttnArgs& a, int tile_mode, int kv_fp8, hipStream_t stream) {
+hipError_t launch_attention(const AttnArgs& a, int tile_mode, int kv_fp8, hipStream_t stream, hipEvent_t t0,
+                            hipEvent_t t1) {
   if (a.num_wgs <= 0) return hipSuccess;
   const int pc = a.page_shift >= 6 ? kPageBig : (a.page_shift >= 3 ? kPageMid : kPageSmall);
   if (tile_mode == 3) {
     if (kv_fp8) return hipErrorNotSupported;  // rejected when the plan is made
-    if (pc == kPageBig) return launch_quad<kPageBig>(a, stream);
-    if (pc == kPageMid) return launch_quad<kPageMid>(a, stream);
-    return launch_quad<kPageSmall>(a, stream);
+    if (pc == kPageBig) return launch_quad<kPageBig>(a, stream, t0, t1);
+    if (pc == kPageMid) return launch_quad<kPageMid>(a, stream, t0, t1);
+    return launch_quad<kPageSmall>(a, stream, t0, t1);
   }
   if (tile_mode == 4) {
     if (kv_fp8) return hipErrorNotSupported;  // rejected when the plan is made
-    if (pc == kPageBig) return launch_mode<4, kPageBig>(a, 0, stream);
-    if (pc == kPageMid) return launch_mode<4, kPageMid>(a, 0, stream);
-    return launch_mode<4, kPageSmall>(a, 0, stream);
+    if (pc == kPageBig) return launch_mode<4, kPageBig>(a, 0, stream, t0, t1);
+    if (pc == kPageMid) return launch_mode<4, kPageMid>(a, 0, stream, t0, t1);
+    return launch_mode<4, kPageSmall>(a, 0, stream, t0, t1);
   }
   if (tile_mode == 1) {
-    if (pc == kPageBig) return launch_mode<1, kPageBig>(a, kv_fp8, stream);
-    if (pc == kPageMid) return launch_mode<1, kPageMid>(a, kv_fp8, stream);
-    return launch_mode<1, kPageSmall>(a, kv_fp8, stream);
+    if (pc == kPageBig) return launch_mode<1, kPageBig>(a, kv_fp8, stream, t0, t1);
+    if (pc == kPageMid) return launch_mode<1, kPageMid>(a, kv_fp8, stream, t0, t1);
+    return launch_mode<1, kPageSmall>(a, kv_fp8, stream, t0, t1);
   }
-  if (pc == kPageBig) return launch_mode<2, kPageBig>(a, kv_fp8, stream);
-  if (pc == kPageMid) return launch_mode<2, kPageMid>(a, kv_fp8, stream);
-  return launch_mode<2, kPageSmall>(a, kv_fp8, stream);
+  if (pc == kPageBig) return launch_mode<2, kPageBig>(a, kv_fp8, stream, t0, t1);
+  if (pc == kPageMid) return launch_mode<2, kPageMid>(a, kv_fp8, stream, t0, t1);
+  return launch_mode<2, kPageSmall>(a, kv_fp8, stream, t0, t1);
 }
 
 hipError_t launch_combine(const AttnArgs& a, hipStream_t stream) {

@@ -72,7 +72,10 @@ struct AttnArgs {
 };
 
 // Launchers (mla_attn.hip).  They only enqueue on `stream`; return hipError_t.
-hipError_t launch_attention(const AttnArgs& a, int tile_mode, int kv_fp8, hipStream_t stream);
+// t0 / t1: optional events recorded by the attention kernel's own dispatch
+// at the start and end of its execution (null: none).
+hipError_t launch_attention(const AttnArgs& a, int tile_mode, int kv_fp8, hipStream_t stream, hipEvent_t t0,
+                            hipEvent_t t1);
 hipError_t launch_combine(const AttnArgs& a, hipStream_t stream);
 
 }  // namespace mla
