@@ -168,74 +168,52 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// One 16-byte-per-lane direct-to-LDS load: lane l reads 16 bytes at
-// sbase + voff and writes them to LDS bytes [lds + 16 l, lds + 16 l + 16).
-// The scalar base / 32-bit lane offset form keeps the address in one VGPR.
-// Issued through asm so the compiler neither hoists 64-bit per-lane
-// addresses nor inserts waits for it: the caller waits with vmcnt and a
-// barrier before any wave reads the destination.  M0 (the LDS address) is
-// saved and restored around the load.
-__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
-  uint32_t save;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(save)
-      : "v"(voff), "s"(sbase), "s"(lds));
-}
-
-// dma16 gated by `on` (all ones or zero, an SGPR; every lane active at the
-// call): with zero the load executes with an empty EXEC mask and moves
-// nothing.  Lets a loop issue its prefetch slices without a branch.
-__device__ __forceinline__ void dma16_on(const void* sbase, uint32_t voff, uint32_t lds, uint32_t on) {
+// Direct-to-LDS loads, 16 bytes per lane: lane l reads 16 bytes at
+// sbase + voff (or at its own 64-bit address) and writes them to LDS bytes
+// [lds + 16 l, lds + 16 l + 16).  The scalar base / 32-bit lane offset form
+// keeps the address in one VGPR.  Issued through asm so the compiler neither
+// hoists 64-bit per-lane addresses nor inserts waits for them: the caller
+// waits with vmcnt and a barrier before any wave reads the destination.  M0
+// (the LDS address) and EXEC are saved and restored around the load.
+// dma16 / dma16_v with EXEC = {lo, hi} for the load (every lane active at
+// the call): zero halves make those lanes move nothing.  Lets a loop issue
+// prefetch slices, or a partial slice, without a branch.
+__device__ __forceinline__ void dma16_x(const void* sbase, uint32_t voff, uint32_t lds, uint32_t lo, uint32_t hi) {
   uint32_t save;
   uint64_t save_exec;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b64 %1, exec\n\t"
       "s_mov_b32 exec_lo, %5\n\t"
-      "s_mov_b32 exec_hi, %5\n\t"
+      "s_mov_b32 exec_hi, %6\n\t"
       "s_mov_b32 m0, %4\n\t"
       "s_nop 0\n\t"
       "global_load_lds_dwordx4 %2, %3\n\t"
       "s_mov_b64 exec, %1\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(save), "=&s"(save_exec)
-      : "v"(voff), "s"(sbase), "s"(lds), "s"(on));
+      : "v"(voff), "s"(sbase), "s"(lds), "s"(lo), "s"(hi));
 }
-
-// The same with a full 64-bit per-lane address (lanes reading unrelated pages).
-__device__ __forceinline__ void dma16_v(const void* vaddr, uint32_t lds) {
-  uint32_t save;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(save)
-      : "v"(vaddr), "s"(lds));
-}
-
-__device__ __forceinline__ void dma16_v_on(const void* vaddr, uint32_t lds, uint32_t on) {
+__device__ __forceinline__ void dma16_vx(const void* vaddr, uint32_t lds, uint32_t lo, uint32_t hi) {
   uint32_t save;
   uint64_t save_exec;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b64 %1, exec\n\t"
       "s_mov_b32 exec_lo, %4\n\t"
-      "s_mov_b32 exec_hi, %4\n\t"
+      "s_mov_b32 exec_hi, %5\n\t"
       "s_mov_b32 m0, %3\n\t"
       "s_nop 0\n\t"
       "global_load_lds_dwordx4 %2, off\n\t"
       "s_mov_b64 exec, %1\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(save), "=&s"(save_exec)
-      : "v"(vaddr), "s"(lds), "s"(on));
+      : "v"(vaddr), "s"(lds), "s"(lo), "s"(hi));
 }
+__device__ __forceinline__ void dma16_on(const void* sbase, uint32_t voff, uint32_t lds, uint32_t on) {
+  dma16_x(sbase, voff, lds, on, on);
+}
+__device__ __forceinline__ void dma16_v_on(const void* vaddr, uint32_t lds, uint32_t on) { dma16_vx(vaddr, lds, on, on); }
 
 // The lane id, re-materialised where it is used: values derived from it are
 // cheap to recompute, and keeping them live across the stage loop only
@@ -287,6 +265,7 @@ struct StageLoader {
   int s_tok0;
   LDS_AS char* st;
   uint32_t on = ~0u;        // EXEC mask (both halves) of the slices: zero turns issue() into no-ops
+  static constexpr int kSlices = kDmaPerWave;
 
   __device__ __forceinline__ void begin(const AttnArgs& a, LDS_AS char* stage, int page_base, int tok0,
                                         int tok_end, int wave) {
@@ -401,6 +380,8 @@ struct RecordLoader {
   int last;          // last live key of the stage, relative to s_tok0
   int s_tok0;
   LDS_AS char* raw;
+  uint32_t on = ~0u;  // EXEC mask (both halves) of the slices: zero turns issue() into no-ops
+  static constexpr int kSlices = kFp8DmaPerWave;
 
   __device__ __forceinline__ void begin(const AttnArgs& a, LDS_AS char* raw_stage, int page_base, int tok0,
                                         int tok_end, int wave) {
@@ -433,15 +414,20 @@ struct RecordLoader {
     const int k = cc - kRecChunks * tr;
     const int tc = min(wave * 16 + tr, last);
     LDS_AS char* dst = raw + (wave * 16 * kRecChunks + 64 * i) * 16;
+    // the last slice holds the 16 chunks 640..655: lanes 0..15 only
+    constexpr int kTail = 16 * kRecChunks - 64 * (kFp8DmaPerWave - 1);
+    static_assert(kTail == 16, "tail slice is lanes 0..15");
+    const uint32_t lo = (i == kFp8DmaPerWave - 1) ? (on & 0xFFFFu) : on;
+    const uint32_t hi = (i == kFp8DmaPerWave - 1) ? 0u : on;
     if (kPageClass == kPageBig) {
-      if (c < 16 * kRecChunks) dma16(base, (uint32_t)(tc * kFp8RecordBytes + 16 * k), lds_addr(dst));
+      dma16_x(base, (uint32_t)(tc * kFp8RecordBytes + 16 * k), lds_addr(dst), lo, hi);
     } else {
       const int p = __shfl(page, tr);
       const int sh = a.page_shift;
       const int T = s_tok0 + tc;
       const char* src = (const char*)a.kv_fp8 + (((size_t)p << sh) + (T & ((1 << sh) - 1))) * kFp8RecordBytes +
                         16 * k;
-      if (c < 16 * kRecChunks) dma16_v(src, lds_addr(dst));
+      dma16_vx(src, lds_addr(dst), lo, hi);
     }
   }
 };
@@ -455,17 +441,17 @@ __device__ __forceinline__ void issue_stage_fp8(const AttnArgs& a, LDS_AS char* 
   for (int i = 0; i < kFp8DmaPerWave; ++i) ld.issue(a, i, wave);
 }
 
-// Four e4m3 codes (one per byte of x) as bf16, exactly: the OCP e4m3 decode
-// is the hardware conversion of gfx950, and every e4m3 value (3 mantissa
-// bits, exponents 2^-9 .. 2^8) is a bf16 value.
+// Four e4m3 codes (one per byte of x) as bf16, exactly: gfx950's scaled
+// OCP fp8 -> bf16 conversion with scale 1 (every e4m3 value - 3 mantissa
+// bits, exponents 2^-9 .. 2^8 - is a bf16 value).
 __device__ __forceinline__ void codes_to_bf16(uint32_t x, bf16x8& h, int at) {
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(x, false);
-  const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(x, true);
-  h[at + 0] = (__bf16)lo[0];
-  h[at + 1] = (__bf16)lo[1];
-  h[at + 2] = (__bf16)hi[0];
-  h[at + 3] = (__bf16)hi[1];
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false);
+  const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true);
+  h[at + 0] = lo[0];
+  h[at + 1] = lo[1];
+  h[at + 2] = hi[0];
+  h[at + 3] = hi[1];
 }
 
 // Wave w unpacks the records of keys [16w, 16w+16) from the raw stage: the
@@ -474,28 +460,36 @@ __device__ __forceinline__ void codes_to_bf16(uint32_t x, bf16x8& h, int at) {
 // scale table sct[tile][key].  The scale is applied in fp32 by the consumer:
 // to each tile's partial dot product in Q.K^T, and to P for the tile's
 // output dims in P.V, so no dequantised key is ever rounded.  Lane l
-// handles ckv chunk l (dims 8l..8l+7) of every key, then two rope chunks.
+// handles ckv chunk l (dims 8l..8l+7) of every key, then two rope chunks;
+// all reads are issued before the first conversion.
 __device__ __forceinline__ void dequant_stage(const LDS_AS char* __restrict__ raw, LDS_AS char* __restrict__ st,
                                               LDS_AS float* __restrict__ sct, int wave, int lane) {
-#pragma unroll 4
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  u32x2 codes[16];
+  u32x4 rope[2];
+  float sc = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) codes[i] = *(const LDS_AS u32x2*)(raw + (wave * 16 + i) * kFp8RecordBytes + 8 * lane);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int t = wave * 16 + 8 * i + (lane >> 3);
+    rope[i] = *(const LDS_AS u32x4*)(raw + t * kFp8RecordBytes + kDimCkv + 16 + 16 * (lane & 7));
+  }
+  // scales: lane l < 64 holds scale (l & 3) of key 16w + (l >> 2)
+  sc = *(const LDS_AS float*)(raw + (wave * 16 + (lane >> 2)) * kFp8RecordBytes + kDimCkv + 4 * (lane & 3));
+#pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const int t = wave * 16 + i;
-    const LDS_AS char* rec = raw + t * kFp8RecordBytes;
-    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-    const u32x2 codes = *(const LDS_AS u32x2*)(rec + 8 * lane);
     bf16x8 h;
-    codes_to_bf16(codes[0], h, 0);
-    codes_to_bf16(codes[1], h, 4);
-    *(LDS_AS bf16x8*)(st + ckv_off(t, lane)) = h;
-    if ((lane & 15) == 0) sct[(lane >> 4) * kStageTokens + t] = *(const LDS_AS float*)(rec + kDimCkv + (lane >> 2));
+    codes_to_bf16(codes[i][0], h, 0);
+    codes_to_bf16(codes[i][1], h, 4);
+    *(LDS_AS bf16x8*)(st + ckv_off(wave * 16 + i, lane)) = h;
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int t = wave * 16 + 8 * i + (lane >> 3);
-    const int c = lane & 7;
-    const u32x4 r = *(const LDS_AS u32x4*)(raw + t * kFp8RecordBytes + kDimCkv + 16 + 16 * c);
-    *(LDS_AS u32x4*)(st + kpe_off(t, c)) = r;
+    *(LDS_AS u32x4*)(st + kpe_off(t, lane & 7)) = rope[i];
   }
+  sct[(lane & 3) * kStageTokens + wave * 16 + (lane >> 2)] = sc;
 }
 
 // ---------------------------------------------------------------------------
@@ -590,12 +584,11 @@ struct WideSoftmax {
   float mref = 0.f;
 };
 
-template <int kPC, bool kFp8, bool kPrefetch>
+template <int kPC, bool kFp8, bool kPrefetch, class Loader>
 __device__ __forceinline__ void wide_stage(const AttnArgs& a, const bf16x8 (&qf)[36], WideState& st,
                                            const LDS_AS char* __restrict__ cur, int stage_tok, int bound,
                                            const int (&kb)[8], const int (&pb)[4], const int (&vb)[8],
-                                           int g, StageLoader<kPC>& ld, int wave,
-                                           const LDS_AS float* __restrict__ sct) {
+                                           int g, Loader& ld, int wave, const LDS_AS float* __restrict__ sct) {
   // fp8 cache: scales of this lane's keys tb + 8q + 4g + (0..3) in tile t
   auto scales = [&](int tb, int t, int q) -> f32x4 {
     return *(const LDS_AS f32x4*)(sct + t * kStageTokens + tb + 8 * q + 4 * g);
@@ -660,7 +653,8 @@ __device__ __forceinline__ void wide_stage(const AttnArgs& a, const bf16x8 (&qf)
 #pragma unroll
     for (int ks = 0; ks < 36; ++ks) {
       pin_loads();
-      if (kPrefetch && (ks & 3) == 0) ld.issue(a, dma0 + (ks >> 2), wave);  // 9 slices per sub-tile
+      if (kPrefetch && (ks & 3) == 0 && dma0 + (ks >> 2) < Loader::kSlices)
+        ld.issue(a, dma0 + (ks >> 2), wave);  // up to 9 slices per sub-tile
       const bf16x8 k0 = kr[ks % KD];
       if (kFp8 && ks < 32) {
         if ((ks & 7) == 0) {
@@ -790,6 +784,7 @@ __device__ __forceinline__ void wide_body(const AttnArgs& a, const bf16x8 (&qf)[
   ld.begin(a, nxt, page_base, prefetch ? next_tok : stage_tok, tok_end, wave);
   ld.on = __builtin_amdgcn_readfirstlane(prefetch ? ~0u : 0u);
   wide_stage<kPC, false, true>(a, qf, st, cur, stage_tok, bound, kb, pb, vb, lane >> 5, ld, wave, nullptr);
+  static_assert(StageLoader<kPC>::kSlices == 18, "two sub-tiles of 9 slices");
 }
 
 template <int kPC, bool kFp8>
@@ -843,6 +838,8 @@ __device__ void wide_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* sm
     if (nstage > 0) issue_stage_fp8<kPC>(a, raw, page_base, it.tok0, it.tok1, wave);
     if (nstage > 1) issue_stage_fp8<kPC>(a, raw + kFp8RawBytes, page_base, it.tok0 + kStageTokens, it.tok1, wave);
     for (int s = 0; s < nstage; ++s) {
+      // stage s must have landed; stage s+1's records may still be in flight
+      // (stage s+2's, issued during stage s, are not yet)
       if (s + 1 < nstage) {
         wait_vmcnt<kFp8DmaPerWave>();
       } else {
@@ -851,12 +848,14 @@ __device__ void wide_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* sm
       __syncthreads();  // raw stage s landed; every wave is done with the bf16 stage
       dequant_stage(raw + (s & 1) * kFp8RawBytes, smem, sct, wave, lane);
       __syncthreads();  // bf16 stage complete; raw stage s consumed
-      if (s + 2 < nstage)
-        issue_stage_fp8<kPC>(a, raw + (s & 1) * kFp8RawBytes, page_base, it.tok0 + (s + 2) * kStageTokens, it.tok1,
-                             wave);
-      StageLoader<kPC> none;
-      wide_stage<kPC, true, false>(a, qf, st, smem, it.tok0 + s * kStageTokens, bound, kb, pb, vb, g, none, wave,
-                                   sct);
+      // stage s+2's records ride along this stage's Q.K^T (EXEC-gated past the
+      // end, with addresses of this stage so every page lookup is in range)
+      const bool more = s + 2 < nstage;
+      RecordLoader<kPC> ld;
+      ld.begin(a, raw + (s & 1) * kFp8RawBytes, page_base, it.tok0 + (more ? s + 2 : s) * kStageTokens, it.tok1,
+               wave);
+      ld.on = __builtin_amdgcn_readfirstlane(more ? ~0u : 0u);
+      wide_stage<kPC, true, true>(a, qf, st, smem, it.tok0 + s * kStageTokens, bound, kb, pb, vb, g, ld, wave, sct);
     }
     __syncthreads();  // the bf16 stage is free for the next item
   } else {
