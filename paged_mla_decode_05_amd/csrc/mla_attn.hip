@@ -142,16 +142,21 @@ __device__ __forceinline__ void pin_loads() { asm volatile("" ::: "memory"); }
 // S^T chains on mfma_f32_32x32x16_bf16 with the accumulator in VGPRs.  The
 // compiler gives every builtin MFMA of these kernels an AGPR accumulator,
 // and the 256 AGPRs are O's; S must live in VGPRs, so its MFMAs are written
-// here.  mfma32_first starts a chain (inline-zero C operand), mfma32_acc
-// continues it (C = D exactly: the hardware's back-to-back accumulation,
-// no wait states), and mfma32_drain puts 24 wait states between the last
-// MFMA and the first other reader or writer of the accumulator (the XDL
-// write -> VALU read / SrcC read -> VALU write distance of gfx950 is less).
+// here.  The compiler does not see inside the asm, so the hazard distances
+// it would insert are written out: each MFMA is preceded by 4 wait states
+// (a VALU write of an operand -- converted fp8 codes, a rescaled
+// accumulator -- must be that far ahead of the MFMA reading it), which
+// overlap the previous MFMA's execution.  mfma32_first starts a chain
+// (inline-zero C operand), mfma32_acc continues it (C = D exactly: the
+// hardware's back-to-back accumulation), and mfma32_drain puts 24 wait
+// states between the last MFMA and the first other reader or writer of the
+// accumulator (the XDL write -> VALU read / SrcC read -> VALU write
+// distances of gfx950 are shorter).
 __device__ __forceinline__ void mfma32_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+  asm volatile("s_nop 3\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void mfma32_acc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+  asm volatile("s_nop 3\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void mfma32_drain(f32x16& x) { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x)); }
 __device__ __forceinline__ void mfma32_drain(f32x16& x, f32x16& y) {
@@ -787,6 +792,58 @@ __device__ __forceinline__ void wide_body(const AttnArgs& a, const bf16x8 (&qf)[
   static_assert(StageLoader<kPC>::kSlices == 18, "two sub-tiles of 9 slices");
 }
 
+// WIDE epilogue: lane (n, g) owns row n of the wave's 32 rows, the partner
+// lane (n, 1-g) holds the other dims.  bf16 rows (final or partial) are
+// staged in LDS and stored whole; fp32 rows are stored in place.
+__device__ __forceinline__ void wide_epilogue(const AttnArgs& a, const WorkItem& it, WideState& st, const RowInfo& ri,
+                                              int rib, LDS_AS char* smem, int wave, int lane) {
+  const int g = lane >> 5;
+  const int n = lane & 31;
+  const float l_tot = sum_xor32(st.l_run);
+  const bool empty = !(l_tot > 0.f);
+  const float inv = empty ? 0.f : 1.f / l_tot;
+  if (ri.ok && g == 0) store_lse(a, it, ri, rib, empty ? kNegInf : (st.m_run + __log2f(l_tot)) * kLn2);
+  if (a.out_bf16 || it.slot >= 0) {
+    // bf16 rows: stage the wave's 32 rows in LDS (free after the loop; 16-byte
+    // chunks XOR-swizzled by row), then store each row as one coalesced 1 KB
+    LDS_AS char* ob = smem + wave * 32 * kCkvRowBytes;
+#pragma unroll
+    for (int cb = 0; cb < 16; ++cb) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        bf16x4 h;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[e] = (__bf16)(st.o[cb][4 * q + e] * inv);
+        *(LDS_AS bf16x4*)(ob + n * kCkvRowBytes + (((4 * cb + q) ^ (n & 7)) << 4) + 8 * g) = h;
+      }
+    }
+#pragma unroll 4
+    for (int rr = 0; rr < 32; ++rr) {
+      const RowInfo rj = row_info(a, it, wave * 32 + rr);
+      const u32x4 v = *(const LDS_AS u32x4*)(ob + rr * kCkvRowBytes + ((lane ^ (rr & 7)) << 4));
+      if (rj.ok) {
+        __bf16* dst = (it.slot < 0)
+                          ? (__bf16*)a.out + rj.qrow * kDimCkv
+                          : a.part_o + ((size_t)it.slot * a.rows_per_block + wave * 32 + rr) * kDimCkv;
+        *(u32x4*)(dst + 8 * lane) = v;
+      }
+    }
+    __syncthreads();  // the staging rows overlap the next item's first stage
+    return;
+  }
+  if (ri.ok) {
+#pragma unroll
+    for (int cb = 0; cb < 16; ++cb) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 v = {st.o[cb][4 * q] * inv, st.o[cb][4 * q + 1] * inv, st.o[cb][4 * q + 2] * inv,
+                         st.o[cb][4 * q + 3] * inv};
+        store4(a, it, ri, rib, 32 * cb + 8 * q + 4 * g, v);
+      }
+    }
+  }
+}
+
 template <int kPC, bool kFp8>
 __device__ void wide_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* smem, int wave, int lane) {
   const int g = lane >> 5;   // lane half
@@ -870,22 +927,214 @@ __device__ void wide_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* sm
     }
   }
 
-  // epilogue: lane owns row n; the partner lane (n, 1-g) holds the other dims
-  const float l_tot = sum_xor32(st.l_run);
-  const bool empty = !(l_tot > 0.f);
-  const float inv = empty ? 0.f : 1.f / l_tot;
-  if (ri.ok) {
+  wide_epilogue(a, it, st, ri, rib, smem, wave, lane);
+}
+
+// ---------------------------------------------------------------------------
+// WIDE mode over the fp8 record cache, keys dequantised in registers.
+//
+// The 656-byte records of a stage stay raw in LDS (three stage buffers, the
+// loads running two stages ahead); no bf16 copy of the stage is made.
+//  * Q.K^T: lane (key n, half h) reads 16 codes, dims 32m + 16h .. +15 of
+//    its key, with one ds_read_b128 and converts them exactly to two bf16
+//    A fragments (k-steps 2m and 2m+1).  The query fragments follow the same
+//    dim order (a permutation inside each 32-dim block), so the product is
+//    unchanged.  As in the bf16-staged path, each 128-dim tile's partial dot
+//    product is scaled by the key's fp32 tile scale before it is summed.
+//  * P.V: the V^T operand (32 dims x 8 keys per lane half) comes from one
+//    ds_read_b64_tr_b8 of the raw codes, converted in registers; P is
+//    scaled per key by the tile scale of the output dims, as before.
+//  * The rope dims are bf16 in the record and are read as they are.
+// This halves the LDS bytes per MFMA of the key stream and drops the
+// unpack pass; the conversions (one VALU op per 2 codes) issue beside the
+// MFMAs.
+// ---------------------------------------------------------------------------
+constexpr int kW8Bufs = 3;
+constexpr int kW8TabOff = kW8Bufs * kFp8RawBytes;                   // per-wave scale tables
+constexpr int kW8LdsBytes = kW8TabOff + 4 * 4 * kStageTokens * 4;   // [4 waves][4 tiles][64 keys] f32
+static_assert(kW8LdsBytes <= 160 * 1024, "fp8 wide LDS budget");
+static_assert(kW8LdsBytes <= kFp8LdsBytes && 4 * 32 * kCkvRowBytes <= kFp8LdsBytes, "fits the fp8 kernels' LDS");
+
+__device__ __forceinline__ bf16x8 codes8(uint32_t lo, uint32_t hi) {
+  bf16x8 h;
+  codes_to_bf16(lo, h, 0);
+  codes_to_bf16(hi, h, 4);
+  return h;
+}
+
+template <int kPC>
+__device__ void wide8_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* smem, int wave, int lane) {
+  const int g = lane >> 5;
+  const int n = lane & 31;
+  const int rib = wave * 32 + n;
+  const RowInfo ri = row_info(a, it, rib);
+  const int bound = row_key_bound(a, it, ri);
+
+  // Query fragments in the codes' dim order: nope k-step 2m+s, half g holds
+  // dims 32m + 16g + 8s .. +7; rope k-steps as in the bf16 path.
+  bf16x8 qf[36];
+  {
+    const bf16x8 z = {};
+    const __bf16* qn = (const __bf16*)a.q_nope + ri.qrow * kDimCkv + 16 * g;
+    const __bf16* qp = (const __bf16*)a.q_pe + ri.qrow * kDimKpe + 8 * g;
 #pragma unroll
-    for (int cb = 0; cb < 16; ++cb) {
+    for (int m = 0; m < 16; ++m)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4 v = {st.o[cb][4 * q] * inv, st.o[cb][4 * q + 1] * inv, st.o[cb][4 * q + 2] * inv,
-                         st.o[cb][4 * q + 3] * inv};
-        store4(a, it, ri, rib, 32 * cb + 8 * q + 4 * g, v);
-      }
-    }
-    if (g == 0) store_lse(a, it, ri, rib, empty ? kNegInf : (st.m_run + __log2f(l_tot)) * kLn2);
+      for (int sh = 0; sh < 2; ++sh) qf[2 * m + sh] = ri.ok ? *(const bf16x8*)(qn + 32 * m + 8 * sh) : z;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qf[32 + ks] = ri.ok ? *(const bf16x8*)(qp + 16 * ks) : z;
   }
+  // byte offsets inside a raw stage
+  const int kaddr = n * kFp8RecordBytes + 16 * g;                       // + tb*656 + 32m
+  const int raddr = n * kFp8RecordBytes + kDimCkv + 16 + 16 * g;        // rope: + tb*656 + 32kr
+  int vaddr;
+  {
+    // tr_b8: in each 16-lane group, lane pair j supplies key 8(j/4) + 4h + j%4
+    // of the 16-key step (h = lane / 32), dims 16((lane/16)%2) + 8(lane%2) ..
+    const int p = lane & 15, j = p >> 1;
+    const int vkey = 8 * (j >> 2) + 4 * g + (j & 3);
+    vaddr = vkey * kFp8RecordBytes + 16 * ((lane >> 4) & 1) + 8 * (p & 1);  // + (tb + 16kk)*656 + 32cb
+  }
+  LDS_AS float* tab = (LDS_AS float*)(smem + kW8TabOff) + wave * 4 * kStageTokens;
+
+  WideState st;
+#pragma unroll
+  for (int cb = 0; cb < 16; ++cb) st.o[cb] = f32x16{};
+  st.m_run = kNegInf;
+  st.l_run = 0.f;
+
+  const int page_base = ld_const(a.kv_indptr, it.b);
+  const int nstage = (it.tok1 - it.tok0 + kStageTokens - 1) / kStageTokens;
+  if (nstage > 0) issue_stage_fp8<kPC>(a, smem, page_base, it.tok0, it.tok1, wave);
+  if (nstage > 1) issue_stage_fp8<kPC>(a, smem + kFp8RawBytes, page_base, it.tok0 + kStageTokens, it.tok1, wave);
+  for (int s = 0; s < nstage; ++s) {
+    // stage s must have landed; stage s+1's records may still be in flight
+    if (s + 1 < nstage) {
+      wait_vmcnt<kFp8DmaPerWave>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    __syncthreads();  // stage s visible; every wave is done with stage s-1 (its buffer is refilled below)
+    const int buf = s % kW8Bufs;
+    const LDS_AS char* __restrict__ raw = smem + buf * kFp8RawBytes;
+    const bool more = s + 2 < nstage;
+    RecordLoader<kPC> ld;
+    ld.begin(a, smem + ((s + 2) % kW8Bufs) * kFp8RawBytes, page_base, it.tok0 + (more ? s + 2 : s) * kStageTokens,
+             it.tok1, wave);
+    ld.on = __builtin_amdgcn_readfirstlane(more ? ~0u : 0u);
+    {
+      // this wave's copy of the stage's tile scales: tab[t][key]
+      const f32x4 sc = *(const LDS_AS f32x4*)(raw + lane * kFp8RecordBytes + kDimCkv);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) tab[t * kStageTokens + lane] = sc[t];
+    }
+    const int stage_tok = it.tok0 + s * kStageTokens;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int tb = sub * 32;
+      auto scales = [&](int t, int q) -> f32x4 {
+        return *(const LDS_AS f32x4*)(tab + t * kStageTokens + tb + 8 * q + 4 * g);
+      };
+      // ---- S^T[32 keys x 32 rows]
+      f32x16 sacc, part;
+      constexpr int KD = 3;  // 16-code reads in flight
+      u32x4 kr[KD];
+      auto kread = [&](int m) -> u32x4 { return *(const LDS_AS u32x4*)(raw + kaddr + tb * kFp8RecordBytes + 32 * m); };
+#pragma unroll
+      for (int i = 0; i < KD; ++i) kr[i] = kread(i);
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        pin_loads();
+        if ((m & 1) == 0 && sub * 8 + (m >> 1) < RecordLoader<kPC>::kSlices) ld.issue(a, sub * 8 + (m >> 1), wave);
+        const u32x4 c = kr[m % KD];
+        if (m + KD < 16) kr[m % KD] = kread(m + KD);
+        const bf16x8 a0 = codes8(c[0], c[1]), a1 = codes8(c[2], c[3]);
+        if ((m & 3) == 0) {
+          mfma32_first(part, a0, qf[2 * m]);
+        } else {
+          mfma32_acc(part, a0, qf[2 * m]);
+        }
+        mfma32_acc(part, a1, qf[2 * m + 1]);
+        if ((m & 3) == 3) {
+          mfma32_drain(part);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x4 sc = scales(m >> 2, q);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float t = part[4 * q + r] * sc[r];
+              sacc[4 * q + r] = (m == 3) ? t : sacc[4 * q + r] + t;
+            }
+          }
+        }
+      }
+      pin_loads();
+#pragma unroll
+      for (int kr2 = 0; kr2 < 4; ++kr2) {
+        const bf16x8 rp = *(const LDS_AS bf16x8*)(raw + raddr + tb * kFp8RecordBytes + 32 * kr2);
+        mfma32_acc(sacc, rp, qf[32 + kr2]);
+      }
+      mfma32_drain(sacc);
+      // ---- online softmax (base 2); lane holds keys 8(r/4) + 4g + r%4 of the sub-tile
+      float sv[16];
+      float mx = kNegInf;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int tok = stage_tok + tb + 8 * (r >> 2) + 4 * g + (r & 3);
+        const float x = sacc[r] * a.scale_log2;
+        sv[r] = tok < bound ? x : kNegInf;
+        mx = fmaxf(mx, sv[r]);
+      }
+      mx = max_xor32(mx);
+      if (__builtin_amdgcn_ballot_w64(mx > st.m_run + kRescaleSlack) != 0) {
+        const float m_new = fmaxf(st.m_run, mx);
+        const float alpha = (st.m_run == kNegInf) ? 0.f : fast_exp2(st.m_run - m_new);
+        st.l_run *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < 16; ++cb) scale_acc<16>(st.o[cb], alpha);
+        st.m_run = m_new;
+      }
+      const float mref = (st.m_run == kNegInf) ? 0.f : st.m_run;
+      float pf[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        pf[r] = fast_exp2(sv[r] - mref);
+        st.l_run += pf[r];
+      }
+      // ---- O^T[32 dims x 32 rows] += V^T[32 dims x 16 keys] . P^T[16 keys x 32 rows]
+      constexpr int VD = 3;
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      typedef int i32x2 __attribute__((ext_vector_type(2)));
+      auto vread = [&](int j) -> u32x2 {  // j = 2*cb + kk
+        const int cb = j >> 1, kk = j & 1;
+        const LDS_AS char* src = raw + vaddr + (tb + 16 * kk) * kFp8RecordBytes + 32 * cb;
+        return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS i32x2*)src));
+      };
+      u32x2 vr[VD];
+#pragma unroll
+      for (int i = 0; i < VD; ++i) vr[i] = vread(i);
+      bf16x8 pt[2];
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        pin_loads();
+        if ((j & 7) == 0) {
+          // output dims of tile j/8: P scaled by each key's tile scale
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x4 sc = scales(j >> 3, q);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) pt[q >> 1][4 * (q & 1) + r] = (__bf16)(pf[4 * q + r] * sc[r]);
+          }
+        }
+        const u32x2 v = vr[j % VD];
+        if (j + VD < 32) vr[j % VD] = vread(j + VD);
+        st.o[j >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(codes8(v[0], v[1]), pt[j & 1], st.o[j >> 1], 0, 0, 0);
+      }
+      pin_loads();
+    }
+  }
+  __syncthreads();  // every wave is done with the stage buffers before the epilogue stages rows there
+  wide_epilogue(a, it, st, ri, rib, smem, wave, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -1633,6 +1882,20 @@ void mla_attn_quad_kernel(AttnArgs a) {
   }
 }
 
+// Workgroup -> work list.  Workgroups are dealt to the 8 XCDs round-robin
+// (blockIdx mod 8); lists are numbered so that consecutive lists land on
+// one XCD.  The planner fills lists in request order, so the pieces of a
+// split request, or the row blocks of a prefill request, share an L2 (their
+// query rows, and keys read at the same time, come from HBM once).  A
+// bijection for any list count n: XCD x runs ceil((n - x) / 8) lists.
+__device__ __forceinline__ int xcd_list(int b, int n) {
+  const int x = b & 7;
+  int base = 0;
+#pragma unroll
+  for (int y = 0; y < 7; ++y) base += (y < x) ? (n - y + 7) >> 3 : 0;
+  return base + (b >> 3);
+}
+
 template <int kMode, int kPC, bool kFp8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_attn_kernel(AttnArgs a) {
@@ -1640,8 +1903,9 @@ void mla_attn_kernel(AttnArgs a) {
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int i0 = ld_const(a.wg_ptr, blockIdx.x);
-  const int i1 = ld_const(a.wg_ptr, blockIdx.x + 1);
+  const int list = xcd_list(blockIdx.x, a.num_wgs);
+  const int i0 = ld_const(a.wg_ptr, list);
+  const int i1 = ld_const(a.wg_ptr, list + 1);
   for (int i = i0; i < i1; ++i) {
     const int32_t* ip = (const int32_t*)(a.items + i);
     WorkItem it;
@@ -1653,7 +1917,9 @@ void mla_attn_kernel(AttnArgs a) {
     it.kv_len = ld_const(ip, 5);
     it.q_len = ld_const(ip, 6);
     it.slot = ld_const(ip, 7);
-    if (kMode == 1) {
+    if (kMode == 1 && kFp8) {
+      wide8_item<kPC>(a, it, smem, wave, lane);
+    } else if (kMode == 1) {
       wide_item<kPC, kFp8>(a, it, smem, wave, lane);
     } else if (kMode == 4) {
       split_item<kPC>(a, it, smem, wave, lane);
