@@ -241,7 +241,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tile-mode", type=int, default=0,
-                    help="0 = planner's choice; 1 wide, 2 narrow, 3 quad, 4 split")
+                    help="0 = planner's choice; 1 wide, 2 narrow, 3 quad")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES (counter calibration) and exit")
     ap.add_argument("--write-counters", metavar="PMC_DIR",

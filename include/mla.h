@@ -73,16 +73,12 @@ typedef enum mla_kind { MLA_KIND_DECODE = 0, MLA_KIND_PREFILL = 1 } mla_kind;
  *   MLA_TILE_QUAD:   a workgroup holds 32 rows; its waves split each key tile
  *                    for Q.K^T and the 512 output columns for P.V; up to four
  *                    sibling workgroups on one XCD hold the other 32-row
- *                    slices of the same rows and walk the same keys.
- *   MLA_TILE_SPLIT:  128 rows like WIDE for Q.K^T and the softmax; P goes
- *                    through LDS and wave w computes P.V for output dims
- *                    [128w, 128w+128) of all rows (bf16 caches only).     */
+ *                    slices of the same rows and walk the same keys (bf16 caches only).  */
 typedef enum mla_tile_mode {
   MLA_TILE_AUTO = 0,
   MLA_TILE_WIDE = 1,
   MLA_TILE_NARROW = 2,
-  MLA_TILE_QUAD = 3,
-  MLA_TILE_SPLIT = 4
+  MLA_TILE_QUAD = 3
 } mla_tile_mode;
 
 typedef struct mla_plan_desc {

@@ -28,5 +28,4 @@ from ._binding import (  # noqa: F401
     MLA_TILE_WIDE,
     MLA_TILE_NARROW,
     MLA_TILE_QUAD,
-    MLA_TILE_SPLIT,
 )

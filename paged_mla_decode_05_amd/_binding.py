@@ -22,7 +22,6 @@ MLA_TILE_AUTO = 0
 MLA_TILE_WIDE = 1
 MLA_TILE_NARROW = 2
 MLA_TILE_QUAD = 3
-MLA_TILE_SPLIT = 4
 
 _DIM_CKV = 512
 _DIM_KPE = 64

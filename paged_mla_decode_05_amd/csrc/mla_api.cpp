@@ -27,7 +27,7 @@ using mla::WorkItem;
 
 struct mla_plan {
   mla_plan_desc d;
-  int32_t tile_mode = 0;       // resolved: MLA_TILE_WIDE, _NARROW, _QUAD or _SPLIT
+  int32_t tile_mode = 0;       // resolved: MLA_TILE_WIDE, _NARROW or _QUAD
   int32_t rows_per_block = 0;  // rows one workgroup holds
   int32_t num_wgs = 0;         // work lists (per workgroup; per sibling group in quad mode)
   int32_t grid = 0;            // workgroups launched
@@ -140,7 +140,7 @@ mla_status build_schedule(mla_plan* p, const std::vector<int32_t>& kv_len,
   // otherwise the 16-row tile, which splits keys across waves.
   if (mode == MLA_TILE_AUTO) mode = (max_rows >= mla::kWideRows / 2) ? MLA_TILE_WIDE : MLA_TILE_NARROW;
   p->tile_mode = mode;
-  int32_t RB = (mode == MLA_TILE_WIDE || mode == MLA_TILE_SPLIT) ? mla::kWideRows : mla::kNarrowRows;
+  int32_t RB = (mode == MLA_TILE_WIDE) ? mla::kWideRows : mla::kNarrowRows;
   int64_t lists = std::max<int32_t>(1, num_cus);
   p->group_size = 1;
   p->xcd_map = 0;
@@ -230,9 +230,8 @@ mla_status mla_plan_create(mla_plan** out, const mla_plan_desc* d, const int32_t
   if (!is_pow2(d->page_size) || d->page_size > 4096) return MLA_ERR_UNSUPPORTED;
   if (d->kv_format != MLA_KV_BF16 && d->kv_format != MLA_KV_FP8_E4M3_T128) return MLA_ERR_UNSUPPORTED;
   if (d->kv_format == MLA_KV_FP8_E4M3_T128 && d->kind != MLA_KIND_DECODE) return MLA_ERR_UNSUPPORTED;
-  if (d->tile_mode < MLA_TILE_AUTO || d->tile_mode > MLA_TILE_SPLIT) return MLA_ERR_INVALID_ARGUMENT;
-  if (d->kv_format == MLA_KV_FP8_E4M3_T128 && (d->tile_mode == MLA_TILE_QUAD || d->tile_mode == MLA_TILE_SPLIT))
-    return MLA_ERR_UNSUPPORTED;
+  if (d->tile_mode < MLA_TILE_AUTO || d->tile_mode > MLA_TILE_QUAD) return MLA_ERR_INVALID_ARGUMENT;
+  if (d->kv_format == MLA_KV_FP8_E4M3_T128 && d->tile_mode == MLA_TILE_QUAD) return MLA_ERR_UNSUPPORTED;
   if (d->max_splits < 0 || d->force_splits < 0 || d->num_cus < 0) return MLA_ERR_INVALID_ARGUMENT;
   if (d->batch > 0 && !kv_indptr_host) return MLA_ERR_INVALID_ARGUMENT;
   if (d->kind == MLA_KIND_PREFILL && d->batch > 0 && !qo_indptr_host) return MLA_ERR_INVALID_ARGUMENT;

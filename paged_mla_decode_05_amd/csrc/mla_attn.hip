@@ -152,11 +152,23 @@ __device__ __forceinline__ void pin_loads() { asm volatile("" ::: "memory"); }
 // states between the last MFMA and the first other reader or writer of the
 // accumulator (the XDL write -> VALU read / SrcC read -> VALU write
 // distances of gfx950 are shorter).
+// kValu = false drops the leading wait states where no operand can have
+// been written by a VALU instruction (LDS / global loads only, and C = D).
+template <bool kValu = true>
 __device__ __forceinline__ void mfma32_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("s_nop 3\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+  if (kValu) {
+    asm volatile("s_nop 3\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+  } else {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+  }
 }
+template <bool kValu = true>
 __device__ __forceinline__ void mfma32_acc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("s_nop 3\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+  if (kValu) {
+    asm volatile("s_nop 3\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+  } else {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+  }
 }
 __device__ __forceinline__ void mfma32_drain(f32x16& x) { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x)); }
 __device__ __forceinline__ void mfma32_drain(f32x16& x, f32x16& y) {
@@ -589,15 +601,11 @@ struct WideSoftmax {
   float mref = 0.f;
 };
 
-template <int kPC, bool kFp8, bool kPrefetch, class Loader>
+template <int kPC, bool kPrefetch, class Loader>
 __device__ __forceinline__ void wide_stage(const AttnArgs& a, const bf16x8 (&qf)[36], WideState& st,
                                            const LDS_AS char* __restrict__ cur, int stage_tok, int bound,
                                            const int (&kb)[8], const int (&pb)[4], const int (&vb)[8],
-                                           int g, Loader& ld, int wave, const LDS_AS float* __restrict__ sct) {
-  // fp8 cache: scales of this lane's keys tb + 8q + 4g + (0..3) in tile t
-  auto scales = [&](int tb, int t, int q) -> f32x4 {
-    return *(const LDS_AS f32x4*)(sct + t * kStageTokens + tb + 8 * q + 4 * g);
-  };
+                                           int g, Loader& ld, int wave) {
   auto kread = [&](int tb, int ks) -> bf16x8 {
     return ks < 32 ? lds_read_b128(cur, kb[ks & 7] + 256 * (ks >> 3) + tb * kCkvRowBytes)
                    : lds_read_b128(cur, pb[ks - 32] + tb * kKpeRowBytes);
@@ -650,7 +658,6 @@ __device__ __forceinline__ void wide_stage(const AttnArgs& a, const bf16x8 (&qf)
   // ---- S^T[32 keys x 32 rows] = K . Q^T over 576 dims for sub-tile tb, with
   // `side(ks)` run after MFMA ks (interleaved VALU work of another phase)
   auto qk = [&](f32x16& sacc, int tb, int dma0, auto&& side) {
-    f32x16 part;  // fp8: one 128-dim tile of the codes' dot products
     constexpr int KD = 4;  // K fragments in flight
     bf16x8 kr[KD];
 #pragma unroll
@@ -661,28 +668,10 @@ __device__ __forceinline__ void wide_stage(const AttnArgs& a, const bf16x8 (&qf)
       if (kPrefetch && (ks & 3) == 0 && dma0 + (ks >> 2) < Loader::kSlices)
         ld.issue(a, dma0 + (ks >> 2), wave);  // up to 9 slices per sub-tile
       const bf16x8 k0 = kr[ks % KD];
-      if (kFp8 && ks < 32) {
-        if ((ks & 7) == 0) {
-          mfma32_first(part, k0, qf[ks]);
-        } else {
-          mfma32_acc(part, k0, qf[ks]);
-        }
-        if ((ks & 7) == 7) {
-          mfma32_drain(part);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const f32x4 sc = scales(tb, ks >> 3, q);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const float t = part[4 * q + r] * sc[r];
-              sacc[4 * q + r] = (ks == 7) ? t : sacc[4 * q + r] + t;
-            }
-          }
-        }
-      } else if (ks == 0) {
-        mfma32_first(sacc, k0, qf[0]);
+      if (ks == 0) {
+        mfma32_first<false>(sacc, k0, qf[0]);
       } else {
-        mfma32_acc(sacc, k0, qf[ks]);
+        mfma32_acc<false>(sacc, k0, qf[ks]);
       }
       if (ks + KD < 36) kr[ks % KD] = kread(tb, ks + KD);
       side(ks);
@@ -700,15 +689,6 @@ __device__ __forceinline__ void wide_stage(const AttnArgs& a, const bf16x8 (&qf)
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
       pin_loads();
-      if (kFp8 && (j & 7) == 0) {
-        // output dims of tile j/8: P scaled by each key's tile scale
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4 sc = scales(tb, j >> 3, q);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) pt[q >> 1][4 * (q & 1) + r] = (__bf16)(pf[4 * q + r] * sc[r]);
-        }
-      }
       st.o[j >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[j % VD], pt[j & 1], st.o[j >> 1], 0, 0, 0);
       if (j + VD < 32) vr[j % VD] = vread(tb, j + VD);
       side(j);
@@ -726,24 +706,7 @@ __device__ __forceinline__ void wide_stage(const AttnArgs& a, const bf16x8 (&qf)
   WideSoftmax sm0, sm1;
   bf16x8 pt0[2], pt1[2];
   float pf0[16], pf1[16];
-  if constexpr (kFp8) {
-    // fp8: the per-tile scale work already rides along both products, and
-    // its registers leave no room for a second sub-tile in flight
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      qk(sa0, 32 * sub, 9 * sub, [&](int) {});
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s0[r] = sa0[r];
-      WideSoftmax sm;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sm_scale_mask(s0, sm, 32 * sub, r);
-      sm_decide(sm);
-      if (sm.raise) rescale_o(sm.alpha);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sm_exp(s0, sm, pt0, pf0, r);
-      pv(32 * sub, pt0, pf0, [&](int) {});
-    }
-  } else {
+  {
     // Software pipeline over the two sub-tiles:
     //   QK(0);  QK(1) + softmax(0);  PV(0) + softmax(1);  PV(1)
     // The softmax VALU work issues between MFMAs of the other phase.  A
@@ -788,7 +751,7 @@ __device__ __forceinline__ void wide_body(const AttnArgs& a, const bf16x8 (&qf)[
   StageLoader<kPC> ld;
   ld.begin(a, nxt, page_base, prefetch ? next_tok : stage_tok, tok_end, wave);
   ld.on = __builtin_amdgcn_readfirstlane(prefetch ? ~0u : 0u);
-  wide_stage<kPC, false, true>(a, qf, st, cur, stage_tok, bound, kb, pb, vb, lane >> 5, ld, wave, nullptr);
+  wide_stage<kPC, true>(a, qf, st, cur, stage_tok, bound, kb, pb, vb, lane >> 5, ld, wave);
   static_assert(StageLoader<kPC>::kSlices == 18, "two sub-tiles of 9 slices");
 }
 
@@ -844,7 +807,7 @@ __device__ __forceinline__ void wide_epilogue(const AttnArgs& a, const WorkItem&
   }
 }
 
-template <int kPC, bool kFp8>
+template <int kPC>
 __device__ void wide_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* smem, int wave, int lane) {
   const int g = lane >> 5;   // lane half
   const int n = lane & 31;   // row within the wave (S^T / O^T column)
@@ -888,45 +851,15 @@ __device__ void wide_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* sm
 
   const int page_base = ld_const(a.kv_indptr, it.b);
   const int nstage = (it.tok1 - it.tok0 + kStageTokens - 1) / kStageTokens;
-  if (kFp8) {
-    // raw records two stages ahead; one stage unpacked per step
-    LDS_AS char* raw = smem + kFp8RawOff;
-    LDS_AS float* sct = (LDS_AS float*)(smem + kFp8ScaleOff);
-    if (nstage > 0) issue_stage_fp8<kPC>(a, raw, page_base, it.tok0, it.tok1, wave);
-    if (nstage > 1) issue_stage_fp8<kPC>(a, raw + kFp8RawBytes, page_base, it.tok0 + kStageTokens, it.tok1, wave);
-    for (int s = 0; s < nstage; ++s) {
-      // stage s must have landed; stage s+1's records may still be in flight
-      // (stage s+2's, issued during stage s, are not yet)
-      if (s + 1 < nstage) {
-        wait_vmcnt<kFp8DmaPerWave>();
-      } else {
-        wait_vmcnt<0>();
-      }
-      __syncthreads();  // raw stage s landed; every wave is done with the bf16 stage
-      dequant_stage(raw + (s & 1) * kFp8RawBytes, smem, sct, wave, lane);
-      __syncthreads();  // bf16 stage complete; raw stage s consumed
-      // stage s+2's records ride along this stage's Q.K^T (EXEC-gated past the
-      // end, with addresses of this stage so every page lookup is in range)
-      const bool more = s + 2 < nstage;
-      RecordLoader<kPC> ld;
-      ld.begin(a, raw + (s & 1) * kFp8RawBytes, page_base, it.tok0 + (more ? s + 2 : s) * kStageTokens, it.tok1,
-               wave);
-      ld.on = __builtin_amdgcn_readfirstlane(more ? ~0u : 0u);
-      wide_stage<kPC, true, true>(a, qf, st, smem, it.tok0 + s * kStageTokens, bound, kb, pb, vb, g, ld, wave, sct);
-    }
-    __syncthreads();  // the bf16 stage is free for the next item
-  } else {
-    if (nstage > 0) issue_stage_bf16<kPC>(a, smem, page_base, it.tok0, it.tok1, wave, lane);
-    for (int s = 0; s < nstage; ++s) {
-      wait_vmcnt<0>();
-      __syncthreads();
-      wide_body<kPC>(a, qf, st, smem + (s & 1) * kStageBytes, smem + ((s + 1) & 1) * kStageBytes,
-                     s + 1 < nstage, page_base, it.tok0 + (s + 1) * kStageTokens, it.tok1,
-                     it.tok0 + s * kStageTokens, bound, kb, pb, vb, wave, lane);
-      __syncthreads();  // every wave is done with this stage before it is refilled
-    }
+  if (nstage > 0) issue_stage_bf16<kPC>(a, smem, page_base, it.tok0, it.tok1, wave, lane);
+  for (int s = 0; s < nstage; ++s) {
+    wait_vmcnt<0>();
+    __syncthreads();
+    wide_body<kPC>(a, qf, st, smem + (s & 1) * kStageBytes, smem + ((s + 1) & 1) * kStageBytes,
+                   s + 1 < nstage, page_base, it.tok0 + (s + 1) * kStageTokens, it.tok1,
+                   it.tok0 + s * kStageTokens, bound, kb, pb, vb, wave, lane);
+    __syncthreads();  // every wave is done with this stage before it is refilled
   }
-
   wide_epilogue(a, it, st, ri, rib, smem, wave, lane);
 }
 
@@ -1042,9 +975,14 @@ __device__ void wide8_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* s
       auto kread = [&](int m) -> u32x4 { return *(const LDS_AS u32x4*)(raw + kaddr + tb * kFp8RecordBytes + 32 * m); };
 #pragma unroll
       for (int i = 0; i < KD; ++i) kr[i] = kread(i);
+      f32x4 tsc[4];  // this tile's scales of the lane's keys, read as the tile starts
 #pragma unroll
       for (int m = 0; m < 16; ++m) {
         pin_loads();
+        if ((m & 3) == 0) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) tsc[q] = scales(m >> 2, q);
+        }
         if ((m & 1) == 0 && sub * 8 + (m >> 1) < RecordLoader<kPC>::kSlices) ld.issue(a, sub * 8 + (m >> 1), wave);
         const u32x4 c = kr[m % KD];
         if (m + KD < 16) kr[m % KD] = kread(m + KD);
@@ -1059,10 +997,9 @@ __device__ void wide8_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* s
           mfma32_drain(part);
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const f32x4 sc = scales(m >> 2, q);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              const float t = part[4 * q + r] * sc[r];
+              const float t = part[4 * q + r] * tsc[q][r];
               sacc[4 * q + r] = (m == 3) ? t : sacc[4 * q + r] + t;
             }
           }
@@ -1114,17 +1051,22 @@ __device__ void wide8_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* s
 #pragma unroll
       for (int i = 0; i < VD; ++i) vr[i] = vread(i);
       bf16x8 pt[2];
+      f32x4 nsc[4];  // scales of the next tile, read half a tile ahead
+#pragma unroll
+      for (int q = 0; q < 4; ++q) nsc[q] = scales(0, q);
 #pragma unroll
       for (int j = 0; j < 32; ++j) {
         pin_loads();
         if ((j & 7) == 0) {
           // output dims of tile j/8: P scaled by each key's tile scale
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const f32x4 sc = scales(j >> 3, q);
+          for (int q = 0; q < 4; ++q)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) pt[q >> 1][4 * (q & 1) + r] = (__bf16)(pf[4 * q + r] * sc[r]);
-          }
+            for (int r = 0; r < 4; ++r) pt[q >> 1][4 * (q & 1) + r] = (__bf16)(pf[4 * q + r] * nsc[q][r]);
+        }
+        if ((j & 7) == 4 && j < 24) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) nsc[q] = scales((j >> 3) + 1, q);
         }
         const u32x2 v = vr[j % VD];
         if (j + VD < 32) vr[j % VD] = vread(j + VD);
@@ -1135,259 +1077,6 @@ __device__ void wide8_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* s
   }
   __syncthreads();  // every wave is done with the stage buffers before the epilogue stages rows there
   wide_epilogue(a, it, st, ri, rib, smem, wave, lane);
-}
-
-// ---------------------------------------------------------------------------
-// SPLIT mode: 128 rows per workgroup like WIDE, but P.V is split by output
-// columns.  Wave w computes S^T = K . Q^T for its own rows [32w, 32w+32)
-// (Q stays in its registers) and owns their softmax state; P goes through
-// LDS, and wave w then computes O^T for output dims [128w, 128w+128) of all
-// 128 rows.  Each wave reads a quarter of V instead of all of it, which
-// quarters the transposed LDS reads, the costliest LDS traffic of WIDE.
-//
-// A stage's P is exchanged in two 32-key halves: keys 0..31 through a
-// dedicated 8 KB buffer (written before barrier A), keys 32..63 through the
-// stage's kpe region (free once every wave is past Q.K^T, i.e. after A;
-// visible after barrier B).  When an owner raises a row's running max it
-// publishes the row's factor alpha and a flag; after A every wave applies
-// the factors to its O columns (rare: lazy rescale as in WIDE).
-// ---------------------------------------------------------------------------
-constexpr int kSplitP0Off = 2 * kStageBytes;                   // P keys 0..31: [128 rows][64 B]
-constexpr int kSplitXOff = kSplitP0Off + kWideRows * 64;       // alpha / l [128] f32, flags [4] i32
-constexpr int kSplitLdsBytes = kSplitXOff + kWideRows * 4 + 16;
-static_assert(kSplitLdsBytes <= 160 * 1024, "split-mode LDS budget");
-
-// P row layout: 32 keys of bf16 = four 16-byte chunks, XOR-swizzled by row
-// so that 8 consecutive rows reading one chunk hit distinct banks.
-__device__ __forceinline__ int p_off(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 1) & 3)) << 4); }
-
-struct SplitState {
-  f32x16 o[4][4];  // O^T tiles [ct][rt]: lane holds row 32rt + n, dims 128w + 32ct + 8(r/4) + 4g + r%4
-  float m_run;     // owner: running max (log2 units) of row 32w + n
-  float l_run;     // owner: running sum of this lane's keys
-};
-
-template <int kPC, bool kPrefetch>
-__device__ __forceinline__ void split_stage(const AttnArgs& a, const bf16x8 (&qf)[36], SplitState& st,
-                                            LDS_AS char* __restrict__ cur, LDS_AS char* __restrict__ p0,
-                                            LDS_AS char* __restrict__ xch, int stage_tok, int bound,
-                                            const int (&kb)[8], const int (&pb)[4], const int (&vb)[4][2],
-                                            const int (&pr)[2], const int (&pw)[4], int g, int n,
-                                            StageLoader<kPC>& ld, int wave) {
-  // ---- S^T[64 keys x 32 rows] = K . Q^T: two 32-key chains sharing each Q fragment
-  f32x16 s0, s1;
-  auto kread = [&](int ks, int tb) -> bf16x8 {
-    return ks < 32 ? lds_read_b128(cur, kb[ks & 7] + 256 * (ks >> 3) + tb * kCkvRowBytes)
-                   : lds_read_b128(cur, pb[ks - 32] + tb * kKpeRowBytes);
-  };
-  constexpr int D = 3;  // k-steps of K fragments in flight
-  bf16x8 kr0[D], kr1[D];
-#pragma unroll
-  for (int i = 0; i < D; ++i) {
-    kr0[i] = kread(i, 0);
-    kr1[i] = kread(i, 32);
-  }
-#pragma unroll
-  for (int ks = 0; ks < 36; ++ks) {
-    if (kPrefetch && (ks & 1) == 0) ld.issue(a, ks >> 1, wave);  // 18 slices over 36 k-steps
-    const bf16x8 a0 = kr0[ks % D], a1 = kr1[ks % D];
-    if (ks + D < 36) {
-      kr0[ks % D] = kread(ks + D, 0);
-      kr1[ks % D] = kread(ks + D, 32);
-    }
-    if (ks == 0) {
-      mfma32_first(s0, a0, qf[0]);
-      mfma32_first(s1, a1, qf[0]);
-    } else {
-      mfma32_acc(s0, a0, qf[ks]);
-      mfma32_acc(s1, a1, qf[ks]);
-    }
-  }
-  mfma32_drain(s0, s1);
-
-  // ---- owner softmax over the 64 keys of row 32w + n
-  // lane holds keys 8(r/4) + 4g + r%4 of each 32-key half
-  float mx = kNegInf;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int k0 = stage_tok + 8 * (r >> 2) + 4 * g + (r & 3);
-    s0[r] = k0 < bound ? s0[r] * a.scale_log2 : kNegInf;
-    s1[r] = k0 + 32 < bound ? s1[r] * a.scale_log2 : kNegInf;
-    mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-  }
-  mx = max_xor32(mx);
-  const bool raise = __builtin_amdgcn_ballot_w64(mx > st.m_run + kRescaleSlack) != 0;
-  float alpha = 1.f;
-  if (raise) {
-    const float m_new = fmaxf(st.m_run, mx);
-    alpha = (st.m_run == kNegInf) ? 0.f : fast_exp2(st.m_run - m_new);
-    st.l_run *= alpha;
-    st.m_run = m_new;
-  }
-  const float mref = (st.m_run == kNegInf) ? 0.f : st.m_run;
-  bf16x4 h0[4], h1[4];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const float p0v = fast_exp2(s0[r] - mref);
-    const float p1v = fast_exp2(s1[r] - mref);
-    st.l_run += p0v + p1v;
-    h0[r >> 2][r & 3] = (__bf16)p0v;
-    h1[r >> 2][r & 3] = (__bf16)p1v;
-  }
-#pragma unroll
-  for (int q = 0; q < 4; ++q) *(LDS_AS bf16x4*)(p0 + pw[q]) = h0[q];
-  LDS_AS float* xa = (LDS_AS float*)xch;
-  if (raise && g == 0) xa[32 * wave + n] = alpha;
-  if (lane_here() == 0) ((LDS_AS int*)(xch + kWideRows * 4))[wave] = raise ? 1 : 0;
-  __syncthreads();  // A: P keys 0..31, factors and flags published; every wave is past Q.K^T
-
-  LDS_AS char* p1 = cur + kStageCkvBytes;  // the stage's kpe region now holds P keys 32..63
-#pragma unroll
-  for (int q = 0; q < 4; ++q) *(LDS_AS bf16x4*)(p1 + pw[q]) = h1[q];
-  {
-    typedef int i32x4 __attribute__((ext_vector_type(4)));
-    const i32x4 fl = *(const LDS_AS i32x4*)(xch + kWideRows * 4);
-    if ((fl[0] | fl[1] | fl[2] | fl[3]) != 0) {
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        const float f = fl[rt] ? xa[32 * rt + n] : 1.f;
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) scale_acc<16>(st.o[ct][rt], f);
-      }
-    }
-  }
-
-  // ---- O^T[128 dims x 128 rows] += V^T . P^T, 16 keys per k-step
-  auto vread = [&](int ct, int kk) -> bf16x8 {  // kk = 16-key step within the stage
-    const i16x4 v0 = lds_read_tr(cur, vb[ct][0] + kk * 16 * kCkvRowBytes);
-    const i16x4 v1 = lds_read_tr(cur, vb[ct][1] + kk * 16 * kCkvRowBytes);
-    const i16x8 v = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-    return __builtin_bit_cast(bf16x8, v);
-  };
-  auto pv_half = [&](const LDS_AS char* __restrict__ pbuf, int kk0) {
-    // per 16-key step: the 4 P^T fragments (one per row tile) stay in
-    // registers; V^T fragments (one per dim tile) stream two ahead
-    bf16x8 pf[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) pf[r] = lds_read_b128(pbuf, pr[0] + r * 32 * 64);
-    bf16x8 v0 = vread(0, kk0), v1 = vread(1, kk0);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {  // j = 4 kk + ct
-      const int kk = j >> 2, c = j & 3;
-      const bf16x8 v2 = (j + 2 < 8) ? vread((j + 2) & 3, kk0 + ((j + 2) >> 2)) : v1;
-      if (j == 4) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) pf[r] = lds_read_b128(pbuf, pr[1] + r * 32 * 64);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        st.o[c][r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, pf[r], st.o[c][r], 0, 0, 0);
-      (void)kk;
-      v0 = v1;
-      v1 = v2;
-    }
-  };
-  pv_half(p0, 0);
-  __syncthreads();  // B: P keys 32..63 visible
-  pv_half(p1, 2);
-}
-
-template <int kPC>
-__device__ void split_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* smem, int wave, int lane) {
-  const int g = lane >> 5;
-  const int n = lane & 31;
-  const int rib = wave * 32 + n;  // the row this lane owns for Q.K^T and the softmax
-  const RowInfo ri = row_info(a, it, rib);
-  const int bound = row_key_bound(a, it, ri);
-
-  bf16x8 qf[36];
-  {
-    const bf16x8 z = {};
-    const __bf16* qn = (const __bf16*)a.q_nope + ri.qrow * kDimCkv + 8 * g;
-    const __bf16* qp = (const __bf16*)a.q_pe + ri.qrow * kDimKpe + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < 32; ++ks) qf[ks] = ri.ok ? *(const bf16x8*)(qn + 16 * ks) : z;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qf[32 + ks] = ri.ok ? *(const bf16x8*)(qp + 16 * ks) : z;
-  }
-  int kb[8], pb[4], vb[4][2], pr[2], pw[4];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) kb[k] = ckv_off(n, 2 * k + g);
-#pragma unroll
-  for (int k = 0; k < 4; ++k) pb[k] = kpe_off(n, 2 * k + g);
-  {
-    // V^T operand (32 dims x 16 keys): lane l reads key 8(l/32) + (l%16)/4 (+4),
-    // dims 128w + 32ct + 16((l/16)%2) + 4(l%4) .. +3
-    const int t = 8 * g + ((lane & 15) >> 2);
-    const int cl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-    const int w8 = (lane & 1) ? 8 : 0;
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      vb[ct][0] = ckv_off(t, 4 * ct + cl) + w8 + 256 * wave;
-      vb[ct][1] = ckv_off(t + 4, 4 * ct + cl) + w8 + 256 * wave;
-    }
-  }
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk) pr[kk] = p_off(n, 2 * kk + g);       // P^T operand: row n, keys 16kk + 8g ..
-#pragma unroll
-  for (int q = 0; q < 4; ++q) pw[q] = p_off(rib, q) + 8 * g;         // P writer: keys 8q + 4g .. +3
-
-  SplitState st;
-#pragma unroll
-  for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) st.o[ct][rt] = f32x16{};
-  st.m_run = kNegInf;
-  st.l_run = 0.f;
-
-  LDS_AS char* p0 = smem + kSplitP0Off;
-  LDS_AS char* xch = smem + kSplitXOff;
-  const int page_base = ld_const(a.kv_indptr, it.b);
-  const int nstage = (it.tok1 - it.tok0 + kStageTokens - 1) / kStageTokens;
-  if (nstage > 0) issue_stage_bf16<kPC>(a, smem, page_base, it.tok0, it.tok1, wave, lane);
-  for (int s = 0; s < nstage; ++s) {
-    wait_vmcnt<0>();
-    __syncthreads();  // stage s landed; every wave is done with stage s-1 (its buffer, P, factors)
-    LDS_AS char* cur = smem + (s & 1) * kStageBytes;
-    StageLoader<kPC> ld;
-    if (s + 1 < nstage) {
-      ld.begin(a, smem + ((s + 1) & 1) * kStageBytes, page_base, it.tok0 + (s + 1) * kStageTokens, it.tok1, wave);
-      split_stage<kPC, true>(a, qf, st, cur, p0, xch, it.tok0 + s * kStageTokens, bound, kb, pb, vb, pr, pw, g, n,
-                             ld, wave);
-    } else {
-      split_stage<kPC, false>(a, qf, st, cur, p0, xch, it.tok0 + s * kStageTokens, bound, kb, pb, vb, pr, pw, g,
-                              n, ld, wave);
-    }
-  }
-
-  // ---- epilogue: owners publish l; every wave normalises its dims of all 128 rows
-  const float l_tot = sum_xor32(st.l_run);
-  __syncthreads();  // every wave is done reading the factors of the last stage
-  if (g == 0) ((LDS_AS float*)xch)[rib] = l_tot;
-  if (ri.ok && g == 0) {
-    const bool empty = !(l_tot > 0.f);
-    store_lse(a, it, ri, rib, empty ? kNegInf : (st.m_run + __log2f(l_tot)) * kLn2);
-  }
-  __syncthreads();
-#pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    const int row = 32 * rt + n;
-    const RowInfo rj = row_info(a, it, row);
-    const float l = ((const LDS_AS float*)xch)[row];
-    const float inv = (l > 0.f) ? 1.f / l : 0.f;
-    if (rj.ok) {
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4 v = {st.o[ct][rt][4 * q] * inv, st.o[ct][rt][4 * q + 1] * inv, st.o[ct][rt][4 * q + 2] * inv,
-                           st.o[ct][rt][4 * q + 3] * inv};
-          store4(a, it, rj, row, 128 * wave + 32 * ct + 8 * q + 4 * g, v);
-        }
-      }
-    }
-  }
-  __syncthreads();  // the exchange area is reused by the next item
 }
 
 // ---------------------------------------------------------------------------
@@ -1899,7 +1588,7 @@ __device__ __forceinline__ int xcd_list(int b, int n) {
 template <int kMode, int kPC, bool kFp8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_attn_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem_raw[kFp8 ? kFp8LdsBytes : (kMode == 4 ? kSplitLdsBytes : kLdsBytes)];
+  __shared__ __attribute__((aligned(1024))) char smem_raw[kFp8 ? kFp8LdsBytes : kLdsBytes];
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -1920,9 +1609,7 @@ void mla_attn_kernel(AttnArgs a) {
     if (kMode == 1 && kFp8) {
       wide8_item<kPC>(a, it, smem, wave, lane);
     } else if (kMode == 1) {
-      wide_item<kPC, kFp8>(a, it, smem, wave, lane);
-    } else if (kMode == 4) {
-      split_item<kPC>(a, it, smem, wave, lane);
+      wide_item<kPC>(a, it, smem, wave, lane);
     } else {
       narrow_item<kPC, kFp8>(a, it, smem, wave, lane);
     }
@@ -2016,15 +1703,10 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(AttnArgs a) {
 // its execution, no queue gaps); with null events it is a plain launch.
 template <int kMode, int kPC>
 hipError_t launch_mode(const AttnArgs& a, int kv_fp8, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
-  if constexpr (kMode == 4) {
-    hipExtLaunchKernelGGL((mla_attn_kernel<kMode, kPC, false>), dim3(a.num_wgs), dim3(256), 0, stream, t0, t1, 0, a);
+  if (kv_fp8) {
+    hipExtLaunchKernelGGL((mla_attn_kernel<kMode, kPC, true>), dim3(a.num_wgs), dim3(256), 0, stream, t0, t1, 0, a);
   } else {
-    if (kv_fp8) {
-      hipExtLaunchKernelGGL((mla_attn_kernel<kMode, kPC, true>), dim3(a.num_wgs), dim3(256), 0, stream, t0, t1, 0, a);
-    } else {
-      hipExtLaunchKernelGGL((mla_attn_kernel<kMode, kPC, false>), dim3(a.num_wgs), dim3(256), 0, stream, t0, t1, 0,
-                            a);
-    }
+    hipExtLaunchKernelGGL((mla_attn_kernel<kMode, kPC, false>), dim3(a.num_wgs), dim3(256), 0, stream, t0, t1, 0, a);
   }
   return hipGetLastError();
 }
@@ -2044,12 +1726,6 @@ hipError_t launch_attention(const AttnArgs& a, int tile_mode, int kv_fp8, hipStr
     if (pc == kPageBig) return launch_quad<kPageBig>(a, stream, t0, t1);
     if (pc == kPageMid) return launch_quad<kPageMid>(a, stream, t0, t1);
     return launch_quad<kPageSmall>(a, stream, t0, t1);
-  }
-  if (tile_mode == 4) {
-    if (kv_fp8) return hipErrorNotSupported;  // rejected when the plan is made
-    if (pc == kPageBig) return launch_mode<4, kPageBig>(a, 0, stream, t0, t1);
-    if (pc == kPageMid) return launch_mode<4, kPageMid>(a, 0, stream, t0, t1);
-    return launch_mode<4, kPageSmall>(a, 0, stream, t0, t1);
   }
   if (tile_mode == 1) {
     if (pc == kPageBig) return launch_mode<1, kPageBig>(a, kv_fp8, stream, t0, t1);

@@ -79,7 +79,7 @@ def _check_cover(plan, kv_len, q_len, H, causal=False, prefill=False):
     return items, ptr
 
 
-@pytest.mark.parametrize("tile_mode", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("tile_mode", [0, 1, 2, 3])
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_decode_schedule_covers_every_key_once(mla, tile_mode, seed):
     rng = np.random.default_rng(seed)
@@ -171,8 +171,7 @@ def test_plan_argument_errors(mla):
     assert _status(mla, **{**pre, "qo_indptr": [0, 3, 2]}) == -1        # decreasing
     assert _status(mla, **{**pre, "kv_format": 1}) == -2                # fp8 prefill
     assert _status(mla, **{**ok, "batch": 0, "kv_len": [], "kv_indptr": [0]}) == 0
-    assert _status(mla, **{**ok, "tile_mode": 5}) == -1
-    assert _status(mla, **{**ok, "kv_format": 1, "tile_mode": 4}) == -2  # fp8 has no split tile
+    assert _status(mla, **{**ok, "tile_mode": 4}) == -1
     assert _status(mla, **{**ok, "kv_format": 1}) == 0                  # fp8 decode
     assert _status(mla, **{**ok, "kv_format": 1, "tile_mode": 3}) == -2  # fp8 has no quad tile
 

@@ -127,10 +127,6 @@ CASES = [
     (256, 64, [150, 90], 3, 2, False),
     (16, 64, [10000, 3], 2, 100, False),      # more than 64 splits of one request
     (128, 64, [9000], 1, 80, True),
-    (128, 64, [1, 37, 64, 200], 4, 0, False),
-    (128, 16, [700, 3, 65], 4, 3, True),
-    (64, 1, [2, 130], 4, 2, False),
-    (40, 8, [100, 400, 0, 33], 4, 2, False),
 ]
 
 
@@ -175,8 +171,6 @@ PREFILL_CASES = [
     (128, 64, [3, 1, 8, 5], [64, 100, 700, 5], True, 3, 0),
     (128, 16, [2, 4], [300, 17], True, 3, 3),
     (32, 64, [8, 1, 3], [500, 9, 64], True, 3, 2),
-    (128, 64, [3, 1, 8, 5], [64, 100, 700, 5], True, 4, 0),
-    (16, 16, [8, 1, 3], [500, 9, 64], True, 4, 2),
 ]
 
 
@@ -206,7 +200,7 @@ def test_empty_batch_is_a_no_op(mla):
 # bit-exact properties of the paged gather
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("H,mode", [(16, 2), (128, 1), (128, 3), (128, 4)])
+@pytest.mark.parametrize("H,mode", [(16, 2), (128, 1), (128, 3)])
 def test_page_permutation_is_bitwise_invariant(mla, H, mode):
     say(f"page permutation H={H} mode={mode}")
     w = make_workload(kv_lens=[130, 64, 1, 900], heads=H, page_size=16, seed=55)
