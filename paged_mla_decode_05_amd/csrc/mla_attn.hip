@@ -1350,8 +1350,11 @@ __device__ __forceinline__ void quad_body(const AttnArgs& a, const bf16x8 (&qf)[
                                           int next_tok, int tok_end, int stage_tok, const int (&bound)[2],
                                           const int (&kb)[4], const int (&pb)[2], const int (&vb)[2],
                                           const int (&vx)[2], int wave, int lane) {
+  // next stage's slices ride along Q.K^T; past the last stage they are
+  // issued with an empty EXEC mask (addresses of this stage, always valid)
   StageLoader<kPC> ld;
-  if (prefetch) ld.begin(a, nxt, page_base, next_tok, tok_end, wave);
+  ld.begin(a, nxt, page_base, prefetch ? next_tok : stage_tok, tok_end, wave);
+  ld.on = __builtin_amdgcn_readfirstlane(prefetch ? ~0u : 0u);
   const int g4 = lane >> 4, n = lane & 15;
   LDS_AS char* pbuf = scr;
   LDS_AS float* tmax = (LDS_AS float*)(scr + (kTmaxOff - kPBufOff));
@@ -1361,16 +1364,20 @@ __device__ __forceinline__ void quad_body(const AttnArgs& a, const bf16x8 (&qf)[
   auto kread = [&](int ks) -> bf16x8 {
     return ks < 16 ? lds_read_b128(cur, kb[ks & 3] + 256 * (ks >> 2)) : lds_read_b128(cur, pb[ks - 16]);
   };
-  bf16x8 k0 = kread(0), k1 = kread(1);
+  constexpr int KD = 4;  // K fragments in flight
+  bf16x8 kr[KD];
+#pragma unroll
+  for (int i = 0; i < KD; ++i) kr[i] = kread(i);
 #pragma unroll
   for (int ks = 0; ks < 18; ++ks) {
-    if (prefetch) ld.issue(a, ks, wave);  // one prefetch slice per k-step
-    const bf16x8 k2 = (ks + 2 < 18) ? kread(ks + 2) : k1;
+    pin_loads();
+    ld.issue(a, ks, wave);  // one prefetch slice per k-step
+    const bf16x8 k0 = kr[ks % KD];
+    if (ks + KD < 18) kr[ks % KD] = kread(ks + KD);
     sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[0][ks], sacc[0], 0, 0, 0);
     sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[1][ks], sacc[1], 0, 0, 0);
-    k0 = k1;
-    k1 = k2;
   }
+  pin_loads();
   // scale, mask, tile max over this wave's 16 keys
   float sv[2][4], tm[2];
 #pragma unroll
@@ -1418,25 +1425,34 @@ __device__ __forceinline__ void quad_body(const AttnArgs& a, const bf16x8 (&qf)[
   for (int t = 0; t < 2; ++t) st.l[t] += (p[t][0] + p[t][1]) + (p[t][2] + p[t][3]);
 
   // O^T[128 dims x 32 rows] += V^T[128 dims x 64 keys] . P^T[64 keys x 32 rows]
+  auto vread = [&](int j) -> bf16x8 {  // j = 8 kk + c: keys 32kk + 8g4 + 0..3, +4..7 of dims 128w + 16c + lane%16
+    const int kk = j >> 3, c = j & 7;
+    const int cx0 = (32 * c) ^ vx[0];
+    const int cx1 = (32 * c) ^ vx[1];
+    const i16x4 v0 = lds_read_tr(cur, vb[0] + cx0 + 32 * kk * kCkvRowBytes);
+    const i16x4 v1 = lds_read_tr(cur, vb[1] + cx1 + 32 * kk * kCkvRowBytes);
+    const i16x8 v = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    return __builtin_bit_cast(bf16x8, v);
+  };
+  constexpr int VD = 4;  // V^T fragments in flight
+  bf16x8 vr[VD];
+  bf16x8 pt[2][2];
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-    bf16x8 pt[2];
+  for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-      pt[t] = lds_read_b128(pbuf, (16 * t + n) * kPRowBytes + (32 * kk + 8 * g4) * 2);
+    for (int t = 0; t < 2; ++t) pt[kk][t] = lds_read_b128(pbuf, (16 * t + n) * kPRowBytes + (32 * kk + 8 * g4) * 2);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      // keys 32kk + 8g4 + 0..3 and +4..7 of dims 128w + 16c + (lane & 15)
-      const int cx0 = (32 * c) ^ vx[0];
-      const int cx1 = (32 * c) ^ vx[1];
-      const i16x4 v0 = lds_read_tr(cur, vb[0] + cx0 + 32 * kk * kCkvRowBytes);
-      const i16x4 v1 = lds_read_tr(cur, vb[1] + cx1 + 32 * kk * kCkvRowBytes);
-      const i16x8 v = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-      const bf16x8 vf = __builtin_bit_cast(bf16x8, v);
-      st.o[c][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pt[0], st.o[c][0], 0, 0, 0);
-      st.o[c][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pt[1], st.o[c][1], 0, 0, 0);
-    }
+  for (int i = 0; i < VD; ++i) vr[i] = vread(i);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    pin_loads();
+    const int kk = j >> 3, c = j & 7;
+    const bf16x8 vf = vr[j % VD];
+    if (j + VD < 16) vr[j % VD] = vread(j + VD);
+    st.o[c][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pt[kk][0], st.o[c][0], 0, 0, 0);
+    st.o[c][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pt[kk][1], st.o[c][1], 0, 0, 0);
   }
+  pin_loads();
 }
 
 template <int kPC, bool kFp8>
