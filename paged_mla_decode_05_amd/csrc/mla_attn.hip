@@ -284,8 +284,10 @@ struct StageLoader {
   uint32_t on = ~0u;        // EXEC mask (both halves) of the slices: zero turns issue() into no-ops
   static constexpr int kSlices = kDmaPerWave;
 
+  // page_hint (kPageBig): the stage's page, when the caller looked it up
+  // ahead of time (the scalar load then has a whole stage to land).
   __device__ __forceinline__ void begin(const AttnArgs& a, LDS_AS char* stage, int page_base, int tok0,
-                                        int tok_end, int wave) {
+                                        int tok_end, int wave, int page_hint = -1) {
     const int sh = a.page_shift;
     const int mask = (1 << sh) - 1;
     const char* ckv = (const char*)a.ckv;
@@ -294,7 +296,7 @@ struct StageLoader {
     s_tok0 = tok0;
     last = tok_end - 1 - tok0;
     if (kPageClass == kPageBig) {
-      const int page = ld_const(a.kv_indices, page_base + (tok0 >> sh));
+      const int page = page_hint >= 0 ? page_hint : ld_const(a.kv_indices, page_base + (tok0 >> sh));
       const size_t row0 = ((size_t)page << sh) + (tok0 & mask);
       ckv_row[0] = ckv + row0 * kCkvRowBytes;
       kpe_base[0] = kpe + row0 * kKpeRowBytes;
@@ -743,13 +745,13 @@ __device__ __forceinline__ void wide_body(const AttnArgs& a, const bf16x8 (&qf)[
                                           const LDS_AS char* __restrict__ cur, LDS_AS char* __restrict__ nxt,
                                           bool prefetch, int page_base, int next_tok, int tok_end,
                                           int stage_tok, int bound, const int (&kb)[8], const int (&pb)[4],
-                                          const int (&vb)[8], int wave, int lane) {
+                                          const int (&vb)[8], int wave, int lane, int page_hint) {
   // The slices of the next stage ride along this stage's Q.K^T.  For the
   // last stage they are issued with an empty EXEC mask (and addresses of
   // this stage, so every page lookup stays inside the request): one
   // instruction stream, no branch in the MFMA loop.
   StageLoader<kPC> ld;
-  ld.begin(a, nxt, page_base, prefetch ? next_tok : stage_tok, tok_end, wave);
+  ld.begin(a, nxt, page_base, prefetch ? next_tok : stage_tok, tok_end, wave, page_hint);
   ld.on = __builtin_amdgcn_readfirstlane(prefetch ? ~0u : 0u);
   wide_stage<kPC, true>(a, qf, st, cur, stage_tok, bound, kb, pb, vb, lane >> 5, ld, wave);
   static_assert(StageLoader<kPC>::kSlices == 18, "two sub-tiles of 9 slices");
@@ -852,13 +854,21 @@ __device__ void wide_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* sm
   const int page_base = ld_const(a.kv_indptr, it.b);
   const int nstage = (it.tok1 - it.tok0 + kStageTokens - 1) / kStageTokens;
   if (nstage > 0) issue_stage_bf16<kPC>(a, smem, page_base, it.tok0, it.tok1, wave, lane);
+  // one-page stages: the page of stage s+1 is looked up a stage ahead (stage 0's when none is next)
+  auto page_at = [&](int stage) -> int {
+    return kPC == kPageBig ? ld_const(a.kv_indices, page_base + ((it.tok0 + stage * kStageTokens) >> a.page_shift))
+                           : -1;
+  };
+  int pg_next = page_at(nstage > 1 ? 1 : 0);
   for (int s = 0; s < nstage; ++s) {
+    const int pg_after = page_at(s + 2 < nstage ? s + 2 : 0);
     wait_vmcnt<0>();
     __syncthreads();
     wide_body<kPC>(a, qf, st, smem + (s & 1) * kStageBytes, smem + ((s + 1) & 1) * kStageBytes,
-                   s + 1 < nstage, page_base, it.tok0 + (s + 1) * kStageTokens, it.tok1,
-                   it.tok0 + s * kStageTokens, bound, kb, pb, vb, wave, lane);
+                   s + 1 < nstage, page_base, it.tok0 + (s + 1 < nstage ? s + 1 : 0) * kStageTokens, it.tok1,
+                   it.tok0 + s * kStageTokens, bound, kb, pb, vb, wave, lane, pg_next);
     __syncthreads();  // every wave is done with this stage before it is refilled
+    pg_next = pg_after;
   }
   wide_epilogue(a, it, st, ri, rib, smem, wave, lane);
 }
@@ -1349,11 +1359,11 @@ __device__ __forceinline__ void quad_body(const AttnArgs& a, const bf16x8 (&qf)[
                                           LDS_AS char* __restrict__ scr, bool prefetch, int page_base,
                                           int next_tok, int tok_end, int stage_tok, const int (&bound)[2],
                                           const int (&kb)[4], const int (&pb)[2], const int (&vb)[2],
-                                          const int (&vx)[2], int wave, int lane) {
+                                          const int (&vx)[2], int wave, int lane, int page_hint) {
   // next stage's slices ride along Q.K^T; past the last stage they are
-  // issued with an empty EXEC mask (addresses of this stage, always valid)
+  // issued with an empty EXEC mask (addresses inside the request)
   StageLoader<kPC> ld;
-  ld.begin(a, nxt, page_base, prefetch ? next_tok : stage_tok, tok_end, wave);
+  ld.begin(a, nxt, page_base, prefetch ? next_tok : stage_tok, tok_end, wave, page_hint);
   ld.on = __builtin_amdgcn_readfirstlane(prefetch ? ~0u : 0u);
   const int g4 = lane >> 4, n = lane & 15;
   LDS_AS char* pbuf = scr;
@@ -1513,12 +1523,20 @@ __device__ void quad_item(const AttnArgs& a, const WorkItem& it, int role, LDS_A
   const int page_base = ld_const(a.kv_indptr, it.b);
   const int nstage = (it.tok1 - it.tok0 + kStageTokens - 1) / kStageTokens;
   if (nstage > 0) issue_stage_bf16<kPC>(a, smem, page_base, it.tok0, it.tok1, wave, lane);
+  // one-page stages: the page of stage s+1 is looked up a stage ahead (stage 0's when none is next)
+  auto page_at = [&](int stage) -> int {
+    return kPC == kPageBig ? ld_const(a.kv_indices, page_base + ((it.tok0 + stage * kStageTokens) >> a.page_shift))
+                           : -1;
+  };
+  int pg_next = page_at(nstage > 1 ? 1 : 0);
   for (int s = 0; s < nstage; ++s) {
+    const int pg_after = page_at(s + 2 < nstage ? s + 2 : 0);
     wait_vmcnt<0>();
     __syncthreads();  // stage s landed; every wave is done with stage s-1
     quad_body<kPC>(a, qf, st, smem + (s & 1) * kStageBytes, smem + ((s + 1) & 1) * kStageBytes, scr,
-                   s + 1 < nstage, page_base, it.tok0 + (s + 1) * kStageTokens, it.tok1,
-                   it.tok0 + s * kStageTokens, bound, kb, pb, vb, vx, wave, lane);
+                   s + 1 < nstage, page_base, it.tok0 + (s + 1 < nstage ? s + 1 : 0) * kStageTokens, it.tok1,
+                   it.tok0 + s * kStageTokens, bound, kb, pb, vb, vx, wave, lane, pg_next);
+    pg_next = pg_after;
   }
 
   // row sums: this lane's keys -> this wave's keys -> all waves
