@@ -55,7 +55,7 @@ int32_t ilog2(int32_t x) {
 
 // Fixed per-item cost in key-token units: loading Q, the epilogue, and the
 // pipeline fill.  Used only to balance the schedule.
-constexpr int64_t kItemOverhead = 64;
+constexpr int64_t kItemOverhead = 256;
 // Smallest key chunk worth a separate work item (unless it is a remainder).
 constexpr int64_t kMinChunk = 128;
 
@@ -105,8 +105,13 @@ void pack_units(mla_plan* p, const std::vector<Unit>& units, int64_t budget) {
           left = budget;
         }
         int64_t take = std::max<int64_t>(left - kItemOverhead, stage) / stage * stage;
-        // never leave a remainder smaller than a minimum chunk behind
-        if (rest - take < kMinChunk) take = rest;
+        // never leave a remainder smaller than a minimum chunk behind: take
+        // less (the next workgroup gets a minimum chunk) rather than overrun
+        // this workgroup's budget, unless the whole rest is small
+        if (rest > take && rest - take < kMinChunk) {
+          const int64_t shorter = (rest - kMinChunk) / stage * stage;
+          take = shorter >= stage ? shorter : rest;
+        }
         if (d.max_splits > 0 && npieces + 1 >= d.max_splits) take = rest;
         take = std::min<int64_t>(take, rest);
         p->items.push_back({u.b, u.row0, u.nrows, (int32_t)t, (int32_t)(t + take), u.kv_len, u.q_len, -1});

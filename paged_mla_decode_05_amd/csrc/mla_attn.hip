@@ -660,7 +660,7 @@ __device__ __forceinline__ void wide_stage(const AttnArgs& a, const bf16x8 (&qf)
   // ---- S^T[32 keys x 32 rows] = K . Q^T over 576 dims for sub-tile tb, with
   // `side(ks)` run after MFMA ks (interleaved VALU work of another phase)
   auto qk = [&](f32x16& sacc, int tb, int dma0, auto&& side) {
-    constexpr int KD = 4;  // K fragments in flight
+    constexpr int KD = 3;  // K fragments in flight
     bf16x8 kr[KD];
 #pragma unroll
     for (int i = 0; i < KD; ++i) kr[i] = kread(tb, i);
@@ -1654,11 +1654,12 @@ void mla_attn_kernel(AttnArgs a) {
 // Combine: merge the partial results of each split (request, row block).
 // out = sum_s w_s o_s / sum_s w_s with w_s = exp(lse_s - max lse), and
 // lse = max lse + ln sum w (the log-sum-exp identity).  One wave per row:
-// lane s < nsplit reads lse_s, lane l then owns dims 8l..8l+7 and issues
-// the loads of up to 8 splits before it uses any, so the row's reads are in
-// flight together.
+// lane l owns dims 8l..8l+7.  The loads of the first 8 splits' partial rows
+// are issued together with the lse reads (they do not depend on them), so a
+// row costs one memory round trip when it has at most 8 splits.
 // ---------------------------------------------------------------------------
 constexpr int kCombineRows = 4;  // rows per combine workgroup (one per wave)
+constexpr int kCombineBatch = 8;  // partial rows in flight per lane
 
 __global__ __launch_bounds__(256) void mla_combine_kernel(AttnArgs a) {
   const int chunks_per_group = a.rows_per_block / kCombineRows;
@@ -1671,42 +1672,43 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(AttnArgs a) {
   if (r >= g_nrows) return;
   const size_t row0 = (size_t)slot0 * a.rows_per_block + r;  // row r of the group's first slot
   const size_t stride = (size_t)a.rows_per_block;             // rows between consecutive slots
-  // max and weight sum over the splits, 64 splits per pass (lane s + 64k)
-  float M = kNegInf;
-  for (int sp = lane; sp < nsplit; sp += 64) M = fmaxf(M, a.part_lse[row0 + sp * stride]);
+  const int d0 = lane * 8;
+  auto prow = [&](int sp) { return *(const bf16x8*)(a.part_o + (row0 + (size_t)sp * stride) * kDimCkv + d0); };
+  bf16x8 v[kCombineBatch];
+#pragma unroll
+  for (int j = 0; j < kCombineBatch; ++j)
+    if (j < nsplit) v[j] = prow(j);
+  // lse of split `lane` (splits >= 64 are read where they are needed)
+  const float ls_lane = lane < nsplit ? a.part_lse[row0 + (size_t)lane * stride] : kNegInf;
+  auto lse_of = [&](int sp) -> float {  // sp wave-uniform
+    return sp < 64 ? __shfl(ls_lane, sp) : a.part_lse[row0 + (size_t)sp * stride];
+  };
+  float M = ls_lane;
+  for (int sp = lane + 64; sp < nsplit; sp += 64) M = fmaxf(M, a.part_lse[row0 + (size_t)sp * stride]);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
   float W = 0.f;
   for (int sp = lane; sp < nsplit; sp += 64) {
-    const float ls = a.part_lse[row0 + sp * stride];
+    const float ls = sp < 64 ? ls_lane : a.part_lse[row0 + (size_t)sp * stride];
     W += (ls == kNegInf) ? 0.f : __expf(ls - M);
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) W += __shfl_xor(W, o);
-  const int d0 = lane * 8;
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if (M != kNegInf) {
-    for (int c = 0; c < nsplit; c += 64) {
-      // weight of split c + lane in lane `lane`
-      float wl = 0.f;
-      if (c + lane < nsplit) {
-        const float ls = a.part_lse[row0 + (c + lane) * stride];
-        wl = (ls == kNegInf) ? 0.f : __expf(ls - M);
+    for (int c = 0; c < nsplit; c += kCombineBatch) {
+      if (c > 0) {
+#pragma unroll
+        for (int j = 0; j < kCombineBatch; ++j)
+          if (c + j < nsplit) v[j] = prow(c + j);
       }
-      const int n_here = min(64, nsplit - c);
-      for (int s0 = 0; s0 < n_here; s0 += 8) {
-        bf16x8 v[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (s0 + j < n_here)
-            v[j] = *(const bf16x8*)(a.part_o + (row0 + (size_t)(c + s0 + j) * stride) * kDimCkv + d0);
+      for (int j = 0; j < kCombineBatch; ++j) {
+        if (c + j < nsplit) {
+          const float ls = lse_of(c + j);
+          const float w = (ls == kNegInf) ? 0.f : __expf(ls - M);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float w = __shfl(wl, s0 + j);
-          if (s0 + j < n_here) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] += w * (float)v[j][e];
-          }
+          for (int e = 0; e < 8; ++e) acc[e] += w * (float)v[j][e];
         }
       }
     }
