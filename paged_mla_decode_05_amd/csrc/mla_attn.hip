@@ -585,6 +585,7 @@ struct WideState {
   f32x16 o[16];   // O^T: lane holds row n, dims 32cb + 8(r/4) + 4g + r%4
   float m_run;    // running max (log2 units), per row
   float l_run;    // running sum of this lane's keys
+  bool o_live;    // wave-uniform: a P.V has run (before that O is zero and needs no rescale)
 };
 
 // Value fences for hand-interleaving VALU work into an MFMA stream: code
@@ -724,12 +725,13 @@ __device__ __forceinline__ void wide_stage(const AttnArgs& a, const bf16x8 (&qf)
     });
 #pragma unroll
     for (int r = 0; r < 16; ++r) s1[r] = sa1[r];
-    if (sm0.raise) rescale_o(sm0.alpha);  // no P.V is in flight here
+    if (sm0.raise && st.o_live) rescale_o(sm0.alpha);  // no P.V is in flight here; O is zero until the first P.V
     pv(0, pt0, pf0, [&](int j) {
       if (j < 16) sm_scale_mask(s1, sm1, 32, j);
       if (j == 16) sm_decide(sm1);
       if (j >= 17) sm_exp(s1, sm1, pt1, pf1, j - 17);
     });
+    st.o_live = true;
     sm_exp(s1, sm1, pt1, pf1, 15);
     if (sm1.raise) {
       // the last P.V MFMAs write O: let them retire before the AGPRs are read
@@ -850,6 +852,7 @@ __device__ void wide_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* sm
   for (int cb = 0; cb < 16; ++cb) st.o[cb] = f32x16{};
   st.m_run = kNegInf;
   st.l_run = 0.f;
+  st.o_live = false;
 
   const int page_base = ld_const(a.kv_indptr, it.b);
   const int nstage = (it.tok1 - it.tok0 + kStageTokens - 1) / kStageTokens;
@@ -945,6 +948,7 @@ __device__ void wide8_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* s
   for (int cb = 0; cb < 16; ++cb) st.o[cb] = f32x16{};
   st.m_run = kNegInf;
   st.l_run = 0.f;
+  st.o_live = false;
 
   const int page_base = ld_const(a.kv_indptr, it.b);
   const int nstage = (it.tok1 - it.tok0 + kStageTokens - 1) / kStageTokens;
@@ -1037,8 +1041,10 @@ __device__ void wide8_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* s
         const float m_new = fmaxf(st.m_run, mx);
         const float alpha = (st.m_run == kNegInf) ? 0.f : fast_exp2(st.m_run - m_new);
         st.l_run *= alpha;
+        if (__builtin_amdgcn_ballot_w64(st.m_run != kNegInf) != 0) {  // else O is still zero
 #pragma unroll
-        for (int cb = 0; cb < 16; ++cb) scale_acc<16>(st.o[cb], alpha);
+          for (int cb = 0; cb < 16; ++cb) scale_acc<16>(st.o[cb], alpha);
+        }
         st.m_run = m_new;
       }
       const float mref = (st.m_run == kNegInf) ? 0.f : st.m_run;
@@ -1147,10 +1153,12 @@ __device__ __forceinline__ void narrow_body(const AttnArgs& a, const bf16x8 (&qf
     const float m_new = fmaxf(st.m_run, mx);
     const float alpha = (st.m_run == kNegInf) ? 0.f : fast_exp2(st.m_run - m_new);
     st.l_run *= alpha;
+    if (__builtin_amdgcn_ballot_w64(st.m_run != kNegInf) != 0) {  // else O is still zero
 #pragma unroll
-    for (int cb = 0; cb < 32; ++cb) {
-      st.o[cb] *= alpha;
-      __builtin_amdgcn_sched_barrier(0);
+      for (int cb = 0; cb < 32; ++cb) {
+        st.o[cb] *= alpha;
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     st.m_run = m_new;
   }
@@ -1423,8 +1431,10 @@ __device__ __forceinline__ void quad_body(const AttnArgs& a, const bf16x8 (&qf)[
       const float m_new = fmaxf(st.m[t], smax[t]);
       const float alpha = (st.m[t] == kNegInf) ? 0.f : fast_exp2(st.m[t] - m_new);
       st.l[t] *= alpha;
+      if (__builtin_amdgcn_ballot_w64(st.m[t] != kNegInf) != 0) {  // else O is still zero
 #pragma unroll
-      for (int c = 0; c < 8; ++c) scale_acc<4>(st.o[c][t], alpha);
+        for (int c = 0; c < 8; ++c) scale_acc<4>(st.o[c][t], alpha);
+      }
       st.m[t] = m_new;
     }
     // nobody has read P yet (only the tile maxima): rewrite it, publish again
