@@ -520,6 +520,13 @@ struct RowInfo {
   bool ok;      // row exists in this block
 };
 
+// Flattened [total_q * H] index of the request's first row: rows r of a
+// request (r = query token * H + head) sit at row_base + r.
+__device__ __forceinline__ size_t row_base(const AttnArgs& a, const WorkItem& it) {
+  const int q_start = a.qo_indptr ? ld_const(a.qo_indptr, it.b) : it.b;
+  return (size_t)q_start * a.num_heads;
+}
+
 __device__ __forceinline__ RowInfo row_info(const AttnArgs& a, const WorkItem& it, int r_in_block) {
   RowInfo ri;
   const int H = a.num_heads;
@@ -527,9 +534,7 @@ __device__ __forceinline__ RowInfo row_info(const AttnArgs& a, const WorkItem& i
   ri.ok = r_in_block < it.nrows;
   const int rr = ri.ok ? r : it.row0;
   ri.qi = rr / H;
-  const int head = rr - ri.qi * H;
-  const int q_start = a.qo_indptr ? ld_const(a.qo_indptr, it.b) : it.b;
-  ri.qrow = (size_t)(q_start + ri.qi) * H + head;
+  ri.qrow = row_base(a, it) + rr;  // (q_start + qi) * H + head
   return ri;
 }
 
@@ -784,13 +789,13 @@ __device__ __forceinline__ void wide_epilogue(const AttnArgs& a, const WorkItem&
         *(LDS_AS bf16x4*)(ob + n * kCkvRowBytes + (((4 * cb + q) ^ (n & 7)) << 4) + 8 * g) = h;
       }
     }
+    const size_t out_row0 = row_base(a, it) + it.row0 + wave * 32;  // output row of rr = 0
 #pragma unroll 4
     for (int rr = 0; rr < 32; ++rr) {
-      const RowInfo rj = row_info(a, it, wave * 32 + rr);
       const u32x4 v = *(const LDS_AS u32x4*)(ob + rr * kCkvRowBytes + ((lane ^ (rr & 7)) << 4));
-      if (rj.ok) {
+      if (wave * 32 + rr < it.nrows) {
         __bf16* dst = (it.slot < 0)
-                          ? (__bf16*)a.out + rj.qrow * kDimCkv
+                          ? (__bf16*)a.out + (out_row0 + rr) * kDimCkv
                           : a.part_o + ((size_t)it.slot * a.rows_per_block + wave * 32 + rr) * kDimCkv;
         *(u32x4*)(dst + 8 * lane) = v;
       }
