@@ -875,9 +875,12 @@ __device__ void wide_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* sm
     wide_body<kPC>(a, qf, st, smem + (s & 1) * kStageBytes, smem + ((s + 1) & 1) * kStageBytes,
                    s + 1 < nstage, page_base, it.tok0 + (s + 1 < nstage ? s + 1 : 0) * kStageTokens, it.tok1,
                    it.tok0 + s * kStageTokens, bound, kb, pb, vb, wave, lane, pg_next);
-    __syncthreads();  // every wave is done with this stage before it is refilled
+    // no barrier here: the buffer of stage s is refilled during stage s + 1,
+    // after that stage's top barrier, which every wave passes only once done
+    // with stage s
     pg_next = pg_after;
   }
+  __syncthreads();  // every wave is done with the last stage before the epilogue stages rows over it
   wide_epilogue(a, it, st, ri, rib, smem, wave, lane);
 }
 
@@ -1259,8 +1262,9 @@ __device__ void narrow_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* 
       narrow_body<kPC, false>(a, qf, st, smem + (s & 1) * kStageBytes, smem + ((s + 1) & 1) * kStageBytes,
                        s + 1 < nstage, page_base, it.tok0 + (s + 1) * kStageTokens, it.tok1,
                        it.tok0 + s * kStageTokens, bound, kb, pb, vb, wave, lane, nullptr);
-      __syncthreads();
+      // stage s's buffer is refilled during stage s + 1, after its top barrier
     }
+    __syncthreads();  // every wave is done with the last stage before the merge buffer is written
   }
 
   // ---- merge the four waves' partial results through LDS ----
