@@ -429,7 +429,7 @@ struct RecordLoader {
     const int lane = lane_here();
     const int c = 64 * i + lane;
     const int cc = min(c, 16 * kRecChunks - 1);
-    const int tr = (cc * 200) >> 13;  // cc / 41 for cc < 704
+    const int tr = (int)(__umul24((uint32_t)cc, 200u) >> 13);  // cc / 41 for cc < 704 (24-bit multiply: full rate)
     const int k = cc - kRecChunks * tr;
     const int tc = min(wave * 16 + tr, last);
     LDS_AS char* dst = raw + (wave * 16 * kRecChunks + 64 * i) * 16;
@@ -439,7 +439,7 @@ struct RecordLoader {
     const uint32_t lo = (i == kFp8DmaPerWave - 1) ? (on & 0xFFFFu) : on;
     const uint32_t hi = (i == kFp8DmaPerWave - 1) ? 0u : on;
     if (kPageClass == kPageBig) {
-      dma16_x(base, (uint32_t)(tc * kFp8RecordBytes + 16 * k), lds_addr(dst), lo, hi);
+      dma16_x(base, __umul24((uint32_t)tc, (uint32_t)kFp8RecordBytes) + 16u * k, lds_addr(dst), lo, hi);
     } else {
       const int p = __shfl(page, tr);
       const int sh = a.page_shift;
@@ -767,6 +767,18 @@ __device__ __forceinline__ void wide_body(const AttnArgs& a, const bf16x8 (&qf)[
 // WIDE epilogue: lane (n, g) owns row n of the wave's 32 rows, the partner
 // lane (n, 1-g) holds the other dims.  bf16 rows (final or partial) are
 // staged in LDS and stored whole; fp32 rows are stored in place.
+// O^T tile cb, rows 8q + 4g .. +3 (q = 0..3) hold these output dims: 32 cb + 8q + 4g
+// in the bf16 tile; in the fp8 tile a tile's upper 16 rows are the dims
+// 64 above its lower 16 (the two 16-lane halves of a V^T read then sit on
+// disjoint LDS banks), so cb covers dims D + [0, 16) and D + [64, 80) with
+// D = 128 (cb / 4) + 16 (cb % 4).
+template <bool kPairedDims>
+__device__ __forceinline__ int wide_dim(int cb, int q, int g) {
+  if (!kPairedDims) return 32 * cb + 8 * q + 4 * g;
+  return 128 * (cb >> 2) + 16 * (cb & 3) + (q < 2 ? 8 * q : 64 + 8 * (q - 2)) + 4 * g;
+}
+
+template <bool kPairedDims = false>
 __device__ __forceinline__ void wide_epilogue(const AttnArgs& a, const WorkItem& it, WideState& st, const RowInfo& ri,
                                               int rib, LDS_AS char* smem, int wave, int lane) {
   const int g = lane >> 5;
@@ -786,7 +798,8 @@ __device__ __forceinline__ void wide_epilogue(const AttnArgs& a, const WorkItem&
         bf16x4 h;
 #pragma unroll
         for (int e = 0; e < 4; ++e) h[e] = (__bf16)(st.o[cb][4 * q + e] * inv);
-        *(LDS_AS bf16x4*)(ob + n * kCkvRowBytes + (((4 * cb + q) ^ (n & 7)) << 4) + 8 * g) = h;
+        const int chunk = wide_dim<kPairedDims>(cb, q, 0) >> 3;  // 16-byte chunk of the row
+        *(LDS_AS bf16x4*)(ob + n * kCkvRowBytes + ((chunk ^ (n & 7)) << 4) + 8 * g) = h;
       }
     }
     const size_t out_row0 = row_base(a, it) + it.row0 + wave * 32;  // output row of rr = 0
@@ -810,7 +823,7 @@ __device__ __forceinline__ void wide_epilogue(const AttnArgs& a, const WorkItem&
       for (int q = 0; q < 4; ++q) {
         const f32x4 v = {st.o[cb][4 * q] * inv, st.o[cb][4 * q + 1] * inv, st.o[cb][4 * q + 2] * inv,
                          st.o[cb][4 * q + 3] * inv};
-        store4(a, it, ri, rib, 32 * cb + 8 * q + 4 * g, v);
+        store4(a, it, ri, rib, wide_dim<kPairedDims>(cb, q, g), v);
       }
     }
   }
@@ -944,10 +957,11 @@ __device__ void wide8_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* s
   int vaddr;
   {
     // tr_b8: in each 16-lane group, lane pair j supplies key 8(j/4) + 4h + j%4
-    // of the 16-key step (h = lane / 32), dims 16((lane/16)%2) + 8(lane%2) ..
+    // of the 16-key step (h = lane / 32), dims 64((lane/16)%2) + 8(lane%2) ..
+    // of the tile's paired dims (see wide_dim)
     const int p = lane & 15, j = p >> 1;
     const int vkey = 8 * (j >> 2) + 4 * g + (j & 3);
-    vaddr = vkey * kFp8RecordBytes + 16 * ((lane >> 4) & 1) + 8 * (p & 1);  // + (tb + 16kk)*656 + 32cb
+    vaddr = vkey * kFp8RecordBytes + 64 * ((lane >> 4) & 1) + 8 * (p & 1);  // + (tb + 16kk)*656 + D(cb)
   }
   LDS_AS float* tab = (LDS_AS float*)(smem + kW8TabOff) + wave * 4 * kStageTokens;
 
@@ -972,6 +986,13 @@ __device__ void wide8_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* s
     __syncthreads();  // stage s visible; every wave is done with stage s-1 (its buffer is refilled below)
     const int buf = s % kW8Bufs;
     const LDS_AS char* __restrict__ raw = smem + buf * kFp8RawBytes;
+    // this lane's K codes and V^T rows: the sums are kept in registers (the
+    // empty asm makes them opaque), so every read below is base + immediate
+    uint32_t kb_u = lds_addr(raw) + kaddr, vb_u = lds_addr(raw) + vaddr, rb_u = lds_addr(raw) + raddr;
+    asm volatile("" : "+v"(kb_u), "+v"(vb_u), "+v"(rb_u));
+    const LDS_AS char* __restrict__ kbase = (const LDS_AS char*)(uintptr_t)kb_u;
+    const LDS_AS char* __restrict__ vbase = (const LDS_AS char*)(uintptr_t)vb_u;
+    const LDS_AS char* __restrict__ rbase = (const LDS_AS char*)(uintptr_t)rb_u;  // rope dims
     const bool more = s + 2 < nstage;
     RecordLoader<kPC> ld;
     ld.begin(a, smem + ((s + 2) % kW8Bufs) * kFp8RawBytes, page_base, it.tok0 + (more ? s + 2 : s) * kStageTokens,
@@ -990,50 +1011,57 @@ __device__ void wide8_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* s
       auto scales = [&](int t, int q) -> f32x4 {
         return *(const LDS_AS f32x4*)(tab + t * kStageTokens + tb + 8 * q + 4 * g);
       };
-      // ---- S^T[32 keys x 32 rows]
-      f32x16 sacc, part;
+      // ---- S^T[32 keys x 32 rows]: the rope chain starts the accumulator,
+      // then each 128-dim tile t runs its own chain into part[t % 2]; its
+      // per-key scaling into sacc is issued two steps into the next tile's
+      // chain, so the VALU work and its wait states overlap MFMAs.
+      f32x16 sacc, part[2];
+#pragma unroll
+      for (int kr2 = 0; kr2 < 4; ++kr2) {
+        const bf16x8 rp = *(const LDS_AS bf16x8*)(rbase + tb * kFp8RecordBytes + 32 * kr2);
+        if (kr2 == 0) {
+          mfma32_first<false>(sacc, rp, qf[32]);
+        } else {
+          mfma32_acc<false>(sacc, rp, qf[32 + kr2]);
+        }
+      }
       constexpr int KD = 3;  // 16-code reads in flight
       u32x4 kr[KD];
-      auto kread = [&](int m) -> u32x4 { return *(const LDS_AS u32x4*)(raw + kaddr + tb * kFp8RecordBytes + 32 * m); };
+      auto kread = [&](int m) -> u32x4 { return *(const LDS_AS u32x4*)(kbase + tb * kFp8RecordBytes + 32 * m); };
 #pragma unroll
       for (int i = 0; i < KD; ++i) kr[i] = kread(i);
-      f32x4 tsc[4];  // this tile's scales of the lane's keys, read as the tile starts
+      f32x4 tsc[4];  // the scales of the lane's keys in the tile being folded in
+      auto fold = [&](int t) {  // sacc += part[t % 2] * (tile t's key scales)
+        mfma32_drain(part[t & 1], sacc);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sacc[4 * q + r] += part[t & 1][4 * q + r] * tsc[q][r];
+      };
 #pragma unroll
       for (int m = 0; m < 16; ++m) {
         pin_loads();
-        if ((m & 3) == 0) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) tsc[q] = scales(m >> 2, q);
-        }
         if ((m & 1) == 0 && sub * 8 + (m >> 1) < RecordLoader<kPC>::kSlices) ld.issue(a, sub * 8 + (m >> 1), wave);
         const u32x4 c = kr[m % KD];
         if (m + KD < 16) kr[m % KD] = kread(m + KD);
         const bf16x8 a0 = codes8(c[0], c[1]), a1 = codes8(c[2], c[3]);
+        f32x16& pa = part[(m >> 2) & 1];
         if ((m & 3) == 0) {
-          mfma32_first(part, a0, qf[2 * m]);
+          mfma32_first(pa, a0, qf[2 * m]);
         } else {
-          mfma32_acc(part, a0, qf[2 * m]);
+          mfma32_acc(pa, a0, qf[2 * m]);
         }
-        mfma32_acc(part, a1, qf[2 * m + 1]);
-        if ((m & 3) == 3) {
-          mfma32_drain(part);
+        mfma32_acc(pa, a1, qf[2 * m + 1]);
+        if ((m & 3) == 0 && m > 0) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const float t = part[4 * q + r] * tsc[q][r];
-              sacc[4 * q + r] = (m == 3) ? t : sacc[4 * q + r] + t;
-            }
-          }
+          for (int q = 0; q < 4; ++q) tsc[q] = scales((m >> 2) - 1, q);
         }
+        if ((m & 3) == 1 && m > 1) fold((m >> 2) - 1);
       }
       pin_loads();
 #pragma unroll
-      for (int kr2 = 0; kr2 < 4; ++kr2) {
-        const bf16x8 rp = *(const LDS_AS bf16x8*)(raw + raddr + tb * kFp8RecordBytes + 32 * kr2);
-        mfma32_acc(sacc, rp, qf[32 + kr2]);
-      }
-      mfma32_drain(sacc);
+      for (int q = 0; q < 4; ++q) tsc[q] = scales(3, q);
+      fold(3);
       // ---- online softmax (base 2); lane holds keys 8(r/4) + 4g + r%4 of the sub-tile
       float sv[16];
       float mx = kNegInf;
@@ -1068,7 +1096,7 @@ __device__ void wide8_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* s
       typedef int i32x2 __attribute__((ext_vector_type(2)));
       auto vread = [&](int j) -> u32x2 {  // j = 2*cb + kk
         const int cb = j >> 1, kk = j & 1;
-        const LDS_AS char* src = raw + vaddr + (tb + 16 * kk) * kFp8RecordBytes + 32 * cb;
+        const LDS_AS char* src = vbase + (tb + 16 * kk) * kFp8RecordBytes + 128 * (cb >> 2) + 16 * (cb & 3);
         return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS i32x2*)src));
       };
       u32x2 vr[VD];
@@ -1100,7 +1128,7 @@ __device__ void wide8_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* s
     }
   }
   __syncthreads();  // every wave is done with the stage buffers before the epilogue stages rows there
-  wide_epilogue(a, it, st, ri, rib, smem, wave, lane);
+  wide_epilogue<true>(a, it, st, ri, rib, smem, wave, lane);
 }
 
 // ---------------------------------------------------------------------------
