@@ -127,6 +127,9 @@ CASES = [
     (256, 64, [150, 90], 3, 2, False),
     (16, 64, [10000, 3], 2, 100, False),      # more than 64 splits of one request
     (128, 64, [9000], 1, 80, True),
+    (128, 256, [1000, 300, 2], 1, 3, False),  # pages spanning several stages
+    (16, 1024, [2500, 7], 2, 2, False),
+    (128, 512, [1500, 64], 0, 0, True),
 ]
 
 
@@ -149,6 +152,8 @@ FP8_CASES = [
     (16, 64, [1, 37, 64, 200], 2, 0, True),
     (16, 8, [5, 300, 64, 1], 2, 3, False),
     (40, 4, [100, 400, 0, 33], 0, 2, False),
+    (128, 256, [700, 33], 1, 2, False),
+    (16, 512, [1200, 5], 2, 0, False),
 ]
 
 
@@ -171,6 +176,7 @@ PREFILL_CASES = [
     (128, 64, [3, 1, 8, 5], [64, 100, 700, 5], True, 3, 0),
     (128, 16, [2, 4], [300, 17], True, 3, 3),
     (32, 64, [8, 1, 3], [500, 9, 64], True, 3, 2),
+    (128, 256, [4, 2], [800, 300], True, 1, 2),
 ]
 
 
