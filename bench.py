@@ -247,6 +247,8 @@ def main():
     ap.add_argument("--write-counters", metavar="PMC_DIR",
                     help="summarise rocprofv3 FETCH_SIZE/WRITE_SIZE runs under PMC_DIR into profiles/ and exit")
     ap.add_argument("--copy-bytes", type=int, default=1 << 30)
+    ap.add_argument("--layout", choices=("split", "packed"), default="split",
+                    help="bf16 q / cache as separate latent and rope tensors, or one 576-wide row per token")
     ap.add_argument("--command", action="append", default=[], help="command lines recorded with --write-counters")
     args = ap.parse_args()
 
@@ -292,6 +294,13 @@ def main():
     for _ in range(reps - 1):
         pools.append((w.ckv.clone() if w.ckv is not None else None, w.kpe.clone() if w.kpe is not None else None,
                       w.kv_fp8.clone() if w.kv_fp8 is not None else None))
+    packed = args.layout == "packed"
+    if packed:
+        if fmt:
+            raise SystemExit("--layout packed applies to the bf16 cache only")
+        q_cat = torch.cat([w.q_nope, w.q_pe], dim=-1).contiguous()
+        pools = [(torch.cat([c, k], dim=-1).contiguous(), None, None) for c, k, _ in pools]
+        torch.cuda.empty_cache()
     out = torch.empty((w.rows, w.num_heads, 512), dtype=w.out_dtype, device=dev)
     lse = torch.empty((w.rows, w.num_heads), dtype=torch.float32, device=dev)
     ws = plan.workspace(dev)
@@ -304,6 +313,11 @@ def main():
         if fmt:
             mla.mla_decode_fp8(plan, w.q_nope, w.q_pe, kv8, kv_indptr, kv_indices, w.sm_scale, out=out, lse=lse,
                                workspace=ws)
+        elif packed and kind == mla.MLA_KIND_PREFILL:
+            mla.mla_prefill_packed(plan, q_cat, ckv, qo_indptr, kv_indptr, kv_indices, w.sm_scale, out=out, lse=lse,
+                                   workspace=ws)
+        elif packed:
+            mla.mla_decode_packed(plan, q_cat, ckv, kv_indptr, kv_indices, w.sm_scale, out=out, lse=lse, workspace=ws)
         elif kind == mla.MLA_KIND_PREFILL:
             mla.mla_prefill(plan, w.q_nope, w.q_pe, ckv, kpe, qo_indptr, kv_indptr, kv_indices, w.sm_scale,
                             out=out, lse=lse, workspace=ws)
@@ -395,7 +409,8 @@ def main():
         "data": "synthetic (seeded N(0,1) bf16 inputs shaped like the workload)",
         "config": {"workload": w.name, "batch": w.batch, "num_qo_heads": w.num_heads, "head_dim_ckv": 512,
                    "head_dim_kpe": 64, "page_size": w.page_size, "kv_format": w.kv_format,
-                   "kv_len_total": int(w.kv_len.sum()), "rows": w.rows, "parallelism": "single GPU"},
+                   "kv_len_total": int(w.kv_len.sum()), "rows": w.rows, "parallelism": "single GPU",
+                   "layout": args.layout},
         "kv_gb_per_s": round(kv_gbs, 1),
         "pct_of_roofline": round(pct, 2),
         "plan_ms": round(plan_ms, 3),

@@ -191,13 +191,51 @@ mla_status mla_prefill(const mla_plan* plan, const void* q_nope, const void* q_p
 
 /* Decode over the fp8 record cache (MLA_KV_FP8_E4M3_T128 above):
  *   kv_cache [num_pages, page_size, 656] uint8; q_nope / q_pe bf16 as in
- *   mla_decode.  Keys are dequantised in the kernel (code * scale, rounded to
- *   bf16); everything else as for mla_decode.  Plan: fp8 decode plan.     */
+ *   mla_decode.  Keys are dequantised in the kernel ("FP8 KV Cache
+ *   Quantization and Dequantization" of the FlashMLA digest): each code is
+ *   converted exactly, each 128-dim tile's partial dot product is scaled by
+ *   the key's fp32 tile scale, and P is scaled per key before P.V; everything
+ *   else as for mla_decode.  Plan: fp8 decode plan.                       */
 mla_status mla_decode_fp8(const mla_plan* plan, const void* q_nope, const void* q_pe,
                           const void* kv_cache, const int32_t* kv_indptr,
                           const int32_t* kv_indices, float sm_scale, void* out,
                           int32_t out_dtype, float* lse, void* workspace,
                           size_t workspace_bytes, hipStream_t stream);
+
+/* The concatenated layout ("MLA Paged" ckv/kpe as one tensor; FlashMLA's
+ * "flash_mla_with_kvcache" q and k_cache with head_dim 576): one 576-wide
+ * bf16 row per query (token, head) and per cached token, latent dims 0..511
+ * then rope dims 512..575.
+ *   q [rows, H, 576] bf16 (rows = batch for decode, total_q for prefill)
+ *   kv_cache [num_pages, page_size, 576] bf16
+ *   out_scale: factor applied to every output row (the output scaling of
+ *   "batch_mla_decode_with_paged_kv_cache", bmm2_scale); lse is unchanged.
+ * Everything else, errors included (a non-finite out_scale is
+ * MLA_ERR_INVALID_ARGUMENT), as for mla_decode / mla_prefill; the same
+ * bf16 plans serve both layouts, and with out_scale = 1 the results are
+ * bit-identical to the split layout's.                                   */
+mla_status mla_decode_packed(const mla_plan* plan, const void* q, const void* kv_cache,
+                             const int32_t* kv_indptr, const int32_t* kv_indices, float sm_scale,
+                             float out_scale, void* out, int32_t out_dtype, float* lse, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+mla_status mla_prefill_packed(const mla_plan* plan, const void* q, const void* kv_cache,
+                              const int32_t* qo_indptr, const int32_t* kv_indptr, const int32_t* kv_indices,
+                              float sm_scale, float out_scale, void* out, int32_t out_dtype, float* lse,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Dense block tables ("batch_mla_decode_with_paged_kv_cache" block_tables,
+ * FlashMLA block_table) to the page lists of the run calls: enqueues on
+ * `stream` kv_indices[kv_indptr[b] + j] = block_table[b * max_blocks + j]
+ * for j < kv_indptr[b+1] - kv_indptr[b] (the pages the plan's lengths
+ * need; later table entries are padding and are not read).
+ *   block_table [batch, max_blocks] int32 device; kv_indptr [batch+1]
+ *   int32 device, equal to the plan's; kv_indices [kv_indptr[batch]] int32
+ *   device, written.
+ * Errors: MLA_ERR_INVALID_ARGUMENT (null pointer, max_blocks < 0 or smaller
+ * than a request's page count), MLA_ERR_DEVICE (launch failed).  Allocates
+ * nothing; capture-safe.                                                 */
+mla_status mla_block_table_to_indices(const mla_plan* plan, const int32_t* block_table, int32_t max_blocks,
+                                      const int32_t* kv_indptr, int32_t* kv_indices, hipStream_t stream);
 
 /* Diagnostics for timing: the next run call made on this host thread has
  * the attention kernel's own dispatch record `before` when the kernel

@@ -7,7 +7,9 @@ library's HIP kernels.  If the library is missing or cannot be loaded, every
 call raises; there is no fallback.
 
 Names follow the C ABI: :func:`mla_plan_create`, :func:`mla_decode`,
-:func:`mla_prefill`, :func:`mla_decode_fp8`.
+:func:`mla_prefill`, :func:`mla_decode_fp8`, the concatenated-layout
+:func:`mla_decode_packed` / :func:`mla_prefill_packed`, and
+:func:`mla_block_table_to_indices`.
 """
 
 from ._binding import (  # noqa: F401
@@ -15,10 +17,13 @@ from ._binding import (  # noqa: F401
     Plan,
     lib_path,
     load_library,
+    mla_block_table_to_indices,
     mla_decode,
     mla_decode_fp8,
+    mla_decode_packed,
     mla_plan_create,
     mla_prefill,
+    mla_prefill_packed,
     mla_record_attention_events,
     MLA_KIND_DECODE,
     MLA_KIND_PREFILL,

@@ -88,6 +88,12 @@ def load_library():
         L.mla_prefill.restype = i32
         L.mla_decode_fp8.argtypes = [vp, vp, vp, vp, vp, vp, f32, vp, i32, vp, vp, sz, vp]
         L.mla_decode_fp8.restype = i32
+        L.mla_decode_packed.argtypes = [vp, vp, vp, vp, vp, f32, f32, vp, i32, vp, vp, sz, vp]
+        L.mla_decode_packed.restype = i32
+        L.mla_prefill_packed.argtypes = [vp, vp, vp, vp, vp, vp, f32, f32, vp, i32, vp, vp, sz, vp]
+        L.mla_prefill_packed.restype = i32
+        L.mla_block_table_to_indices.argtypes = [vp, vp, i32, vp, vp, vp]
+        L.mla_block_table_to_indices.restype = i32
         L.mla_record_attention_events.argtypes = [vp, vp]
         L.mla_record_attention_events.restype = i32
         L.mla_status_str.argtypes = [i32]
@@ -305,3 +311,72 @@ def mla_decode_fp8(plan: Plan, q_nope, q_pe, kv_cache, kv_indptr, kv_indices, sm
     _check(L.mla_decode_fp8(plan.handle, qn, qp, kv, ip, ix, float(sm_scale), out.data_ptr(), code,
                             lse.data_ptr(), ws.data_ptr(), ws.numel(), stream), "mla_decode_fp8")
     return out, lse
+
+
+def _packed_q(plan: Plan, q, rows: int):
+    return _dev(q, "q", torch.bfloat16, (rows, plan.num_heads, _DIM_CKV + _DIM_KPE))
+
+
+def _packed_outputs(q: torch.Tensor, out, lse, out_dtype):
+    rows, H = q.shape[0], q.shape[1]
+    if out is None:
+        out = torch.empty((rows, H, _DIM_CKV), dtype=out_dtype, device=q.device)
+    return _outputs(out, out, lse, out.dtype)
+
+
+def mla_decode_packed(plan: Plan, q, kv_cache, kv_indptr, kv_indices, sm_scale: float, out_scale: float = 1.0,
+                      out=None, lse=None, out_dtype=torch.bfloat16, workspace=None):
+    """Paged MLA decode over the concatenated layout: q [B, H, 576], kv_cache
+    [num_pages, page_size, 576] (latent dims, then rope dims); out is scaled
+    by out_scale.  Returns (out [B, H, 512], lse [B, H])."""
+    L = load_library()
+    B, P, ps = plan.desc.batch, plan.desc.num_pages, plan.desc.page_size
+    qq = _packed_q(plan, q, B)
+    kv = _dev(kv_cache, "kv_cache", torch.bfloat16, (P, ps, _DIM_CKV + _DIM_KPE))
+    ip, ix = _paging(plan, kv_indptr, kv_indices)
+    out, lse, code = _packed_outputs(q, out, lse, out_dtype)
+    ws = plan.workspace(q.device) if workspace is None else workspace
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(L.mla_decode_packed(plan.handle, qq, kv, ip, ix, float(sm_scale), float(out_scale), out.data_ptr(), code,
+                               lse.data_ptr(), ws.data_ptr(), ws.numel(), stream), "mla_decode_packed")
+    return out, lse
+
+
+def mla_prefill_packed(plan: Plan, q, kv_cache, qo_indptr, kv_indptr, kv_indices, sm_scale: float,
+                       out_scale: float = 1.0, out=None, lse=None, out_dtype=torch.bfloat16, workspace=None):
+    """Paged MLA prefill over packed queries in the concatenated layout:
+    q [total_q, H, 576], kv_cache [num_pages, page_size, 576]."""
+    L = load_library()
+    B, P, ps = plan.desc.batch, plan.desc.num_pages, plan.desc.page_size
+    total_q = int(plan.qo_indptr[-1]) if plan.qo_indptr is not None else 0
+    qq = _packed_q(plan, q, total_q)
+    kv = _dev(kv_cache, "kv_cache", torch.bfloat16, (P, ps, _DIM_CKV + _DIM_KPE))
+    qo = _dev(qo_indptr, "qo_indptr", torch.int32, (B + 1,))
+    ip, ix = _paging(plan, kv_indptr, kv_indices)
+    out, lse, code = _packed_outputs(q, out, lse, out_dtype)
+    ws = plan.workspace(q.device) if workspace is None else workspace
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(L.mla_prefill_packed(plan.handle, qq, kv, qo, ip, ix, float(sm_scale), float(out_scale), out.data_ptr(),
+                                code, lse.data_ptr(), ws.data_ptr(), ws.numel(), stream), "mla_prefill_packed")
+    return out, lse
+
+
+def mla_block_table_to_indices(plan: Plan, block_table, kv_indptr, kv_indices=None):
+    """kv_indices (int32 device) from a dense block table [batch, max_blocks]:
+    the first kv_indptr[b+1] - kv_indptr[b] entries of each row, in order."""
+    L = load_library()
+    B = plan.desc.batch
+    bt = _dev(block_table, "block_table", torch.int32)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError(f"block_table must be [batch={B}, max_blocks]")
+    ip = _dev(kv_indptr, "kv_indptr", torch.int32, (B + 1,))
+    n = int(plan.kv_indptr[-1]) if B > 0 else 0
+    if kv_indices is None:
+        kv_indices = torch.empty((max(n, 1),), dtype=torch.int32, device=block_table.device)
+    ix = _dev(kv_indices, "kv_indices", torch.int32)
+    if kv_indices.numel() < n:
+        raise ValueError("kv_indices is shorter than kv_indptr[-1]")
+    stream = torch.cuda.current_stream(block_table.device).cuda_stream
+    _check(L.mla_block_table_to_indices(plan.handle, bt, int(block_table.shape[1]), ip, ix, stream),
+           "mla_block_table_to_indices")
+    return kv_indices

@@ -34,6 +34,7 @@ struct mla_plan {
   int32_t group_size = 1;      // quad mode: sibling workgroups per work list
   int32_t xcd_map = 0;         // quad mode: siblings share blockIdx.x mod 8
   int32_t num_slots = 0;       // partial-result slots
+  std::vector<int32_t> kv_indptr;  // [batch + 1] host copy of the page offsets the plan was made for
   std::vector<int32_t> wg_ptr;  // [num_wgs + 1] item range of each workgroup
   std::vector<WorkItem> items;
   std::vector<SplitGroup> groups;
@@ -271,6 +272,8 @@ mla_status mla_plan_create(mla_plan** out, const mla_plan_desc* d, const int32_t
   mla_plan* p = new (std::nothrow) mla_plan();
   if (!p) return MLA_ERR_INVALID_ARGUMENT;
   p->d = *d;
+  p->kv_indptr.assign(kv_indptr_host ? kv_indptr_host : nullptr, kv_indptr_host ? kv_indptr_host + d->batch + 1 : nullptr);
+  if (p->kv_indptr.empty()) p->kv_indptr.assign(1, 0);
   mla_status st = build_schedule(p, kv_len, q_len, num_cus);
   if (st != MLA_OK) {
     delete p;
@@ -318,15 +321,24 @@ namespace {
 thread_local hipEvent_t t_ev_before = nullptr;
 thread_local hipEvent_t t_ev_after = nullptr;
 
+// Row strides of the two bf16 layouts: split ckv / kpe tensors and q_nope /
+// q_pe, or one concatenated 576-wide row per token (latent then rope).
+struct Layout {
+  int32_t ckv_stride, kpe_stride, q_stride, qpe_stride;
+};
+constexpr Layout kSplit{mla::kDimCkv * 2, mla::kDimKpe * 2, mla::kDimCkv, mla::kDimKpe};
+constexpr Layout kPacked{(mla::kDimCkv + mla::kDimKpe) * 2, (mla::kDimCkv + mla::kDimKpe) * 2,
+                         mla::kDimCkv + mla::kDimKpe, mla::kDimCkv + mla::kDimKpe};
+
 mla_status run(const mla_plan* p, int32_t want_kind, int32_t want_format, const void* q_nope,
                const void* q_pe, const void* ckv, const void* kpe, const void* kv_fp8,
                const int32_t* qo_indptr, const int32_t* kv_indptr, const int32_t* kv_indices,
                float sm_scale, void* out, int32_t out_dtype, float* lse, void* ws, size_t ws_bytes,
-               hipStream_t stream) {
+               hipStream_t stream, const Layout& lay = kSplit, float out_scale = 1.f) {
   if (!p) return MLA_ERR_INVALID_ARGUMENT;
   if (p->d.kind != want_kind || p->d.kv_format != want_format) return MLA_ERR_PLAN_MISMATCH;
   if (out_dtype != MLA_DTYPE_BF16 && out_dtype != MLA_DTYPE_FP32) return MLA_ERR_INVALID_ARGUMENT;
-  if (!std::isfinite(sm_scale)) return MLA_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(sm_scale) || !std::isfinite(out_scale)) return MLA_ERR_INVALID_ARGUMENT;
   if (p->items.empty()) return MLA_OK;  // nothing to compute (batch 0 or no rows)
   if (!q_nope || !q_pe || !kv_indptr || !kv_indices || !out || !lse) return MLA_ERR_INVALID_ARGUMENT;
   if (want_format == MLA_KV_BF16 && (!ckv || !kpe)) return MLA_ERR_INVALID_ARGUMENT;
@@ -363,6 +375,11 @@ mla_status run(const mla_plan* p, int32_t want_kind, int32_t want_format, const 
   a.xcd_map = p->xcd_map;
   a.num_items = (int32_t)p->items.size();
   a.num_groups = (int32_t)p->groups.size();
+  a.ckv_stride = lay.ckv_stride;
+  a.kpe_stride = lay.kpe_stride;
+  a.q_stride = lay.q_stride;
+  a.qpe_stride = lay.qpe_stride;
+  a.out_scale = out_scale;
   hipEvent_t ev0 = t_ev_before, ev1 = t_ev_after;
   t_ev_before = t_ev_after = nullptr;
   hipError_t e = mla::launch_attention(a, p->tile_mode, want_format == MLA_KV_FP8_E4M3_T128, stream, ev0, ev1);
@@ -407,6 +424,39 @@ mla_status mla_decode_fp8(const mla_plan* p, const void* q_nope, const void* q_p
                           hipStream_t stream) {
   return run(p, MLA_KIND_DECODE, MLA_KV_FP8_E4M3_T128, q_nope, q_pe, nullptr, nullptr, kv, nullptr,
              kv_indptr, kv_indices, sm_scale, out, out_dtype, lse, ws, ws_bytes, stream);
+}
+
+mla_status mla_decode_packed(const mla_plan* p, const void* q, const void* kv_cache, const int32_t* kv_indptr,
+                             const int32_t* kv_indices, float sm_scale, float out_scale, void* out,
+                             int32_t out_dtype, float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const char* qb = (const char*)q;
+  const char* kb = (const char*)kv_cache;
+  return run(p, MLA_KIND_DECODE, MLA_KV_BF16, q, q ? qb + mla::kDimCkv * 2 : nullptr, kv_cache,
+             kv_cache ? kb + mla::kDimCkv * 2 : nullptr, nullptr, nullptr, kv_indptr, kv_indices, sm_scale, out,
+             out_dtype, lse, ws, ws_bytes, stream, kPacked, out_scale);
+}
+
+mla_status mla_prefill_packed(const mla_plan* p, const void* q, const void* kv_cache, const int32_t* qo_indptr,
+                              const int32_t* kv_indptr, const int32_t* kv_indices, float sm_scale, float out_scale,
+                              void* out, int32_t out_dtype, float* lse, void* ws, size_t ws_bytes,
+                              hipStream_t stream) {
+  const char* qb = (const char*)q;
+  const char* kb = (const char*)kv_cache;
+  return run(p, MLA_KIND_PREFILL, MLA_KV_BF16, q, q ? qb + mla::kDimCkv * 2 : nullptr, kv_cache,
+             kv_cache ? kb + mla::kDimCkv * 2 : nullptr, nullptr, qo_indptr, kv_indptr, kv_indices, sm_scale, out,
+             out_dtype, lse, ws, ws_bytes, stream, kPacked, out_scale);
+}
+
+mla_status mla_block_table_to_indices(const mla_plan* p, const int32_t* block_table, int32_t max_blocks,
+                                      const int32_t* kv_indptr, int32_t* kv_indices, hipStream_t stream) {
+  if (!p || max_blocks < 0) return MLA_ERR_INVALID_ARGUMENT;
+  if (p->d.batch == 0) return MLA_OK;
+  for (int32_t b = 0; b < p->d.batch; ++b)
+    if (p->kv_indptr[b + 1] - p->kv_indptr[b] > max_blocks) return MLA_ERR_INVALID_ARGUMENT;
+  if (!block_table || !kv_indptr || (!kv_indices && p->kv_indptr[p->d.batch] > 0)) return MLA_ERR_INVALID_ARGUMENT;
+  if (mla::launch_block_table(block_table, p->d.batch, max_blocks, kv_indptr, kv_indices, stream) != hipSuccess)
+    return MLA_ERR_DEVICE;
+  return MLA_OK;
 }
 
 }  // extern "C"

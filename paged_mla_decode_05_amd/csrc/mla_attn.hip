@@ -298,15 +298,15 @@ struct StageLoader {
     if (kPageClass == kPageBig) {
       const int page = page_hint >= 0 ? page_hint : ld_const(a.kv_indices, page_base + (tok0 >> sh));
       const size_t row0 = ((size_t)page << sh) + (tok0 & mask);
-      ckv_row[0] = ckv + row0 * kCkvRowBytes;
-      kpe_base[0] = kpe + row0 * kKpeRowBytes;
+      ckv_row[0] = ckv + row0 * a.ckv_stride;
+      kpe_base[0] = kpe + row0 * a.kpe_stride;
       return;
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int T = tok0 + min(wave * 16 + i, last);
       const int page = ld_const(a.kv_indices, page_base + (T >> sh));
-      ckv_row[i] = ckv + (((size_t)page << sh) + (T & mask)) * kCkvRowBytes;
+      ckv_row[i] = ckv + (((size_t)page << sh) + (T & mask)) * a.ckv_stride;
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -315,7 +315,7 @@ struct StageLoader {
         // the 8 keys of this slice share one page (clamped keys included)
         const int T0 = tok0 + min(grp * 8, last);
         const int page = ld_const(a.kv_indices, page_base + (T0 >> sh));
-        kpe_base[i] = kpe + (((size_t)page << sh) + (T0 & mask)) * kKpeRowBytes;
+        kpe_base[i] = kpe + (((size_t)page << sh) + (T0 & mask)) * a.kpe_stride;
         kpe_t0[i] = T0 - tok0;
       } else {
         // one scalar page lookup per key, then each lane keeps its key's page
@@ -338,7 +338,7 @@ struct StageLoader {
       const int t = wave * 16 + i;
       const uint32_t swz_off = (uint32_t)((lane ^ ckv_swz(t)) << 4);
       if (kPageClass == kPageBig) {
-        dma16_on(ckv_row[0], (uint32_t)(min(t, last) * kCkvRowBytes) + swz_off, lds_addr(st + t * kCkvRowBytes), on);
+        dma16_on(ckv_row[0], (uint32_t)(min(t, last) * a.ckv_stride) + swz_off, lds_addr(st + t * kCkvRowBytes), on);
       } else {
         dma16_on(ckv_row[i], swz_off, lds_addr(st + t * kCkvRowBytes), on);
       }
@@ -351,13 +351,14 @@ struct StageLoader {
     const int c = (lane & 7) ^ kpe_swz(t);
     LDS_AS char* dst = st + kStageCkvBytes + grp * 1024;
     if (kPageClass == kPageBig) {
-      dma16_on(kpe_base[0], (uint32_t)(tc * kKpeRowBytes + (c << 4)), lds_addr(dst), on);
+      dma16_on(kpe_base[0], __umul24((uint32_t)tc, (uint32_t)a.kpe_stride) + (uint32_t)(c << 4), lds_addr(dst), on);
     } else if (kPageClass == kPageMid) {
-      dma16_on(kpe_base[k], (uint32_t)((tc - kpe_t0[k]) * kKpeRowBytes + (c << 4)), lds_addr(dst), on);
+      dma16_on(kpe_base[k], __umul24((uint32_t)(tc - kpe_t0[k]), (uint32_t)a.kpe_stride) + (uint32_t)(c << 4),
+               lds_addr(dst), on);
     } else {
       const int sh = a.page_shift;
       const int T = s_tok0 + tc;
-      const char* src = (const char*)a.kpe + (((size_t)kpe_page[k] << sh) + (T & ((1 << sh) - 1))) * kKpeRowBytes +
+      const char* src = (const char*)a.kpe + (((size_t)kpe_page[k] << sh) + (T & ((1 << sh) - 1))) * a.kpe_stride +
                         (c << 4);
       dma16_v_on(src, lds_addr(dst), on);
     }
@@ -785,7 +786,7 @@ __device__ __forceinline__ void wide_epilogue(const AttnArgs& a, const WorkItem&
   const int n = lane & 31;
   const float l_tot = sum_xor32(st.l_run);
   const bool empty = !(l_tot > 0.f);
-  const float inv = empty ? 0.f : 1.f / l_tot;
+  const float inv = empty ? 0.f : (it.slot < 0 ? a.out_scale : 1.f) / l_tot;  // final rows carry the output scale
   if (ri.ok && g == 0) store_lse(a, it, ri, rib, empty ? kNegInf : (st.m_run + __log2f(l_tot)) * kLn2);
   if (a.out_bf16 || it.slot >= 0) {
     // bf16 rows: stage the wave's 32 rows in LDS (free after the loop; 16-byte
@@ -841,8 +842,8 @@ __device__ void wide_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* sm
   bf16x8 qf[36];
   {
     const bf16x8 z = {};
-    const __bf16* qn = (const __bf16*)a.q_nope + ri.qrow * kDimCkv + 8 * g;
-    const __bf16* qp = (const __bf16*)a.q_pe + ri.qrow * kDimKpe + 8 * g;
+    const __bf16* qn = (const __bf16*)a.q_nope + ri.qrow * a.q_stride + 8 * g;
+    const __bf16* qp = (const __bf16*)a.q_pe + ri.qrow * a.qpe_stride + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < 32; ++ks) qf[ks] = ri.ok ? *(const bf16x8*)(qn + 16 * ks) : z;
 #pragma unroll
@@ -942,8 +943,8 @@ __device__ void wide8_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* s
   bf16x8 qf[36];
   {
     const bf16x8 z = {};
-    const __bf16* qn = (const __bf16*)a.q_nope + ri.qrow * kDimCkv + 16 * g;
-    const __bf16* qp = (const __bf16*)a.q_pe + ri.qrow * kDimKpe + 8 * g;
+    const __bf16* qn = (const __bf16*)a.q_nope + ri.qrow * a.q_stride + 16 * g;
+    const __bf16* qp = (const __bf16*)a.q_pe + ri.qrow * a.qpe_stride + 8 * g;
 #pragma unroll
     for (int m = 0; m < 16; ++m)
 #pragma unroll
@@ -1232,8 +1233,8 @@ __device__ void narrow_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* 
   bf16x8 qf[18];
   {
     const bf16x8 z = {};
-    const __bf16* qn = (const __bf16*)a.q_nope + ri.qrow * kDimCkv + 8 * g4;
-    const __bf16* qp = (const __bf16*)a.q_pe + ri.qrow * kDimKpe + 8 * g4;
+    const __bf16* qn = (const __bf16*)a.q_nope + ri.qrow * a.q_stride + 8 * g4;
+    const __bf16* qp = (const __bf16*)a.q_pe + ri.qrow * a.qpe_stride + 8 * g4;
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks) qf[ks] = ri.ok ? *(const bf16x8*)(qn + 32 * ks) : z;
 #pragma unroll
@@ -1319,7 +1320,7 @@ __device__ void narrow_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* 
     if (w == wave) my_f = f;
   }
   const bool empty = !(l_all > 0.f);
-  const float sc = empty ? 0.f : my_f / l_all;
+  const float sc = empty ? 0.f : (it.slot < 0 ? a.out_scale : 1.f) * my_f / l_all;
 #pragma unroll
   for (int cb = 0; cb < 32; ++cb) {
     const int dim = 16 * cb + 4 * g4;
@@ -1529,8 +1530,8 @@ __device__ void quad_item(const AttnArgs& a, const WorkItem& it, int role, LDS_A
     const bf16x8 z = {};
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const __bf16* qn = (const __bf16*)a.q_nope + ri[t].qrow * kDimCkv + 8 * g4;
-      const __bf16* qp = (const __bf16*)a.q_pe + ri[t].qrow * kDimKpe + 8 * g4;
+      const __bf16* qn = (const __bf16*)a.q_nope + ri[t].qrow * a.q_stride + 8 * g4;
+      const __bf16* qp = (const __bf16*)a.q_pe + ri[t].qrow * a.qpe_stride + 8 * g4;
 #pragma unroll
       for (int ks = 0; ks < 16; ++ks) qf[t][ks] = ri[t].ok ? *(const bf16x8*)(qn + 32 * ks) : z;
 #pragma unroll
@@ -1605,7 +1606,7 @@ __device__ void quad_item(const AttnArgs& a, const WorkItem& it, int role, LDS_A
     const int r = 16 * t + n;
     const float L = (lsum[r] + lsum[kQuadRows + r]) + (lsum[2 * kQuadRows + r] + lsum[3 * kQuadRows + r]);
     const bool empty = !(L > 0.f);
-    const float inv = empty ? 0.f : 1.f / L;
+    const float inv = empty ? 0.f : (it.slot < 0 ? a.out_scale : 1.f) / L;
     if (ri[t].ok) {
 #pragma unroll
       for (int c = 0; c < 8; ++c) store4(a, it, ri[t], rbase + r, 128 * wave + 16 * c + 4 * g4, st.o[c][t] * inv);
@@ -1760,7 +1761,7 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(AttnArgs a) {
       }
     }
   }
-  const float inv = (W > 0.f) ? 1.f / W : 0.f;
+  const float inv = (W > 0.f) ? a.out_scale / W : 0.f;
   const int H = a.num_heads;
   const int q_start = a.qo_indptr ? ld_const(a.qo_indptr, g_b) : g_b;
   const int rr = g_row0 + r;
@@ -1818,6 +1819,26 @@ hipError_t launch_attention(const AttnArgs& a, int tile_mode, int kv_fp8, hipStr
   if (pc == kPageBig) return launch_mode<2, kPageBig>(a, kv_fp8, stream, t0, t1);
   if (pc == kPageMid) return launch_mode<2, kPageMid>(a, kv_fp8, stream, t0, t1);
   return launch_mode<2, kPageSmall>(a, kv_fp8, stream, t0, t1);
+}
+
+// Page list of the dense block-table interface: one workgroup per request
+// copies the request's first kv_indptr[b+1] - kv_indptr[b] table entries.
+__global__ __launch_bounds__(256) void mla_block_table_kernel(const int32_t* __restrict__ block_table,
+                                                              int32_t max_blocks, const int32_t* __restrict__ kv_indptr,
+                                                              int32_t* __restrict__ kv_indices) {
+  const int b = blockIdx.x;
+  const int p0 = kv_indptr[b];
+  const int n = min(kv_indptr[b + 1] - p0, max_blocks);
+  const int32_t* row = block_table + (size_t)b * max_blocks;
+  for (int j = threadIdx.x; j < n; j += 256) kv_indices[p0 + j] = row[j];
+}
+
+hipError_t launch_block_table(const int32_t* block_table, int32_t batch, int32_t max_blocks,
+                              const int32_t* kv_indptr, int32_t* kv_indices, hipStream_t stream) {
+  if (batch <= 0) return hipSuccess;
+  hipLaunchKernelGGL(mla_block_table_kernel, dim3(batch), dim3(256), 0, stream, block_table, max_blocks, kv_indptr,
+                     kv_indices);
+  return hipGetLastError();
 }
 
 hipError_t launch_combine(const AttnArgs& a, hipStream_t stream) {

@@ -69,6 +69,11 @@ struct AttnArgs {
   int32_t xcd_map;         // quad mode: siblings share blockIdx.x mod 8
   int32_t num_items;
   int32_t num_groups;
+  int32_t ckv_stride;      // bytes between consecutive token rows of ckv (1024 split, 1152 concatenated)
+  int32_t kpe_stride;      // bytes between consecutive token rows of kpe (128 split, 1152 concatenated)
+  int32_t q_stride;        // elements between consecutive (token, head) rows of q_nope (512 or 576)
+  int32_t qpe_stride;      // elements between consecutive rows of q_pe (64 or 576)
+  float out_scale;         // factor applied to the final output rows (1: none)
 };
 
 // Launchers (mla_attn.hip).  They only enqueue on `stream`; return hipError_t.
@@ -77,5 +82,8 @@ struct AttnArgs {
 hipError_t launch_attention(const AttnArgs& a, int tile_mode, int kv_fp8, hipStream_t stream, hipEvent_t t0,
                             hipEvent_t t1);
 hipError_t launch_combine(const AttnArgs& a, hipStream_t stream);
+// kv_indices[kv_indptr[b] + j] = block_table[b * max_blocks + j] for j < kv_indptr[b+1] - kv_indptr[b].
+hipError_t launch_block_table(const int32_t* block_table, int32_t batch, int32_t max_blocks,
+                              const int32_t* kv_indptr, int32_t* kv_indices, hipStream_t stream);
 
 }  // namespace mla

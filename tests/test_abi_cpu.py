@@ -28,7 +28,8 @@ def mla():
 def test_library_exports_every_declared_function(mla):
     header = open(os.path.join(ROOT, "include", "mla.h")).read()
     names = set(re.findall(r"^\s*(?:mla_status|void|size_t|int32_t|const char\*)\s+(mla_\w+)\s*\(", header, re.M))
-    assert {"mla_plan_create", "mla_decode", "mla_prefill", "mla_decode_fp8"} <= names
+    assert {"mla_plan_create", "mla_decode", "mla_prefill", "mla_decode_fp8", "mla_decode_packed",
+            "mla_prefill_packed", "mla_block_table_to_indices"} <= names
     lib = mla.load_library()
     for n in sorted(names):
         assert hasattr(lib, n), n
@@ -208,6 +209,28 @@ def test_run_call_errors_before_any_launch(mla):
     assert lib.mla_decode(dec.handle, *args, 0.1, fake, 0, fake, fake, 16, None) == -3
     assert lib.mla_decode(None, *args, 0.1, fake, 0, fake, fake, 1 << 20, None) == -1
     assert lib.mla_status_str(-4).decode().startswith("plan")
+
+
+def test_packed_layout_and_block_table_errors(mla):
+    lib = mla.load_library()
+    dec = mla.mla_plan_create(0, 2, 16, 64, 4, [10, 70], [0, 1, 3], num_cus=4)
+    pre = mla.mla_plan_create(1, 2, 16, 64, 4, [10, 70], [0, 1, 3], qo_indptr=[0, 1, 2], num_cus=4)
+    fake = ctypes.c_void_p(0x1000)
+    tail = (fake, 0, fake, fake, 1 << 20, None)
+    # wrong plan kind, non-finite output scale, missing q or cache
+    assert lib.mla_decode_packed(pre.handle, fake, fake, fake, fake, 0.1, 1.0, *tail) == -4
+    assert lib.mla_prefill_packed(dec.handle, fake, fake, fake, fake, fake, 0.1, 1.0, *tail) == -4
+    assert lib.mla_decode_packed(dec.handle, fake, fake, fake, fake, 0.1, float("inf"), *tail) == -1
+    assert lib.mla_decode_packed(dec.handle, None, fake, fake, fake, 0.1, 1.0, *tail) == -1
+    assert lib.mla_decode_packed(dec.handle, fake, None, fake, fake, 0.1, 1.0, *tail) == -1
+    assert lib.mla_prefill_packed(pre.handle, fake, fake, None, fake, fake, 0.1, 1.0, *tail) == -1
+    # block table: a request with more pages than the table has columns, null table, null plan
+    assert lib.mla_block_table_to_indices(dec.handle, fake, 1, fake, fake, None) == -1
+    assert lib.mla_block_table_to_indices(dec.handle, None, 2, fake, fake, None) == -1
+    assert lib.mla_block_table_to_indices(dec.handle, fake, -1, fake, fake, None) == -1
+    assert lib.mla_block_table_to_indices(None, fake, 2, fake, fake, None) == -1
+    empty = mla.mla_plan_create(0, 0, 16, 64, 1, [], [0], num_cus=4)
+    assert lib.mla_block_table_to_indices(empty.handle, None, 0, None, None, None) == 0
 
 
 def test_workspace_grows_with_splits(mla):
