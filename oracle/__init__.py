@@ -16,7 +16,9 @@ Every function states the passage of the source pages it follows.  Pages:
 * FlashMLA digest (context7 llms.txt): "Sparse MLA Prefill Kernel"
   (the written softmax-attention formula with lse), "FP8 KV Cache
   Quantization and Dequantization" / "... Utilities" (656-byte token record,
-  block/offset slot mapping).
+  block/offset slot mapping), "flash_mla_with_kvcache (Sparse Attention
+  with FP8 KV Cache)" and "Sparse Attention Decoding with KV Cache" (token
+  lists per query, the attention sink).
 
 Pinning: every function here is checked by ``tests/test_oracle_*.py`` against
 brute force, ``torch`` library routines in float64, closed forms and
@@ -42,4 +44,8 @@ from .mla_oracle import (  # noqa: F401
     mla_decode_ref,
     mla_prefill_ref,
     mla_decode_fp8_ref,
+    sparse_valid_indices,
+    sparse_attend,
+    mla_sparse_decode_fp8_ref,
+    mla_sparse_prefill_ref,
 )

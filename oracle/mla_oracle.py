@@ -39,6 +39,17 @@ Per-request key counts ``kv_len`` are explicit inputs (the pages give
 lives in page ``kv_indices[kv_indptr[b] + j // page_size]`` at slot
 ``j % page_size`` (the block/offset mapping of FlashMLA's
 ``abs_indices2indices_in_kvcache``).
+
+Token-sparse attention (:func:`mla_sparse_decode_fp8_ref`,
+:func:`mla_sparse_prefill_ref`): the same formula over a per-query-token
+list of key slots instead of a request's keys, as in FlashMLA "Sparse MLA
+Prefill Kernel" (``focused_kv = kv[indices]``; -1 or an index past the end
+is invalid) and "flash_mla_with_kvcache (Sparse Attention with FP8 KV
+Cache)" (flat slots ``block * block_size + offset`` into the 656-byte
+record cache).  It also returns ``max_logits`` (the largest logit, natural
+units) and takes the optional ``topk_length`` and ``attn_sink`` of those
+passages; the readings are stated on :func:`sparse_valid_indices` and
+:func:`sparse_attend`.
 """
 
 from __future__ import annotations
@@ -443,3 +454,127 @@ def mla_decode_fp8_ref(q_nope, q_pe, kv_cache_fp8, kv_indptr, kv_indices, kv_len
         Kn, Kp = gather_request_fp8(kv_cache_fp8, kv_indptr, kv_indices, b, L)
         out[b], lse[b] = attend(qn[b], qp[b], Kn, Kp, sm_scale, L)
     return out, lse
+
+
+# ---------------------------------------------------------------------------
+# Token-sparse attention (DSA): each query token attends to its own key list
+# ---------------------------------------------------------------------------
+
+def sparse_valid_indices(index_row, num_slots: int, topk_length=None) -> np.ndarray:
+    """The key slots one query token attends to, in list order.
+
+    FlashMLA "Sparse MLA Prefill Kernel": query i attends to the KV rows
+    named by indices[i, :]; an entry of -1, or one at or past the number of
+    KV rows, is invalid and ignored.  The optional ``topk_length`` of
+    flash_mla_sparse_fwd bounds the entries used; reading: the first
+    topk_length[i] entries of row i.  A slot listed twice counts twice (the
+    selection is a gather, kv[indices]).
+    """
+    idx = np.asarray(index_row, dtype=np.int64).reshape(-1)
+    if topk_length is not None:
+        idx = idx[:max(0, int(topk_length))]
+    return idx[(idx >= 0) & (idx < num_slots)]
+
+
+def sparse_attend(qn, qp, kn, kp, sm_scale: float, attn_sink=None):
+    """out [H, 512], lse [H], max_logits [H] of one query token's H heads
+    against its gathered keys kn [n, 512], kp [n, 64] (float64).
+
+    The "Sparse MLA Prefill Kernel" formula in natural-log units: logits
+    s_j = sm_scale * (q_nope . kn_j + q_pe . kp_j), max_logits = max_j s_j,
+    lse = ln sum_j exp(s_j), out = sum_j exp(s_j - lse) kn_j (V = the first
+    512 dims).  ``attn_sink`` [H] (reading of the optional per-head sink "for
+    output scaling"): one more logit per head that joins the softmax
+    denominator and has no value row, out = sum_j exp(s_j) kn_j /
+    (sum_j exp(s_j) + exp(sink_h)); lse and max_logits are those of the keys
+    alone.  No key: out = 0, lse = max_logits = -inf.
+    """
+    qn = np.asarray(qn, dtype=np.float64)
+    qp = np.asarray(qp, dtype=np.float64)
+    H = qn.shape[0]
+    if kn.shape[0] == 0:
+        return np.zeros((H, HEAD_DIM_CKV)), np.full(H, -np.inf), np.full(H, -np.inf)
+    s = sm_scale * (qn @ kn.T + qp @ kp.T)  # [H, n]
+    mx = s.max(axis=1)
+    lse = mx + np.log(np.exp(s - mx[:, None]).sum(axis=1))
+    denom = lse
+    if attn_sink is not None:
+        sink = np.asarray(attn_sink, dtype=np.float64).reshape(H)
+        denom = np.logaddexp(lse, sink)  # ln(sum_j exp(s_j) + exp(sink))
+    out = np.exp(s - denom[:, None]) @ kn
+    return out, lse, mx
+
+
+def _sparse_run(q, indices, num_slots, gather, sm_scale, topk_length, attn_sink, tokens):
+    qq = as_f64(q)
+    if qq.shape[-1] != HEAD_DIM_CKV + HEAD_DIM_KPE:
+        raise ValueError("q must hold 576 dims per head (latent, then rope)")
+    H = qq.shape[-2]
+    qq = qq.reshape(-1, H, HEAD_DIM_CKV + HEAD_DIM_KPE)
+    T = qq.shape[0]
+    idx = _as_int(indices)
+    idx = idx.reshape(T, -1)
+    lens = None if topk_length is None else _as_int(topk_length).reshape(T)
+    sink = None if attn_sink is None else as_f64(attn_sink).reshape(H)
+    out = np.full((T, H, HEAD_DIM_CKV), np.nan)
+    lse = np.full((T, H), np.nan)
+    mx = np.full((T, H), np.nan)
+    for t in (range(T) if tokens is None else tokens):
+        sel = sparse_valid_indices(idx[t], num_slots, None if lens is None else lens[t])
+        kn, kp = gather(sel)
+        out[t], lse[t], mx[t] = sparse_attend(qq[t, :, :HEAD_DIM_CKV], qq[t, :, HEAD_DIM_CKV:], kn, kp,
+                                              sm_scale, sink)
+    return out, lse, mx
+
+
+def _flat_rows(cache, width: int, sel):
+    """Rows sel of a cache viewed as [num_slots, width] (no widening)."""
+    try:
+        import torch
+
+        if isinstance(cache, torch.Tensor):
+            flat = cache.detach().reshape(-1, width)
+            return flat[torch.from_numpy(np.asarray(sel, dtype=np.int64)).to(flat.device)].cpu()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.asarray(cache).reshape(-1, width)[sel]
+
+
+def mla_sparse_decode_fp8_ref(q, kv_cache_fp8, indices, sm_scale: float, topk_length=None, attn_sink=None,
+                              tokens=None):
+    """Token-sparse decode over the 656-byte fp8 record cache, as in FlashMLA
+    "flash_mla_with_kvcache (Sparse Attention with FP8 KV Cache)".
+
+    q [..., H, 576] bf16 (latent dims, then rope); kv_cache_fp8
+    [num_blocks, block_size, (1,) 656]; indices [..., topk] int of flat token
+    slots block * block_size + offset (the mapping of
+    abs_indices2indices_in_kvcache).  The leading dims of q and indices
+    (batch, s_q) are flattened into T query tokens.  topk_length [T] and
+    attn_sink [H] are optional.  Returns out [T, H, 512], lse [T, H] and
+    max_logits [T, H] in float64; ``tokens`` restricts the work to those
+    query tokens (the others are NaN).
+    """
+    num_slots = int(np.prod(kv_cache_fp8.shape[:-1]))
+    if kv_cache_fp8.shape[-1] != FP8_RECORD_BYTES:
+        raise ValueError("fp8 records must be 656 bytes")
+    return _sparse_run(q, indices, num_slots,
+                       lambda sel: fp8_record_decode(_flat_rows(kv_cache_fp8, FP8_RECORD_BYTES, sel)),
+                       sm_scale, topk_length, attn_sink, tokens)
+
+
+def mla_sparse_prefill_ref(q, kv, indices, sm_scale: float, topk_length=None, attn_sink=None, tokens=None):
+    """FlashMLA "Sparse MLA Prefill Kernel" (flash_mla_sparse_fwd): q [s_q, H, 576]
+    bf16, kv [s_kv, (1,) 576] bf16 (one KV head, no paging), indices
+    [s_q, (1,) topk] int into the s_kv rows.  Returns out [s_q, H, 512],
+    lse [s_q, H], max_logits [s_q, H] in float64 (natural-log units).
+    """
+    width = HEAD_DIM_CKV + HEAD_DIM_KPE
+    if kv.shape[-1] != width:
+        raise ValueError("kv must hold 576 dims per token")
+    num_slots = int(np.prod(kv.shape[:-1]))
+
+    def gather(sel):
+        rows = as_f64(_flat_rows(kv, width, sel))
+        return rows[:, :HEAD_DIM_CKV], rows[:, HEAD_DIM_CKV:]
+
+    return _sparse_run(q, indices, num_slots, gather, sm_scale, topk_length, attn_sink, tokens)

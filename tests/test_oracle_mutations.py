@@ -137,3 +137,78 @@ def test_e4m3_exponent_bias_mistake_is_caught(monkeypatch):
     monkeypatch.setattr(om, "e4m3_decode", lambda c: real(c) * 2.0)
     monkeypatch.setattr(oracle, "e4m3_decode", lambda c: real(c) * 2.0)
     assert _pin_suite() > 0
+
+
+# ---------------------------------------------------------------------------
+# token-sparse oracle
+# ---------------------------------------------------------------------------
+
+from tests import test_oracle_sparse as sparsepins  # noqa: E402
+
+
+def _sparse_pin_suite():
+    checks = [
+        sparsepins.test_sparse_fp8_matches_bruteforce,
+        sparsepins.test_sparse_list_of_all_keys_equals_dense_fp8_decode,
+        sparsepins.test_sparse_prefill_matches_torch_sdpa,
+        sparsepins.test_sink_only_rescales_the_output,
+        sparsepins.test_sink_equals_an_extra_key_with_a_zero_value_row,
+        sparsepins.test_single_key_and_zero_scale_closed_forms,
+    ]
+    failed = 0
+    for c in checks:
+        try:
+            c()
+        except (AssertionError, ValueError, IndexError):
+            failed += 1
+    return failed
+
+
+def _valid_variant(mistake):
+    def sparse_valid_indices(index_row, num_slots, topk_length=None):
+        idx = np.asarray(index_row, dtype=np.int64).reshape(-1)
+        if topk_length is not None and mistake != "ignore_topk_length":
+            idx = idx[:max(0, int(topk_length) + (1 if mistake == "topk_length_plus_one" else 0))]
+        if mistake == "keep_end_slot":
+            return idx[(idx >= 0) & (idx <= num_slots)]
+        sel = idx[(idx >= 0) & (idx < num_slots)]
+        return np.unique(sel) if mistake == "drop_duplicates" else sel
+    return sparse_valid_indices
+
+
+@pytest.mark.parametrize("mistake", ["ignore_topk_length", "topk_length_plus_one", "keep_end_slot",
+                                     "drop_duplicates"])
+def test_sparse_index_mistakes_are_caught(monkeypatch, mistake):
+    assert _sparse_pin_suite() == 0
+    monkeypatch.setattr(om, "sparse_valid_indices", _valid_variant(mistake))
+    assert _sparse_pin_suite() > 0
+
+
+def _sparse_attend_variant(mistake):
+    def sparse_attend(qn, qp, kn, kp, sm_scale, attn_sink=None):
+        qn = np.asarray(qn, dtype=np.float64)
+        qp = np.asarray(qp, dtype=np.float64)
+        H = qn.shape[0]
+        if kn.shape[0] == 0:
+            return np.zeros((H, 512)), np.full(H, -np.inf), np.full(H, -np.inf)
+        s = sm_scale * (qn @ kn.T + (0 if mistake == "drop_rope" else qp @ kp.T))
+        mx = s.max(axis=1)
+        lse = mx + np.log(np.exp(s - mx[:, None]).sum(axis=1))
+        denom = lse
+        if attn_sink is not None and mistake != "sink_ignored":
+            sink = np.asarray(attn_sink, dtype=np.float64).reshape(H)
+            denom = np.logaddexp(lse, -sink if mistake == "sink_sign" else sink)
+        out = np.exp(s - denom[:, None]) @ kn
+        if mistake == "sink_in_lse":
+            lse = denom
+        if mistake == "max_base2":
+            mx = mx / math.log(2.0)
+        return out, lse, mx
+    return sparse_attend
+
+
+@pytest.mark.parametrize("mistake", ["drop_rope", "sink_ignored", "sink_sign", "sink_in_lse", "max_base2"])
+def test_sparse_attend_mistakes_are_caught(monkeypatch, mistake):
+    assert _sparse_pin_suite() == 0
+    monkeypatch.setattr(om, "sparse_attend", _sparse_attend_variant(mistake))
+    assert _sparse_pin_suite() > 0

@@ -22,6 +22,18 @@ Recipe (for workload seed ``k``):
   slots past ``kv_len`` in each last page) is NaN (fp8: all-ones bytes, which
   are NaN codes, NaN scales and NaN bf16).  Results must not depend on them.
 
+Token-sparse workloads (:func:`make_sparse_workload`) start from the fp8
+decode workload of the same seed (lengths, pages, pool) and then draw from a
+second CPU generator seeded ``k + 1`` on the host: for each query token
+(request b, MTP position i < s_q) ``min(topk, L_b)`` distinct positions of
+``randperm(L_b)``, mapped to flat slots ``page * page_size + offset``
+through b's page list and padded with -1 to ``topk``; a fraction
+``invalid_frac`` of entries replaced by -1 or by a slot at or past the pool
+end (half each); ``topk_length`` ~ U[topk_min, topk] when asked for; the
+attention sink ln(topk) + 1.5 + 2 N(0, 1) per head (near the lse of topk
+N(0,1) keys at sm_scale 1/sqrt(192), so that it matters); then q [T, H, 576] as N(0,1) bf16 on the target
+device from a generator seeded ``k + 1``.
+
 fp8 quantisation of the source pool (the 656-byte record of FlashMLA's
 "FP8 KV Cache Quantization and Dequantization"): per token and 128-dim tile,
 ``scale = amax / 448`` in fp32 and ``code = e4m3(clamp(x / scale, +-448))``
@@ -61,6 +73,13 @@ CONFIGS = {
     # B=128, H=128, L ~ U[4096, 16384], 656-byte fp8 records
     "decode_fp8_b128_h128": dict(seed=5, kind="decode", kv_format="fp8", batch=128, heads=128,
                                  page_size=64, kv_lens=("uniform", 4096, 16384), pool_factor=2),
+}
+
+# Token-sparse decode over the fp8 records: B=128 requests with L ~ U[4096,
+# 16384], s_q = 2 query tokens each (MTP), H=128, 2048 keys per query token
+SPARSE_CONFIGS = {
+    "sparse_fp8_b128_sq2_h128_topk2048": dict(seed=6, batch=128, s_q=2, heads=128, topk=2048, page_size=64,
+                                              kv_lens=("uniform", 4096, 16384), pool_factor=2),
 }
 
 SM_SCALE_DEFAULT = 1.0 / math.sqrt(192.0)
@@ -231,3 +250,84 @@ def make_workload(name: Optional[str] = None, *, device: Union[str, torch.device
                     kv_indices=kv_indices, qo_indptr=qo_indptr, q_nope=q_nope, q_pe=q_pe,
                     ckv=ckv, kpe=kpe, kv_fp8=kv_fp8, sm_scale=sm_scale, out_dtype=out_dtype,
                     causal=causal, seed=seed)
+
+
+@dataclasses.dataclass
+class SparseWorkload:
+    name: str
+    batch: int
+    s_q: int
+    num_heads: int
+    topk: int
+    page_size: int
+    num_pages: int
+    kv_len: torch.Tensor                 # int32 [B], CPU
+    kv_indptr: torch.Tensor              # int32 [B+1], CPU (page lists the indices were drawn through)
+    kv_indices: torch.Tensor             # int32 [nnz], CPU
+    q: torch.Tensor                      # bf16 [T, H, 576], T = B * s_q (latent, then rope)
+    kv_fp8: torch.Tensor                 # uint8 [P, ps, 656]
+    indices: torch.Tensor                # int32 [T, topk] flat slots, -1 / >= P*ps invalid (CPU)
+    topk_length: Optional[torch.Tensor]  # int32 [T] (CPU) or None
+    attn_sink: Optional[torch.Tensor]    # fp32 [H] (CPU) or None
+    sm_scale: float
+    out_dtype: torch.dtype
+    seed: int
+
+    @property
+    def tokens(self) -> int:
+        return self.q.shape[0]
+
+    @property
+    def num_slots(self) -> int:
+        return self.num_pages * self.page_size
+
+
+def make_sparse_workload(name: Optional[str] = None, *, device: Union[str, torch.device] = "cpu",
+                         poison: bool = True, seed: Optional[int] = None, batch: Optional[int] = None,
+                         s_q: int = 2, heads: int = 128, topk: int = 2048, page_size: int = 64, kv_lens=None,
+                         pool_factor: int = 2, invalid_frac: float = 0.0, topk_min: Optional[int] = None,
+                         sink: bool = False, sm_scale: float = SM_SCALE_DEFAULT,
+                         out_dtype: torch.dtype = torch.bfloat16) -> SparseWorkload:
+    """Build one token-sparse fp8 workload: a named one from SPARSE_CONFIGS, or a custom one."""
+    if name is not None:
+        spec = dict(SPARSE_CONFIGS[name])
+        seed = spec.pop("seed") if seed is None else seed
+        batch, s_q, heads, topk = spec.pop("batch"), spec.pop("s_q"), spec.pop("heads"), spec.pop("topk")
+        page_size, kv_lens, pool_factor = spec.pop("page_size"), spec.pop("kv_lens"), spec.pop("pool_factor")
+    else:
+        name = "custom_sparse"
+        seed = 0 if seed is None else seed
+        if batch is None:
+            batch = len(kv_lens)
+    base = make_workload(device=device, poison=poison, seed=seed, kind="decode", kv_format="fp8", batch=batch,
+                         heads=1, page_size=page_size, kv_lens=kv_lens, pool_factor=pool_factor)
+    g = torch.Generator().manual_seed(seed + 1)
+    num_slots = base.num_pages * page_size
+    T = batch * s_q
+    indices = torch.full((T, topk), -1, dtype=torch.int32)
+    for b in range(batch):
+        L = int(base.kv_len[b])
+        pages = base.kv_indices[int(base.kv_indptr[b]):int(base.kv_indptr[b + 1])].to(torch.int64)
+        for i in range(s_q):
+            n = min(topk, L)
+            pos = torch.randperm(L, generator=g)[:n]
+            slots = pages[pos // page_size] * page_size + pos % page_size
+            indices[b * s_q + i, :n] = slots.to(torch.int32)
+    if invalid_frac > 0:
+        hit = torch.rand((T, topk), generator=g) < invalid_frac
+        past = torch.randint(num_slots, num_slots + 1000, (T, topk), generator=g, dtype=torch.int32)
+        kind = torch.rand((T, topk), generator=g) < 0.5
+        indices = torch.where(hit, torch.where(kind, torch.full_like(indices, -1), past), indices)
+    topk_length = None
+    if topk_min is not None:
+        topk_length = torch.randint(topk_min, topk + 1, (T,), generator=g, dtype=torch.int64).to(torch.int32)
+    attn_sink = (math.log(topk) + 1.5 + 2.0 * torch.randn(heads, generator=g)).to(torch.float32) if sink else None
+    dev = torch.device(device)
+    gv = torch.Generator().manual_seed(seed + 1) if dev.type == "cpu" else \
+        torch.Generator(device=dev).manual_seed(seed + 1)
+    q = _randn_bf16((T, heads, HEAD_DIM_CKV + HEAD_DIM_KPE), gv, dev)
+    return SparseWorkload(name=name, batch=batch, s_q=s_q, num_heads=heads, topk=topk, page_size=page_size,
+                          num_pages=base.num_pages, kv_len=base.kv_len, kv_indptr=base.kv_indptr,
+                          kv_indices=base.kv_indices, q=q, kv_fp8=base.kv_fp8, indices=indices,
+                          topk_length=topk_length, attn_sink=attn_sink, sm_scale=sm_scale, out_dtype=out_dtype,
+                          seed=seed)
