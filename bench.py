@@ -230,51 +230,12 @@ def cpu_baseline(w, flops_total, min_seconds):
                       f"{w.batch} requests of {w.name}), {dt:.1f} s wall, float64 NumPy"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="decode_b64_h128")
-    ap.add_argument("--rotate-bytes", type=float, default=1.5e9,
-                    help="replicate the cache pool until consecutive steps are this many bytes apart")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--tile-mode", type=int, default=0,
-                    help="0 = planner's choice; 1 wide, 2 narrow, 3 quad")
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
-                    help="only run a plain copy of BYTES (counter calibration) and exit")
-    ap.add_argument("--write-counters", metavar="PMC_DIR",
-                    help="summarise rocprofv3 FETCH_SIZE/WRITE_SIZE runs under PMC_DIR into profiles/ and exit")
-    ap.add_argument("--copy-bytes", type=int, default=1 << 30)
-    ap.add_argument("--layout", choices=("split", "packed"), default="split",
-                    help="bf16 q / cache as separate latent and rope tensors, or one 576-wide row per token")
-    ap.add_argument("--command", action="append", default=[], help="command lines recorded with --write-counters")
-    args = ap.parse_args()
-
-    if args.write_counters:
-        print(write_counters(args.config, args.write_counters, args.copy_bytes, args.command))
-        return
-    if args.copy_calibration:
-        copy_calibration(args.copy_calibration)
-        return
-
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(one MI355X share of the workload is what it measures).", file=sys.stderr)
-        sys.exit(2)
-
+def setup_dense(args, mla, dev):
+    """Plan, inputs and step of a paged dense workload (decode, prefill, fp8 decode)."""
     import torch
 
-    import paged_mla_decode_05_amd as mla
     from workloads import make_workload
 
-    if not os.path.exists(mla.lib_path()):
-        import __graft_entry__
-
-        __graft_entry__.build()
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     log(f"bench: generating {args.config} on {dev}")
     w = make_workload(args.config, device=dev, poison=False)
     flops, live_kv, bytes_alg = workload_counts(w)
@@ -324,6 +285,136 @@ def main():
         else:
             mla.mla_decode(plan, w.q_nope, w.q_pe, ckv, kpe, kv_indptr, kv_indices, w.sm_scale, out=out,
                            lse=lse, workspace=ws)
+
+    config = {"workload": w.name, "batch": w.batch, "num_qo_heads": w.num_heads, "head_dim_ckv": 512,
+              "head_dim_kpe": 64, "page_size": w.page_size, "kv_format": w.kv_format,
+              "kv_len_total": int(w.kv_len.sum()), "rows": w.rows, "parallelism": "single GPU",
+              "layout": args.layout}
+    return {"step": step, "flops": flops, "live_kv": live_kv, "bytes_alg": bytes_alg, "plan_ms": plan_ms,
+            "config": config, "kernel": "mla_attn_kernel",
+            "dtype": "bf16" if w.kv_format == "bf16" else "fp8-e4m3 cache, bf16 math",
+            "cpu_baseline": lambda secs: cpu_baseline(w, flops, secs)}
+
+
+def setup_sparse(args, mla, dev):
+    """Plan, inputs and step of a token-sparse fp8 workload.
+
+    Algorithmic units: each valid (query token, list entry) reads one
+    656-byte record and costs 2176 flops per head; the lists themselves
+    (4 bytes per entry), q (1152 B per row), out, lse and max_logits count
+    as bytes too."""
+    import numpy as np
+    import torch
+
+    from workloads import make_sparse_workload
+
+    log(f"bench: generating {args.config} on {dev}")
+    w = make_sparse_workload(args.config, device=dev, poison=False)
+    idx = w.indices.numpy().astype(np.int64)
+    lim = idx.shape[1] if w.topk_length is None else w.topk_length.numpy()[:, None]
+    valid = (idx >= 0) & (idx < w.num_slots) & (np.arange(idx.shape[1])[None, :] < lim)
+    n_valid = valid.sum(axis=1)
+    H, T = w.num_heads, w.tokens
+    flops = int(n_valid.sum()) * H * FLOPS_PER_ROW_KEY
+    live_kv = int(n_valid.sum()) * KV_BYTES["fp8"]
+    out_bytes = 4 if str(w.out_dtype).endswith("float32") else 2
+    bytes_alg = live_kv + T * H * (576 * 2 + 512 * out_bytes + 4 + 4) + idx.size * 4
+    t_plan = time.perf_counter()
+    plan = mla.mla_sparse_plan_create(T, H, w.num_slots, w.topk)
+    plan_ms = (time.perf_counter() - t_plan) * 1e3
+    indices = w.indices.to(dev)
+    reps = max(1, min(16, math.ceil(args.rotate_bytes / max(live_kv, 1))))
+    pools = [w.kv_fp8] + [w.kv_fp8.clone() for _ in range(reps - 1)]
+    out = torch.empty((T, H, 512), dtype=w.out_dtype, device=dev)
+    lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    mx = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ws = plan.workspace(dev)
+    log(f"bench: {plan.num_work_items} work items on {plan.workgroup_ptr().numel() - 1} workgroups, "
+        f"{plan.num_split_groups} split groups, workspace {plan.workspace_bytes / 1e6:.1f} MB, "
+        f"{reps} pool replicas of {w.kv_fp8.numel() / 1e6:.0f} MB, {int(n_valid.sum())} valid entries")
+
+    def step(i):
+        mla.mla_sparse_decode_fp8(plan, w.q, pools[i % reps], indices, w.sm_scale, out=out, lse=lse,
+                                  max_logits=mx, workspace=ws)
+
+    def cpu(secs):
+        import oracle
+
+        try:
+            from threadpoolctl import threadpool_info
+
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        except Exception:  # pragma: no cover
+            threads = os.cpu_count()
+        q_host, kv_host = w.q.cpu(), w.kv_fp8.cpu()
+        done, n = 0.0, 0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < secs:
+            t = n % T
+            oracle.mla_sparse_decode_fp8_ref(q_host, kv_host, w.indices, w.sm_scale, tokens=[t])
+            done += int(n_valid[t]) * H * FLOPS_PER_ROW_KEY
+            n += 1
+        dt = time.perf_counter() - t0
+        return {"value": done / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+                "sample": f"{n} query-token evaluations of {w.name} ({n / T:.2f} passes over its {T} tokens), "
+                          f"{dt:.1f} s wall, float64 NumPy"}
+
+    config = {"workload": w.name, "batch": w.batch, "s_q": w.s_q, "num_qo_heads": H, "topk": w.topk,
+              "head_dim_ckv": 512, "head_dim_kpe": 64, "kv_format": "fp8", "page_size": w.page_size,
+              "valid_entries": int(n_valid.sum()), "rows": T, "parallelism": "single GPU"}
+    return {"step": step, "flops": flops, "live_kv": live_kv, "bytes_alg": bytes_alg, "plan_ms": plan_ms,
+            "config": config, "kernel": "mla_attn_kernel (token-sparse fp8)",
+            "dtype": "fp8-e4m3 cache, bf16 math", "cpu_baseline": cpu}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="decode_b64_h128")
+    ap.add_argument("--rotate-bytes", type=float, default=1.5e9,
+                    help="replicate the cache pool until consecutive steps are this many bytes apart")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--tile-mode", type=int, default=0,
+                    help="0 = planner's choice; 1 wide, 2 narrow, 3 quad")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain copy of BYTES (counter calibration) and exit")
+    ap.add_argument("--write-counters", metavar="PMC_DIR",
+                    help="summarise rocprofv3 FETCH_SIZE/WRITE_SIZE runs under PMC_DIR into profiles/ and exit")
+    ap.add_argument("--copy-bytes", type=int, default=1 << 30)
+    ap.add_argument("--layout", choices=("split", "packed"), default="split",
+                    help="bf16 q / cache as separate latent and rope tensors, or one 576-wide row per token")
+    ap.add_argument("--command", action="append", default=[], help="command lines recorded with --write-counters")
+    args = ap.parse_args()
+
+    if args.write_counters:
+        print(write_counters(args.config, args.write_counters, args.copy_bytes, args.command))
+        return
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(one MI355X share of the workload is what it measures).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_mla_decode_05_amd as mla
+    from workloads import SPARSE_CONFIGS
+
+    if not os.path.exists(mla.lib_path()):
+        import __graft_entry__
+
+        __graft_entry__.build()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    setup = setup_sparse if args.config in SPARSE_CONFIGS else setup_dense
+    S = setup(args, mla, dev)
+    step, flops, live_kv, bytes_alg, plan_ms = S["step"], S["flops"], S["live_kv"], S["bytes_alg"], S["plan_ms"]
 
     for i in range(args.warmup):
         step(i)
@@ -381,7 +472,7 @@ def main():
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
                 "traffic": (round(traffic / ta_s / 1e9, 1) if traffic is not None else None)}
-    roof["kernel"] = "mla_attn_kernel"
+    roof["kernel"] = S["kernel"]
     roof["kernel_avg_us"] = round(attn_avg * 1e3, 2)
     roof["algorithmic_bytes_per_launch"] = bytes_alg
     roof["algorithmic_flops_per_launch"] = flops
@@ -405,12 +496,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.kv_format == "bf16" else "fp8-e4m3 cache, bf16 math",
+        "dtype": S["dtype"],
         "data": "synthetic (seeded N(0,1) bf16 inputs shaped like the workload)",
-        "config": {"workload": w.name, "batch": w.batch, "num_qo_heads": w.num_heads, "head_dim_ckv": 512,
-                   "head_dim_kpe": 64, "page_size": w.page_size, "kv_format": w.kv_format,
-                   "kv_len_total": int(w.kv_len.sum()), "rows": w.rows, "parallelism": "single GPU",
-                   "layout": args.layout},
+        "config": S["config"],
         "kv_gb_per_s": round(kv_gbs, 1),
         "pct_of_roofline": round(pct, 2),
         "plan_ms": round(plan_ms, 3),
@@ -418,7 +506,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle")
-        result["cpu_baseline"] = cpu_baseline(w, flops, args.cpu_seconds)
+        result["cpu_baseline"] = S["cpu_baseline"](args.cpu_seconds)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

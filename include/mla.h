@@ -61,7 +61,8 @@ typedef enum mla_dtype { MLA_DTYPE_BF16 = 0, MLA_DTYPE_FP32 = 1 } mla_dtype;
  *     64 rope dims as bf16.  Key value = code * scale; rope as stored.   */
 typedef enum mla_kv_format { MLA_KV_BF16 = 0, MLA_KV_FP8_E4M3_T128 = 1 } mla_kv_format;
 
-typedef enum mla_kind { MLA_KIND_DECODE = 0, MLA_KIND_PREFILL = 1 } mla_kind;
+/* MLA_KIND_SPARSE_DECODE: plans made by mla_sparse_plan_create only. */
+typedef enum mla_kind { MLA_KIND_DECODE = 0, MLA_KIND_PREFILL = 1, MLA_KIND_SPARSE_DECODE = 2 } mla_kind;
 
 /* Tile modes of the attention kernel (0 lets the planner choose: WIDE when
  * some request holds at least 64 query rows (heads x query tokens), NARROW
@@ -236,6 +237,52 @@ mla_status mla_prefill_packed(const mla_plan* plan, const void* q, const void* k
  * nothing; capture-safe.                                                 */
 mla_status mla_block_table_to_indices(const mla_plan* plan, const int32_t* block_table, int32_t max_blocks,
                                       const int32_t* kv_indptr, int32_t* kv_indices, hipStream_t stream);
+
+/* Token-sparse decode over the 656-byte fp8 record cache (DSA): FlashMLA
+ * digest, "flash_mla_with_kvcache (Sparse Attention with FP8 KV Cache)" and
+ * "Sparse Attention Decoding with KV Cache"; the formula of "Sparse MLA
+ * Prefill Kernel".  Every query token t has its own list of key slots;
+ * for each head h:
+ *   s_j = sm_scale * (q[t,h,:512] . nope_j + q[t,h,512:] . rope_j) over the
+ *         valid entries j of indices[t, :], nope_j = code * tile scale;
+ *   max_logits[t,h] = max_j s_j,  lse[t,h] = ln sum_j exp(s_j),
+ *   out[t,h] = sum_j exp(s_j) nope_j / (sum_j exp(s_j) + exp(attn_sink[h]))
+ *   (without attn_sink: the plain softmax average).  No valid entry: out 0,
+ *   lse and max_logits -inf.
+ *
+ * mla_sparse_plan_create: the schedule for num_tokens query tokens of
+ * num_heads heads, each with a list of topk entries into a pool of
+ * num_slots records (num_blocks * block_size).  Work is balanced as if every
+ * entry were valid.  num_cus = 0 asks the current device; force_splits > 0
+ * cuts every list into that many chunks (testing).  Errors:
+ * MLA_ERR_INVALID_ARGUMENT (sizes < 1 where 1 is needed, force_splits < 0),
+ * MLA_ERR_DEVICE (device query failed).  The workspace holds the compacted
+ * lists; its size is mla_plan_workspace_bytes and it is uploaded with
+ * mla_plan_upload like any plan's.
+ *
+ * mla_sparse_decode_fp8 arguments (device pointers unless noted):
+ *   q          [num_tokens, H, 576] bf16, latent dims then rope dims (the
+ *              pages' q [batch, s_q, H, 576] with batch and s_q flattened)
+ *   kv_cache   [num_slots, 656] uint8 records (a [num_blocks, block_size,
+ *              (1,) 656] cache viewed flat)
+ *   indices    [num_tokens, topk] int32 flat slots block * block_size +
+ *              offset; -1, a negative value or a slot >= num_slots is an
+ *              invalid entry and is skipped; a slot listed twice counts twice
+ *   topk_length [num_tokens] int32 or NULL: only the first
+ *              min(topk_length[t], topk) entries of row t are used
+ *   attn_sink  [H] fp32 or NULL: per-head sink logit (natural-log units)
+ *   out        [num_tokens, H, 512] bf16 or fp32 (out_dtype); lse and
+ *              max_logits [num_tokens, H] fp32 (max_logits may be NULL)
+ * The lists are compacted into the workspace on `stream` first, so the
+ * workspace may not be shared by calls that overlap.  Errors as for
+ * mla_decode; a plan not made by mla_sparse_plan_create is
+ * MLA_ERR_PLAN_MISMATCH.  Allocates nothing and never synchronises.     */
+mla_status mla_sparse_plan_create(mla_plan** plan, int32_t num_tokens, int32_t num_heads, int32_t num_slots,
+                                  int32_t topk, int32_t num_cus, int32_t force_splits);
+mla_status mla_sparse_decode_fp8(const mla_plan* plan, const void* q, const void* kv_cache, const int32_t* indices,
+                                 const int32_t* topk_length, const float* attn_sink, float sm_scale, void* out,
+                                 int32_t out_dtype, float* lse, float* max_logits, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
 
 /* Diagnostics for timing: the next run call made on this host thread has
  * the attention kernel's own dispatch record `before` when the kernel

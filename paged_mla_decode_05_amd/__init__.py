@@ -8,8 +8,9 @@ call raises; there is no fallback.
 
 Names follow the C ABI: :func:`mla_plan_create`, :func:`mla_decode`,
 :func:`mla_prefill`, :func:`mla_decode_fp8`, the concatenated-layout
-:func:`mla_decode_packed` / :func:`mla_prefill_packed`, and
-:func:`mla_block_table_to_indices`.
+:func:`mla_decode_packed` / :func:`mla_prefill_packed`,
+:func:`mla_block_table_to_indices`, and the token-sparse
+:func:`mla_sparse_plan_create` / :func:`mla_sparse_decode_fp8`.
 """
 
 from ._binding import (  # noqa: F401
@@ -25,8 +26,11 @@ from ._binding import (  # noqa: F401
     mla_prefill,
     mla_prefill_packed,
     mla_record_attention_events,
+    mla_sparse_decode_fp8,
+    mla_sparse_plan_create,
     MLA_KIND_DECODE,
     MLA_KIND_PREFILL,
+    MLA_KIND_SPARSE_DECODE,
     MLA_KV_BF16,
     MLA_KV_FP8_E4M3_T128,
     MLA_TILE_AUTO,

@@ -14,6 +14,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 MLA_OK = 0
 MLA_KIND_DECODE = 0
 MLA_KIND_PREFILL = 1
+MLA_KIND_SPARSE_DECODE = 2
 MLA_KV_BF16 = 0
 MLA_KV_FP8_E4M3_T128 = 1
 MLA_DTYPE_BF16 = 0
@@ -94,6 +95,10 @@ def load_library():
         L.mla_prefill_packed.restype = i32
         L.mla_block_table_to_indices.argtypes = [vp, vp, i32, vp, vp, vp]
         L.mla_block_table_to_indices.restype = i32
+        L.mla_sparse_plan_create.argtypes = [ctypes.POINTER(vp), i32, i32, i32, i32, i32, i32]
+        L.mla_sparse_plan_create.restype = i32
+        L.mla_sparse_decode_fp8.argtypes = [vp, vp, vp, vp, vp, vp, f32, vp, i32, vp, vp, vp, sz, vp]
+        L.mla_sparse_decode_fp8.restype = i32
         L.mla_record_attention_events.argtypes = [vp, vp]
         L.mla_record_attention_events.restype = i32
         L.mla_status_str.argtypes = [i32]
@@ -213,6 +218,49 @@ def mla_plan_create(kind: int, batch: int, num_heads: int, page_size: int, num_p
     _check(L.mla_plan_create(ctypes.byref(h), ctypes.byref(d), cast(kl_p), cast(ki_p), cast(qo_p)),
            "mla_plan_create")
     return Plan(h, d, kl, ki, qo)
+
+
+def mla_sparse_plan_create(num_tokens: int, num_heads: int, num_slots: int, topk: int, num_cus: int = 0,
+                           force_splits: int = 0) -> Plan:
+    """Host plan of the token-sparse fp8 decode: num_tokens query tokens, each
+    with a list of topk entries into num_slots records (see include/mla.h)."""
+    L = load_library()
+    h = ctypes.c_void_p()
+    _check(L.mla_sparse_plan_create(ctypes.byref(h), num_tokens, num_heads, num_slots, topk, num_cus, force_splits),
+           "mla_sparse_plan_create")
+    d = _Desc(kind=MLA_KIND_SPARSE_DECODE, batch=num_tokens, num_qo_heads=num_heads, head_dim_ckv=_DIM_CKV,
+              head_dim_kpe=_DIM_KPE, page_size=1, num_pages=num_slots, kv_format=MLA_KV_FP8_E4M3_T128, causal=0,
+              num_cus=num_cus, max_splits=0, force_splits=force_splits, tile_mode=MLA_TILE_WIDE)
+    plan = Plan(h, d, None, None, None)
+    plan.topk = topk
+    return plan
+
+
+def mla_sparse_decode_fp8(plan: Plan, q, kv_cache, indices, sm_scale: float, topk_length=None, attn_sink=None,
+                          out=None, lse=None, max_logits=None, out_dtype=torch.bfloat16, workspace=None):
+    """Token-sparse decode over 656-byte fp8 records: q [T, H, 576] bf16,
+    kv_cache [..., 656] uint8 (num_slots records), indices [T, topk] int32 flat
+    slots (-1 / out of range: skipped), optional topk_length [T] int32 and
+    attn_sink [H] fp32.  Returns (out [T, H, 512], lse [T, H], max_logits [T, H])."""
+    L = load_library()
+    T, H, topk = plan.desc.batch, plan.desc.num_qo_heads, plan.topk
+    qq = _dev(q, "q", torch.bfloat16, (T, H, _DIM_CKV + _DIM_KPE))
+    if not isinstance(kv_cache, torch.Tensor) or kv_cache.shape[-1] != _FP8_RECORD or \
+            kv_cache.numel() // _FP8_RECORD != plan.desc.num_pages:
+        raise ValueError(f"kv_cache must hold {plan.desc.num_pages} records of {_FP8_RECORD} bytes")
+    kv = _dev(kv_cache, "kv_cache", torch.uint8)
+    ix = _dev(indices, "indices", torch.int32, (T, topk))
+    tl = _dev(topk_length, "topk_length", torch.int32, (T,)) if topk_length is not None else None
+    sk = _dev(attn_sink, "attn_sink", torch.float32, (H,)) if attn_sink is not None else None
+    out, lse, code = _packed_outputs(q, out, lse, out_dtype)
+    if max_logits is None:
+        max_logits = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    mx = _dev(max_logits, "max_logits", torch.float32, (T, H))
+    ws = plan.workspace(q.device) if workspace is None else workspace
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(L.mla_sparse_decode_fp8(plan.handle, qq, kv, ix, tl, sk, float(sm_scale), out.data_ptr(), code,
+                                   lse.data_ptr(), mx, ws.data_ptr(), ws.numel(), stream), "mla_sparse_decode_fp8")
+    return out, lse, max_logits
 
 
 def mla_record_attention_events(before, after):

@@ -40,6 +40,11 @@ struct mla_plan {
   std::vector<SplitGroup> groups;
   std::vector<int32_t> blob;    // uploaded image: wg_ptr | items | groups
   size_t off_items = 0, off_groups = 0, off_part_lse = 0, off_part_o = 0, ws_bytes = 0;
+  // token-sparse plans: entries per list, and the workspace regions of the
+  // compacted lists [batch][topk], their counts [batch], page offsets
+  // [batch + 1] and the partial maxima [slots][rows_per_block]
+  int32_t topk = 0;
+  size_t off_sp_list = 0, off_sp_count = 0, off_sp_indptr = 0, off_part_max = 0;
 };
 
 namespace {
@@ -203,6 +208,13 @@ mla_status build_schedule(mla_plan* p, const std::vector<int32_t>& kv_len,
   p->off_part_lse = align_up(blob_bytes, mla::kWsAlign);
   p->off_part_o = align_up(p->off_part_lse + (size_t)p->num_slots * RB * 4, mla::kWsAlign);
   p->ws_bytes = align_up(p->off_part_o + (size_t)p->num_slots * RB * mla::kDimCkv * 2, mla::kWsAlign);
+  if (d.kind == MLA_KIND_SPARSE_DECODE) {
+    p->off_sp_list = p->ws_bytes;
+    p->off_sp_count = align_up(p->off_sp_list + (size_t)d.batch * p->topk * 4, mla::kWsAlign);
+    p->off_sp_indptr = align_up(p->off_sp_count + (size_t)d.batch * 4, mla::kWsAlign);
+    p->off_part_max = align_up(p->off_sp_indptr + (size_t)(d.batch + 1) * 4, mla::kWsAlign);
+    p->ws_bytes = align_up(p->off_part_max + (size_t)p->num_slots * RB * 4, mla::kWsAlign);
+  }
   p->blob.assign(blob_bytes / 4, 0);
   std::memcpy(p->blob.data(), p->wg_ptr.data(), p->wg_ptr.size() * 4);
   std::memcpy((char*)p->blob.data() + p->off_items, p->items.data(), p->items.size() * sizeof(WorkItem));
@@ -283,6 +295,48 @@ mla_status mla_plan_create(mla_plan** out, const mla_plan_desc* d, const int32_t
   return MLA_OK;
 }
 
+mla_status mla_sparse_plan_create(mla_plan** out, int32_t num_tokens, int32_t num_heads, int32_t num_slots,
+                                  int32_t topk, int32_t num_cus, int32_t force_splits) {
+  if (!out) return MLA_ERR_INVALID_ARGUMENT;
+  *out = nullptr;
+  if (num_tokens < 0 || num_heads < 1 || num_slots < 1 || topk < 1 || num_cus < 0 || force_splits < 0)
+    return MLA_ERR_INVALID_ARGUMENT;
+  if ((int64_t)num_tokens * topk > ((int64_t)1 << 31) - 1) return MLA_ERR_INVALID_ARGUMENT;
+  if (num_cus == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_DEVICE;
+    if (hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return MLA_ERR_DEVICE;
+  }
+  mla_plan* p = new (std::nothrow) mla_plan();
+  if (!p) return MLA_ERR_INVALID_ARGUMENT;
+  // Each query token is a request of one query row block whose "pages" are
+  // the topk single-token slots of its list (page size 1).
+  mla_plan_desc& d = p->d;
+  d.kind = MLA_KIND_SPARSE_DECODE;
+  d.batch = num_tokens;
+  d.num_qo_heads = num_heads;
+  d.head_dim_ckv = mla::kDimCkv;
+  d.head_dim_kpe = mla::kDimKpe;
+  d.page_size = 1;
+  d.num_pages = num_slots;
+  d.kv_format = MLA_KV_FP8_E4M3_T128;
+  d.num_cus = num_cus;
+  d.force_splits = force_splits;
+  d.tile_mode = MLA_TILE_WIDE;
+  p->topk = topk;
+  std::vector<int32_t> kv_len(num_tokens, topk), q_len(num_tokens, 1);
+  p->kv_indptr.resize((size_t)num_tokens + 1);
+  for (int32_t t = 0; t <= num_tokens; ++t) p->kv_indptr[t] = t * topk;
+  mla_status st = build_schedule(p, kv_len, q_len, num_cus);
+  if (st != MLA_OK) {
+    delete p;
+    return st;
+  }
+  *out = p;
+  return MLA_OK;
+}
+
 void mla_plan_destroy(mla_plan* p) { delete p; }
 
 size_t mla_plan_workspace_bytes(const mla_plan* p) { return p ? p->ws_bytes : 0; }
@@ -330,21 +384,45 @@ constexpr Layout kSplit{mla::kDimCkv * 2, mla::kDimKpe * 2, mla::kDimCkv, mla::k
 constexpr Layout kPacked{(mla::kDimCkv + mla::kDimKpe) * 2, (mla::kDimCkv + mla::kDimKpe) * 2,
                          mla::kDimCkv + mla::kDimKpe, mla::kDimCkv + mla::kDimKpe};
 
+// Inputs of the token-sparse decode beyond the dense ones.
+struct Sparse {
+  const int32_t* indices = nullptr;
+  const int32_t* topk_length = nullptr;
+  const float* attn_sink = nullptr;
+  float* max_logits = nullptr;
+};
+
 mla_status run(const mla_plan* p, int32_t want_kind, int32_t want_format, const void* q_nope,
                const void* q_pe, const void* ckv, const void* kpe, const void* kv_fp8,
                const int32_t* qo_indptr, const int32_t* kv_indptr, const int32_t* kv_indices,
                float sm_scale, void* out, int32_t out_dtype, float* lse, void* ws, size_t ws_bytes,
-               hipStream_t stream, const Layout& lay = kSplit, float out_scale = 1.f) {
+               hipStream_t stream, const Layout& lay = kSplit, float out_scale = 1.f,
+               const Sparse* sparse = nullptr) {
   if (!p) return MLA_ERR_INVALID_ARGUMENT;
   if (p->d.kind != want_kind || p->d.kv_format != want_format) return MLA_ERR_PLAN_MISMATCH;
   if (out_dtype != MLA_DTYPE_BF16 && out_dtype != MLA_DTYPE_FP32) return MLA_ERR_INVALID_ARGUMENT;
   if (!std::isfinite(sm_scale) || !std::isfinite(out_scale)) return MLA_ERR_INVALID_ARGUMENT;
   if (p->items.empty()) return MLA_OK;  // nothing to compute (batch 0 or no rows)
-  if (!q_nope || !q_pe || !kv_indptr || !kv_indices || !out || !lse) return MLA_ERR_INVALID_ARGUMENT;
+  if (!q_nope || !q_pe || !out || !lse) return MLA_ERR_INVALID_ARGUMENT;
+  if (sparse ? !sparse->indices : (!kv_indptr || !kv_indices)) return MLA_ERR_INVALID_ARGUMENT;
   if (want_format == MLA_KV_BF16 && (!ckv || !kpe)) return MLA_ERR_INVALID_ARGUMENT;
   if (want_format == MLA_KV_FP8_E4M3_T128 && !kv_fp8) return MLA_ERR_INVALID_ARGUMENT;
   if (want_kind == MLA_KIND_PREFILL && !qo_indptr) return MLA_ERR_INVALID_ARGUMENT;
   if (!ws || ws_bytes < p->ws_bytes || ((uintptr_t)ws % mla::kWsAlign) != 0) return MLA_ERR_WORKSPACE;
+  char* w = (char*)ws;
+  if (sparse) {
+    // the lists are compacted into the workspace first; the attention kernel
+    // then reads them as page lists of page size 1
+    int32_t* list = (int32_t*)(w + p->off_sp_list);
+    int32_t* count = (int32_t*)(w + p->off_sp_count);
+    int32_t* indptr = (int32_t*)(w + p->off_sp_indptr);
+    if (mla::launch_sparse_lists(sparse->indices, p->d.batch, p->topk, sparse->topk_length,
+                                 (int64_t)p->d.num_pages * p->d.page_size, list, count, indptr,
+                                 stream) != hipSuccess)
+      return MLA_ERR_DEVICE;
+    kv_indptr = indptr;
+    kv_indices = list;
+  }
 
   mla::AttnArgs a{};
   a.q_nope = q_nope;
@@ -355,7 +433,6 @@ mla_status run(const mla_plan* p, int32_t want_kind, int32_t want_format, const 
   a.kv_indptr = kv_indptr;
   a.kv_indices = kv_indices;
   a.qo_indptr = (want_kind == MLA_KIND_PREFILL) ? qo_indptr : nullptr;
-  char* w = (char*)ws;
   a.wg_ptr = (const int32_t*)w;
   a.items = (const WorkItem*)(w + p->off_items);
   a.groups = (const SplitGroup*)(w + p->off_groups);
@@ -380,9 +457,17 @@ mla_status run(const mla_plan* p, int32_t want_kind, int32_t want_format, const 
   a.q_stride = lay.q_stride;
   a.qpe_stride = lay.qpe_stride;
   a.out_scale = out_scale;
+  if (sparse) {
+    a.sparse_len = (const int32_t*)(w + p->off_sp_count);
+    a.attn_sink = sparse->attn_sink;
+    a.max_logits = sparse->max_logits;
+    a.part_max = (float*)(w + p->off_part_max);
+  }
   hipEvent_t ev0 = t_ev_before, ev1 = t_ev_after;
   t_ev_before = t_ev_after = nullptr;
-  hipError_t e = mla::launch_attention(a, p->tile_mode, want_format == MLA_KV_FP8_E4M3_T128, stream, ev0, ev1);
+  hipError_t e = sparse ? mla::launch_sparse_attention(a, stream, ev0, ev1)
+                        : mla::launch_attention(a, p->tile_mode, want_format == MLA_KV_FP8_E4M3_T128, stream, ev0,
+                                                ev1);
   if (e != hipSuccess) return MLA_ERR_DEVICE;
   if (!p->groups.empty()) {
     e = mla::launch_combine(a, stream);
@@ -445,6 +530,21 @@ mla_status mla_prefill_packed(const mla_plan* p, const void* q, const void* kv_c
   return run(p, MLA_KIND_PREFILL, MLA_KV_BF16, q, q ? qb + mla::kDimCkv * 2 : nullptr, kv_cache,
              kv_cache ? kb + mla::kDimCkv * 2 : nullptr, nullptr, qo_indptr, kv_indptr, kv_indices, sm_scale, out,
              out_dtype, lse, ws, ws_bytes, stream, kPacked, out_scale);
+}
+
+mla_status mla_sparse_decode_fp8(const mla_plan* p, const void* q, const void* kv_cache, const int32_t* indices,
+                                 const int32_t* topk_length, const float* attn_sink, float sm_scale, void* out,
+                                 int32_t out_dtype, float* lse, float* max_logits, void* ws, size_t ws_bytes,
+                                 hipStream_t stream) {
+  Sparse sp;
+  sp.indices = indices;
+  sp.topk_length = topk_length;
+  sp.attn_sink = attn_sink;
+  sp.max_logits = max_logits;
+  const char* qb = (const char*)q;
+  return run(p, MLA_KIND_SPARSE_DECODE, MLA_KV_FP8_E4M3_T128, q, q ? qb + mla::kDimCkv * 2 : nullptr, nullptr, nullptr,
+             kv_cache, nullptr, nullptr, nullptr, sm_scale, out, out_dtype, lse, ws, ws_bytes, stream, kPacked, 1.f,
+             &sp);
 }
 
 mla_status mla_block_table_to_indices(const mla_plan* p, const int32_t* block_table, int32_t max_blocks,

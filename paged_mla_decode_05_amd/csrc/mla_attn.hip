@@ -66,6 +66,7 @@ constexpr int kLdsBytes = 2 * kStageBytes;                      // 147456
 constexpr float kRescaleSlack = 8.0f;                           // log2 units
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kLn2 = 0.69314718055994531f;
+constexpr float kLog2e = 1.44269504088896341f;
 
 // ---------------------------------------------------------------------------
 // LDS layout of one stage: ckv rows [64][1024 B] then kpe rows [64][128 B].
@@ -779,15 +780,31 @@ __device__ __forceinline__ int wide_dim(int cb, int q, int g) {
   return 128 * (cb >> 2) + 16 * (cb & 3) + (q < 2 ? 8 * q : 64 + 8 * (q - 2)) + 4 * g;
 }
 
-template <bool kPairedDims = false>
+// kSparse: token-sparse items also store their largest logit (m_top, log2
+// units) and final rows take the attention sink of their head into the
+// softmax denominator (one more logit with no value row).
+template <bool kPairedDims = false, bool kSparse = false>
 __device__ __forceinline__ void wide_epilogue(const AttnArgs& a, const WorkItem& it, WideState& st, const RowInfo& ri,
-                                              int rib, LDS_AS char* smem, int wave, int lane) {
+                                              int rib, LDS_AS char* smem, int wave, int lane, float m_top = 0.f) {
   const int g = lane >> 5;
   const int n = lane & 31;
   const float l_tot = sum_xor32(st.l_run);
   const bool empty = !(l_tot > 0.f);
-  const float inv = empty ? 0.f : (it.slot < 0 ? a.out_scale : 1.f) / l_tot;  // final rows carry the output scale
+  float den = l_tot;
+  if (kSparse && it.slot < 0 && a.attn_sink != nullptr && !empty) {
+    const int head = (it.row0 + rib) % a.num_heads;
+    den += fast_exp2(a.attn_sink[head] * kLog2e - st.m_run);
+  }
+  const float inv = empty ? 0.f : (it.slot < 0 ? a.out_scale : 1.f) / den;  // final rows carry the output scale
   if (ri.ok && g == 0) store_lse(a, it, ri, rib, empty ? kNegInf : (st.m_run + __log2f(l_tot)) * kLn2);
+  if (kSparse && ri.ok && g == 0) {
+    const float mx = empty ? kNegInf : m_top * kLn2;
+    if (it.slot >= 0) {
+      a.part_max[(size_t)it.slot * a.rows_per_block + rib] = mx;
+    } else if (a.max_logits != nullptr) {
+      a.max_logits[ri.qrow] = mx;
+    }
+  }
   if (a.out_bf16 || it.slot >= 0) {
     // bf16 rows: stage the wave's 32 rows in LDS (free after the loop; 16-byte
     // chunks XOR-swizzled by row), then store each row as one coalesced 1 KB
@@ -930,7 +947,7 @@ __device__ __forceinline__ bf16x8 codes8(uint32_t lo, uint32_t hi) {
   return h;
 }
 
-template <int kPC>
+template <int kPC, bool kSparse = false>
 __device__ void wide8_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* smem, int wave, int lane) {
   const int g = lane >> 5;
   const int n = lane & 31;
@@ -972,6 +989,7 @@ __device__ void wide8_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* s
   st.m_run = kNegInf;
   st.l_run = 0.f;
   st.o_live = false;
+  float m_top = kNegInf;  // token-sparse: the row's largest logit (log2 units)
 
   const int page_base = ld_const(a.kv_indptr, it.b);
   const int nstage = (it.tok1 - it.tok0 + kStageTokens - 1) / kStageTokens;
@@ -1074,6 +1092,7 @@ __device__ void wide8_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* s
         mx = fmaxf(mx, sv[r]);
       }
       mx = max_xor32(mx);
+      if (kSparse) m_top = fmaxf(m_top, mx);
       if (__builtin_amdgcn_ballot_w64(mx > st.m_run + kRescaleSlack) != 0) {
         const float m_new = fmaxf(st.m_run, mx);
         const float alpha = (st.m_run == kNegInf) ? 0.f : fast_exp2(st.m_run - m_new);
@@ -1129,7 +1148,7 @@ __device__ void wide8_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* s
     }
   }
   __syncthreads();  // every wave is done with the stage buffers before the epilogue stages rows there
-  wide_epilogue<true>(a, it, st, ri, rib, smem, wave, lane);
+  wide_epilogue<true, kSparse>(a, it, st, ri, rib, smem, wave, lane, m_top);
 }
 
 // ---------------------------------------------------------------------------
@@ -1667,7 +1686,7 @@ __device__ __forceinline__ int xcd_list(int b, int n) {
   return base + (b >> 3);
 }
 
-template <int kMode, int kPC, bool kFp8>
+template <int kMode, int kPC, bool kFp8, bool kSparse = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_attn_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem_raw[kFp8 ? kFp8LdsBytes : kLdsBytes];
@@ -1688,8 +1707,14 @@ void mla_attn_kernel(AttnArgs a) {
     it.kv_len = ld_const(ip, 5);
     it.q_len = ld_const(ip, 6);
     it.slot = ld_const(ip, 7);
+    if (kSparse) {
+      // the list's valid keys were counted on the device: pieces past them are empty
+      const int L = ld_const(a.sparse_len, it.b);
+      it.kv_len = L;
+      it.tok1 = max(it.tok0, min(it.tok1, L));
+    }
     if (kMode == 1 && kFp8) {
-      wide8_item<kPC>(a, it, smem, wave, lane);
+      wide8_item<kPC, kSparse>(a, it, smem, wave, lane);
     } else if (kMode == 1) {
       wide_item<kPC>(a, it, smem, wave, lane);
     } else {
@@ -1761,12 +1786,19 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(AttnArgs a) {
       }
     }
   }
-  const float inv = (W > 0.f) ? a.out_scale / W : 0.f;
   const int H = a.num_heads;
   const int q_start = a.qo_indptr ? ld_const(a.qo_indptr, g_b) : g_b;
   const int rr = g_row0 + r;
   const int qi = rr / H;
   const size_t qrow = (size_t)(q_start + qi) * H + (rr - qi * H);
+  float den = W;
+  if (a.attn_sink != nullptr && W > 0.f) den += __expf(a.attn_sink[rr - qi * H] - M);  // the sink's share
+  const float inv = (W > 0.f) ? a.out_scale / den : 0.f;
+  if (a.max_logits != nullptr && lane == 0) {
+    float mx = kNegInf;
+    for (int sp = 0; sp < nsplit; ++sp) mx = fmaxf(mx, a.part_max[row0 + (size_t)sp * stride]);
+    a.max_logits[qrow] = mx;
+  }
   if (a.out_bf16) {
     bf16x8 h;
 #pragma unroll
@@ -1819,6 +1851,58 @@ hipError_t launch_attention(const AttnArgs& a, int tile_mode, int kv_fp8, hipStr
   if (pc == kPageBig) return launch_mode<2, kPageBig>(a, kv_fp8, stream, t0, t1);
   if (pc == kPageMid) return launch_mode<2, kPageMid>(a, kv_fp8, stream, t0, t1);
   return launch_mode<2, kPageSmall>(a, kv_fp8, stream, t0, t1);
+}
+
+hipError_t launch_sparse_attention(const AttnArgs& a, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
+  if (a.num_wgs <= 0) return hipSuccess;
+  if (a.page_shift != 0 || a.sparse_len == nullptr) return hipErrorInvalidValue;
+  hipExtLaunchKernelGGL((mla_attn_kernel<1, kPageSmall, true, true>), dim3(a.num_wgs), dim3(256), 0, stream, t0, t1,
+                        0, a);
+  return hipGetLastError();
+}
+
+// Key lists of the token-sparse decode: one workgroup per query token
+// compacts its list (valid entries in order) with a ballot prefix count per
+// 256-entry chunk.
+__global__ __launch_bounds__(256) void mla_sparse_lists_kernel(const int32_t* __restrict__ indices, int32_t num_tokens,
+                                                               int32_t topk, const int32_t* __restrict__ topk_length,
+                                                               int64_t num_slots, int32_t* __restrict__ list,
+                                                               int32_t* __restrict__ count,
+                                                               int32_t* __restrict__ indptr) {
+  __shared__ int wave_n[4];
+  const int t = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = topk_length ? min(max(topk_length[t], 0), topk) : topk;
+  const int32_t* src = indices + (size_t)t * topk;
+  int32_t* dst = list + (size_t)t * topk;
+  int base = 0;
+  for (int c0 = 0; c0 < n; c0 += 256) {
+    const int k = c0 + (int)threadIdx.x;
+    const int32_t v = k < n ? src[k] : -1;
+    const bool ok = k < n && v >= 0 && (int64_t)v < num_slots;
+    const uint64_t bal = __ballot(ok);
+    if (lane == 0) wave_n[wave] = __popcll(bal);
+    __syncthreads();
+    int off = base;
+    for (int w = 0; w < wave; ++w) off += wave_n[w];
+    if (ok) dst[off + __popcll(bal & ((1ull << lane) - 1))] = v;
+    base += wave_n[0] + wave_n[1] + wave_n[2] + wave_n[3];
+    __syncthreads();  // wave_n is rewritten by the next chunk
+  }
+  if (threadIdx.x == 0) {
+    count[t] = base;
+    indptr[t] = t * topk;
+    if (t == num_tokens - 1) indptr[num_tokens] = num_tokens * topk;
+  }
+}
+
+hipError_t launch_sparse_lists(const int32_t* indices, int32_t num_tokens, int32_t topk, const int32_t* topk_length,
+                               int64_t num_slots, int32_t* list, int32_t* count, int32_t* indptr,
+                               hipStream_t stream) {
+  if (num_tokens <= 0) return hipSuccess;
+  hipLaunchKernelGGL(mla_sparse_lists_kernel, dim3(num_tokens), dim3(256), 0, stream, indices, num_tokens, topk,
+                     topk_length, num_slots, list, count, indptr);
+  return hipGetLastError();
 }
 
 // Page list of the dense block-table interface: one workgroup per request

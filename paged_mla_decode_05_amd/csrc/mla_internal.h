@@ -74,6 +74,12 @@ struct AttnArgs {
   int32_t q_stride;        // elements between consecutive (token, head) rows of q_nope (512 or 576)
   int32_t qpe_stride;      // elements between consecutive rows of q_pe (64 or 576)
   float out_scale;         // factor applied to the final output rows (1: none)
+  // token-sparse decode (all null otherwise): each "request" is one query
+  // token whose key list (page size 1) was compacted on the device
+  const int32_t* sparse_len;  // [requests] valid keys of each list
+  const float* attn_sink;     // [H] sink logit per head (natural-log units), or null
+  float* max_logits;          // [rows_total, H] largest logit per row (natural units), or null
+  float* part_max;            // [slots][rows_per_block] largest logit of each partial row
 };
 
 // Launchers (mla_attn.hip).  They only enqueue on `stream`; return hipError_t.
@@ -81,6 +87,16 @@ struct AttnArgs {
 // at the start and end of its execution (null: none).
 hipError_t launch_attention(const AttnArgs& a, int tile_mode, int kv_fp8, hipStream_t stream, hipEvent_t t0,
                             hipEvent_t t1);
+// Token-sparse decode over fp8 records (WIDE tile, page size 1, key lists
+// bounded by a.sparse_len).
+hipError_t launch_sparse_attention(const AttnArgs& a, hipStream_t stream, hipEvent_t t0, hipEvent_t t1);
+// Stable compaction of each query token's key list: entries k < n_t (n_t =
+// min(topk_length[t], topk), or topk when topk_length is null) with
+// 0 <= idx < num_slots are copied, in order, to list[t * topk ...];
+// count[t] = their number; indptr[t] = t * topk (t <= num_tokens).
+hipError_t launch_sparse_lists(const int32_t* indices, int32_t num_tokens, int32_t topk,
+                               const int32_t* topk_length, int64_t num_slots, int32_t* list, int32_t* count,
+                               int32_t* indptr, hipStream_t stream);
 hipError_t launch_combine(const AttnArgs& a, hipStream_t stream);
 // kv_indices[kv_indptr[b] + j] = block_table[b * max_blocks + j] for j < kv_indptr[b+1] - kv_indptr[b].
 hipError_t launch_block_table(const int32_t* block_table, int32_t batch, int32_t max_blocks,

@@ -269,3 +269,29 @@ def test_quad_mode_groups_siblings(mla):
     assert all(it["nrows"] == 128 for it in items)
     # a request mostly fits one work list: few split groups
     assert plan.num_split_groups <= 48
+
+
+def test_sparse_plan_and_call_errors(mla):
+    lib = mla.load_library()
+    sp = mla.mla_sparse_plan_create(6, 128, 1000, 300, num_cus=4)
+    items = sp.work_items().numpy()
+    # every query token's topk entries are covered once, in stage-aligned pieces
+    for t in range(6):
+        mine = sorted((int(r[3]), int(r[4])) for r in items if r[0] == t)
+        assert mine[0][0] == 0 and mine[-1][1] == 300
+        assert all(a[1] == b[0] for a, b in zip(mine, mine[1:]))
+        assert all(a % 64 == 0 for a, _ in mine)
+    assert sp.workspace_bytes >= 6 * 300 * 4
+    dec = mla.mla_plan_create(0, 2, 16, 64, 4, [10, 70], [0, 1, 3], num_cus=4, kv_format=1)
+    fake = ctypes.c_void_p(0x1000)
+    tail = (0.1, fake, 0, fake, fake, fake, 1 << 24, None)
+    assert lib.mla_sparse_decode_fp8(dec.handle, fake, fake, fake, None, None, *tail) == -4
+    assert lib.mla_decode_fp8(sp.handle, *[fake] * 5, 0.1, fake, 0, fake, fake, 1 << 24, None) == -4
+    assert lib.mla_sparse_decode_fp8(sp.handle, fake, fake, None, None, None, *tail) == -1
+    assert lib.mla_sparse_decode_fp8(sp.handle, None, fake, fake, None, None, *tail) == -1
+    assert lib.mla_sparse_decode_fp8(sp.handle, fake, fake, fake, None, None, 0.1, fake, 0, fake, fake, fake, 64,
+                                     None) == -3
+    h = ctypes.c_void_p()
+    for args in ((-1, 128, 10, 8), (4, 0, 10, 8), (4, 128, 0, 8), (4, 128, 10, 0)):
+        assert lib.mla_sparse_plan_create(ctypes.byref(h), *args, 4, 0) == -1
+    assert lib.mla_sparse_plan_create(ctypes.byref(h), 1 << 20, 128, 10, 1 << 12, 4, 0) == -1
