@@ -297,45 +297,54 @@ def setup_dense(args, mla, dev):
 
 
 def setup_sparse(args, mla, dev):
-    """Plan, inputs and step of a token-sparse fp8 workload.
+    """Plan, inputs and step of a token-sparse workload (fp8 records, or bf16
+    KV rows for the sparse prefill form).
 
-    Algorithmic units: each valid (query token, list entry) reads one
-    656-byte record and costs 2176 flops per head; the lists themselves
-    (4 bytes per entry), q (1152 B per row), out, lse and max_logits count
-    as bytes too."""
+    Algorithmic units: each valid (query token, list entry) costs 2176 flops
+    per head; bytes are the distinct key rows the lists name (656 B per fp8
+    record, 1152 B per bf16 row: a row named by several lists is needed once
+    per launch), the lists (4 B per entry), q (1152 B per row), out, lse and
+    max_logits."""
     import numpy as np
     import torch
 
-    from workloads import make_sparse_workload
+    from workloads import SPARSE_PREFILL_CONFIGS, make_sparse_prefill_workload, make_sparse_workload
 
     log(f"bench: generating {args.config} on {dev}")
-    w = make_sparse_workload(args.config, device=dev, poison=False)
+    bf16_rows = args.config in SPARSE_PREFILL_CONFIGS
+    if bf16_rows:
+        w = make_sparse_prefill_workload(args.config, device=dev)
+        cache, row_bytes, fmt = w.kv, KV_BYTES["bf16"], mla.MLA_KV_BF16
+    else:
+        w = make_sparse_workload(args.config, device=dev, poison=False)
+        cache, row_bytes, fmt = w.kv_fp8, KV_BYTES["fp8"], mla.MLA_KV_FP8_E4M3_T128
     idx = w.indices.numpy().astype(np.int64)
     lim = idx.shape[1] if w.topk_length is None else w.topk_length.numpy()[:, None]
     valid = (idx >= 0) & (idx < w.num_slots) & (np.arange(idx.shape[1])[None, :] < lim)
     n_valid = valid.sum(axis=1)
     H, T = w.num_heads, w.tokens
     flops = int(n_valid.sum()) * H * FLOPS_PER_ROW_KEY
-    live_kv = int(n_valid.sum()) * KV_BYTES["fp8"]
+    live_kv = int(np.unique(idx[valid]).size) * row_bytes
     out_bytes = 4 if str(w.out_dtype).endswith("float32") else 2
     bytes_alg = live_kv + T * H * (576 * 2 + 512 * out_bytes + 4 + 4) + idx.size * 4
     t_plan = time.perf_counter()
-    plan = mla.mla_sparse_plan_create(T, H, w.num_slots, w.topk)
+    plan = mla.mla_sparse_plan_create(T, H, w.num_slots, w.topk, kv_format=fmt)
     plan_ms = (time.perf_counter() - t_plan) * 1e3
     indices = w.indices.to(dev)
     reps = max(1, min(16, math.ceil(args.rotate_bytes / max(live_kv, 1))))
-    pools = [w.kv_fp8] + [w.kv_fp8.clone() for _ in range(reps - 1)]
+    pools = [cache] + [cache.clone() for _ in range(reps - 1)]
     out = torch.empty((T, H, 512), dtype=w.out_dtype, device=dev)
     lse = torch.empty((T, H), dtype=torch.float32, device=dev)
     mx = torch.empty((T, H), dtype=torch.float32, device=dev)
     ws = plan.workspace(dev)
     log(f"bench: {plan.num_work_items} work items on {plan.workgroup_ptr().numel() - 1} workgroups, "
         f"{plan.num_split_groups} split groups, workspace {plan.workspace_bytes / 1e6:.1f} MB, "
-        f"{reps} pool replicas of {w.kv_fp8.numel() / 1e6:.0f} MB, {int(n_valid.sum())} valid entries")
+        f"{reps} pool replicas of {cache.numel() * cache.element_size() / 1e6:.0f} MB, "
+        f"{int(n_valid.sum())} valid entries")
+    run = mla.mla_sparse_prefill if bf16_rows else mla.mla_sparse_decode_fp8
 
     def step(i):
-        mla.mla_sparse_decode_fp8(plan, w.q, pools[i % reps], indices, w.sm_scale, out=out, lse=lse,
-                                  max_logits=mx, workspace=ws)
+        run(plan, w.q, pools[i % reps], indices, w.sm_scale, out=out, lse=lse, max_logits=mx, workspace=ws)
 
     def cpu(secs):
         import oracle
@@ -346,12 +355,13 @@ def setup_sparse(args, mla, dev):
             threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
         except Exception:  # pragma: no cover
             threads = os.cpu_count()
-        q_host, kv_host = w.q.cpu(), w.kv_fp8.cpu()
+        q_host, kv_host = w.q.cpu(), cache.cpu()
+        ref = oracle.mla_sparse_prefill_ref if bf16_rows else oracle.mla_sparse_decode_fp8_ref
         done, n = 0.0, 0
         t0 = time.perf_counter()
         while time.perf_counter() - t0 < secs:
             t = n % T
-            oracle.mla_sparse_decode_fp8_ref(q_host, kv_host, w.indices, w.sm_scale, tokens=[t])
+            ref(q_host, kv_host, w.indices, w.sm_scale, tokens=[t])
             done += int(n_valid[t]) * H * FLOPS_PER_ROW_KEY
             n += 1
         dt = time.perf_counter() - t0
@@ -359,12 +369,17 @@ def setup_sparse(args, mla, dev):
                 "sample": f"{n} query-token evaluations of {w.name} ({n / T:.2f} passes over its {T} tokens), "
                           f"{dt:.1f} s wall, float64 NumPy"}
 
-    config = {"workload": w.name, "batch": w.batch, "s_q": w.s_q, "num_qo_heads": H, "topk": w.topk,
-              "head_dim_ckv": 512, "head_dim_kpe": 64, "kv_format": "fp8", "page_size": w.page_size,
-              "valid_entries": int(n_valid.sum()), "rows": T, "parallelism": "single GPU"}
+    if bf16_rows:
+        config = {"workload": w.name, "s_q": T, "s_kv": w.num_slots, "num_qo_heads": H, "topk": w.topk,
+                  "head_dim_ckv": 512, "head_dim_kpe": 64, "kv_format": "bf16"}
+    else:
+        config = {"workload": w.name, "batch": w.batch, "s_q": w.s_q, "num_qo_heads": H, "topk": w.topk,
+                  "head_dim_ckv": 512, "head_dim_kpe": 64, "kv_format": "fp8", "page_size": w.page_size}
+    config.update({"valid_entries": int(n_valid.sum()), "distinct_key_rows": live_kv // row_bytes, "rows": T,
+                   "parallelism": "single GPU"})
     return {"step": step, "flops": flops, "live_kv": live_kv, "bytes_alg": bytes_alg, "plan_ms": plan_ms,
-            "config": config, "kernel": "mla_attn_kernel (token-sparse fp8)",
-            "dtype": "fp8-e4m3 cache, bf16 math", "cpu_baseline": cpu}
+            "config": config, "kernel": "mla_attn_kernel (token-sparse " + ("bf16)" if bf16_rows else "fp8)"),
+            "dtype": "bf16" if bf16_rows else "fp8-e4m3 cache, bf16 math", "cpu_baseline": cpu}
 
 
 def main():
@@ -404,7 +419,7 @@ def main():
     import torch
 
     import paged_mla_decode_05_amd as mla
-    from workloads import SPARSE_CONFIGS
+    from workloads import SPARSE_CONFIGS, SPARSE_PREFILL_CONFIGS
 
     if not os.path.exists(mla.lib_path()):
         import __graft_entry__
@@ -412,7 +427,7 @@ def main():
         __graft_entry__.build()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    setup = setup_sparse if args.config in SPARSE_CONFIGS else setup_dense
+    setup = setup_sparse if (args.config in SPARSE_CONFIGS or args.config in SPARSE_PREFILL_CONFIGS) else setup_dense
     S = setup(args, mla, dev)
     step, flops, live_kv, bytes_alg, plan_ms = S["step"], S["flops"], S["live_kv"], S["bytes_alg"], S["plan_ms"]
 

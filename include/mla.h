@@ -238,9 +238,11 @@ mla_status mla_prefill_packed(const mla_plan* plan, const void* q, const void* k
 mla_status mla_block_table_to_indices(const mla_plan* plan, const int32_t* block_table, int32_t max_blocks,
                                       const int32_t* kv_indptr, int32_t* kv_indices, hipStream_t stream);
 
-/* Token-sparse decode over the 656-byte fp8 record cache (DSA): FlashMLA
- * digest, "flash_mla_with_kvcache (Sparse Attention with FP8 KV Cache)" and
- * "Sparse Attention Decoding with KV Cache"; the formula of "Sparse MLA
+/* Token-sparse attention (DSA) over the 656-byte fp8 record cache
+ * (mla_sparse_decode_fp8: FlashMLA digest, "flash_mla_with_kvcache (Sparse
+ * Attention with FP8 KV Cache)" and "Sparse Attention Decoding with KV
+ * Cache") or over bf16 576-wide KV rows (mla_sparse_prefill: "Sparse MLA
+ * Prefill Kernel", flash_mla_sparse_fwd); the formula of "Sparse MLA
  * Prefill Kernel".  Every query token t has its own list of key slots;
  * for each head h:
  *   s_j = sm_scale * (q[t,h,:512] . nope_j + q[t,h,512:] . rope_j) over the
@@ -252,10 +254,13 @@ mla_status mla_block_table_to_indices(const mla_plan* plan, const int32_t* block
  *
  * mla_sparse_plan_create: the schedule for num_tokens query tokens of
  * num_heads heads, each with a list of topk entries into a pool of
- * num_slots records (num_blocks * block_size).  Work is balanced as if every
+ * num_slots key rows (fp8: num_blocks * block_size records), for kv_format
+ * MLA_KV_FP8_E4M3_T128 (mla_sparse_decode_fp8) or MLA_KV_BF16
+ * (mla_sparse_prefill).  Work is balanced as if every
  * entry were valid.  num_cus = 0 asks the current device; force_splits > 0
  * cuts every list into that many chunks (testing).  Errors:
- * MLA_ERR_INVALID_ARGUMENT (sizes < 1 where 1 is needed, force_splits < 0),
+ * MLA_ERR_INVALID_ARGUMENT (sizes < 1 where 1 is needed, force_splits < 0,
+ * num_tokens * topk >= 2^31), MLA_ERR_UNSUPPORTED (another kv_format),
  * MLA_ERR_DEVICE (device query failed).  The workspace holds the compacted
  * lists; its size is mla_plan_workspace_bytes and it is uploaded with
  * mla_plan_upload like any plan's.
@@ -273,16 +278,25 @@ mla_status mla_block_table_to_indices(const mla_plan* plan, const int32_t* block
  *   attn_sink  [H] fp32 or NULL: per-head sink logit (natural-log units)
  *   out        [num_tokens, H, 512] bf16 or fp32 (out_dtype); lse and
  *              max_logits [num_tokens, H] fp32 (max_logits may be NULL)
+ * mla_sparse_prefill takes the same arguments with
+ *   kv         [num_slots, 576] bf16 rows (latent dims then rope dims; the
+ *              page's kv [s_kv, h_kv = 1, 576]), indices into its rows
+ *   q          [num_tokens, H, 576] bf16 (the page's q [s_q, H, 576])
  * The lists are compacted into the workspace on `stream` first, so the
  * workspace may not be shared by calls that overlap.  Errors as for
- * mla_decode; a plan not made by mla_sparse_plan_create is
- * MLA_ERR_PLAN_MISMATCH.  Allocates nothing and never synchronises.     */
+ * mla_decode; a plan not made by mla_sparse_plan_create for the call's
+ * cache format is MLA_ERR_PLAN_MISMATCH.  Allocates nothing and never
+ * synchronises.                                                          */
 mla_status mla_sparse_plan_create(mla_plan** plan, int32_t num_tokens, int32_t num_heads, int32_t num_slots,
-                                  int32_t topk, int32_t num_cus, int32_t force_splits);
+                                  int32_t topk, int32_t kv_format, int32_t num_cus, int32_t force_splits);
 mla_status mla_sparse_decode_fp8(const mla_plan* plan, const void* q, const void* kv_cache, const int32_t* indices,
                                  const int32_t* topk_length, const float* attn_sink, float sm_scale, void* out,
                                  int32_t out_dtype, float* lse, float* max_logits, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream);
+mla_status mla_sparse_prefill(const mla_plan* plan, const void* q, const void* kv, const int32_t* indices,
+                              const int32_t* topk_length, const float* attn_sink, float sm_scale, void* out,
+                              int32_t out_dtype, float* lse, float* max_logits, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
 
 /* Diagnostics for timing: the next run call made on this host thread has
  * the attention kernel's own dispatch record `before` when the kernel

@@ -10,7 +10,8 @@ Names follow the C ABI: :func:`mla_plan_create`, :func:`mla_decode`,
 :func:`mla_prefill`, :func:`mla_decode_fp8`, the concatenated-layout
 :func:`mla_decode_packed` / :func:`mla_prefill_packed`,
 :func:`mla_block_table_to_indices`, and the token-sparse
-:func:`mla_sparse_plan_create` / :func:`mla_sparse_decode_fp8`.
+:func:`mla_sparse_plan_create` / :func:`mla_sparse_decode_fp8` /
+:func:`mla_sparse_prefill`.
 """
 
 from ._binding import (  # noqa: F401
@@ -28,6 +29,7 @@ from ._binding import (  # noqa: F401
     mla_record_attention_events,
     mla_sparse_decode_fp8,
     mla_sparse_plan_create,
+    mla_sparse_prefill,
     MLA_KIND_DECODE,
     MLA_KIND_PREFILL,
     MLA_KIND_SPARSE_DECODE,

@@ -95,10 +95,12 @@ def load_library():
         L.mla_prefill_packed.restype = i32
         L.mla_block_table_to_indices.argtypes = [vp, vp, i32, vp, vp, vp]
         L.mla_block_table_to_indices.restype = i32
-        L.mla_sparse_plan_create.argtypes = [ctypes.POINTER(vp), i32, i32, i32, i32, i32, i32]
+        L.mla_sparse_plan_create.argtypes = [ctypes.POINTER(vp), i32, i32, i32, i32, i32, i32, i32]
         L.mla_sparse_plan_create.restype = i32
         L.mla_sparse_decode_fp8.argtypes = [vp, vp, vp, vp, vp, vp, f32, vp, i32, vp, vp, vp, sz, vp]
         L.mla_sparse_decode_fp8.restype = i32
+        L.mla_sparse_prefill.argtypes = [vp, vp, vp, vp, vp, vp, f32, vp, i32, vp, vp, vp, sz, vp]
+        L.mla_sparse_prefill.restype = i32
         L.mla_record_attention_events.argtypes = [vp, vp]
         L.mla_record_attention_events.restype = i32
         L.mla_status_str.argtypes = [i32]
@@ -220,16 +222,17 @@ def mla_plan_create(kind: int, batch: int, num_heads: int, page_size: int, num_p
     return Plan(h, d, kl, ki, qo)
 
 
-def mla_sparse_plan_create(num_tokens: int, num_heads: int, num_slots: int, topk: int, num_cus: int = 0,
-                           force_splits: int = 0) -> Plan:
-    """Host plan of the token-sparse fp8 decode: num_tokens query tokens, each
-    with a list of topk entries into num_slots records (see include/mla.h)."""
+def mla_sparse_plan_create(num_tokens: int, num_heads: int, num_slots: int, topk: int,
+                           kv_format: int = MLA_KV_FP8_E4M3_T128, num_cus: int = 0, force_splits: int = 0) -> Plan:
+    """Host plan of the token-sparse attention: num_tokens query tokens, each
+    with a list of topk entries into num_slots key rows (fp8 records for
+    mla_sparse_decode_fp8, bf16 rows for mla_sparse_prefill; see include/mla.h)."""
     L = load_library()
     h = ctypes.c_void_p()
-    _check(L.mla_sparse_plan_create(ctypes.byref(h), num_tokens, num_heads, num_slots, topk, num_cus, force_splits),
-           "mla_sparse_plan_create")
+    _check(L.mla_sparse_plan_create(ctypes.byref(h), num_tokens, num_heads, num_slots, topk, kv_format, num_cus,
+                                    force_splits), "mla_sparse_plan_create")
     d = _Desc(kind=MLA_KIND_SPARSE_DECODE, batch=num_tokens, num_qo_heads=num_heads, head_dim_ckv=_DIM_CKV,
-              head_dim_kpe=_DIM_KPE, page_size=1, num_pages=num_slots, kv_format=MLA_KV_FP8_E4M3_T128, causal=0,
+              head_dim_kpe=_DIM_KPE, page_size=1, num_pages=num_slots, kv_format=kv_format, causal=0,
               num_cus=num_cus, max_splits=0, force_splits=force_splits, tile_mode=MLA_TILE_WIDE)
     plan = Plan(h, d, None, None, None)
     plan.topk = topk
@@ -243,12 +246,24 @@ def mla_sparse_decode_fp8(plan: Plan, q, kv_cache, indices, sm_scale: float, top
     slots (-1 / out of range: skipped), optional topk_length [T] int32 and
     attn_sink [H] fp32.  Returns (out [T, H, 512], lse [T, H], max_logits [T, H])."""
     L = load_library()
-    T, H, topk = plan.desc.batch, plan.desc.num_qo_heads, plan.topk
-    qq = _dev(q, "q", torch.bfloat16, (T, H, _DIM_CKV + _DIM_KPE))
+    if plan.desc.kv_format != MLA_KV_FP8_E4M3_T128:
+        raise ValueError("mla_sparse_decode_fp8 needs a plan made with kv_format=MLA_KV_FP8_E4M3_T128")
     if not isinstance(kv_cache, torch.Tensor) or kv_cache.shape[-1] != _FP8_RECORD or \
             kv_cache.numel() // _FP8_RECORD != plan.desc.num_pages:
         raise ValueError(f"kv_cache must hold {plan.desc.num_pages} records of {_FP8_RECORD} bytes")
     kv = _dev(kv_cache, "kv_cache", torch.uint8)
+    qq, ix, tl, sk, out, lse, code, max_logits, mx = _sparse_extras(plan, q, indices, topk_length, attn_sink, out,
+                                                                     lse, max_logits, out_dtype)
+    ws = plan.workspace(q.device) if workspace is None else workspace
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(L.mla_sparse_decode_fp8(plan.handle, qq, kv, ix, tl, sk, float(sm_scale), out.data_ptr(), code,
+                                   lse.data_ptr(), mx, ws.data_ptr(), ws.numel(), stream), "mla_sparse_decode_fp8")
+    return out, lse, max_logits
+
+
+def _sparse_extras(plan, q, indices, topk_length, attn_sink, out, lse, max_logits, out_dtype):
+    T, H, topk = plan.desc.batch, plan.desc.num_qo_heads, plan.topk
+    qq = _dev(q, "q", torch.bfloat16, (T, H, _DIM_CKV + _DIM_KPE))
     ix = _dev(indices, "indices", torch.int32, (T, topk))
     tl = _dev(topk_length, "topk_length", torch.int32, (T,)) if topk_length is not None else None
     sk = _dev(attn_sink, "attn_sink", torch.float32, (H,)) if attn_sink is not None else None
@@ -256,10 +271,28 @@ def mla_sparse_decode_fp8(plan: Plan, q, kv_cache, indices, sm_scale: float, top
     if max_logits is None:
         max_logits = torch.empty((T, H), dtype=torch.float32, device=q.device)
     mx = _dev(max_logits, "max_logits", torch.float32, (T, H))
+    return qq, ix, tl, sk, out, lse, code, max_logits, mx
+
+
+def mla_sparse_prefill(plan: Plan, q, kv, indices, sm_scale: float, topk_length=None, attn_sink=None, out=None,
+                       lse=None, max_logits=None, out_dtype=torch.bfloat16, workspace=None):
+    """Token-sparse attention over bf16 KV rows (FlashMLA's sparse prefill):
+    q [s_q, H, 576] bf16, kv [s_kv, 576] (or [s_kv, 1, 576]) bf16, indices
+    [s_q, topk] int32 (-1 / out of range: skipped), optional topk_length [s_q]
+    and attn_sink [H].  Returns (out [s_q, H, 512], lse [s_q, H], max_logits [s_q, H])."""
+    L = load_library()
+    if plan.desc.kv_format != MLA_KV_BF16:
+        raise ValueError("mla_sparse_prefill needs a plan made with kv_format=MLA_KV_BF16")
+    width = _DIM_CKV + _DIM_KPE
+    if not isinstance(kv, torch.Tensor) or kv.shape[-1] != width or kv.numel() // width != plan.desc.num_pages:
+        raise ValueError(f"kv must hold {plan.desc.num_pages} rows of {width} bf16 values")
+    k = _dev(kv, "kv", torch.bfloat16)
+    qq, ix, tl, sk, out, lse, code, max_logits, mx = _sparse_extras(plan, q, indices, topk_length, attn_sink, out,
+                                                                     lse, max_logits, out_dtype)
     ws = plan.workspace(q.device) if workspace is None else workspace
     stream = torch.cuda.current_stream(q.device).cuda_stream
-    _check(L.mla_sparse_decode_fp8(plan.handle, qq, kv, ix, tl, sk, float(sm_scale), out.data_ptr(), code,
-                                   lse.data_ptr(), mx, ws.data_ptr(), ws.numel(), stream), "mla_sparse_decode_fp8")
+    _check(L.mla_sparse_prefill(plan.handle, qq, k, ix, tl, sk, float(sm_scale), out.data_ptr(), code,
+                                lse.data_ptr(), mx, ws.data_ptr(), ws.numel(), stream), "mla_sparse_prefill")
     return out, lse, max_logits
 
 

@@ -296,11 +296,12 @@ mla_status mla_plan_create(mla_plan** out, const mla_plan_desc* d, const int32_t
 }
 
 mla_status mla_sparse_plan_create(mla_plan** out, int32_t num_tokens, int32_t num_heads, int32_t num_slots,
-                                  int32_t topk, int32_t num_cus, int32_t force_splits) {
+                                  int32_t topk, int32_t kv_format, int32_t num_cus, int32_t force_splits) {
   if (!out) return MLA_ERR_INVALID_ARGUMENT;
   *out = nullptr;
   if (num_tokens < 0 || num_heads < 1 || num_slots < 1 || topk < 1 || num_cus < 0 || force_splits < 0)
     return MLA_ERR_INVALID_ARGUMENT;
+  if (kv_format != MLA_KV_BF16 && kv_format != MLA_KV_FP8_E4M3_T128) return MLA_ERR_UNSUPPORTED;
   if ((int64_t)num_tokens * topk > ((int64_t)1 << 31) - 1) return MLA_ERR_INVALID_ARGUMENT;
   if (num_cus == 0) {
     int dev = 0;
@@ -320,7 +321,7 @@ mla_status mla_sparse_plan_create(mla_plan** out, int32_t num_tokens, int32_t nu
   d.head_dim_kpe = mla::kDimKpe;
   d.page_size = 1;
   d.num_pages = num_slots;
-  d.kv_format = MLA_KV_FP8_E4M3_T128;
+  d.kv_format = kv_format;
   d.num_cus = num_cus;
   d.force_splits = force_splits;
   d.tile_mode = MLA_TILE_WIDE;
@@ -545,6 +546,22 @@ mla_status mla_sparse_decode_fp8(const mla_plan* p, const void* q, const void* k
   return run(p, MLA_KIND_SPARSE_DECODE, MLA_KV_FP8_E4M3_T128, q, q ? qb + mla::kDimCkv * 2 : nullptr, nullptr, nullptr,
              kv_cache, nullptr, nullptr, nullptr, sm_scale, out, out_dtype, lse, ws, ws_bytes, stream, kPacked, 1.f,
              &sp);
+}
+
+mla_status mla_sparse_prefill(const mla_plan* p, const void* q, const void* kv, const int32_t* indices,
+                              const int32_t* topk_length, const float* attn_sink, float sm_scale, void* out,
+                              int32_t out_dtype, float* lse, float* max_logits, void* ws, size_t ws_bytes,
+                              hipStream_t stream) {
+  Sparse sp;
+  sp.indices = indices;
+  sp.topk_length = topk_length;
+  sp.attn_sink = attn_sink;
+  sp.max_logits = max_logits;
+  const char* qb = (const char*)q;
+  const char* kb = (const char*)kv;
+  return run(p, MLA_KIND_SPARSE_DECODE, MLA_KV_BF16, q, q ? qb + mla::kDimCkv * 2 : nullptr, kv,
+             kv ? kb + mla::kDimCkv * 2 : nullptr, nullptr, nullptr, nullptr, nullptr, sm_scale, out, out_dtype, lse,
+             ws, ws_bytes, stream, kPacked, 1.f, &sp);
 }
 
 mla_status mla_block_table_to_indices(const mla_plan* p, const int32_t* block_table, int32_t max_blocks,

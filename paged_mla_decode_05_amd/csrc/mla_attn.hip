@@ -593,6 +593,7 @@ struct WideState {
   float m_run;    // running max (log2 units), per row
   float l_run;    // running sum of this lane's keys
   bool o_live;    // wave-uniform: a P.V has run (before that O is zero and needs no rescale)
+  float m_top;    // token-sparse items: the row's largest logit so far (log2 units)
 };
 
 // Value fences for hand-interleaving VALU work into an MFMA stream: code
@@ -611,7 +612,7 @@ struct WideSoftmax {
   float mref = 0.f;
 };
 
-template <int kPC, bool kPrefetch, class Loader>
+template <int kPC, bool kPrefetch, bool kSparse = false, class Loader>
 __device__ __forceinline__ void wide_stage(const AttnArgs& a, const bf16x8 (&qf)[36], WideState& st,
                                            const LDS_AS char* __restrict__ cur, int stage_tok, int bound,
                                            const int (&kb)[8], const int (&pb)[4], const int (&vb)[8],
@@ -641,6 +642,7 @@ __device__ __forceinline__ void wide_stage(const AttnArgs& a, const bf16x8 (&qf)
   };
   auto sm_decide = [&](WideSoftmax& sm) {  // row max over the sub-tile; raise the running max if needed
     sm.mx = max_xor32(sm.mx);
+    if (kSparse) st.m_top = fmaxf(st.m_top, sm.mx);
     sm.raise = __builtin_amdgcn_ballot_w64(sm.mx > st.m_run + kRescaleSlack) != 0;
     if (sm.raise) {
       const float m_new = fmaxf(st.m_run, sm.mx);
@@ -749,7 +751,7 @@ __device__ __forceinline__ void wide_stage(const AttnArgs& a, const bf16x8 (&qf)
   }
 }
 
-template <int kPC>
+template <int kPC, bool kSparse = false>
 __device__ __forceinline__ void wide_body(const AttnArgs& a, const bf16x8 (&qf)[36], WideState& st,
                                           const LDS_AS char* __restrict__ cur, LDS_AS char* __restrict__ nxt,
                                           bool prefetch, int page_base, int next_tok, int tok_end,
@@ -762,7 +764,7 @@ __device__ __forceinline__ void wide_body(const AttnArgs& a, const bf16x8 (&qf)[
   StageLoader<kPC> ld;
   ld.begin(a, nxt, page_base, prefetch ? next_tok : stage_tok, tok_end, wave, page_hint);
   ld.on = __builtin_amdgcn_readfirstlane(prefetch ? ~0u : 0u);
-  wide_stage<kPC, true>(a, qf, st, cur, stage_tok, bound, kb, pb, vb, lane >> 5, ld, wave);
+  wide_stage<kPC, true, kSparse>(a, qf, st, cur, stage_tok, bound, kb, pb, vb, lane >> 5, ld, wave);
   static_assert(StageLoader<kPC>::kSlices == 18, "two sub-tiles of 9 slices");
 }
 
@@ -847,7 +849,7 @@ __device__ __forceinline__ void wide_epilogue(const AttnArgs& a, const WorkItem&
   }
 }
 
-template <int kPC>
+template <int kPC, bool kSparse = false>
 __device__ void wide_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* smem, int wave, int lane) {
   const int g = lane >> 5;   // lane half
   const int n = lane & 31;   // row within the wave (S^T / O^T column)
@@ -889,6 +891,7 @@ __device__ void wide_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* sm
   st.m_run = kNegInf;
   st.l_run = 0.f;
   st.o_live = false;
+  st.m_top = kNegInf;
 
   const int page_base = ld_const(a.kv_indptr, it.b);
   const int nstage = (it.tok1 - it.tok0 + kStageTokens - 1) / kStageTokens;
@@ -903,7 +906,7 @@ __device__ void wide_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* sm
     const int pg_after = page_at(s + 2 < nstage ? s + 2 : 0);
     wait_vmcnt<0>();
     __syncthreads();
-    wide_body<kPC>(a, qf, st, smem + (s & 1) * kStageBytes, smem + ((s + 1) & 1) * kStageBytes,
+    wide_body<kPC, kSparse>(a, qf, st, smem + (s & 1) * kStageBytes, smem + ((s + 1) & 1) * kStageBytes,
                    s + 1 < nstage, page_base, it.tok0 + (s + 1 < nstage ? s + 1 : 0) * kStageTokens, it.tok1,
                    it.tok0 + s * kStageTokens, bound, kb, pb, vb, wave, lane, pg_next);
     // no barrier here: the buffer of stage s is refilled during stage s + 1,
@@ -912,7 +915,7 @@ __device__ void wide_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* sm
     pg_next = pg_after;
   }
   __syncthreads();  // every wave is done with the last stage before the epilogue stages rows over it
-  wide_epilogue(a, it, st, ri, rib, smem, wave, lane);
+  wide_epilogue<false, kSparse>(a, it, st, ri, rib, smem, wave, lane, st.m_top);
 }
 
 // ---------------------------------------------------------------------------
@@ -1716,7 +1719,7 @@ void mla_attn_kernel(AttnArgs a) {
     if (kMode == 1 && kFp8) {
       wide8_item<kPC, kSparse>(a, it, smem, wave, lane);
     } else if (kMode == 1) {
-      wide_item<kPC>(a, it, smem, wave, lane);
+      wide_item<kPC, kSparse>(a, it, smem, wave, lane);
     } else {
       narrow_item<kPC, kFp8>(a, it, smem, wave, lane);
     }
@@ -1856,8 +1859,13 @@ hipError_t launch_attention(const AttnArgs& a, int tile_mode, int kv_fp8, hipStr
 hipError_t launch_sparse_attention(const AttnArgs& a, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
   if (a.num_wgs <= 0) return hipSuccess;
   if (a.page_shift != 0 || a.sparse_len == nullptr) return hipErrorInvalidValue;
-  hipExtLaunchKernelGGL((mla_attn_kernel<1, kPageSmall, true, true>), dim3(a.num_wgs), dim3(256), 0, stream, t0, t1,
-                        0, a);
+  if (a.kv_fp8 != nullptr) {
+    hipExtLaunchKernelGGL((mla_attn_kernel<1, kPageSmall, true, true>), dim3(a.num_wgs), dim3(256), 0, stream, t0,
+                          t1, 0, a);
+  } else {
+    hipExtLaunchKernelGGL((mla_attn_kernel<1, kPageSmall, false, true>), dim3(a.num_wgs), dim3(256), 0, stream, t0,
+                          t1, 0, a);
+  }
   return hipGetLastError();
 }
 

@@ -87,8 +87,8 @@ struct AttnArgs {
 // at the start and end of its execution (null: none).
 hipError_t launch_attention(const AttnArgs& a, int tile_mode, int kv_fp8, hipStream_t stream, hipEvent_t t0,
                             hipEvent_t t1);
-// Token-sparse decode over fp8 records (WIDE tile, page size 1, key lists
-// bounded by a.sparse_len).
+// Token-sparse attention (WIDE tile, page size 1, key lists bounded by
+// a.sparse_len) over fp8 records (a.kv_fp8 set) or bf16 rows.
 hipError_t launch_sparse_attention(const AttnArgs& a, hipStream_t stream, hipEvent_t t0, hipEvent_t t1);
 // Stable compaction of each query token's key list: entries k < n_t (n_t =
 // min(topk_length[t], topk), or topk when topk_length is null) with

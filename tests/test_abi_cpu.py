@@ -293,5 +293,11 @@ def test_sparse_plan_and_call_errors(mla):
                                      None) == -3
     h = ctypes.c_void_p()
     for args in ((-1, 128, 10, 8), (4, 0, 10, 8), (4, 128, 0, 8), (4, 128, 10, 0)):
-        assert lib.mla_sparse_plan_create(ctypes.byref(h), *args, 4, 0) == -1
-    assert lib.mla_sparse_plan_create(ctypes.byref(h), 1 << 20, 128, 10, 1 << 12, 4, 0) == -1
+        assert lib.mla_sparse_plan_create(ctypes.byref(h), *args, 1, 4, 0) == -1
+    assert lib.mla_sparse_plan_create(ctypes.byref(h), 1 << 20, 128, 10, 1 << 12, 1, 4, 0) == -1
+    assert lib.mla_sparse_plan_create(ctypes.byref(h), 4, 128, 10, 8, 7, 4, 0) == -2
+    # a bf16 sparse plan is not an fp8 one, and the other way round
+    spb = mla.mla_sparse_plan_create(6, 128, 1000, 300, kv_format=0, num_cus=4)
+    assert lib.mla_sparse_decode_fp8(spb.handle, fake, fake, fake, None, None, *tail) == -4
+    assert lib.mla_sparse_prefill(sp.handle, fake, fake, fake, None, None, *tail) == -4
+    assert lib.mla_sparse_prefill(spb.handle, fake, None, fake, None, None, *tail) == -1

@@ -3,8 +3,9 @@ float64 oracle on the same seeded inputs.
 
 Tolerances as for the dense fp8 cache, against the oracle on the
 dequantised records: output max |err| <= 6e-2 and relative L2 <= 3e-2, lse
-and max_logits max |err| <= 1e-3.  Query tokens with no valid entry must
-give out = 0 and lse = max_logits = -inf exactly.  Pool slots that no list
+and max_logits max |err| <= 1e-3; over bf16 KV rows (the sparse prefill
+form) the bf16 gate, 2e-2 / 1e-2 / 1e-3.  Query tokens with no valid entry
+must give out = 0 and lse = max_logits = -inf exactly.  Pool slots that no list
 names hold NaN codes, scales and rope values.
 """
 
@@ -15,7 +16,7 @@ import pytest
 import torch
 
 import oracle
-from workloads import make_sparse_workload
+from workloads import make_sparse_prefill_workload, make_sparse_workload
 
 pytestmark = pytest.mark.gpu
 
@@ -37,7 +38,8 @@ def mla():
 
 
 def run_sparse(mla, w, **plan_kw):
-    plan = mla.mla_sparse_plan_create(w.tokens, w.num_heads, w.num_slots, w.topk, **plan_kw)
+    plan = mla.mla_sparse_plan_create(w.tokens, w.num_heads, w.num_slots, w.topk, kv_format=mla.MLA_KV_FP8_E4M3_T128,
+                                      **plan_kw)
     out, lse, mx = mla.mla_sparse_decode_fp8(
         plan, w.q.to(DEV), w.kv_fp8.to(DEV), w.indices.to(DEV), w.sm_scale,
         topk_length=None if w.topk_length is None else w.topk_length.to(DEV),
@@ -46,7 +48,7 @@ def run_sparse(mla, w, **plan_kw):
     return out, lse, mx, plan
 
 
-def compare(out, lse, mx, ref, tokens=None):
+def compare(out, lse, mx, ref, tokens=None, tol=TOL):
     ref_o, ref_l, ref_m = ref
     o = out.double().cpu().numpy()
     l = lse.double().cpu().numpy()
@@ -63,7 +65,7 @@ def compare(out, lse, mx, ref, tokens=None):
     lerr = np.abs(l[~empty] - ref_l[~empty]).max() if (~empty).any() else 0.0
     merr = np.abs(m[~empty] - ref_m[~empty]).max() if (~empty).any() else 0.0
     say(f"    max|dout|={err:.3e} relL2={rel:.3e} max|dlse|={lerr:.3e} max|dmax|={merr:.3e} empty={empty.sum()}")
-    assert err <= TOL["max_abs"] and rel <= TOL["rel_l2"] and lerr <= TOL["lse"] and merr <= TOL["lse"]
+    assert err <= tol["max_abs"] and rel <= tol["rel_l2"] and lerr <= tol["lse"] and merr <= tol["lse"]
 
 
 def ref_sparse(w, tokens=None):
@@ -113,7 +115,7 @@ def test_invalid_entries_do_not_change_a_bit(mla):
 
 
 def test_no_tokens_is_a_no_op(mla):
-    plan = mla.mla_sparse_plan_create(0, 128, 64, 32)
+    plan = mla.mla_sparse_plan_create(0, 128, 64, 32, kv_format=mla.MLA_KV_FP8_E4M3_T128)
     q = torch.zeros((0, 128, 576), dtype=torch.bfloat16, device=DEV)
     kv = torch.zeros((64, 656), dtype=torch.uint8, device=DEV)
     out, lse, mx = mla.mla_sparse_decode_fp8(plan, q, kv, torch.zeros((0, 32), dtype=torch.int32, device=DEV), 0.1)
@@ -127,3 +129,54 @@ def test_sparse_full_size(mla):
     out, lse, mx, plan = run_sparse(mla, w)
     tokens = sorted(np.random.default_rng(3).choice(w.tokens, size=6, replace=False).tolist())
     compare(out, lse, mx, ref_sparse(w, tokens=tokens), tokens=tokens)
+
+
+# ---------------------------------------------------------------------------
+# bf16 KV rows (the sparse prefill form)
+# ---------------------------------------------------------------------------
+
+def run_sparse_prefill(mla, w, **plan_kw):
+    plan = mla.mla_sparse_plan_create(w.tokens, w.num_heads, w.num_slots, w.topk, kv_format=mla.MLA_KV_BF16,
+                                      **plan_kw)
+    out, lse, mx = mla.mla_sparse_prefill(
+        plan, w.q.to(DEV), w.kv.to(DEV), w.indices.to(DEV), w.sm_scale,
+        topk_length=None if w.topk_length is None else w.topk_length.to(DEV),
+        attn_sink=None if w.attn_sink is None else w.attn_sink.to(DEV), out_dtype=w.out_dtype)
+    torch.cuda.synchronize()
+    return out, lse, mx, plan
+
+
+def ref_sparse_prefill(w, tokens=None):
+    return oracle.mla_sparse_prefill_ref(w.q, w.kv, w.indices, w.sm_scale, topk_length=w.topk_length,
+                                         attn_sink=w.attn_sink, tokens=tokens)
+
+
+TOL_BF16 = dict(max_abs=2e-2, rel_l2=1e-2, lse=1e-3)
+
+PREFILL_CASES = [
+    # (s_q, s_kv, heads, topk, invalid_frac, topk_min, sink, force_splits, out fp32)
+    (5, 300, 128, 256, 0.1, None, True, 0, False),
+    (3, 1000, 64, 700, 0.2, 50, False, 3, True),
+    (4, 50, 16, 128, 0.5, 0, True, 0, False),     # more entries than rows: repeats
+    (2, 5000, 128, 2048, 0.0, None, False, 2, False),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=[f"sq{c[0]}-skv{c[1]}-H{c[2]}-k{c[3]}-s{c[7]}" for c in PREFILL_CASES])
+def test_sparse_prefill_small_cases(mla, case):
+    s_q, s_kv, H, topk, inv, tmin, sink, fs, f32 = case
+    say(f"sparse prefill s_q={s_q} s_kv={s_kv} H={H} topk={topk} invalid={inv} topk_min={tmin} sink={sink} splits={fs}")
+    w = make_sparse_prefill_workload(s_q=s_q, s_kv=s_kv, heads=H, topk=topk, invalid_frac=inv, topk_min=tmin,
+                                     sink=sink, seed=700 + s_kv, out_dtype=torch.float32 if f32 else torch.bfloat16)
+    out, lse, mx, plan = run_sparse_prefill(mla, w, num_cus=0, force_splits=fs)
+    if fs > 1:
+        assert plan.num_split_groups > 0
+    compare(out, lse, mx, ref_sparse_prefill(w), tol=TOL_BF16)
+
+
+def test_sparse_prefill_full_size(mla):
+    say("sparse_prefill_sq4096_skv32768_h128_topk2048 (bench launch configuration), sampled tokens")
+    w = make_sparse_prefill_workload("sparse_prefill_sq4096_skv32768_h128_topk2048", device=DEV)
+    out, lse, mx, plan = run_sparse_prefill(mla, w)
+    tokens = sorted(np.random.default_rng(4).choice(w.tokens, size=6, replace=False).tolist())
+    compare(out, lse, mx, ref_sparse_prefill(w, tokens=tokens), tokens=tokens, tol=TOL_BF16)

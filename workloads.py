@@ -34,6 +34,13 @@ attention sink ln(topk) + 1.5 + 2 N(0, 1) per head (near the lse of topk
 N(0,1) keys at sm_scale 1/sqrt(192), so that it matters); then q [T, H, 576] as N(0,1) bf16 on the target
 device from a generator seeded ``k + 1``.
 
+Token-sparse prefill workloads (:func:`make_sparse_prefill_workload`, bf16
+KV rows without paging): a CPU generator seeded ``k`` draws the key lists
+as ``randint(0, s_kv)`` per entry (repeats allowed, as in the FlashMLA
+sparse-prefill example), then invalid entries, ``topk_length`` and the sink
+as above; then q [s_q, H, 576] and kv [s_kv, 576] as N(0,1) bf16 from a
+generator seeded ``k`` on the target device.
+
 fp8 quantisation of the source pool (the 656-byte record of FlashMLA's
 "FP8 KV Cache Quantization and Dequantization"): per token and 128-dim tile,
 ``scale = amax / 448`` in fp32 and ``code = e4m3(clamp(x / scale, +-448))``
@@ -80,6 +87,12 @@ CONFIGS = {
 SPARSE_CONFIGS = {
     "sparse_fp8_b128_sq2_h128_topk2048": dict(seed=6, batch=128, s_q=2, heads=128, topk=2048, page_size=64,
                                               kv_lens=("uniform", 4096, 16384), pool_factor=2),
+}
+
+# Token-sparse prefill over bf16 KV rows: 4096 query tokens, 32768 KV rows,
+# H=128, 2048 keys per query token
+SPARSE_PREFILL_CONFIGS = {
+    "sparse_prefill_sq4096_skv32768_h128_topk2048": dict(seed=7, s_q=4096, s_kv=32768, heads=128, topk=2048),
 }
 
 SM_SCALE_DEFAULT = 1.0 / math.sqrt(192.0)
@@ -331,3 +344,59 @@ def make_sparse_workload(name: Optional[str] = None, *, device: Union[str, torch
                           kv_indices=base.kv_indices, q=q, kv_fp8=base.kv_fp8, indices=indices,
                           topk_length=topk_length, attn_sink=attn_sink, sm_scale=sm_scale, out_dtype=out_dtype,
                           seed=seed)
+
+
+@dataclasses.dataclass
+class SparsePrefillWorkload:
+    name: str
+    num_heads: int
+    topk: int
+    q: torch.Tensor                      # bf16 [s_q, H, 576]
+    kv: torch.Tensor                     # bf16 [s_kv, 576]
+    indices: torch.Tensor                # int32 [s_q, topk] (CPU), -1 / >= s_kv invalid
+    topk_length: Optional[torch.Tensor]  # int32 [s_q] (CPU) or None
+    attn_sink: Optional[torch.Tensor]    # fp32 [H] (CPU) or None
+    sm_scale: float
+    out_dtype: torch.dtype
+    seed: int
+
+    @property
+    def tokens(self) -> int:
+        return self.q.shape[0]
+
+    @property
+    def num_slots(self) -> int:
+        return self.kv.shape[0]
+
+
+def make_sparse_prefill_workload(name: Optional[str] = None, *, device: Union[str, torch.device] = "cpu",
+                                 seed: Optional[int] = None, s_q: int = 4, s_kv: int = 256, heads: int = 128,
+                                 topk: int = 128, invalid_frac: float = 0.0, topk_min: Optional[int] = None,
+                                 sink: bool = False, sm_scale: float = SM_SCALE_DEFAULT,
+                                 out_dtype: torch.dtype = torch.bfloat16) -> SparsePrefillWorkload:
+    """Build one token-sparse prefill workload: named (SPARSE_PREFILL_CONFIGS) or custom."""
+    if name is not None:
+        spec = dict(SPARSE_PREFILL_CONFIGS[name])
+        seed = spec.pop("seed") if seed is None else seed
+        s_q, s_kv, heads, topk = spec.pop("s_q"), spec.pop("s_kv"), spec.pop("heads"), spec.pop("topk")
+    else:
+        name = "custom_sparse_prefill"
+        seed = 0 if seed is None else seed
+    g = torch.Generator().manual_seed(seed)
+    indices = torch.randint(0, s_kv, (s_q, topk), generator=g, dtype=torch.int64).to(torch.int32)
+    if invalid_frac > 0:
+        hit = torch.rand((s_q, topk), generator=g) < invalid_frac
+        past = torch.randint(s_kv, s_kv + 1000, (s_q, topk), generator=g, dtype=torch.int32)
+        kind = torch.rand((s_q, topk), generator=g) < 0.5
+        indices = torch.where(hit, torch.where(kind, torch.full_like(indices, -1), past), indices)
+    topk_length = None
+    if topk_min is not None:
+        topk_length = torch.randint(topk_min, topk + 1, (s_q,), generator=g, dtype=torch.int64).to(torch.int32)
+    attn_sink = (math.log(topk) + 1.5 + 2.0 * torch.randn(heads, generator=g)).to(torch.float32) if sink else None
+    dev = torch.device(device)
+    gv = g if dev.type == "cpu" else torch.Generator(device=dev).manual_seed(seed)
+    q = _randn_bf16((s_q, heads, HEAD_DIM_CKV + HEAD_DIM_KPE), gv, dev)
+    kv = _randn_bf16((s_kv, HEAD_DIM_CKV + HEAD_DIM_KPE), gv, dev, chunk_rows=65536)
+    return SparsePrefillWorkload(name=name, num_heads=heads, topk=topk, q=q, kv=kv, indices=indices,
+                                 topk_length=topk_length, attn_sink=attn_sink, sm_scale=sm_scale,
+                                 out_dtype=out_dtype, seed=seed)
