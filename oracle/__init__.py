@@ -12,7 +12,8 @@ Every function states the passage of the source pages it follows.  Pages:
 * "flashinfer.attention.prims_ts.batch_mla_decode_with_paged_kv_cache"
   (FlashInfer API docs): host-side planning, ``mask_type``, ``seq_lens``.
 * "mla_decoding_single_batch" (Modular MAX Mojo docs): V is the first
-  ``depth_v`` dims of K; split-K stats ``exp_sum`` / ``qk_max``.
+  ``depth_v`` dims of K; split-K stats ``exp_sum`` / ``qk_max``; the
+  float8_e4m3fn query type.
 * FlashMLA digest (context7 llms.txt): "Sparse MLA Prefill Kernel"
   (the written softmax-attention formula with lse), "FP8 KV Cache
   Quantization and Dequantization" / "... Utilities" (656-byte token record,
@@ -44,6 +45,7 @@ from .mla_oracle import (  # noqa: F401
     mla_decode_ref,
     mla_prefill_ref,
     mla_decode_fp8_ref,
+    mla_decode_fp8_q8_ref,
     sparse_valid_indices,
     sparse_attend,
     mla_sparse_decode_fp8_ref,

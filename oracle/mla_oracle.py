@@ -456,6 +456,22 @@ def mla_decode_fp8_ref(q_nope, q_pe, kv_cache_fp8, kv_indptr, kv_indices, kv_len
     return out, lse
 
 
+
+def mla_decode_fp8_q8_ref(q_codes, kv_cache_fp8, kv_indptr, kv_indices, kv_len, sm_scale: float,
+                          requests=None):
+    """Decode over the 656-byte records with an fp8 query.
+
+    "mla_decoding_single_batch" allows q_type float8_e4m3fn (output bf16).
+    Reading: q_codes [B, H, 576] are e4m3 codes of the 576 query dims
+    (latent, then rope), taken at their exact values with no scale; the
+    attention is then exactly :func:`mla_decode_fp8_ref`'s.
+    """
+    q = e4m3_decode(_as_u8(q_codes))
+    if q.shape[-1] != HEAD_DIM_CKV + HEAD_DIM_KPE:
+        raise ValueError("q must hold 576 codes per head")
+    return mla_decode_fp8_ref(q[..., :HEAD_DIM_CKV], q[..., HEAD_DIM_CKV:], kv_cache_fp8, kv_indptr, kv_indices,
+                              kv_len, sm_scale, requests=requests)
+
 # ---------------------------------------------------------------------------
 # Token-sparse attention (DSA): each query token attends to its own key list
 # ---------------------------------------------------------------------------

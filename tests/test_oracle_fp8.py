@@ -125,3 +125,24 @@ def test_fp8_decode_equals_bf16_decode_on_dequantised_cache():
     out, lse = oracle.mla_decode_ref(w.q_nope, w.q_pe, nope, rope, w.kv_indptr, w.kv_indices,
                                      w.kv_len, w.sm_scale)
     assert np.array_equal(out, out8) and np.array_equal(lse, lse8)
+
+
+def test_fp8_query_decode_reduces_to_the_fp8_decode():
+    # Every e4m3 value is a bf16 value: the fp8-query oracle must equal the
+    # (pinned) fp8-cache decode fed the decoded query as bf16 tensors.
+    import torch
+
+    from workloads import make_workload, quantize_q_e4m3
+
+    w = make_workload(kv_lens=[1, 70, 300], heads=8, page_size=16, seed=31, kv_format="fp8")
+    q8 = quantize_q_e4m3(w.q_nope, w.q_pe)
+    qv = torch.from_numpy(oracle.e4m3_decode(q8.numpy())).to(torch.bfloat16)
+    assert torch.equal(qv.to(torch.float64), torch.from_numpy(oracle.e4m3_decode(q8.numpy())))
+    o1, l1 = oracle.mla_decode_fp8_q8_ref(q8, w.kv_fp8, w.kv_indptr, w.kv_indices, w.kv_len, w.sm_scale)
+    o2, l2 = oracle.mla_decode_fp8_ref(qv[..., :512], qv[..., 512:], w.kv_fp8, w.kv_indptr, w.kv_indices, w.kv_len,
+                                       w.sm_scale)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    # the codes are the round-to-nearest e4m3 of the bf16 query (within half an e4m3 step)
+    q = torch.cat([w.q_nope, w.q_pe], dim=-1).double().numpy()
+    err = np.abs(oracle.e4m3_decode(q8.numpy()) - q)
+    assert np.all(err <= np.maximum(np.abs(q) * 2.0 ** -4, 2.0 ** -10) + 1e-12)

@@ -400,3 +400,12 @@ def make_sparse_prefill_workload(name: Optional[str] = None, *, device: Union[st
     return SparsePrefillWorkload(name=name, num_heads=heads, topk=topk, q=q, kv=kv, indices=indices,
                                  topk_length=topk_length, attn_sink=attn_sink, sm_scale=sm_scale,
                                  out_dtype=out_dtype, seed=seed)
+
+
+def quantize_q_e4m3(q_nope: torch.Tensor, q_pe: torch.Tensor) -> torch.Tensor:
+    """[rows, H, 512] + [rows, H, 64] bf16 -> [rows, H, 576] uint8 e4m3 codes of
+    the concatenated query (clamp to +-448, then torch's float8_e4m3fn cast,
+    round to nearest even; no scale).  Input preparation for the fp8-query
+    decode."""
+    q = torch.cat([q_nope, q_pe], dim=-1).to(torch.float32).clamp(-448.0, 448.0)
+    return q.to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
