@@ -255,6 +255,14 @@ def setup_dense(args, mla, dev):
     for _ in range(reps - 1):
         pools.append((w.ckv.clone() if w.ckv is not None else None, w.kpe.clone() if w.kpe is not None else None,
                       w.kv_fp8.clone() if w.kv_fp8 is not None else None))
+    if args.q_fp8 and not fmt:
+        raise SystemExit("--q-fp8 applies to the fp8 cache only")
+    q8 = None
+    if args.q_fp8:
+        from workloads import quantize_q_e4m3
+
+        q8 = quantize_q_e4m3(w.q_nope, w.q_pe)
+        bytes_alg -= w.rows * w.num_heads * 576  # one byte per query dim instead of two
     packed = args.layout == "packed"
     if packed:
         if fmt:
@@ -271,7 +279,9 @@ def setup_dense(args, mla, dev):
 
     def step(i):
         ckv, kpe, kv8 = pools[i % reps]
-        if fmt:
+        if q8 is not None:
+            mla.mla_decode_fp8_q8(plan, q8, kv8, kv_indptr, kv_indices, w.sm_scale, out=out, lse=lse, workspace=ws)
+        elif fmt:
             mla.mla_decode_fp8(plan, w.q_nope, w.q_pe, kv8, kv_indptr, kv_indices, w.sm_scale, out=out, lse=lse,
                                workspace=ws)
         elif packed and kind == mla.MLA_KIND_PREFILL:
@@ -289,10 +299,13 @@ def setup_dense(args, mla, dev):
     config = {"workload": w.name, "batch": w.batch, "num_qo_heads": w.num_heads, "head_dim_ckv": 512,
               "head_dim_kpe": 64, "page_size": w.page_size, "kv_format": w.kv_format,
               "kv_len_total": int(w.kv_len.sum()), "rows": w.rows, "parallelism": "single GPU",
-              "layout": args.layout}
+              "layout": args.layout, "q_dtype": "fp8-e4m3" if q8 is not None else "bf16"}
+    dtype = "bf16" if w.kv_format == "bf16" else "fp8-e4m3 cache, bf16 math"
+    if q8 is not None:
+        dtype = "fp8-e4m3 q and cache: fp8 x fp8 MFMA for the latent q.k, bf16 P.V"
     return {"step": step, "flops": flops, "live_kv": live_kv, "bytes_alg": bytes_alg, "plan_ms": plan_ms,
             "config": config, "kernel": "mla_attn_kernel",
-            "dtype": "bf16" if w.kv_format == "bf16" else "fp8-e4m3 cache, bf16 math",
+            "dtype": dtype,
             "cpu_baseline": lambda secs: cpu_baseline(w, flops, secs)}
 
 
@@ -401,6 +414,8 @@ def main():
     ap.add_argument("--copy-bytes", type=int, default=1 << 30)
     ap.add_argument("--layout", choices=("split", "packed"), default="split",
                     help="bf16 q / cache as separate latent and rope tensors, or one 576-wide row per token")
+    ap.add_argument("--q-fp8", action="store_true",
+                    help="fp8 cache workloads: an e4m3 query (fp8 x fp8 matrix cores for the latent q.k)")
     ap.add_argument("--command", action="append", default=[], help="command lines recorded with --write-counters")
     args = ap.parse_args()
 

@@ -203,6 +203,23 @@ mla_status mla_decode_fp8(const mla_plan* plan, const void* q_nope, const void* 
                           int32_t out_dtype, float* lse, void* workspace,
                           size_t workspace_bytes, hipStream_t stream);
 
+/* Decode over the fp8 record cache with an fp8 query ("mla_decoding_single_batch":
+ * q_type float8_e4m3fn, bfloat16 output):
+ *   q [batch, H, 576] uint8: OCP e4m3 codes of the query, latent dims then
+ *     rope dims, used as they are (no scale; the caller quantises).
+ * The product over the 512 latent dims runs on the fp8 x fp8 matrix cores
+ * (per-tile key scales applied in fp32 as in mla_decode_fp8); the rope dims
+ * and P.V are as in mla_decode_fp8.  The hardware sums each 64-deep block of
+ * code products with a limited alignment window (measured: error below
+ * 2e-5 of the sum of the products' magnitudes), so the logits are exact to
+ * that bound rather than to fp32 rounding.  Plan: an fp8 decode plan in
+ * the WIDE tile mode (another mode is MLA_ERR_UNSUPPORTED).  Everything
+ * else, errors included, as for mla_decode_fp8.                          */
+mla_status mla_decode_fp8_q8(const mla_plan* plan, const void* q, const void* kv_cache,
+                             const int32_t* kv_indptr, const int32_t* kv_indices, float sm_scale, void* out,
+                             int32_t out_dtype, float* lse, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
 /* The concatenated layout ("MLA Paged" ckv/kpe as one tensor; FlashMLA's
  * "flash_mla_with_kvcache" q and k_cache with head_dim 576): one 576-wide
  * bf16 row per query (token, head) and per cached token, latent dims 0..511

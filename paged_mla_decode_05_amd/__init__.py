@@ -7,7 +7,8 @@ library's HIP kernels.  If the library is missing or cannot be loaded, every
 call raises; there is no fallback.
 
 Names follow the C ABI: :func:`mla_plan_create`, :func:`mla_decode`,
-:func:`mla_prefill`, :func:`mla_decode_fp8`, the concatenated-layout
+:func:`mla_prefill`, :func:`mla_decode_fp8`, :func:`mla_decode_fp8_q8` (e4m3
+query), the concatenated-layout
 :func:`mla_decode_packed` / :func:`mla_prefill_packed`,
 :func:`mla_block_table_to_indices`, and the token-sparse
 :func:`mla_sparse_plan_create` / :func:`mla_sparse_decode_fp8` /
@@ -22,6 +23,7 @@ from ._binding import (  # noqa: F401
     mla_block_table_to_indices,
     mla_decode,
     mla_decode_fp8,
+    mla_decode_fp8_q8,
     mla_decode_packed,
     mla_plan_create,
     mla_prefill,

@@ -89,6 +89,8 @@ def load_library():
         L.mla_prefill.restype = i32
         L.mla_decode_fp8.argtypes = [vp, vp, vp, vp, vp, vp, f32, vp, i32, vp, vp, sz, vp]
         L.mla_decode_fp8.restype = i32
+        L.mla_decode_fp8_q8.argtypes = [vp, vp, vp, vp, vp, f32, vp, i32, vp, vp, sz, vp]
+        L.mla_decode_fp8_q8.restype = i32
         L.mla_decode_packed.argtypes = [vp, vp, vp, vp, vp, f32, f32, vp, i32, vp, vp, sz, vp]
         L.mla_decode_packed.restype = i32
         L.mla_prefill_packed.argtypes = [vp, vp, vp, vp, vp, vp, f32, f32, vp, i32, vp, vp, sz, vp]
@@ -403,6 +405,23 @@ def _packed_outputs(q: torch.Tensor, out, lse, out_dtype):
     if out is None:
         out = torch.empty((rows, H, _DIM_CKV), dtype=out_dtype, device=q.device)
     return _outputs(out, out, lse, out.dtype)
+
+
+def mla_decode_fp8_q8(plan: Plan, q, kv_cache, kv_indptr, kv_indices, sm_scale: float, out=None, lse=None,
+                      out_dtype=torch.bfloat16, workspace=None):
+    """Decode over 656-byte fp8 records with an e4m3 query: q [B, H, 576]
+    uint8 codes (latent then rope dims).  Returns (out [B, H, 512], lse [B, H])."""
+    L = load_library()
+    B, P, ps = plan.desc.batch, plan.desc.num_pages, plan.desc.page_size
+    qq = _dev(q, "q", torch.uint8, (B, plan.num_heads, _DIM_CKV + _DIM_KPE))
+    kv = _dev(kv_cache, "kv_cache", torch.uint8, (P, ps, _FP8_RECORD))
+    ip, ix = _paging(plan, kv_indptr, kv_indices)
+    out, lse, code = _packed_outputs(q, out, lse, out_dtype)
+    ws = plan.workspace(q.device) if workspace is None else workspace
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(L.mla_decode_fp8_q8(plan.handle, qq, kv, ip, ix, float(sm_scale), out.data_ptr(), code, lse.data_ptr(),
+                               ws.data_ptr(), ws.numel(), stream), "mla_decode_fp8_q8")
+    return out, lse
 
 
 def mla_decode_packed(plan: Plan, q, kv_cache, kv_indptr, kv_indices, sm_scale: float, out_scale: float = 1.0,

@@ -398,7 +398,7 @@ mla_status run(const mla_plan* p, int32_t want_kind, int32_t want_format, const 
                const int32_t* qo_indptr, const int32_t* kv_indptr, const int32_t* kv_indices,
                float sm_scale, void* out, int32_t out_dtype, float* lse, void* ws, size_t ws_bytes,
                hipStream_t stream, const Layout& lay = kSplit, float out_scale = 1.f,
-               const Sparse* sparse = nullptr) {
+               const Sparse* sparse = nullptr, bool q8 = false) {
   if (!p) return MLA_ERR_INVALID_ARGUMENT;
   if (p->d.kind != want_kind || p->d.kv_format != want_format) return MLA_ERR_PLAN_MISMATCH;
   if (out_dtype != MLA_DTYPE_BF16 && out_dtype != MLA_DTYPE_FP32) return MLA_ERR_INVALID_ARGUMENT;
@@ -410,6 +410,7 @@ mla_status run(const mla_plan* p, int32_t want_kind, int32_t want_format, const 
   if (want_format == MLA_KV_FP8_E4M3_T128 && !kv_fp8) return MLA_ERR_INVALID_ARGUMENT;
   if (want_kind == MLA_KIND_PREFILL && !qo_indptr) return MLA_ERR_INVALID_ARGUMENT;
   if (!ws || ws_bytes < p->ws_bytes || ((uintptr_t)ws % mla::kWsAlign) != 0) return MLA_ERR_WORKSPACE;
+  if (q8 && p->tile_mode != MLA_TILE_WIDE) return MLA_ERR_UNSUPPORTED;
   char* w = (char*)ws;
   if (sparse) {
     // the lists are compacted into the workspace first; the attention kernel
@@ -467,8 +468,9 @@ mla_status run(const mla_plan* p, int32_t want_kind, int32_t want_format, const 
   hipEvent_t ev0 = t_ev_before, ev1 = t_ev_after;
   t_ev_before = t_ev_after = nullptr;
   hipError_t e = sparse ? mla::launch_sparse_attention(a, stream, ev0, ev1)
-                        : mla::launch_attention(a, p->tile_mode, want_format == MLA_KV_FP8_E4M3_T128, stream, ev0,
-                                                ev1);
+                 : q8     ? mla::launch_attention_q8(a, stream, ev0, ev1)
+                          : mla::launch_attention(a, p->tile_mode, want_format == MLA_KV_FP8_E4M3_T128, stream, ev0,
+                                                  ev1);
   if (e != hipSuccess) return MLA_ERR_DEVICE;
   if (!p->groups.empty()) {
     e = mla::launch_combine(a, stream);
@@ -510,6 +512,16 @@ mla_status mla_decode_fp8(const mla_plan* p, const void* q_nope, const void* q_p
                           hipStream_t stream) {
   return run(p, MLA_KIND_DECODE, MLA_KV_FP8_E4M3_T128, q_nope, q_pe, nullptr, nullptr, kv, nullptr,
              kv_indptr, kv_indices, sm_scale, out, out_dtype, lse, ws, ws_bytes, stream);
+}
+
+mla_status mla_decode_fp8_q8(const mla_plan* p, const void* q, const void* kv, const int32_t* kv_indptr,
+                             const int32_t* kv_indices, float sm_scale, void* out, int32_t out_dtype, float* lse,
+                             void* ws, size_t ws_bytes, hipStream_t stream) {
+  const char* qb = (const char*)q;
+  // q rows are 576 one-byte codes: the concatenated layout's element strides
+  return run(p, MLA_KIND_DECODE, MLA_KV_FP8_E4M3_T128, q, q ? qb + mla::kDimCkv : nullptr, nullptr, nullptr, kv,
+             nullptr, kv_indptr, kv_indices, sm_scale, out, out_dtype, lse, ws, ws_bytes, stream, kPacked, 1.f, nullptr,
+             true);
 }
 
 mla_status mla_decode_packed(const mla_plan* p, const void* q, const void* kv_cache, const int32_t* kv_indptr,

@@ -55,6 +55,7 @@ typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 #define LDS_AS __attribute__((address_space(3)))
 
@@ -170,6 +171,16 @@ __device__ __forceinline__ void mfma32_acc(f32x16& acc, const bf16x8& a, const b
   } else {
     asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
   }
+}
+// The same for v_mfma_f32_32x32x64_f8f6f4 with e4m3 A and B (32 codes per
+// lane: row / column lane % 32, codes 32 (lane / 32) .. +31 of the 64-deep
+// step, in byte order) and an fp32 accumulator in VGPRs.  The operands come
+// straight from LDS or global loads here, never from a VALU write.
+__device__ __forceinline__ void mfma8_first(f32x16& acc, const i32x8& a, const i32x8& b) {
+  asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma8_acc(f32x16& acc, const i32x8& a, const i32x8& b) {
+  asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void mfma32_drain(f32x16& x) { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x)); }
 __device__ __forceinline__ void mfma32_drain(f32x16& x, f32x16& y) {
@@ -950,7 +961,12 @@ __device__ __forceinline__ bf16x8 codes8(uint32_t lo, uint32_t hi) {
   return h;
 }
 
-template <int kPC, bool kSparse = false>
+// kQ8: the query is e4m3 codes too ([rows, H, 576] bytes, no scale: the
+// fp8 query type of "mla_decoding_single_batch").  Q.K^T over the 512
+// latent dims then runs on the fp8 x fp8 MFMA (32x32x64), 64 dims per step,
+// straight from the key codes in LDS (no conversion); the 64 rope dims are
+// converted to bf16 once (exactly) and stay on the bf16 MFMA, as does P.V.
+template <int kPC, bool kSparse = false, bool kQ8 = false>
 __device__ void wide8_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* smem, int wave, int lane) {
   const int g = lane >> 5;
   const int n = lane & 31;
@@ -959,9 +975,29 @@ __device__ void wide8_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* s
   const int bound = row_key_bound(a, it, ri);
 
   // Query fragments in the codes' dim order: nope k-step 2m+s, half g holds
-  // dims 32m + 16g + 8s .. +7; rope k-steps as in the bf16 path.
-  bf16x8 qf[36];
-  {
+  // dims 32m + 16g + 8s .. +7; rope k-steps as in the bf16 path.  kQ8: step
+  // c of the fp8 MFMA, half g holds the codes of dims 64c + 32g .. +31.
+  bf16x8 qf[kQ8 ? 1 : 32];
+  bf16x8 qr[4];
+  i32x8 q8[kQ8 ? 8 : 1];
+  if constexpr (kQ8) {
+    const i32x8 z = {};
+    const uint8_t* qc = (const uint8_t*)a.q_nope + ri.qrow * a.q_stride;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const u32x4 lo = ri.ok ? *(const u32x4*)(qc + 64 * c + 32 * g) : u32x4{};
+      const u32x4 hi = ri.ok ? *(const u32x4*)(qc + 64 * c + 32 * g + 16) : u32x4{};
+      q8[c] = ri.ok ? i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2],
+                            (int)hi[3]}
+                    : z;
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      const u32x2 c8 = ri.ok ? *(const u32x2*)(qc + kDimCkv + 16 * ks + 8 * g) : u32x2{};
+      qr[ks] = codes8(c8[0], c8[1]);
+    }
+  } else {
     const bf16x8 z = {};
     const __bf16* qn = (const __bf16*)a.q_nope + ri.qrow * a.q_stride + 16 * g;
     const __bf16* qp = (const __bf16*)a.q_pe + ri.qrow * a.qpe_stride + 8 * g;
@@ -970,10 +1006,10 @@ __device__ void wide8_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* s
 #pragma unroll
       for (int sh = 0; sh < 2; ++sh) qf[2 * m + sh] = ri.ok ? *(const bf16x8*)(qn + 32 * m + 8 * sh) : z;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qf[32 + ks] = ri.ok ? *(const bf16x8*)(qp + 16 * ks) : z;
+    for (int ks = 0; ks < 4; ++ks) qr[ks] = ri.ok ? *(const bf16x8*)(qp + 16 * ks) : z;
   }
   // byte offsets inside a raw stage
-  const int kaddr = n * kFp8RecordBytes + 16 * g;                       // + tb*656 + 32m
+  const int kaddr = n * kFp8RecordBytes + (kQ8 ? 32 : 16) * g;           // + tb*656 + 32m (kQ8: + 64c)
   const int raddr = n * kFp8RecordBytes + kDimCkv + 16 + 16 * g;        // rope: + tb*656 + 32kr
   int vaddr;
   {
@@ -1042,16 +1078,11 @@ __device__ void wide8_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* s
       for (int kr2 = 0; kr2 < 4; ++kr2) {
         const bf16x8 rp = *(const LDS_AS bf16x8*)(rbase + tb * kFp8RecordBytes + 32 * kr2);
         if (kr2 == 0) {
-          mfma32_first<false>(sacc, rp, qf[32]);
+          mfma32_first<false>(sacc, rp, qr[0]);
         } else {
-          mfma32_acc<false>(sacc, rp, qf[32 + kr2]);
+          mfma32_acc<false>(sacc, rp, qr[kr2]);
         }
       }
-      constexpr int KD = 3;  // 16-code reads in flight
-      u32x4 kr[KD];
-      auto kread = [&](int m) -> u32x4 { return *(const LDS_AS u32x4*)(kbase + tb * kFp8RecordBytes + 32 * m); };
-#pragma unroll
-      for (int i = 0; i < KD; ++i) kr[i] = kread(i);
       f32x4 tsc[4];  // the scales of the lane's keys in the tile being folded in
       auto fold = [&](int t) {  // sacc += part[t % 2] * (tile t's key scales)
         mfma32_drain(part[t & 1], sacc);
@@ -1060,6 +1091,41 @@ __device__ void wide8_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* s
 #pragma unroll
           for (int r = 0; r < 4; ++r) sacc[4 * q + r] += part[t & 1][4 * q + r] * tsc[q][r];
       };
+      if constexpr (kQ8) {
+        // two 64-deep fp8 steps per 128-dim tile
+        constexpr int KD8 = 2;  // 32-code reads in flight
+        auto kread8 = [&](int c) -> i32x8 {
+          const u32x4 lo = *(const LDS_AS u32x4*)(kbase + tb * kFp8RecordBytes + 64 * c);
+          const u32x4 hi = *(const LDS_AS u32x4*)(kbase + tb * kFp8RecordBytes + 64 * c + 16);
+          return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        };
+        i32x8 kr8[KD8];
+#pragma unroll
+        for (int i = 0; i < KD8; ++i) kr8[i] = kread8(i);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          pin_loads();
+          if (sub * 8 + c < RecordLoader<kPC>::kSlices) ld.issue(a, sub * 8 + c, wave);
+          const i32x8 kc = kr8[c % KD8];
+          if (c + KD8 < 8) kr8[c % KD8] = kread8(c + KD8);
+          f32x16& pa = part[(c >> 1) & 1];
+          if ((c & 1) == 0) {
+            mfma8_first(pa, kc, q8[c]);
+          } else {
+            mfma8_acc(pa, kc, q8[c]);
+          }
+          if ((c & 1) == 0 && c > 0) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) tsc[q] = scales((c >> 1) - 1, q);
+          }
+          if ((c & 1) == 1 && c > 1) fold((c >> 1) - 1);
+        }
+      } else {
+      constexpr int KD = 3;  // 16-code reads in flight
+      u32x4 kr[KD];
+      auto kread = [&](int m) -> u32x4 { return *(const LDS_AS u32x4*)(kbase + tb * kFp8RecordBytes + 32 * m); };
+#pragma unroll
+      for (int i = 0; i < KD; ++i) kr[i] = kread(i);
 #pragma unroll
       for (int m = 0; m < 16; ++m) {
         pin_loads();
@@ -1079,6 +1145,7 @@ __device__ void wide8_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* s
           for (int q = 0; q < 4; ++q) tsc[q] = scales((m >> 2) - 1, q);
         }
         if ((m & 3) == 1 && m > 1) fold((m >> 2) - 1);
+      }
       }
       pin_loads();
 #pragma unroll
@@ -1689,7 +1756,7 @@ __device__ __forceinline__ int xcd_list(int b, int n) {
   return base + (b >> 3);
 }
 
-template <int kMode, int kPC, bool kFp8, bool kSparse = false>
+template <int kMode, int kPC, bool kFp8, bool kSparse = false, bool kQ8 = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_attn_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem_raw[kFp8 ? kFp8LdsBytes : kLdsBytes];
@@ -1717,7 +1784,7 @@ void mla_attn_kernel(AttnArgs a) {
       it.tok1 = max(it.tok0, min(it.tok1, L));
     }
     if (kMode == 1 && kFp8) {
-      wide8_item<kPC, kSparse>(a, it, smem, wave, lane);
+      wide8_item<kPC, kSparse, kQ8>(a, it, smem, wave, lane);
     } else if (kMode == 1) {
       wide_item<kPC, kSparse>(a, it, smem, wave, lane);
     } else {
@@ -1854,6 +1921,22 @@ hipError_t launch_attention(const AttnArgs& a, int tile_mode, int kv_fp8, hipStr
   if (pc == kPageBig) return launch_mode<2, kPageBig>(a, kv_fp8, stream, t0, t1);
   if (pc == kPageMid) return launch_mode<2, kPageMid>(a, kv_fp8, stream, t0, t1);
   return launch_mode<2, kPageSmall>(a, kv_fp8, stream, t0, t1);
+}
+
+hipError_t launch_attention_q8(const AttnArgs& a, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
+  if (a.num_wgs <= 0) return hipSuccess;
+  const int pc = a.page_shift >= 6 ? kPageBig : (a.page_shift >= 3 ? kPageMid : kPageSmall);
+  if (pc == kPageBig) {
+    hipExtLaunchKernelGGL((mla_attn_kernel<1, kPageBig, true, false, true>), dim3(a.num_wgs), dim3(256), 0, stream,
+                          t0, t1, 0, a);
+  } else if (pc == kPageMid) {
+    hipExtLaunchKernelGGL((mla_attn_kernel<1, kPageMid, true, false, true>), dim3(a.num_wgs), dim3(256), 0, stream,
+                          t0, t1, 0, a);
+  } else {
+    hipExtLaunchKernelGGL((mla_attn_kernel<1, kPageSmall, true, false, true>), dim3(a.num_wgs), dim3(256), 0, stream,
+                          t0, t1, 0, a);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_sparse_attention(const AttnArgs& a, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {

@@ -87,6 +87,9 @@ struct AttnArgs {
 // at the start and end of its execution (null: none).
 hipError_t launch_attention(const AttnArgs& a, int tile_mode, int kv_fp8, hipStream_t stream, hipEvent_t t0,
                             hipEvent_t t1);
+// Decode over fp8 records with an fp8 (e4m3) query: WIDE tile, q_nope =
+// the [rows, H, 576] codes with q_stride 576.
+hipError_t launch_attention_q8(const AttnArgs& a, hipStream_t stream, hipEvent_t t0, hipEvent_t t1);
 // Token-sparse attention (WIDE tile, page size 1, key lists bounded by
 // a.sparse_len) over fp8 records (a.kv_fp8 set) or bf16 rows.
 hipError_t launch_sparse_attention(const AttnArgs& a, hipStream_t stream, hipEvent_t t0, hipEvent_t t1);
