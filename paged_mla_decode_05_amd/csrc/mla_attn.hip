@@ -1952,70 +1952,6 @@ hipError_t launch_sparse_attention(const AttnArgs& a, hipStream_t stream, hipEve
   return hipGetLastError();
 }
 
-// Key lists of the token-sparse decode: one workgroup per query token
-// compacts its list (valid entries in order) with a ballot prefix count per
-// 256-entry chunk.
-__global__ __launch_bounds__(256) void mla_sparse_lists_kernel(const int32_t* __restrict__ indices, int32_t num_tokens,
-                                                               int32_t topk, const int32_t* __restrict__ topk_length,
-                                                               int64_t num_slots, int32_t* __restrict__ list,
-                                                               int32_t* __restrict__ count,
-                                                               int32_t* __restrict__ indptr) {
-  __shared__ int wave_n[4];
-  const int t = blockIdx.x;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int n = topk_length ? min(max(topk_length[t], 0), topk) : topk;
-  const int32_t* src = indices + (size_t)t * topk;
-  int32_t* dst = list + (size_t)t * topk;
-  int base = 0;
-  for (int c0 = 0; c0 < n; c0 += 256) {
-    const int k = c0 + (int)threadIdx.x;
-    const int32_t v = k < n ? src[k] : -1;
-    const bool ok = k < n && v >= 0 && (int64_t)v < num_slots;
-    const uint64_t bal = __ballot(ok);
-    if (lane == 0) wave_n[wave] = __popcll(bal);
-    __syncthreads();
-    int off = base;
-    for (int w = 0; w < wave; ++w) off += wave_n[w];
-    if (ok) dst[off + __popcll(bal & ((1ull << lane) - 1))] = v;
-    base += wave_n[0] + wave_n[1] + wave_n[2] + wave_n[3];
-    __syncthreads();  // wave_n is rewritten by the next chunk
-  }
-  if (threadIdx.x == 0) {
-    count[t] = base;
-    indptr[t] = t * topk;
-    if (t == num_tokens - 1) indptr[num_tokens] = num_tokens * topk;
-  }
-}
-
-hipError_t launch_sparse_lists(const int32_t* indices, int32_t num_tokens, int32_t topk, const int32_t* topk_length,
-                               int64_t num_slots, int32_t* list, int32_t* count, int32_t* indptr,
-                               hipStream_t stream) {
-  if (num_tokens <= 0) return hipSuccess;
-  hipLaunchKernelGGL(mla_sparse_lists_kernel, dim3(num_tokens), dim3(256), 0, stream, indices, num_tokens, topk,
-                     topk_length, num_slots, list, count, indptr);
-  return hipGetLastError();
-}
-
-// Page list of the dense block-table interface: one workgroup per request
-// copies the request's first kv_indptr[b+1] - kv_indptr[b] table entries.
-__global__ __launch_bounds__(256) void mla_block_table_kernel(const int32_t* __restrict__ block_table,
-                                                              int32_t max_blocks, const int32_t* __restrict__ kv_indptr,
-                                                              int32_t* __restrict__ kv_indices) {
-  const int b = blockIdx.x;
-  const int p0 = kv_indptr[b];
-  const int n = min(kv_indptr[b + 1] - p0, max_blocks);
-  const int32_t* row = block_table + (size_t)b * max_blocks;
-  for (int j = threadIdx.x; j < n; j += 256) kv_indices[p0 + j] = row[j];
-}
-
-hipError_t launch_block_table(const int32_t* block_table, int32_t batch, int32_t max_blocks,
-                              const int32_t* kv_indptr, int32_t* kv_indices, hipStream_t stream) {
-  if (batch <= 0) return hipSuccess;
-  hipLaunchKernelGGL(mla_block_table_kernel, dim3(batch), dim3(256), 0, stream, block_table, max_blocks, kv_indptr,
-                     kv_indices);
-  return hipGetLastError();
-}
-
 hipError_t launch_combine(const AttnArgs& a, hipStream_t stream) {
   if (a.num_groups <= 0) return hipSuccess;
   const int chunks = a.rows_per_block / kCombineRows;
