@@ -703,18 +703,21 @@ __device__ __forceinline__ void wide_stage(const AttnArgs& a, const bf16x8 (&qf)
     mfma32_drain(sacc);
   };
 
-  // ---- O^T[32 dims x 32 rows] += V^T[32 dims x 16 keys] . P^T[16 keys x 32 rows] for sub-tile tb
+  // ---- O^T[32 dims x 32 rows] += V^T[32 dims x 16 keys] . P^T[16 keys x 32 rows] for sub-tile tb.
+  // Step i covers dims block cb = i % 16 and keys 16 (i / 16) ..: consecutive
+  // MFMAs write different O tiles, so none waits for the one before it.
   auto pv = [&](int tb, bf16x8 (&pt)[2], const float (&pf)[16], auto&& side) {
     constexpr int VD = 3;  // V^T fragments in flight
+    auto vstep = [&](int i) { return vread(tb, 2 * (i & 15) + (i >> 4)); };
     bf16x8 vr[VD];
 #pragma unroll
-    for (int i = 0; i < VD; ++i) vr[i] = vread(tb, i);
+    for (int i = 0; i < VD; ++i) vr[i] = vstep(i);
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
+    for (int i = 0; i < 32; ++i) {
       pin_loads();
-      st.o[j >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[j % VD], pt[j & 1], st.o[j >> 1], 0, 0, 0);
-      if (j + VD < 32) vr[j % VD] = vread(tb, j + VD);
-      side(j);
+      st.o[i & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[i % VD], pt[i >> 4], st.o[i & 15], 0, 0, 0);
+      if (i + VD < 32) vr[i % VD] = vstep(i + VD);
+      side(i);
     }
     pin_loads();
   };
@@ -798,7 +801,8 @@ __device__ __forceinline__ int wide_dim(int cb, int q, int g) {
 // softmax denominator (one more logit with no value row).
 template <bool kPairedDims = false, bool kSparse = false>
 __device__ __forceinline__ void wide_epilogue(const AttnArgs& a, const WorkItem& it, WideState& st, const RowInfo& ri,
-                                              int rib, LDS_AS char* smem, int wave, int lane, float m_top = 0.f) {
+                                              int rib, LDS_AS char* smem, int wave, int, float m_top = 0.f) {
+  const int lane = lane_here();  // recomputed here, not kept (or spilled) across the stage loop
   const int g = lane >> 5;
   const int n = lane & 31;
   const float l_tot = sum_xor32(st.l_run);
@@ -861,23 +865,34 @@ __device__ __forceinline__ void wide_epilogue(const AttnArgs& a, const WorkItem&
 }
 
 template <int kPC, bool kSparse = false>
-__device__ void wide_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* smem, int wave, int lane) {
+__device__ void wide_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* smem, int wave, int) {
+  // lane-derived values are recomputed per item: hoisted out of the item
+  // loop they would be spilled, and each spill reload waits for every load
+  // in flight (the query rows and stage 0)
+  const int lane = lane_here();
   const int g = lane >> 5;   // lane half
   const int n = lane & 31;   // row within the wave (S^T / O^T column)
   const int rib = wave * 32 + n;
   const RowInfo ri = row_info(a, it, rib);
   const int bound = row_key_bound(a, it, ri);
 
+  // Stage 0's direct loads go out first, then the query rows: both streams
+  // are in flight together and the first stage's wait covers them.  The
+  // query loads are unconditional (a missing row reads the item's first row,
+  // and its key bound of 0 masks it), so no wait splits them.
+  const int page_base = ld_const(a.kv_indptr, it.b);
+  const int nstage = (it.tok1 - it.tok0 + kStageTokens - 1) / kStageTokens;
+  if (nstage > 0) issue_stage_bf16<kPC>(a, smem, page_base, it.tok0, it.tok1, wave, lane);
+
   // Query fragments, B operand of S^T = K . Q^T: lane holds row n, dims 8g..8g+7 of each k-step.
   bf16x8 qf[36];
   {
-    const bf16x8 z = {};
     const __bf16* qn = (const __bf16*)a.q_nope + ri.qrow * a.q_stride + 8 * g;
     const __bf16* qp = (const __bf16*)a.q_pe + ri.qrow * a.qpe_stride + 8 * g;
 #pragma unroll
-    for (int ks = 0; ks < 32; ++ks) qf[ks] = ri.ok ? *(const bf16x8*)(qn + 16 * ks) : z;
+    for (int ks = 0; ks < 32; ++ks) qf[ks] = *(const bf16x8*)(qn + 16 * ks);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qf[32 + ks] = ri.ok ? *(const bf16x8*)(qp + 16 * ks) : z;
+    for (int ks = 0; ks < 4; ++ks) qf[32 + ks] = *(const bf16x8*)(qp + 16 * ks);
   }
   // LDS base offsets (see the comment above WideState)
   int kb[8], pb[4], vb[8];
@@ -904,9 +919,6 @@ __device__ void wide_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* sm
   st.o_live = false;
   st.m_top = kNegInf;
 
-  const int page_base = ld_const(a.kv_indptr, it.b);
-  const int nstage = (it.tok1 - it.tok0 + kStageTokens - 1) / kStageTokens;
-  if (nstage > 0) issue_stage_bf16<kPC>(a, smem, page_base, it.tok0, it.tok1, wave, lane);
   // one-page stages: the page of stage s+1 is looked up a stage ahead (stage 0's when none is next)
   auto page_at = [&](int stage) -> int {
     return kPC == kPageBig ? ld_const(a.kv_indices, page_base + ((it.tok0 + stage * kStageTokens) >> a.page_shift))
@@ -926,7 +938,325 @@ __device__ void wide_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* sm
     pg_next = pg_after;
   }
   __syncthreads();  // every wave is done with the last stage before the epilogue stages rows over it
-  wide_epilogue<false, kSparse>(a, it, st, ri, rib, smem, wave, lane, st.m_top);
+  {
+    const int rib_e = wave * 32 + (lane_here() & 31);  // row info recomputed rather than kept across the loop
+    wide_epilogue<false, kSparse>(a, it, st, row_info(a, it, rib_e), rib_e, smem, wave, lane, st.m_top);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// WIDE mode with P.V split by output dims (dense bf16 caches).
+//
+// Q.K^T and the online softmax run as in WIDE: wave w owns query rows
+// 32w..32w+31.  P.V is split the other way: wave w accumulates output dims
+// 128w..128w+127 of all 128 rows, so each V^T fragment it reads from LDS
+// (ds_read_b64_tr_b16, the costly transposed read) feeds four MFMAs, one
+// per row block, and a stage's V^T traffic drops from 4 x 64 KB to 64 KB.
+// P goes through LDS instead (bf16, 16 KB per stage, plain 16-byte reads),
+// with each row's rescale factor.  Per stage:
+//   QK(0); QK(1) + softmax(0); publish P0, alpha0; barrier A;
+//   rescale; PV(0) + softmax(1); publish P1, alpha1; barrier B; rescale; PV(1)
+// P0 has its own 8 KB; P1 goes to the stage's rope rows, which nobody
+// reads after barrier A (every wave's Q.K^T of the stage is done).
+// O tile 4d + r holds O^T for dims 128w + 32d .., rows 32r ..: lane (n, g)
+// is row 32r + n, dims 32d + 8q + 4g + e of the wave's slice (q, e < 4).
+// ---------------------------------------------------------------------------
+constexpr int kDsPOff = 2 * kStageBytes;                 // P of sub-tile 0: [128 rows][64 B]
+constexpr int kDsAlphaOff = kDsPOff + 128 * 64;          // f32 [2 sub-tiles][32 lanes][4 row blocks]
+constexpr int kDsLdsBytes = kDsAlphaOff + 2 * 128 * 4;   // 156672
+static_assert(kDsLdsBytes <= 160 * 1024, "dim-split LDS budget");
+static_assert(kStageBytes - kStageCkvBytes == 128 * 64, "P of sub-tile 1 fills the stage's rope rows");
+
+// Byte offset of lane (n, g)'s 16-byte P^T fragment (k-half kk) of row n of a
+// 32-row block in a P buffer: row R holds 4 chunks, chunk 2kk + g being the
+// 8 keys that lane (R % 32, g) of the row's owner wave holds for half kk;
+// chunks are XOR-swizzled by (R / 2) % 4 so that 8 consecutive rows cover
+// 8 distinct 16-byte bank groups.
+__device__ __forceinline__ int ds_p_off(int n, int g, int kk) { return n * 64 + 16 * ((2 * kk + g) ^ ((n >> 1) & 3)); }
+
+template <int kPC>
+__device__ __forceinline__ void ds_stage(const AttnArgs& a, const bf16x8 (&qf)[36], WideState& st,
+                                         LDS_AS char* __restrict__ cur, LDS_AS char* __restrict__ smem,
+                                         int stage_tok, int bound, const int (&kb)[8], const int (&pb)[4],
+                                         const int (&vb)[8], int g, int n, StageLoader<kPC>& ld, int wave) {
+  auto kread = [&](int tb, int ks) -> bf16x8 {
+    return ks < 32 ? lds_read_b128(cur, kb[ks & 7] + 256 * (ks >> 3) + tb * kCkvRowBytes)
+                   : lds_read_b128(cur, pb[ks - 32] + tb * kKpeRowBytes);
+  };
+  // V^T fragment: dims block 4 wave + d (32 dims), keys tb + 16 kk .. (16 keys)
+  auto vread = [&](int tb, int d, int kk) -> bf16x8 {
+    const int off = (tb + 16 * kk) * kCkvRowBytes + 256 * wave;
+    const i16x4 v0 = lds_read_tr(cur, vb[d] + off);
+    const i16x4 v1 = lds_read_tr(cur, vb[4 + d] + off);
+    const i16x8 v = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    return __builtin_bit_cast(bf16x8, v);
+  };
+
+  auto sm_scale_mask = [&](float (&sv)[16], WideSoftmax& sm, int tb, int r) {
+    float x = sv[r];
+    hold(x);
+    const int tok = stage_tok + tb + 8 * (r >> 2) + 4 * g + (r & 3);
+    x = tok < bound ? x * a.scale_log2 : kNegInf;
+    sv[r] = x;
+    sm.mx = fmaxf(sm.mx, x);
+    done(sm.mx);
+  };
+  auto sm_decide = [&](WideSoftmax& sm) {
+    sm.mx = max_xor32(sm.mx);
+    sm.raise = __builtin_amdgcn_ballot_w64(sm.mx > st.m_run + kRescaleSlack) != 0;
+    sm.alpha = 1.f;
+    if (sm.raise) {
+      const float m_new = fmaxf(st.m_run, sm.mx);
+      sm.alpha = (st.m_run == kNegInf) ? 0.f : fast_exp2(st.m_run - m_new);
+      st.l_run *= sm.alpha;
+      st.m_run = m_new;
+    }
+    sm.mref = (st.m_run == kNegInf) ? 0.f : st.m_run;
+    done(sm.mref);
+  };
+  auto sm_exp = [&](const float (&sv)[16], const WideSoftmax& sm, bf16x8 (&pt)[2], int r) {
+    float x = sv[r];
+    hold(x);
+    const float p = fast_exp2(x - sm.mref);
+    st.l_run += p;
+    pt[r >> 3][r & 7] = (__bf16)p;
+    done(st.l_run);
+  };
+
+  auto qk = [&](f32x16& sacc, int tb, int dma0, auto&& side) {
+    constexpr int KD = 3;  // K fragments in flight
+    bf16x8 kr[KD];
+#pragma unroll
+    for (int i = 0; i < KD; ++i) kr[i] = kread(tb, i);
+#pragma unroll
+    for (int ks = 0; ks < 36; ++ks) {
+      pin_loads();
+      if ((ks & 3) == 0 && dma0 + (ks >> 2) < StageLoader<kPC>::kSlices)
+        ld.issue(a, dma0 + (ks >> 2), wave);  // the next stage, 9 slices per sub-tile
+      const bf16x8 k0 = kr[ks % KD];
+      if (ks == 0) {
+        mfma32_first<false>(sacc, k0, qf[0]);
+      } else {
+        mfma32_acc<false>(sacc, k0, qf[ks]);
+      }
+      if (ks + KD < 36) kr[ks % KD] = kread(tb, ks + KD);
+      side(ks);
+    }
+    pin_loads();
+    mfma32_drain(sacc);
+  };
+
+  // Publish this wave's P (its 32 rows) and rescale factors of a sub-tile.
+  auto publish = [&](LDS_AS char* pbuf, const bf16x8 (&pt)[2], const WideSoftmax& sm, int t) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) *(LDS_AS bf16x8*)(pbuf + wave * 2048 + ds_p_off(n, g, kk)) = pt[kk];
+    if (g == 0) ((LDS_AS float*)(smem + kDsAlphaOff))[t * 128 + n * 4 + wave] = sm.alpha;
+  };
+  // After the barrier: scale O rows by their factors when any row of the
+  // workgroup raised its running max (the factors are 1 otherwise).
+  auto rescale = [&](int t, bool drain) {
+    const f32x4 al = *(const LDS_AS f32x4*)(smem + kDsAlphaOff + t * 512 + n * 16);
+    const bool any = __builtin_amdgcn_ballot_w64(al[0] != 1.f || al[1] != 1.f || al[2] != 1.f || al[3] != 1.f) != 0;
+    if (any && st.o_live) {
+      if (drain) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");  // let the last P.V MFMAs retire
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) scale_acc<16>(st.o[4 * d + r], al[r]);
+    }
+  };
+  // O^T[dims of the wave][128 rows] += V^T . P^T over the 32 keys of sub-tile tb.
+  // Per k-half: 4 V^T and 4 P^T fragments, 16 MFMAs on 16 different tiles.
+  auto pv = [&](int tb, const LDS_AS char* pbuf, auto&& side) {
+    bf16x8 va[4], pa[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pa[r] = lds_read_b128(pbuf, r * 2048 + ds_p_off(n, g, 0));
+#pragma unroll
+    for (int d = 0; d < 4; ++d) va[d] = vread(tb, d, 0);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          pin_loads();
+          const int i = 16 * kk + 4 * r + d;
+          st.o[4 * d + r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[d], pa[r], st.o[4 * d + r], 0, 0, 0);
+          // the other k-half's fragments, each once its last use has issued
+          if (kk == 0 && r == 3) va[d] = vread(tb, d, 1);
+          if (kk == 0 && d == 3) pa[r] = lds_read_b128(pbuf, r * 2048 + ds_p_off(n, g, 1));
+          side(i);
+        }
+      }
+    }
+    pin_loads();
+  };
+
+  f32x16 sa0, sa1;
+  float s0[16], s1[16];
+  WideSoftmax sm0, sm1;
+  bf16x8 pt0[2], pt1[2];
+  LDS_AS char* p0 = smem + kDsPOff;
+  LDS_AS char* p1 = cur + kStageCkvBytes;
+  qk(sa0, 0, 0, [&](int) {});
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s0[r] = sa0[r];
+  qk(sa1, 32, 9, [&](int ks) {
+    if (ks < 16) sm_scale_mask(s0, sm0, 0, ks);
+    if (ks == 16) sm_decide(sm0);
+    if (ks >= 17 && ks < 33) sm_exp(s0, sm0, pt0, ks - 17);
+  });
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s1[r] = sa1[r];
+  publish(p0, pt0, sm0, 0);
+  __syncthreads();  // A: P0 and its factors visible; every wave's Q.K^T of the stage is done
+  rescale(0, false);
+  pv(0, p0, [&](int i) {
+    if (i < 16) sm_scale_mask(s1, sm1, 32, i);
+    if (i == 16) sm_decide(sm1);
+    if (i >= 17) sm_exp(s1, sm1, pt1, i - 17);
+  });
+  sm_exp(s1, sm1, pt1, 15);
+  st.o_live = true;
+  publish(p1, pt1, sm1, 1);
+  __syncthreads();  // B: P1 and its factors visible
+  rescale(1, true);
+  pv(32, p1, [&](int) {});
+}
+
+// Dim-split WIDE epilogue: the row owners share 1 / l (and the output scale
+// of final rows) through LDS; each wave then writes its 128 dims of every
+// row.  bf16 rows are staged in LDS (256 bytes per row slice, 16-byte
+// chunks XOR-swizzled by row) and stored 4 rows per instruction.
+__device__ __forceinline__ void ds_epilogue(const AttnArgs& a, const WorkItem& it, WideState& st,
+                                            LDS_AS char* smem, int wave) {
+  const int lane = lane_here();
+  const int g = lane >> 5;
+  const int n = lane & 31;
+  const int rib = wave * 32 + n;
+  const RowInfo ri = row_info(a, it, rib);
+  const float l_tot = sum_xor32(st.l_run);
+  const bool empty = !(l_tot > 0.f);
+  const float inv = empty ? 0.f : (it.slot < 0 ? a.out_scale : 1.f) / l_tot;
+  if (ri.ok && g == 0) store_lse(a, it, ri, rib, empty ? kNegInf : (st.m_run + __log2f(l_tot)) * kLn2);
+  LDS_AS float* invb = (LDS_AS float*)(smem + kDsAlphaOff);
+  if (g == 0) invb[n * 4 + wave] = inv;
+  __syncthreads();
+  const f32x4 inv4 = *(const LDS_AS f32x4*)(invb + n * 4);
+  if (a.out_bf16 || it.slot >= 0) {
+    LDS_AS char* ob = smem + wave * 128 * 256;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int R = 32 * r + n;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          bf16x4 h;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) h[e] = (__bf16)(st.o[4 * d + r][4 * q + e] * inv4[r]);
+          const int c = 4 * d + q;  // 16-byte chunk of the 256-byte row slice
+          *(LDS_AS bf16x4*)(ob + R * 256 + ((c ^ (R & 15)) << 4) + 8 * g) = h;
+        }
+      }
+    }
+    const size_t out_row0 = row_base(a, it) + it.row0;
+    const int c = lane & 15;
+#pragma unroll 4
+    for (int i = 0; i < 32; ++i) {
+      const int R = 4 * i + (lane >> 4);
+      const u32x4 v = *(const LDS_AS u32x4*)(ob + R * 256 + ((c ^ (R & 15)) << 4));
+      if (R < it.nrows) {
+        __bf16* dst = (it.slot < 0) ? (__bf16*)a.out + (out_row0 + R) * kDimCkv
+                                    : a.part_o + ((size_t)it.slot * a.rows_per_block + R) * kDimCkv;
+        *(u32x4*)(dst + 128 * wave + 8 * c) = v;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const RowInfo rr = row_info(a, it, 32 * r + n);
+      if (!rr.ok) continue;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 v = {st.o[4 * d + r][4 * q] * inv4[r], st.o[4 * d + r][4 * q + 1] * inv4[r],
+                           st.o[4 * d + r][4 * q + 2] * inv4[r], st.o[4 * d + r][4 * q + 3] * inv4[r]};
+          store4(a, it, rr, 32 * r + n, 128 * wave + 32 * d + 8 * q + 4 * g, v);
+        }
+      }
+    }
+  }
+  __syncthreads();  // the staging rows overlap the next item's first stage
+}
+
+template <int kPC>
+__device__ void ds_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* smem, int wave) {
+  const int lane = lane_here();
+  const int g = lane >> 5;
+  const int n = lane & 31;
+  const RowInfo ri = row_info(a, it, wave * 32 + n);
+  const int bound = row_key_bound(a, it, ri);
+
+  // Stage 0's direct loads first, then the query rows (unconditional: a
+  // missing row reads the item's first row and is masked by its bound of 0).
+  const int page_base = ld_const(a.kv_indptr, it.b);
+  const int nstage = (it.tok1 - it.tok0 + kStageTokens - 1) / kStageTokens;
+  if (nstage > 0) issue_stage_bf16<kPC>(a, smem, page_base, it.tok0, it.tok1, wave, lane);
+  bf16x8 qf[36];
+  {
+    const __bf16* qn = (const __bf16*)a.q_nope + ri.qrow * a.q_stride + 8 * g;
+    const __bf16* qp = (const __bf16*)a.q_pe + ri.qrow * a.qpe_stride + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 32; ++ks) qf[ks] = *(const bf16x8*)(qn + 16 * ks);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qf[32 + ks] = *(const bf16x8*)(qp + 16 * ks);
+  }
+  int kb[8], pb[4], vb[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) kb[k] = ckv_off(n, 2 * k + g);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) pb[k] = kpe_off(n, 2 * k + g);
+  {
+    const int t0 = 4 * g + ((lane & 15) >> 2);
+    const int cl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    const int w8 = (lane & 1) ? 8 : 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      vb[k] = ckv_off(t0, 4 * k + cl) + w8;
+      vb[4 + k] = ckv_off(t0 + 8, 4 * k + cl) + w8;
+    }
+  }
+
+  WideState st;
+#pragma unroll
+  for (int cb = 0; cb < 16; ++cb) st.o[cb] = f32x16{};
+  st.m_run = kNegInf;
+  st.l_run = 0.f;
+  st.o_live = false;
+  st.m_top = kNegInf;
+
+  auto page_at = [&](int stage) -> int {
+    return kPC == kPageBig ? ld_const(a.kv_indices, page_base + ((it.tok0 + stage * kStageTokens) >> a.page_shift))
+                           : -1;
+  };
+  int pg_next = page_at(nstage > 1 ? 1 : 0);
+  for (int s = 0; s < nstage; ++s) {
+    const int pg_after = page_at(s + 2 < nstage ? s + 2 : 0);
+    wait_vmcnt<0>();
+    __syncthreads();
+    LDS_AS char* cur = smem + (s & 1) * kStageBytes;
+    StageLoader<kPC> ld;
+    const bool more = s + 1 < nstage;
+    ld.begin(a, smem + ((s + 1) & 1) * kStageBytes, page_base, it.tok0 + (more ? s + 1 : s) * kStageTokens, it.tok1,
+             wave, pg_next);
+    ld.on = __builtin_amdgcn_readfirstlane(more ? ~0u : 0u);
+    ds_stage<kPC>(a, qf, st, cur, smem, it.tok0 + s * kStageTokens, bound, kb, pb, vb, g, n, ld, wave);
+    pg_next = pg_after;
+  }
+  __syncthreads();  // every wave is done with the last stage before the epilogue uses the LDS
+  ds_epilogue(a, it, st, smem, wave);
 }
 
 // ---------------------------------------------------------------------------
@@ -967,12 +1297,21 @@ __device__ __forceinline__ bf16x8 codes8(uint32_t lo, uint32_t hi) {
 // straight from the key codes in LDS (no conversion); the 64 rope dims are
 // converted to bf16 once (exactly) and stay on the bf16 MFMA, as does P.V.
 template <int kPC, bool kSparse = false, bool kQ8 = false>
-__device__ void wide8_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* smem, int wave, int lane) {
+__device__ void wide8_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* smem, int wave, int) {
+  const int lane = lane_here();  // lane-derived values recomputed per item (kept across items they get spilled)
   const int g = lane >> 5;
   const int n = lane & 31;
   const int rib = wave * 32 + n;
   const RowInfo ri = row_info(a, it, rib);
   const int bound = row_key_bound(a, it, ri);
+
+  // Stage 0's records go out first, then the query rows, then stage 1: the
+  // first stage's wait (all but one stage's loads) then covers the query.
+  // The query loads are unconditional (a missing row reads the item's first
+  // row and is masked by its key bound of 0), so no wait splits them.
+  const int page_base = ld_const(a.kv_indptr, it.b);
+  const int nstage = (it.tok1 - it.tok0 + kStageTokens - 1) / kStageTokens;
+  if (nstage > 0) issue_stage_fp8<kPC>(a, smem, page_base, it.tok0, it.tok1, wave);
 
   // Query fragments in the codes' dim order: nope k-step 2m+s, half g holds
   // dims 32m + 16g + 8s .. +7; rope k-steps as in the bf16 path.  kQ8: step
@@ -981,32 +1320,28 @@ __device__ void wide8_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* s
   bf16x8 qr[4];
   i32x8 q8[kQ8 ? 8 : 1];
   if constexpr (kQ8) {
-    const i32x8 z = {};
     const uint8_t* qc = (const uint8_t*)a.q_nope + ri.qrow * a.q_stride;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const u32x4 lo = ri.ok ? *(const u32x4*)(qc + 64 * c + 32 * g) : u32x4{};
-      const u32x4 hi = ri.ok ? *(const u32x4*)(qc + 64 * c + 32 * g + 16) : u32x4{};
-      q8[c] = ri.ok ? i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2],
-                            (int)hi[3]}
-                    : z;
+      const u32x4 lo = *(const u32x4*)(qc + 64 * c + 32 * g);
+      const u32x4 hi = *(const u32x4*)(qc + 64 * c + 32 * g + 16);
+      q8[c] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
     }
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-      const u32x2 c8 = ri.ok ? *(const u32x2*)(qc + kDimCkv + 16 * ks + 8 * g) : u32x2{};
+      const u32x2 c8 = *(const u32x2*)(qc + kDimCkv + 16 * ks + 8 * g);
       qr[ks] = codes8(c8[0], c8[1]);
     }
   } else {
-    const bf16x8 z = {};
     const __bf16* qn = (const __bf16*)a.q_nope + ri.qrow * a.q_stride + 16 * g;
     const __bf16* qp = (const __bf16*)a.q_pe + ri.qrow * a.qpe_stride + 8 * g;
 #pragma unroll
     for (int m = 0; m < 16; ++m)
 #pragma unroll
-      for (int sh = 0; sh < 2; ++sh) qf[2 * m + sh] = ri.ok ? *(const bf16x8*)(qn + 32 * m + 8 * sh) : z;
+      for (int sh = 0; sh < 2; ++sh) qf[2 * m + sh] = *(const bf16x8*)(qn + 32 * m + 8 * sh);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qr[ks] = ri.ok ? *(const bf16x8*)(qp + 16 * ks) : z;
+    for (int ks = 0; ks < 4; ++ks) qr[ks] = *(const bf16x8*)(qp + 16 * ks);
   }
   // byte offsets inside a raw stage
   const int kaddr = n * kFp8RecordBytes + (kQ8 ? 32 : 16) * g;           // + tb*656 + 32m (kQ8: + 64c)
@@ -1030,9 +1365,6 @@ __device__ void wide8_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* s
   st.o_live = false;
   float m_top = kNegInf;  // token-sparse: the row's largest logit (log2 units)
 
-  const int page_base = ld_const(a.kv_indptr, it.b);
-  const int nstage = (it.tok1 - it.tok0 + kStageTokens - 1) / kStageTokens;
-  if (nstage > 0) issue_stage_fp8<kPC>(a, smem, page_base, it.tok0, it.tok1, wave);
   if (nstage > 1) issue_stage_fp8<kPC>(a, smem + kFp8RawBytes, page_base, it.tok0 + kStageTokens, it.tok1, wave);
   for (int s = 0; s < nstage; ++s) {
     // stage s must have landed; stage s+1's records may still be in flight
@@ -1218,7 +1550,10 @@ __device__ void wide8_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* s
     }
   }
   __syncthreads();  // every wave is done with the stage buffers before the epilogue stages rows there
-  wide_epilogue<true, kSparse>(a, it, st, ri, rib, smem, wave, lane, m_top);
+  {
+    const int rib_e = wave * 32 + (lane_here() & 31);  // row info recomputed rather than kept across the loop
+    wide_epilogue<true, kSparse>(a, it, st, row_info(a, it, rib_e), rib_e, smem, wave, lane, m_top);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1742,57 +2077,6 @@ void mla_attn_quad_kernel(AttnArgs a) {
   }
 }
 
-// Workgroup -> work list.  Workgroups are dealt to the 8 XCDs round-robin
-// (blockIdx mod 8); lists are numbered so that consecutive lists land on
-// one XCD.  The planner fills lists in request order, so the pieces of a
-// split request, or the row blocks of a prefill request, share an L2 (their
-// query rows, and keys read at the same time, come from HBM once).  A
-// bijection for any list count n: XCD x runs ceil((n - x) / 8) lists.
-__device__ __forceinline__ int xcd_list(int b, int n) {
-  const int x = b & 7;
-  int base = 0;
-#pragma unroll
-  for (int y = 0; y < 7; ++y) base += (y < x) ? (n - y + 7) >> 3 : 0;
-  return base + (b >> 3);
-}
-
-template <int kMode, int kPC, bool kFp8, bool kSparse = false, bool kQ8 = false>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void mla_attn_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem_raw[kFp8 ? kFp8LdsBytes : kLdsBytes];
-  LDS_AS char* smem = (LDS_AS char*)smem_raw;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int list = xcd_list(blockIdx.x, a.num_wgs);
-  const int i0 = ld_const(a.wg_ptr, list);
-  const int i1 = ld_const(a.wg_ptr, list + 1);
-  for (int i = i0; i < i1; ++i) {
-    const int32_t* ip = (const int32_t*)(a.items + i);
-    WorkItem it;
-    it.b = ld_const(ip, 0);
-    it.row0 = ld_const(ip, 1);
-    it.nrows = ld_const(ip, 2);
-    it.tok0 = ld_const(ip, 3);
-    it.tok1 = ld_const(ip, 4);
-    it.kv_len = ld_const(ip, 5);
-    it.q_len = ld_const(ip, 6);
-    it.slot = ld_const(ip, 7);
-    if (kSparse) {
-      // the list's valid keys were counted on the device: pieces past them are empty
-      const int L = ld_const(a.sparse_len, it.b);
-      it.kv_len = L;
-      it.tok1 = max(it.tok0, min(it.tok1, L));
-    }
-    if (kMode == 1 && kFp8) {
-      wide8_item<kPC, kSparse, kQ8>(a, it, smem, wave, lane);
-    } else if (kMode == 1) {
-      wide_item<kPC, kSparse>(a, it, smem, wave, lane);
-    } else {
-      narrow_item<kPC, kFp8>(a, it, smem, wave, lane);
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Combine: merge the partial results of each split (request, row block).
 // out = sum_s w_s o_s / sum_s w_s with w_s = exp(lse_s - max lse), and
@@ -1804,11 +2088,7 @@ void mla_attn_kernel(AttnArgs a) {
 constexpr int kCombineRows = 4;  // rows per combine workgroup (one per wave)
 constexpr int kCombineBatch = 8;  // partial rows in flight per lane
 
-__global__ __launch_bounds__(256) void mla_combine_kernel(AttnArgs a) {
-  const int chunks_per_group = a.rows_per_block / kCombineRows;
-  const int gi = blockIdx.x / chunks_per_group;
-  const int r = (blockIdx.x - gi * chunks_per_group) * kCombineRows + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
+__device__ __forceinline__ void combine_row(const AttnArgs& a, int gi, int r, int lane) {
   const int32_t* gp = (const int32_t*)(a.groups + gi);
   const int g_b = ld_const(gp, 0), g_row0 = ld_const(gp, 1), g_nrows = ld_const(gp, 2);
   const int nsplit = ld_const(gp, 3), slot0 = ld_const(gp, 4);
@@ -1881,6 +2161,69 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(AttnArgs a) {
   }
   if (lane == 0) a.lse[qrow] = (W > 0.f) ? M + __logf(W) : kNegInf;
 }
+
+__global__ __launch_bounds__(256) void mla_combine_kernel(AttnArgs a) {
+  const int chunks_per_group = a.rows_per_block / kCombineRows;
+  const int gi = blockIdx.x / chunks_per_group;
+  const int r = (blockIdx.x - gi * chunks_per_group) * kCombineRows + (threadIdx.x >> 6);
+  combine_row(a, gi, r, threadIdx.x & 63);
+}
+
+
+// Workgroup -> work list.  Workgroups are dealt to the 8 XCDs round-robin
+// (blockIdx mod 8); lists are numbered so that consecutive lists land on
+// one XCD.  The planner fills lists in request order, so the pieces of a
+// split request, or the row blocks of a prefill request, share an L2 (their
+// query rows, and keys read at the same time, come from HBM once).  A
+// bijection for any list count n: XCD x runs ceil((n - x) / 8) lists.
+__device__ __forceinline__ int xcd_list(int b, int n) {
+  const int x = b & 7;
+  int base = 0;
+#pragma unroll
+  for (int y = 0; y < 7; ++y) base += (y < x) ? (n - y + 7) >> 3 : 0;
+  return base + (b >> 3);
+}
+
+template <int kMode, int kPC, bool kFp8, bool kSparse = false, bool kQ8 = false>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mla_attn_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(1024))) char
+      smem_raw[kFp8 ? kFp8LdsBytes : (kMode == 1 && !kSparse ? kDsLdsBytes : kLdsBytes)];
+  LDS_AS char* smem = (LDS_AS char*)smem_raw;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int list = xcd_list(blockIdx.x, a.num_wgs);
+  const int i0 = ld_const(a.wg_ptr, list);
+  const int i1 = ld_const(a.wg_ptr, list + 1);
+  for (int i = i0; i < i1; ++i) {
+    const int32_t* ip = (const int32_t*)(a.items + i);
+    WorkItem it;
+    it.b = ld_const(ip, 0);
+    it.row0 = ld_const(ip, 1);
+    it.nrows = ld_const(ip, 2);
+    it.tok0 = ld_const(ip, 3);
+    it.tok1 = ld_const(ip, 4);
+    it.kv_len = ld_const(ip, 5);
+    it.q_len = ld_const(ip, 6);
+    it.slot = ld_const(ip, 7);
+    if (kSparse) {
+      // the list's valid keys were counted on the device: pieces past them are empty
+      const int L = ld_const(a.sparse_len, it.b);
+      it.kv_len = L;
+      it.tok1 = max(it.tok0, min(it.tok1, L));
+    }
+    if (kMode == 1 && kFp8) {
+      wide8_item<kPC, kSparse, kQ8>(a, it, smem, wave, lane);
+    } else if (kMode == 1 && !kSparse) {
+      ds_item<kPC>(a, it, smem, wave);
+    } else if (kMode == 1) {
+      wide_item<kPC, kSparse>(a, it, smem, wave, lane);
+    } else {
+      narrow_item<kPC, kFp8>(a, it, smem, wave, lane);
+    }
+  }
+}
+
 
 }  // namespace
 
