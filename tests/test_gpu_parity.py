@@ -177,6 +177,7 @@ PREFILL_CASES = [
     (128, 16, [2, 4], [300, 17], True, 3, 3),
     (32, 64, [8, 1, 3], [500, 9, 64], True, 3, 2),
     (128, 256, [4, 2], [800, 300], True, 1, 2),
+    (40, 16, [3, 5], [200, 37], True, 1, 2),   # WIDE blocks mixing query tokens (per-row causal bounds)
 ]
 
 
