@@ -2081,55 +2081,63 @@ void mla_attn_quad_kernel(AttnArgs a) {
 // Combine: merge the partial results of each split (request, row block).
 // out = sum_s w_s o_s / sum_s w_s with w_s = exp(lse_s - max lse), and
 // lse = max lse + ln sum w (the log-sum-exp identity).  One wave per row:
-// lane l owns dims 8l..8l+7.  The loads of the first 8 splits' partial rows
-// are issued together with the lse reads (they do not depend on them), so a
-// row costs one memory round trip when it has at most 8 splits.
+// lane l owns dims 8l..8l+7.  The split lse values (and partial maxima) are
+// wave-uniform, so they are scalar loads that every lane uses directly: the
+// maximum and the weights need no cross-lane step.  The partial rows of the
+// first 8 splits are loaded together with them, so a row with at most 8
+// splits costs one memory round trip.
 // ---------------------------------------------------------------------------
 constexpr int kCombineRows = 4;  // rows per combine workgroup (one per wave)
 constexpr int kCombineBatch = 8;  // partial rows in flight per lane
+
+__device__ __forceinline__ float ld_const_f(const float* p, size_t i) {
+  return __builtin_bit_cast(float, ((const CONST_AS int32_t*)p)[i]);
+}
 
 __device__ __forceinline__ void combine_row(const AttnArgs& a, int gi, int r, int lane) {
   const int32_t* gp = (const int32_t*)(a.groups + gi);
   const int g_b = ld_const(gp, 0), g_row0 = ld_const(gp, 1), g_nrows = ld_const(gp, 2);
   const int nsplit = ld_const(gp, 3), slot0 = ld_const(gp, 4);
   if (r >= g_nrows) return;
+  const int q_start = a.qo_indptr ? ld_const(a.qo_indptr, g_b) : g_b;
   const size_t row0 = (size_t)slot0 * a.rows_per_block + r;  // row r of the group's first slot
   const size_t stride = (size_t)a.rows_per_block;             // rows between consecutive slots
   const int d0 = lane * 8;
   auto prow = [&](int sp) { return *(const bf16x8*)(a.part_o + (row0 + (size_t)sp * stride) * kDimCkv + d0); };
+  auto lse_at = [&](int sp) { return ld_const_f(a.part_lse, row0 + (size_t)sp * stride); };
   bf16x8 v[kCombineBatch];
+  float ls[kCombineBatch];
 #pragma unroll
-  for (int j = 0; j < kCombineBatch; ++j)
-    if (j < nsplit) v[j] = prow(j);
-  // lse of split `lane` (splits >= 64 are read where they are needed)
-  const float ls_lane = lane < nsplit ? a.part_lse[row0 + (size_t)lane * stride] : kNegInf;
-  auto lse_of = [&](int sp) -> float {  // sp wave-uniform
-    return sp < 64 ? __shfl(ls_lane, sp) : a.part_lse[row0 + (size_t)sp * stride];
-  };
-  float M = ls_lane;
-  for (int sp = lane + 64; sp < nsplit; sp += 64) M = fmaxf(M, a.part_lse[row0 + (size_t)sp * stride]);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-  float W = 0.f;
-  for (int sp = lane; sp < nsplit; sp += 64) {
-    const float ls = sp < 64 ? ls_lane : a.part_lse[row0 + (size_t)sp * stride];
-    W += (ls == kNegInf) ? 0.f : __expf(ls - M);
+  for (int j = 0; j < kCombineBatch; ++j) {
+    if (j < nsplit) {
+      v[j] = prow(j);
+      ls[j] = lse_at(j);
+    } else {
+      ls[j] = kNegInf;
+    }
   }
+  float M = kNegInf;
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) W += __shfl_xor(W, o);
+  for (int j = 0; j < kCombineBatch; ++j) M = fmaxf(M, ls[j]);
+  for (int sp = kCombineBatch; sp < nsplit; ++sp) M = fmaxf(M, lse_at(sp));
+  float W = 0.f;
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if (M != kNegInf) {
     for (int c = 0; c < nsplit; c += kCombineBatch) {
       if (c > 0) {
 #pragma unroll
-        for (int j = 0; j < kCombineBatch; ++j)
-          if (c + j < nsplit) v[j] = prow(c + j);
+        for (int j = 0; j < kCombineBatch; ++j) {
+          if (c + j < nsplit) {
+            v[j] = prow(c + j);
+            ls[j] = lse_at(c + j);
+          }
+        }
       }
 #pragma unroll
       for (int j = 0; j < kCombineBatch; ++j) {
         if (c + j < nsplit) {
-          const float ls = lse_of(c + j);
-          const float w = (ls == kNegInf) ? 0.f : __expf(ls - M);
+          const float w = (ls[j] == kNegInf) ? 0.f : __expf(ls[j] - M);
+          W += w;
 #pragma unroll
           for (int e = 0; e < 8; ++e) acc[e] += w * (float)v[j][e];
         }
@@ -2137,7 +2145,6 @@ __device__ __forceinline__ void combine_row(const AttnArgs& a, int gi, int r, in
     }
   }
   const int H = a.num_heads;
-  const int q_start = a.qo_indptr ? ld_const(a.qo_indptr, g_b) : g_b;
   const int rr = g_row0 + r;
   const int qi = rr / H;
   const size_t qrow = (size_t)(q_start + qi) * H + (rr - qi * H);
@@ -2146,7 +2153,7 @@ __device__ __forceinline__ void combine_row(const AttnArgs& a, int gi, int r, in
   const float inv = (W > 0.f) ? a.out_scale / den : 0.f;
   if (a.max_logits != nullptr && lane == 0) {
     float mx = kNegInf;
-    for (int sp = 0; sp < nsplit; ++sp) mx = fmaxf(mx, a.part_max[row0 + (size_t)sp * stride]);
+    for (int sp = 0; sp < nsplit; ++sp) mx = fmaxf(mx, ld_const_f(a.part_max, row0 + (size_t)sp * stride));
     a.max_logits[qrow] = mx;
   }
   if (a.out_bf16) {
