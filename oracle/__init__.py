@@ -50,4 +50,10 @@ from .mla_oracle import (  # noqa: F401
     sparse_attend,
     mla_sparse_decode_fp8_ref,
     mla_sparse_prefill_ref,
+    M1_NOPE,
+    M1_RECORD_BYTES,
+    f32_to_bf16_rne,
+    model1_record_decode,
+    model1_record_encode,
+    mla_decode_model1_ref,
 )

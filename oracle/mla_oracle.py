@@ -63,6 +63,12 @@ HEAD_DIM_KPE = 64
 FP8_TILE = 128
 FP8_NUM_TILES = HEAD_DIM_CKV // FP8_TILE
 FP8_RECORD_BYTES = HEAD_DIM_CKV + 4 * FP8_NUM_TILES + 2 * HEAD_DIM_KPE  # 656
+# MODEL1_FP8Sparse ("FP8 KV Cache Quantization and Dequantization"): 448 NoPE
+# dims in 7 tiles of 64, 64 RoPE dims, d = 512 for q.k
+M1_NOPE = 448
+M1_TILE = 64
+M1_NUM_TILES = M1_NOPE // M1_TILE
+M1_RECORD_BYTES = M1_NOPE + 4 * M1_NUM_TILES + 2 * HEAD_DIM_KPE  # 604
 
 
 # ---------------------------------------------------------------------------
@@ -223,6 +229,97 @@ def fp8_record_encode(tokens) -> np.ndarray:
     # the rows came from bf16 so the low half is zero: truncation is exact
     out[:, HEAD_DIM_CKV + 16:] = rope_bits.view(np.uint8).reshape(n, 2 * HEAD_DIM_KPE)
     return out.reshape(*lead, FP8_RECORD_BYTES)
+
+
+def f32_to_bf16_rne(x) -> np.ndarray:
+    """float32 values -> the nearest bfloat16 values (ties to even mantissa),
+    returned as float64.  Written out on the fp32 bit pattern: add
+    0x7FFF plus the lowest kept bit, then clear the low 16 bits (finite
+    inputs only; the dequantised keys are bounded by the bf16 source)."""
+    f = np.asarray(x, dtype=np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def model1_record_decode(records) -> tuple[np.ndarray, np.ndarray]:
+    """604-byte MODEL1 token records -> (NoPE [..., 448], RoPE [..., 64]) float64.
+
+    "FP8 KV Cache Quantization and Dequantization" names the MODEL1_FP8Sparse
+    layout by its sizes only (d = 512, d_nope = 448, d_rope = 64, tile 64,
+    7 tiles); it prints the byte layout of V32_FP8Sparse alone.  Reading:
+    the same order as the printed one, packed: bytes 0..447 are the e4m3
+    codes (tile t = dims [64t, 64t+64)), bytes 448..475 seven little-endian
+    fp32 scales, bytes 476..603 the 64 RoPE values as little-endian bf16.
+    The page's dequantize_k_cache returns BF16, so a NoPE value is
+    bf16(fp32(code) * scale): the product in fp32, then rounded to bf16
+    (both round to nearest even).
+    """
+    r = _as_u8(records)
+    assert r.shape[-1] == M1_RECORD_BYTES
+    lead = r.shape[:-1]
+    flat = r.reshape(-1, M1_RECORD_BYTES)
+    codes = flat[:, :M1_NOPE]
+    scales = np.ascontiguousarray(flat[:, M1_NOPE:M1_NOPE + 4 * M1_NUM_TILES]).view("<f4")
+    rope_bits = np.ascontiguousarray(flat[:, M1_NOPE + 4 * M1_NUM_TILES:]).view("<u2")
+    vals = e4m3_decode(codes).astype(np.float32).reshape(-1, M1_NUM_TILES, M1_TILE)
+    prod = (vals * scales[:, :, None]).astype(np.float32)  # fp32 multiply
+    nope = f32_to_bf16_rne(prod).reshape(-1, M1_NOPE)
+    rope = bf16_bits_to_f64(rope_bits)
+    return nope.reshape(*lead, M1_NOPE), rope.reshape(*lead, HEAD_DIM_KPE)
+
+
+def model1_record_encode(tokens) -> np.ndarray:
+    """bf16 token rows [..., 512] (448 NoPE + 64 RoPE) -> 604-byte records
+    (used only by tests).  Quantiser as for the 656-byte records, per
+    64-dim tile: scale = fp32(amax) / 448, codes = e4m3_encode(fp32(x / scale)),
+    a zero tile has scale 0 and codes 0; RoPE stored as its bf16 bits."""
+    x = as_f64(tokens)
+    assert x.shape[-1] == M1_NOPE + HEAD_DIM_KPE
+    lead = x.shape[:-1]
+    x = x.reshape(-1, M1_NOPE + HEAD_DIM_KPE)
+    n = x.shape[0]
+    nope = x[:, :M1_NOPE].astype(np.float32).reshape(n, M1_NUM_TILES, M1_TILE)
+    amax = np.abs(nope).max(axis=2)
+    scale = (amax / np.float32(448.0)).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = (nope / scale[:, :, None]).astype(np.float32)
+    q = np.where(scale[:, :, None] == 0, np.float32(0.0), q)
+    codes = e4m3_encode(q.astype(np.float64)).reshape(n, M1_NOPE)
+    out = np.zeros((n, M1_RECORD_BYTES), dtype=np.uint8)
+    out[:, :M1_NOPE] = codes
+    out[:, M1_NOPE:M1_NOPE + 4 * M1_NUM_TILES] = scale.astype("<f4").view(np.uint8).reshape(n, 4 * M1_NUM_TILES)
+    rope_bits = (x[:, M1_NOPE:].astype(np.float32).view(np.uint32) >> np.uint32(16)).astype("<u2")
+    out[:, M1_NOPE + 4 * M1_NUM_TILES:] = rope_bits.view(np.uint8).reshape(n, 2 * HEAD_DIM_KPE)
+    return out.reshape(*lead, M1_RECORD_BYTES)
+
+
+def mla_decode_model1_ref(q, kv_records, kv_indptr, kv_indices, kv_len, sm_scale: float, requests=None):
+    """Paged decode over MODEL1 records: q [B, H, 512] (448 NoPE + 64 RoPE
+    dims), records [num_pages, page_size, 604].  Returns out [B, H, 448],
+    lse [B, H] in float64.
+
+    Definition as for the 656-byte records ("MLA Paged" decode; slot
+    mapping and sizes from the FlashMLA FP8 section), with d = 512 for
+    q . k and, reading, V = the 448 NoPE dims (as V = the 512 NoPE dims
+    of the 656-byte layout).
+    """
+    qf = as_f64(q)
+    B, H, D = qf.shape
+    assert D == M1_NOPE + HEAD_DIM_KPE
+    kvl = _as_int(kv_len)
+    out = np.zeros((B, H, M1_NOPE))
+    lse = np.full((B, H), -np.inf)
+    for b in (range(B) if requests is None else requests):
+        L = int(kvl[b])
+        if L == 0:
+            continue
+        page, slot = _token_slots(_as_int(kv_indptr), _as_int(kv_indices), b, L, kv_records.shape[1])
+        kn, kp = model1_record_decode(_take_rows(kv_records, page, slot))
+        o, l = attend(qf[b, :, :M1_NOPE], qf[b, :, M1_NOPE:], kn, kp, sm_scale, L)
+        out[b] = o[:, :M1_NOPE]
+        lse[b] = l
+    return out, lse
 
 
 # ---------------------------------------------------------------------------

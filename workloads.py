@@ -97,6 +97,13 @@ SPARSE_PREFILL_CONFIGS = {
 
 SM_SCALE_DEFAULT = 1.0 / math.sqrt(192.0)
 
+# MODEL1 record decode at the shape of the 128-head decode (the pool holds
+# exactly the live pages, shuffled)
+MODEL1_CONFIGS = {
+    "decode_model1_b64_h128": dict(seed=12, batch=64, heads=128, page_size=64, kv_lens=("uniform", 512, 4096),
+                                   pool_factor=1),
+}
+
 
 @dataclasses.dataclass
 class Workload:
@@ -409,3 +416,75 @@ def quantize_q_e4m3(q_nope: torch.Tensor, q_pe: torch.Tensor) -> torch.Tensor:
     decode."""
     q = torch.cat([q_nope, q_pe], dim=-1).to(torch.float32).clamp(-448.0, 448.0)
     return q.to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
+
+
+# MODEL1 records (FlashMLA FP8 section, MODEL1_FP8Sparse: 448 NoPE dims in 7
+# tiles of 64, 64 RoPE dims; byte order as the printed 656-byte layout):
+# [448 e4m3 codes][7 x fp32 scale][64 x bf16 RoPE] = 604 bytes per token.
+MODEL1_NOPE = 448
+MODEL1_RECORD_BYTES = 604
+
+
+def quantize_model1_records(src: torch.Tensor) -> torch.Tensor:
+    """bf16 [..., 512] (448 NoPE + 64 RoPE) -> uint8 [..., 604] records (input
+    preparation): per 64-dim tile scale = amax / 448 in fp32, codes = the
+    float8_e4m3fn cast of x / scale after a clamp to +-448 (round to nearest
+    even); a zero tile has scale 0 and codes 0."""
+    lead = src.shape[:-1]
+    x = src.reshape(-1, MODEL1_NOPE + HEAD_DIM_KPE)
+    n = x.shape[0]
+    nope = x[:, :MODEL1_NOPE].to(torch.float32).reshape(n, 7, 64)
+    scale = nope.abs().amax(dim=-1) / 448.0
+    q = nope / scale.unsqueeze(-1)
+    q = torch.where(scale.unsqueeze(-1) == 0, torch.zeros_like(q), q)
+    out = torch.empty((n, MODEL1_RECORD_BYTES), dtype=torch.uint8, device=src.device)
+    out[:, :MODEL1_NOPE] = q.clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8).reshape(n, MODEL1_NOPE)
+    out[:, MODEL1_NOPE:MODEL1_NOPE + 28] = scale.contiguous().view(torch.uint8).reshape(n, 28)
+    out[:, MODEL1_NOPE + 28:] = x[:, MODEL1_NOPE:].contiguous().view(torch.uint8).reshape(n, 128)
+    return out.reshape(*lead, MODEL1_RECORD_BYTES)
+
+
+@dataclasses.dataclass
+class Model1Workload:
+    name: str
+    batch: int
+    num_heads: int
+    page_size: int
+    num_pages: int
+    q: torch.Tensor           # [B, H, 512] bf16
+    records: torch.Tensor     # [num_pages, page_size, 604] uint8
+    kv_indptr: torch.Tensor   # [B + 1] int32
+    kv_indices: torch.Tensor  # int32
+    kv_len: torch.Tensor      # [B] int32
+    sm_scale: float
+    seed: int
+
+
+def make_model1_workload(kv_lens=None, *, batch: Optional[int] = None, heads: int = 16, page_size: int = 64, seed: int = 0,
+                         device: Union[str, torch.device] = "cpu", pool_factor: int = 2,
+                         sm_scale: float = SM_SCALE_DEFAULT, name: str = "custom_model1") -> Model1Workload:
+    """Decode over MODEL1 records: lengths -> page permutation -> q -> source
+    pool (bf16 N(0,1), 512 dims per token) -> records, in that draw order."""
+    if kv_lens is None:
+        spec = dict(MODEL1_CONFIGS[name])
+        seed, batch, heads = spec["seed"], spec["batch"], spec["heads"]
+        page_size, kv_lens, pool_factor = spec["page_size"], spec["kv_lens"], spec["pool_factor"]
+    if batch is None:
+        batch = len(kv_lens)
+    g = torch.Generator().manual_seed(seed)
+    lens = _draw_lens(kv_lens, batch, g)
+    pages_per = (lens.to(torch.int64) + page_size - 1) // page_size
+    needed = int(pages_per.sum())
+    pool_pages = max(1, pool_factor * needed)
+    perm = torch.randperm(pool_pages, generator=g).to(torch.int32)
+    kv_indptr = torch.zeros(batch + 1, dtype=torch.int32)
+    kv_indptr[1:] = torch.cumsum(pages_per, 0).to(torch.int32)
+    device = torch.device(device)
+    gv = g if device.type == "cpu" else torch.Generator(device=device).manual_seed(seed)
+    q = _randn_bf16((batch, heads, MODEL1_NOPE + HEAD_DIM_KPE), gv, device)
+    src = _randn_bf16((pool_pages, page_size, MODEL1_NOPE + HEAD_DIM_KPE), gv, device,
+                      chunk_rows=max(1, 65536 // page_size))
+    records = quantize_model1_records(src)
+    return Model1Workload(name=name, batch=batch, num_heads=heads, page_size=page_size, num_pages=pool_pages,
+                          q=q, records=records, kv_indptr=kv_indptr, kv_indices=perm[:needed].clone(),
+                          kv_len=lens.to(torch.int32), sm_scale=sm_scale, seed=seed)
