@@ -309,6 +309,72 @@ def setup_dense(args, mla, dev):
             "cpu_baseline": lambda secs: cpu_baseline(w, flops, secs)}
 
 
+def setup_model1(args, mla, dev):
+    """Decode over MODEL1 records (448 NoPE dims in 7 tiles of 64 + 64 RoPE
+    dims, 604 bytes per token): one step expands the record pool to bf16
+    576-wide rows, widens q, and runs the concatenated-layout decode.
+
+    Algorithmic units of the MODEL1 attention: 2*512 + 2*448 = 1920 flops per
+    visible (row, key); bytes = live records (604 B per token) + q (1024 B per
+    row) + out (896 B per row, 448 bf16 dims) + lse + page indices.  The
+    roofline object covers the attention kernel; the expansion kernel's time
+    is in the kernel trace of the same command."""
+    import numpy as np
+    import torch
+
+    from workloads import make_model1_workload
+
+    log(f"bench: generating {args.config} on {dev}")
+    w = make_model1_workload(name=args.config, device=dev)
+    L = w.kv_len.numpy().astype(np.int64)
+    H = w.num_heads
+    flops = int(L.sum()) * H * (2 * 512 + 2 * 448)
+    live = int(L.sum()) * 604
+    bytes_alg = live + w.batch * H * (1024 + 896 + 4) + int(w.kv_indptr[-1]) * 4
+    t_plan = time.perf_counter()
+    plan = mla.mla_plan_create(mla.MLA_KIND_DECODE, w.batch, H, w.page_size, w.num_pages, w.kv_len, w.kv_indptr)
+    plan_ms = (time.perf_counter() - t_plan) * 1e3
+    kv_indptr = w.kv_indptr.to(dev)
+    kv_indices = w.kv_indices.to(dev)
+    reps = max(1, min(16, math.ceil(args.rotate_bytes / max(w.records.numel(), 1))))
+    pools = [w.records] + [w.records.clone() for _ in range(reps - 1)]
+    rows = torch.empty((w.num_pages, w.page_size, 576), dtype=torch.bfloat16, device=dev)
+    q576 = torch.empty((w.batch, H, 576), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((w.batch, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.batch, H), dtype=torch.float32, device=dev)
+    ws = plan.workspace(dev)
+    log(f"bench: {plan.num_work_items} work items on {plan.workgroup_ptr().numel() - 1} workgroups, "
+        f"{plan.num_split_groups} split groups, {reps} record pool replicas of {w.records.numel() / 1e6:.0f} MB")
+
+    def step(i):
+        mla.mla_model1_expand_records(pools[i % reps], rows)
+        mla.mla_model1_expand_q(w.q, q576)
+        mla.mla_decode_packed(plan, q576, rows, kv_indptr, kv_indices, w.sm_scale, out=out, lse=lse, workspace=ws)
+
+    def cpu(secs):
+        import oracle
+
+        args_ = (w.q.cpu(), w.records.cpu(), w.kv_indptr, w.kv_indices, w.kv_len, w.sm_scale)
+        done = 0.0
+        n = 0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < secs:
+            b = n % w.batch
+            oracle.mla_decode_model1_ref(*args_, requests=[b])
+            done += int(L[b]) * H * 1920
+            n += 1
+        dt = time.perf_counter() - t0
+        return {"value": done / dt / 1e12, "unit": "TFLOP/s", "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+                "sample": f"{n} request evaluations of {w.name}, {dt:.1f} s wall, float64 NumPy"}
+
+    config = {"workload": w.name, "batch": w.batch, "num_qo_heads": H, "head_dim_nope": 448, "head_dim_kpe": 64,
+              "page_size": w.page_size, "kv_format": "MODEL1 fp8 records (604 B)", "kv_len_total": int(L.sum()),
+              "rows": w.batch, "parallelism": "single GPU"}
+    return {"step": step, "flops": flops, "live_kv": live, "bytes_alg": bytes_alg, "plan_ms": plan_ms,
+            "config": config, "kernel": "mla_attn_kernel",
+            "dtype": "MODEL1 e4m3 records expanded to bf16 rows, bf16 math", "cpu_baseline": cpu}
+
+
 def setup_sparse(args, mla, dev):
     """Plan, inputs and step of a token-sparse workload (fp8 records, or bf16
     KV rows for the sparse prefill form).
@@ -434,7 +500,7 @@ def main():
     import torch
 
     import paged_mla_decode_05_amd as mla
-    from workloads import SPARSE_CONFIGS, SPARSE_PREFILL_CONFIGS
+    from workloads import MODEL1_CONFIGS, SPARSE_CONFIGS, SPARSE_PREFILL_CONFIGS
 
     if not os.path.exists(mla.lib_path()):
         import __graft_entry__
@@ -442,7 +508,12 @@ def main():
         __graft_entry__.build()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    setup = setup_sparse if (args.config in SPARSE_CONFIGS or args.config in SPARSE_PREFILL_CONFIGS) else setup_dense
+    if args.config in MODEL1_CONFIGS:
+        setup = setup_model1
+    elif args.config in SPARSE_CONFIGS or args.config in SPARSE_PREFILL_CONFIGS:
+        setup = setup_sparse
+    else:
+        setup = setup_dense
     S = setup(args, mla, dev)
     step, flops, live_kv, bytes_alg, plan_ms = S["step"], S["flops"], S["live_kv"], S["bytes_alg"], S["plan_ms"]
 

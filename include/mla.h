@@ -255,6 +255,32 @@ mla_status mla_prefill_packed(const mla_plan* plan, const void* q, const void* k
 mla_status mla_block_table_to_indices(const mla_plan* plan, const int32_t* block_table, int32_t max_blocks,
                                       const int32_t* kv_indptr, int32_t* kv_indices, hipStream_t stream);
 
+/* MODEL1 records (FlashMLA digest, "FP8 KV Cache Quantization and
+ * Dequantization": MODEL1_FP8Sparse, d = 512 for q.k, 448 NoPE dims in 7
+ * tiles of 64 e4m3 codes with one fp32 scale each, 64 bf16 RoPE dims).  The
+ * page gives sizes only; the byte order read here follows its printed
+ * 656-byte layout: [448 codes][7 x fp32 scale][64 x bf16 RoPE], 604 bytes
+ * per token, tile t = NoPE dims [64t, 64t+64).  The page dequantises to
+ * BF16: value = bf16(fp32(code) * scale), both steps round to nearest even.
+ *
+ * mla_model1_expand_records: records [num_tokens, 604] (u8, device, 4-byte
+ * aligned) -> rows [num_tokens, 576] (bf16, device, 16-byte aligned) in the
+ * concatenated layout of mla_decode_packed / mla_prefill_packed /
+ * mla_sparse_prefill: dims 0..447 the dequantised NoPE values, 448..511
+ * zero, 512..575 the RoPE values.  num_tokens counts every record of the
+ * array (a paged pool is num_pages * page_size records, kept in order).
+ * mla_model1_expand_q: query rows [num_rows, 512] (bf16: 448 NoPE + 64
+ * RoPE, 16-byte aligned) -> [num_rows, 576] the same way.
+ * With both expanded, attention through the 576-wide calls is the MODEL1
+ * attention (q.k over 512 dims); the first 448 output dims are its output
+ * (V = the 448 NoPE dims) and dims 448..511 come out 0.
+ * Errors: MLA_ERR_INVALID_ARGUMENT (num_tokens / num_rows < 0, a null or
+ * misaligned pointer with a non-zero count), MLA_ERR_DEVICE (launch
+ * failed).  The caller owns every buffer; nothing is allocated; enqueued on
+ * `stream` only (capture-safe).                                          */
+mla_status mla_model1_expand_records(const uint8_t* records, int64_t num_tokens, void* rows, hipStream_t stream);
+mla_status mla_model1_expand_q(const void* q, int64_t num_rows, void* q576, hipStream_t stream);
+
 /* Token-sparse attention (DSA) over the 656-byte fp8 record cache
  * (mla_sparse_decode_fp8: FlashMLA digest, "flash_mla_with_kvcache (Sparse
  * Attention with FP8 KV Cache)" and "Sparse Attention Decoding with KV

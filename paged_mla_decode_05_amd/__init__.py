@@ -25,6 +25,8 @@ from ._binding import (  # noqa: F401
     mla_decode_fp8,
     mla_decode_fp8_q8,
     mla_decode_packed,
+    mla_model1_expand_q,
+    mla_model1_expand_records,
     mla_plan_create,
     mla_prefill,
     mla_prefill_packed,
@@ -41,4 +43,6 @@ from ._binding import (  # noqa: F401
     MLA_TILE_WIDE,
     MLA_TILE_NARROW,
     MLA_TILE_QUAD,
+    MODEL1_NOPE,
+    MODEL1_RECORD,
 )

@@ -103,6 +103,10 @@ def load_library():
         L.mla_sparse_decode_fp8.restype = i32
         L.mla_sparse_prefill.argtypes = [vp, vp, vp, vp, vp, vp, f32, vp, i32, vp, vp, vp, sz, vp]
         L.mla_sparse_prefill.restype = i32
+        L.mla_model1_expand_records.argtypes = [vp, ctypes.c_int64, vp, vp]
+        L.mla_model1_expand_records.restype = i32
+        L.mla_model1_expand_q.argtypes = [vp, ctypes.c_int64, vp, vp]
+        L.mla_model1_expand_q.restype = i32
         L.mla_record_attention_events.argtypes = [vp, vp]
         L.mla_record_attention_events.restype = i32
         L.mla_status_str.argtypes = [i32]
@@ -480,3 +484,39 @@ def mla_block_table_to_indices(plan: Plan, block_table, kv_indptr, kv_indices=No
     _check(L.mla_block_table_to_indices(plan.handle, bt, int(block_table.shape[1]), ip, ix, stream),
            "mla_block_table_to_indices")
     return kv_indices
+
+
+MODEL1_RECORD = 604
+MODEL1_NOPE = 448
+
+
+def mla_model1_expand_records(records, rows=None):
+    """MODEL1 records [..., 604] (uint8, device) -> bf16 rows [..., 576] in the
+    concatenated layout (dims 448..511 zero); see mla_model1_expand_records in mla.h."""
+    L = load_library()
+    if records.dtype != torch.uint8 or records.shape[-1] != MODEL1_RECORD or not records.is_contiguous():
+        raise ValueError("records must be contiguous uint8 [..., 604]")
+    n = records.numel() // MODEL1_RECORD
+    if rows is None:
+        rows = torch.empty(tuple(records.shape[:-1]) + (_DIM_CKV + _DIM_KPE,), dtype=torch.bfloat16,
+                           device=records.device)
+    if rows.dtype != torch.bfloat16 or rows.numel() != n * (_DIM_CKV + _DIM_KPE) or not rows.is_contiguous():
+        raise ValueError("rows must be contiguous bf16 with 576 values per record")
+    stream = torch.cuda.current_stream(records.device).cuda_stream
+    _check(L.mla_model1_expand_records(records.data_ptr(), n, rows.data_ptr(), stream), "mla_model1_expand_records")
+    return rows
+
+
+def mla_model1_expand_q(q, q576=None):
+    """Query rows [..., 512] (bf16: 448 NoPE + 64 RoPE) -> [..., 576] with zeros in dims 448..511."""
+    L = load_library()
+    if q.dtype != torch.bfloat16 or q.shape[-1] != MODEL1_NOPE + _DIM_KPE or not q.is_contiguous():
+        raise ValueError("q must be contiguous bf16 [..., 512]")
+    n = q.numel() // (MODEL1_NOPE + _DIM_KPE)
+    if q576 is None:
+        q576 = torch.empty(tuple(q.shape[:-1]) + (_DIM_CKV + _DIM_KPE,), dtype=torch.bfloat16, device=q.device)
+    if q576.dtype != torch.bfloat16 or q576.numel() != n * (_DIM_CKV + _DIM_KPE) or not q576.is_contiguous():
+        raise ValueError("q576 must be contiguous bf16 with 576 values per row")
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(L.mla_model1_expand_q(q.data_ptr(), n, q576.data_ptr(), stream), "mla_model1_expand_q")
+    return q576

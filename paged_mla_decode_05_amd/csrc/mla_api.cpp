@@ -588,4 +588,21 @@ mla_status mla_block_table_to_indices(const mla_plan* p, const int32_t* block_ta
   return MLA_OK;
 }
 
+mla_status mla_model1_expand_records(const uint8_t* records, int64_t num_tokens, void* rows, hipStream_t stream) {
+  if (num_tokens < 0) return MLA_ERR_INVALID_ARGUMENT;
+  if (num_tokens == 0) return MLA_OK;
+  if (!records || !rows || ((uintptr_t)records % 4) != 0 || ((uintptr_t)rows % 16) != 0)
+    return MLA_ERR_INVALID_ARGUMENT;
+  if (mla::launch_model1_records(records, num_tokens, (__bf16*)rows, stream) != hipSuccess) return MLA_ERR_DEVICE;
+  return MLA_OK;
+}
+
+mla_status mla_model1_expand_q(const void* q, int64_t num_rows, void* q576, hipStream_t stream) {
+  if (num_rows < 0) return MLA_ERR_INVALID_ARGUMENT;
+  if (num_rows == 0) return MLA_OK;
+  if (!q || !q576 || ((uintptr_t)q % 16) != 0 || ((uintptr_t)q576 % 16) != 0) return MLA_ERR_INVALID_ARGUMENT;
+  if (mla::launch_model1_q((const __bf16*)q, num_rows, (__bf16*)q576, stream) != hipSuccess) return MLA_ERR_DEVICE;
+  return MLA_OK;
+}
+
 }  // extern "C"

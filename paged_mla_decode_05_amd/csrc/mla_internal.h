@@ -101,6 +101,9 @@ hipError_t launch_sparse_lists(const int32_t* indices, int32_t num_tokens, int32
                                const int32_t* topk_length, int64_t num_slots, int32_t* list, int32_t* count,
                                int32_t* indptr, hipStream_t stream);
 hipError_t launch_combine(const AttnArgs& a, hipStream_t stream);
+// MODEL1 records [n, 604] -> bf16 rows [n, 576]; query rows [n, 512] -> [n, 576].
+hipError_t launch_model1_records(const uint8_t* records, int64_t n, __bf16* rows, hipStream_t stream);
+hipError_t launch_model1_q(const __bf16* q, int64_t n, __bf16* q576, hipStream_t stream);
 // kv_indices[kv_indptr[b] + j] = block_table[b * max_blocks + j] for j < kv_indptr[b+1] - kv_indptr[b].
 hipError_t launch_block_table(const int32_t* block_table, int32_t batch, int32_t max_blocks,
                               const int32_t* kv_indptr, int32_t* kv_indices, hipStream_t stream);

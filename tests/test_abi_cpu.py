@@ -301,3 +301,18 @@ def test_sparse_plan_and_call_errors(mla):
     assert lib.mla_sparse_decode_fp8(spb.handle, fake, fake, fake, None, None, *tail) == -4
     assert lib.mla_sparse_prefill(sp.handle, fake, fake, fake, None, None, *tail) == -4
     assert lib.mla_sparse_prefill(spb.handle, fake, None, fake, None, None, *tail) == -1
+
+
+def test_model1_expand_argument_checks(mla):
+    """Rejected before any launch: negative counts, null or misaligned
+    pointers with a non-zero count; a zero count is a no-op."""
+    L = mla.load_library()
+    ok, bad = 0, -1
+    assert L.mla_model1_expand_records(None, 0, None, None) == ok
+    assert L.mla_model1_expand_records(None, -1, None, None) == bad
+    assert L.mla_model1_expand_records(None, 5, None, None) == bad
+    assert L.mla_model1_expand_records(2, 5, 16, None) == bad     # records not 4-byte aligned
+    assert L.mla_model1_expand_records(4, 5, 8, None) == bad      # rows not 16-byte aligned
+    assert L.mla_model1_expand_q(None, 0, None, None) == ok
+    assert L.mla_model1_expand_q(None, -3, None, None) == bad
+    assert L.mla_model1_expand_q(16, 3, 8, None) == bad
