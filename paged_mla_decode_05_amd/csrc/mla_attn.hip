@@ -1406,13 +1406,18 @@ __device__ void wide8_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* s
       // per-key scaling into sacc is issued two steps into the next tile's
       // chain, so the VALU work and its wait states overlap MFMAs.
       f32x16 sacc, part[2];
+      {
+        bf16x8 rp[4];  // all four rope fragments in flight before the chain starts
 #pragma unroll
-      for (int kr2 = 0; kr2 < 4; ++kr2) {
-        const bf16x8 rp = *(const LDS_AS bf16x8*)(rbase + tb * kFp8RecordBytes + 32 * kr2);
-        if (kr2 == 0) {
-          mfma32_first<false>(sacc, rp, qr[0]);
-        } else {
-          mfma32_acc<false>(sacc, rp, qr[kr2]);
+        for (int kr2 = 0; kr2 < 4; ++kr2) rp[kr2] = *(const LDS_AS bf16x8*)(rbase + tb * kFp8RecordBytes + 32 * kr2);
+        pin_loads();
+#pragma unroll
+        for (int kr2 = 0; kr2 < 4; ++kr2) {
+          if (kr2 == 0) {
+            mfma32_first<false>(sacc, rp[0], qr[0]);
+          } else {
+            mfma32_acc<false>(sacc, rp[kr2], qr[kr2]);
+          }
         }
       }
       f32x4 tsc[4];  // the scales of the lane's keys in the tile being folded in
