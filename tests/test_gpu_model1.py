@@ -96,3 +96,42 @@ def test_decode_over_expanded_records(mla, case):
     lerr = np.abs(l[~empty] - ref_l[~empty]).max()
     say(f"    max|dout|={err:.3e} relL2={rel:.3e} max|dlse|={lerr:.3e}")
     assert err <= TOL["max_abs"] and rel <= TOL["rel_l2"] and lerr <= TOL["lse"]
+
+
+def test_sparse_attention_over_expanded_records(mla):
+    """The token-sparse form (MODEL1_FP8Sparse): per-query key lists with
+    invalid entries, an attention sink and forced splits, over rows expanded
+    from MODEL1 records, against the oracle's sparse attention over its own
+    dequantised keys (widened with zeros in dims 448..511, the form the
+    dense MODEL1 oracle test pins as the same attention)."""
+    from workloads import quantize_model1_records
+
+    say("model1 sparse: s_q=6 H=32 s_kv=700 topk=96, sink, 2 splits")
+    g = torch.Generator().manual_seed(77)
+    s_q, H, s_kv, topk = 6, 32, 700, 96
+    src = torch.randn((s_kv, 512), generator=g).to(torch.bfloat16)
+    rec = quantize_model1_records(src)
+    q = torch.randn((s_q, H, 512), generator=g).to(torch.bfloat16)
+    idx = torch.randint(0, s_kv, (s_q, topk), generator=g, dtype=torch.int64).to(torch.int32)
+    idx[:, ::7] = -1
+    sink = (torch.randn(H, generator=g) + 4.0).to(torch.float32)
+    scale = 0.07
+    rows = mla.mla_model1_expand_records(rec.to(DEV))
+    q576 = mla.mla_model1_expand_q(q.to(DEV))
+    plan = mla.mla_sparse_plan_create(s_q, H, s_kv, topk, kv_format=mla.MLA_KV_BF16, force_splits=2)
+    out, lse, mx = mla.mla_sparse_prefill(plan, q576, rows, idx.to(DEV), scale, attn_sink=sink.to(DEV))
+    torch.cuda.synchronize()
+    nope, rope = oracle.model1_record_decode(rec)
+    kv = np.zeros((s_kv, 576))
+    kv[:, :448], kv[:, 512:] = nope, rope
+    qq = np.zeros((s_q, H, 576))
+    qq[..., :448], qq[..., 512:] = q[..., :448].double().numpy(), q[..., 448:].double().numpy()
+    ref_o, ref_l, ref_m = oracle.mla_sparse_prefill_ref(qq, kv, idx.numpy(), scale, attn_sink=sink.numpy())
+    o = out.double().cpu().numpy()
+    assert (o[..., 448:] == 0).all()
+    err = np.abs(o[..., :448] - ref_o[..., :448]).max()
+    rel = np.linalg.norm(o[..., :448] - ref_o[..., :448]) / np.linalg.norm(ref_o[..., :448])
+    lerr = np.abs(lse.double().cpu().numpy() - ref_l).max()
+    merr = np.abs(mx.double().cpu().numpy() - ref_m).max()
+    say(f"    max|dout|={err:.3e} relL2={rel:.3e} max|dlse|={lerr:.3e} max|dmax|={merr:.3e}")
+    assert err <= TOL["max_abs"] and rel <= TOL["rel_l2"] and lerr <= TOL["lse"] and merr <= TOL["lse"]
