@@ -212,3 +212,92 @@ def test_sparse_attend_mistakes_are_caught(monkeypatch, mistake):
     assert _sparse_pin_suite() == 0
     monkeypatch.setattr(om, "sparse_attend", _sparse_attend_variant(mistake))
     assert _sparse_pin_suite() > 0
+
+
+# ---------------------------------------------------------------------------
+# MODEL1 records: planted mistakes in the record decoder and in the decode
+# ---------------------------------------------------------------------------
+
+def _model1_pin_suite():
+    from tests import test_oracle_model1 as m1
+
+    checks = [
+        m1.test_hand_built_record,
+        m1.test_round_trip_within_the_quantisation_bound,
+        m1.test_decode_matches_torch_sdpa_on_the_dequantised_keys,
+        m1.test_input_quantiser_matches_the_oracle_encoder,
+        m1.test_bf16_rounding_matches_torch_and_ties_go_to_even,
+    ]
+    failed = 0
+    for c in checks:
+        try:
+            c()
+        except (AssertionError, ValueError, IndexError):
+            failed += 1
+    return failed
+
+
+def _model1_decode_variant(mistake):
+    M1, REC = om.M1_NOPE, om.M1_RECORD_BYTES
+
+    def decode(records):
+        r = om._as_u8(records)
+        lead = r.shape[:-1]
+        flat = r.reshape(-1, REC)
+        codes = flat[:, :M1]
+        s0 = M1 + (4 if mistake == "scale_offset" else 0)
+        sc = np.ascontiguousarray(flat[:, s0:s0 + 28]) if mistake != "scale_offset" else \
+            np.ascontiguousarray(np.concatenate([flat[:, s0:s0 + 24], flat[:, M1:M1 + 4]], axis=1))
+        scales = sc.view("<f4")
+        r0 = M1 + 28 + (2 if mistake == "rope_offset" else 0)
+        rope_bytes = np.ascontiguousarray(flat[:, r0:r0 + 128]) if mistake != "rope_offset" else \
+            np.ascontiguousarray(np.concatenate([flat[:, r0:REC], flat[:, M1 + 28:M1 + 30]], axis=1))
+        rope = om.bf16_bits_to_f64(rope_bytes.view("<u2"))
+        vals = om.e4m3_decode(codes).astype(np.float32)
+        if mistake == "tile_128":
+            tiles = np.repeat(scales[:, :4], 2, axis=1)[:, :7]  # each scale covering 128 dims
+        else:
+            tiles = scales
+        prod = (vals.reshape(-1, 7, 64) * tiles[:, :, None]).astype(np.float32)
+        if mistake == "no_bf16_rounding":
+            nope = prod.astype(np.float64).reshape(-1, M1)
+        elif mistake == "truncate":
+            u = prod.view(np.uint32) & np.uint32(0xFFFF0000)
+            nope = u.view(np.float32).astype(np.float64).reshape(-1, M1)
+        else:
+            nope = om.f32_to_bf16_rne(prod).reshape(-1, M1)
+        return nope.reshape(*lead, M1), rope.reshape(*lead, 64)
+
+    return decode
+
+
+@pytest.mark.parametrize("mistake", ["scale_offset", "rope_offset", "tile_128", "no_bf16_rounding", "truncate"])
+def test_model1_record_mistakes_are_caught(monkeypatch, mistake):
+    assert _model1_pin_suite() == 0  # the real decoder passes every pin
+    bad = _model1_decode_variant(mistake)
+    monkeypatch.setattr(om, "model1_record_decode", bad)
+    monkeypatch.setattr(oracle, "model1_record_decode", bad)
+    assert _model1_pin_suite() > 0
+
+
+def test_model1_decode_without_the_rope_term_is_caught(monkeypatch):
+    """A MODEL1 decode whose logits miss the 64 RoPE dims (q.k over the 448
+    NoPE dims only)."""
+    def decode(q, kv_records, kv_indptr, kv_indices, kv_len, sm_scale, requests=None):
+        qf = om.as_f64(q)
+        B, H, _ = qf.shape
+        kvl = om._as_int(kv_len)
+        out = np.zeros((B, H, om.M1_NOPE))
+        lse = np.full((B, H), -np.inf)
+        for b in range(B):
+            L = int(kvl[b])
+            if L == 0:
+                continue
+            page, slot = om._token_slots(om._as_int(kv_indptr), om._as_int(kv_indices), b, L, kv_records.shape[1])
+            kn, kp = om.model1_record_decode(om._take_rows(kv_records, page, slot))
+            o, l = om.attend(qf[b, :, :om.M1_NOPE], np.zeros_like(qf[b, :, om.M1_NOPE:]), kn, kp, sm_scale, L)
+            out[b], lse[b] = o[:, :om.M1_NOPE], l
+        return out, lse
+    monkeypatch.setattr(om, "mla_decode_model1_ref", decode)
+    monkeypatch.setattr(oracle, "mla_decode_model1_ref", decode)
+    assert _model1_pin_suite() > 0
