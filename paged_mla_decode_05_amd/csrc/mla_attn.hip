@@ -449,8 +449,9 @@ struct RecordLoader {
     // the last slice holds the 16 chunks 640..655: lanes 0..15 only
     constexpr int kTail = 16 * kRecChunks - 64 * (kFp8DmaPerWave - 1);
     static_assert(kTail == 16, "tail slice is lanes 0..15");
-    const uint32_t lo = (i == kFp8DmaPerWave - 1) ? (on & 0xFFFFu) : on;
-    const uint32_t hi = (i == kFp8DmaPerWave - 1) ? 0u : on;
+    const uint32_t onu = __builtin_amdgcn_readfirstlane(on);  // wave-uniform; keep it scalar for the asm
+    const uint32_t lo = (i == kFp8DmaPerWave - 1) ? (onu & 0xFFFFu) : onu;
+    const uint32_t hi = (i == kFp8DmaPerWave - 1) ? 0u : onu;
     if (kPageClass == kPageBig) {
       dma16_x(base, __umul24((uint32_t)tc, (uint32_t)kFp8RecordBytes) + 16u * k, lds_addr(dst), lo, hi);
     } else {
@@ -1442,7 +1443,6 @@ __device__ void wide8_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* s
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
           pin_loads();
-          if (sub * 8 + c < RecordLoader<kPC>::kSlices) ld.issue(a, sub * 8 + c, wave);
           const i32x8 kc = kr8[c % KD8];
           if (c + KD8 < 8) kr8[c % KD8] = kread8(c + KD8);
           f32x16& pa = part[(c >> 1) & 1];
@@ -1466,7 +1466,6 @@ __device__ void wide8_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* s
 #pragma unroll
       for (int m = 0; m < 16; ++m) {
         pin_loads();
-        if ((m & 1) == 0 && sub * 8 + (m >> 1) < RecordLoader<kPC>::kSlices) ld.issue(a, sub * 8 + (m >> 1), wave);
         const u32x4 c = kr[m % KD];
         if (m + KD < 16) kr[m % KD] = kread(m + KD);
         const bf16x8 a0 = codes8(c[0], c[1]), a1 = codes8(c[2], c[3]);
@@ -1550,6 +1549,8 @@ __device__ void wide8_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* s
         const u32x2 v = vr[j % VD];
         if (j + VD < 32) vr[j % VD] = vread(j + VD);
         st.o[j >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(codes8(v[0], v[1]), pt[j & 1], st.o[j >> 1], 0, 0, 0);
+        // the records of the stage after next ride along P.V (Q.K^T waits on its own LDS reads)
+        if ((j & 3) == 0 && sub * 8 + (j >> 2) < RecordLoader<kPC>::kSlices) ld.issue(a, sub * 8 + (j >> 2), wave);
       }
       pin_loads();
     }
