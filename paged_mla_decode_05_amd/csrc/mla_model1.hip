@@ -30,9 +30,11 @@ constexpr int kM1Record = kM1Nope + 4 * (kM1Nope / kM1Tile) + 2 * kDimKpe;  // 6
 constexpr int kRowChunks = (kDimCkv + kDimKpe) / 8;                        // 72 chunks of 8 dims
 constexpr int kNopeChunks = kM1Nope / 8;                                   // 56
 constexpr int kZeroEnd = kDimCkv / 8;                                      // chunks 56..63 are zero
-constexpr int kRowPairs = kRowChunks / 2;                                  // 36 pairs of chunks
-constexpr int kNopePairs = kNopeChunks / 2;                                // 28
-constexpr int kZeroPairsEnd = kZeroEnd / 2;                                // pairs 28..31 are zero
+constexpr int kChunksPerThread = 2;                                        // divides 8 (a tile's chunks)
+constexpr int kRowUnits = kRowChunks / kChunksPerThread;
+constexpr int kNopeUnits = kNopeChunks / kChunksPerThread;
+constexpr int kZeroUnitsEnd = kZeroEnd / kChunksPerThread;
+static_assert(8 % kChunksPerThread == 0, "a thread's chunks stay in one tile");
 static_assert(kM1Record == 604, "MODEL1 record size");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -48,50 +50,54 @@ __device__ __forceinline__ float e4m3_value(uint32_t c) {
   return (c & 0x80) ? -v : v;
 }
 
-// Thread i writes the 32-byte chunk pair i % 36 of output row i / 36 (pairs
-// 0..27 hold the 16 codes of one half of a 64-dim tile, 28..31 are zero, 32..35
-// the RoPE values).  Index math is 32-bit when the pair count fits.
+// Thread i writes kChunksPerThread consecutive 16-byte chunks (unit i % kRowUnits
+// of output row i / kRowUnits); a unit never straddles a 64-dim tile, so one
+// scale serves all its codes.  Index math is 32-bit when the unit count fits.
 template <typename Index>
-__device__ __forceinline__ void model1_record_pairs(const uint8_t* __restrict__ rec, Index total,
+__device__ __forceinline__ void model1_record_units(const uint8_t* __restrict__ rec, Index total,
                                                     __bf16* __restrict__ rows) {
+  constexpr int K = kChunksPerThread;
   for (Index i = (Index)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (Index)gridDim.x * blockDim.x) {
-    const Index t = i / kRowPairs;
-    const int c = (int)(i - t * kRowPairs);
+    const Index t = i / kRowUnits;
+    const int c = (int)(i - t * kRowUnits);
     const uint8_t* r = rec + (int64_t)t * kM1Record;
-    bf16x8 out0, out1;
-    if (c < kNopePairs) {
-      // 16 codes of tile c / 4; the record is 4-byte aligned
-      const uint32_t* src = (const uint32_t*)(r + 16 * c);
-      const u32x4 w = {src[0], src[1], src[2], src[3]};
-      const float scale = *(const float*)(r + kM1Nope + 4 * (c / (kM1Tile / 16)));
+    bf16x8 out[K];
+    if (c < kNopeUnits) {
+      // 8K codes of tile c * K / 8; the record is 4-byte aligned
+      const uint32_t* src = (const uint32_t*)(r + 8 * K * c);
+      uint32_t w[2 * K];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        out0[k] = (__bf16)(e4m3_value((w[k >> 2] >> (8 * (k & 3))) & 0xFF) * scale);
-        out1[k] = (__bf16)(e4m3_value((w[2 + (k >> 2)] >> (8 * (k & 3))) & 0xFF) * scale);
-      }
-    } else if (c < kZeroPairsEnd) {
-      out0 = bf16x8{};
-      out1 = bf16x8{};
+      for (int j = 0; j < 2 * K; ++j) w[j] = src[j];
+      const float scale = *(const float*)(r + kM1Nope + 4 * (c * K / (kM1Tile / 8)));
+#pragma unroll
+      for (int j = 0; j < K; ++j)
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          out[j][k] = (__bf16)(e4m3_value((w[2 * j + (k >> 2)] >> (8 * (k & 3))) & 0xFF) * scale);
+    } else if (c < kZeroUnitsEnd) {
+#pragma unroll
+      for (int j = 0; j < K; ++j) out[j] = bf16x8{};
     } else {
-      const uint32_t* src = (const uint32_t*)(r + kM1Nope + 4 * (kM1Nope / kM1Tile) + 32 * (c - kZeroPairsEnd));
-      const u32x4 a = {src[0], src[1], src[2], src[3]};
-      const u32x4 b = {src[4], src[5], src[6], src[7]};
-      out0 = __builtin_bit_cast(bf16x8, a);
-      out1 = __builtin_bit_cast(bf16x8, b);
+      const uint32_t* src = (const uint32_t*)(r + kM1Nope + 4 * (kM1Nope / kM1Tile) + 16 * K * (c - kZeroUnitsEnd));
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        const u32x4 v = {src[4 * j], src[4 * j + 1], src[4 * j + 2], src[4 * j + 3]};
+        out[j] = __builtin_bit_cast(bf16x8, v);
+      }
     }
-    bf16x8* dst = (bf16x8*)(rows + (int64_t)t * (kDimCkv + kDimKpe) + 16 * c);
-    dst[0] = out0;
-    dst[1] = out1;
+    bf16x8* dst = (bf16x8*)(rows + (int64_t)t * (kDimCkv + kDimKpe) + 8 * K * c);
+#pragma unroll
+    for (int j = 0; j < K; ++j) dst[j] = out[j];
   }
 }
 
 __global__ __launch_bounds__(256) void mla_model1_records_kernel(const uint8_t* __restrict__ rec, int64_t n,
                                                                   __bf16* __restrict__ rows) {
-  const int64_t total = n * kRowPairs;
+  const int64_t total = n * kRowUnits;
   if (total <= INT32_MAX - 65536LL * 256)
-    model1_record_pairs<uint32_t>(rec, (uint32_t)total, rows);
+    model1_record_units<uint32_t>(rec, (uint32_t)total, rows);
   else
-    model1_record_pairs<int64_t>(rec, total, rows);
+    model1_record_units<int64_t>(rec, total, rows);
 }
 
 // Query rows of 512 dims (448 NoPE + 64 RoPE) widened to 576.
@@ -120,7 +126,7 @@ int grid_for(int64_t n, int per_row) {
 
 hipError_t launch_model1_records(const uint8_t* records, int64_t n, __bf16* rows, hipStream_t stream) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(mla_model1_records_kernel, dim3(grid_for(n, kRowPairs)), dim3(256), 0, stream, records, n, rows);
+  hipLaunchKernelGGL(mla_model1_records_kernel, dim3(grid_for(n, kRowUnits)), dim3(256), 0, stream, records, n, rows);
   return hipGetLastError();
 }
 
