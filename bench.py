@@ -559,7 +559,10 @@ def main():
     kv_gbs = live_kv / t_s / 1e9
     pct = 100.0 * max((bytes_alg / (HBM_PEAK_GBS * 1e9)), flops / (BF16_PEAK_TFLOPS * 1e12)) / t_s
     sha = kernel_sha()
-    traffic = read_counters(args.config, sha)
+    # counters are per kernel variant: the e4m3-query and packed-layout runs
+    # launch other instantiations than the default run they share a workload with
+    variant = args.config + ("_q8" if args.q_fp8 else "") + ("_packed" if args.layout == "packed" else "")
+    traffic = read_counters(variant, sha)
     if traffic is not None:
         log(f"bench: HBM traffic per attention launch {traffic / 1e6:.1f} MB "
             f"({traffic / bytes_alg:.2f}x the algorithmic {bytes_alg / 1e6:.1f} MB)")
