@@ -308,6 +308,7 @@ def mla_decode_model1_ref(q, kv_records, kv_indptr, kv_indices, kv_len, sm_scale
     B, H, D = qf.shape
     assert D == M1_NOPE + HEAD_DIM_KPE
     kvl = _as_int(kv_len)
+    kv_records = _host(kv_records)
     out = np.zeros((B, H, M1_NOPE))
     lse = np.full((B, H), -np.inf)
     for b in (range(B) if requests is None else requests):
@@ -341,15 +342,30 @@ def _token_slots(kv_indptr, kv_indices, b: int, kv_len: int, page_size: int):
     return pages[j // page_size], j % page_size
 
 
+def _host(x):
+    """A torch tensor on a device -> one host copy of it (every gather then
+    runs on the CPU, so nothing the oracle reads is computed on the device
+    under test); anything else as it is."""
+    try:
+        import torch
+
+        if isinstance(x, torch.Tensor) and x.device.type != "cpu":
+            return x.detach().cpu()
+    except ImportError:  # pragma: no cover
+        pass
+    return x
+
+
 def _take_rows(cache, page, slot):
-    """cache[page[i], slot[i], :] for every i, without widening the rest."""
+    """cache[page[i], slot[i], :] for every i, without widening the rest
+    (host arrays only: callers pass device tensors through :func:`_host`)."""
     try:
         import torch
 
         if isinstance(cache, torch.Tensor):
-            dev = cache.device
-            rows = cache.detach()[torch.from_numpy(page).to(dev), torch.from_numpy(slot).to(dev)]
-            return rows.cpu()
+            if cache.device.type != "cpu":
+                raise ValueError("the oracle gathers from host memory only")
+            return cache.detach()[torch.from_numpy(page), torch.from_numpy(slot)]
     except ImportError:  # pragma: no cover
         pass
     return np.asarray(cache)[page, slot]
@@ -476,6 +492,7 @@ def mla_decode_ref(q_nope, q_pe, ckv_cache, kpe_cache, kv_indptr, kv_indices, kv
     qn = as_f64(q_nope)
     qp = as_f64(q_pe)
     _check_heads(qn, qp)
+    ckv_cache, kpe_cache = _host(ckv_cache), _host(kpe_cache)
     lens = _as_int(kv_len)
     B, H, _ = qn.shape
     out = np.full((B, H, HEAD_DIM_CKV), np.nan)
@@ -508,6 +525,7 @@ def mla_prefill_ref(q_nope, q_pe, ckv_cache, kpe_cache, qo_indptr, kv_indptr, kv
     qn = as_f64(q_nope)
     qp = as_f64(q_pe)
     _check_heads(qn, qp)
+    ckv_cache, kpe_cache = _host(ckv_cache), _host(kpe_cache)
     qo = _as_int(qo_indptr)
     lens = _as_int(kv_len)
     T, H, _ = qn.shape
@@ -542,6 +560,7 @@ def mla_decode_fp8_ref(q_nope, q_pe, kv_cache_fp8, kv_indptr, kv_indices, kv_len
     qn = as_f64(q_nope)
     qp = as_f64(q_pe)
     _check_heads(qn, qp)
+    kv_cache_fp8 = _host(kv_cache_fp8)
     lens = _as_int(kv_len)
     B, H, _ = qn.shape
     out = np.full((B, H, HEAD_DIM_CKV), np.nan)
@@ -641,13 +660,16 @@ def _sparse_run(q, indices, num_slots, gather, sm_scale, topk_length, attn_sink,
 
 
 def _flat_rows(cache, width: int, sel):
-    """Rows sel of a cache viewed as [num_slots, width] (no widening)."""
+    """Rows sel of a cache viewed as [num_slots, width] (no widening; host
+    arrays only, see :func:`_host`)."""
     try:
         import torch
 
         if isinstance(cache, torch.Tensor):
+            if cache.device.type != "cpu":
+                raise ValueError("the oracle gathers from host memory only")
             flat = cache.detach().reshape(-1, width)
-            return flat[torch.from_numpy(np.asarray(sel, dtype=np.int64)).to(flat.device)].cpu()
+            return flat[torch.from_numpy(np.asarray(sel, dtype=np.int64))]
     except ImportError:  # pragma: no cover
         pass
     return np.asarray(cache).reshape(-1, width)[sel]
@@ -670,6 +692,7 @@ def mla_sparse_decode_fp8_ref(q, kv_cache_fp8, indices, sm_scale: float, topk_le
     num_slots = int(np.prod(kv_cache_fp8.shape[:-1]))
     if kv_cache_fp8.shape[-1] != FP8_RECORD_BYTES:
         raise ValueError("fp8 records must be 656 bytes")
+    kv_cache_fp8 = _host(kv_cache_fp8)
     return _sparse_run(q, indices, num_slots,
                        lambda sel: fp8_record_decode(_flat_rows(kv_cache_fp8, FP8_RECORD_BYTES, sel)),
                        sm_scale, topk_length, attn_sink, tokens)
@@ -685,6 +708,7 @@ def mla_sparse_prefill_ref(q, kv, indices, sm_scale: float, topk_length=None, at
     if kv.shape[-1] != width:
         raise ValueError("kv must hold 576 dims per token")
     num_slots = int(np.prod(kv.shape[:-1]))
+    kv = _host(kv)
 
     def gather(sel):
         rows = as_f64(_flat_rows(kv, width, sel))

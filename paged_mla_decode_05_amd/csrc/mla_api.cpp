@@ -190,12 +190,17 @@ mla_status build_schedule(mla_plan* p, const std::vector<int32_t>& kv_len,
   const int64_t cus = lists;
   // Smallest per-workgroup budget whose packing needs at most `cus`
   // workgroups: one persistent workgroup per compute unit.
+  // The search always ends: once the budget covers every piece and its
+  // overhead, the packing is one list.  Small steps first (tight balance),
+  // then doubling steps (forced splits add an overhead per piece that the
+  // first budget does not count, and can need several times it).
   int64_t budget = std::max<int64_t>((total + cus - 1) / cus, kItemOverhead + kMinChunk);
-  for (int iter = 0; iter < 400; ++iter) {
+  for (int iter = 0;; ++iter) {
     pack_units(p, units, budget);
     if (p->num_wgs <= cus) break;
-    budget += std::max<int64_t>(16, budget / 256);
+    budget += iter < 400 ? std::max<int64_t>(16, budget / 256) : budget;
   }
+  if (p->num_wgs > cus) return MLA_ERR_INVALID_ARGUMENT;  // unreachable: the loop exits only when they fit
   if (p->tile_mode == MLA_TILE_QUAD) {
     p->grid = p->xcd_map ? (int32_t)cus * p->group_size : p->num_wgs * p->group_size;
   }

@@ -271,6 +271,23 @@ def test_quad_mode_groups_siblings(mla):
     assert plan.num_split_groups <= 48
 
 
+@pytest.mark.parametrize("L,splits", [(6400, 100), (4096, 64), (32768, 512), (64, 1)])
+def test_quad_mode_lists_fit_the_grid(mla, L, splits):
+    # forced splits add a per-piece overhead the first budget does not count;
+    # the budget search must still end with no more lists than the quad grid
+    # runs (num_cus / (8 G) * 8 of them, siblings sharing an XCD)
+    B, H, cus = 64, 128, 256
+    lens = np.full(B, L)
+    indptr = np.concatenate([[0], np.cumsum(-(-lens // 64))])
+    plan = mla.mla_plan_create(0, B, H, 64, int(indptr[-1]), lens, indptr, num_cus=cus,
+                               tile_mode=mla.MLA_TILE_QUAD, force_splits=splits)
+    G = plan.group_size
+    lists = (cus // (8 * G)) * 8
+    ptr = plan.workgroup_ptr()
+    assert len(ptr) - 1 <= lists
+    _check_cover(plan, lens, [1] * B, H)
+
+
 def test_sparse_plan_and_call_errors(mla):
     lib = mla.load_library()
     sp = mla.mla_sparse_plan_create(6, 128, 1000, 300, num_cus=4)
