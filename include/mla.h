@@ -341,6 +341,27 @@ mla_status mla_sparse_prefill(const mla_plan* plan, const void* q, const void* k
                               int32_t out_dtype, float* lse, float* max_logits, void* workspace,
                               size_t workspace_bytes, hipStream_t stream);
 
+/* mla_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and kernels as mla_decode, with the workspace taken
+ * from a fixed array inside the library instead of a caller buffer.
+ *   - The array holds MLA_NOALLOC_SCRATCH_BYTES (64 MiB) on each GPU the
+ *     library runs on, from the first call on that GPU until the process
+ *     ends.  A plan whose mla_plan_workspace_bytes exceeds it is refused
+ *     with MLA_ERR_WORKSPACE before anything is enqueued.
+ *   - Every call uploads the plan's work list into the array (one
+ *     host-to-device copy on `stream`, as mla_plan_upload) and then enqueues
+ *     the kernels of mla_decode.  No device memory is allocated or freed.
+ *   - All calls on one GPU share its array, which keeps the last call's
+ *     contents: calls that overlap in time on one GPU (other streams, other
+ *     host threads) race on it and must be serialised by the caller.
+ * Arguments, results and other errors as for mla_decode.                   */
+#define MLA_NOALLOC_SCRATCH_BYTES (64u << 20)
+mla_status mla_decode_noalloc(const mla_plan* plan, const void* q_nope, const void* q_pe,
+                              const void* ckv_cache, const void* kpe_cache, const int32_t* kv_indptr,
+                              const int32_t* kv_indices, float sm_scale, void* out, int32_t out_dtype,
+                              float* lse, hipStream_t stream);
+
 /* Diagnostics for timing: the next run call made on this host thread has
  * the attention kernel's own dispatch record `before` when the kernel
  * starts and `after` when it ends (hipExtLaunchKernel's start / stop

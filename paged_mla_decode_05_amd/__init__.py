@@ -8,7 +8,7 @@ call raises; there is no fallback.
 
 Names follow the C ABI: :func:`mla_plan_create`, :func:`mla_decode`,
 :func:`mla_prefill`, :func:`mla_decode_fp8`, :func:`mla_decode_fp8_q8` (e4m3
-query), the concatenated-layout
+query), :func:`mla_decode_noalloc` (no device allocation), the concatenated-layout
 :func:`mla_decode_packed` / :func:`mla_prefill_packed`,
 :func:`mla_block_table_to_indices`, and the token-sparse
 :func:`mla_sparse_plan_create` / :func:`mla_sparse_decode_fp8` /
@@ -24,6 +24,7 @@ from ._binding import (  # noqa: F401
     mla_decode,
     mla_decode_fp8,
     mla_decode_fp8_q8,
+    mla_decode_noalloc,
     mla_decode_packed,
     mla_model1_expand_q,
     mla_model1_expand_records,
@@ -45,4 +46,5 @@ from ._binding import (  # noqa: F401
     MLA_TILE_QUAD,
     MODEL1_NOPE,
     MODEL1_RECORD,
+    NOALLOC_SCRATCH_BYTES,
 )

@@ -107,6 +107,8 @@ def load_library():
         L.mla_model1_expand_records.restype = i32
         L.mla_model1_expand_q.argtypes = [vp, ctypes.c_int64, vp, vp]
         L.mla_model1_expand_q.restype = i32
+        L.mla_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32, vp, i32, vp, vp]
+        L.mla_decode_noalloc.restype = i32
         L.mla_record_attention_events.argtypes = [vp, vp]
         L.mla_record_attention_events.restype = i32
         L.mla_status_str.argtypes = [i32]
@@ -362,6 +364,27 @@ def mla_decode(plan: Plan, q_nope, q_pe, ckv_cache, kpe_cache, kv_indptr, kv_ind
     stream = torch.cuda.current_stream(q_nope.device).cuda_stream
     _check(L.mla_decode(plan.handle, qn, qp, c, k, ip, ix, float(sm_scale), out.data_ptr(), code,
                         lse.data_ptr(), ws.data_ptr(), ws.numel(), stream), "mla_decode")
+    return out, lse
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def mla_decode_noalloc(plan: Plan, q_nope, q_pe, ckv_cache, kpe_cache, kv_indptr, kv_indices, sm_scale: float,
+                       out=None, lse=None, out_dtype=torch.bfloat16):
+    """mla_decode with the library's fixed device scratch array as its
+    workspace (no device allocation by the library; see include/mla.h).
+    Calls on one GPU share the array and must not overlap in time."""
+    L = load_library()
+    B, P, ps = plan.desc.batch, plan.desc.num_pages, plan.desc.page_size
+    qn, qp = _q(plan, q_nope, q_pe, B)
+    c = _dev(ckv_cache, "ckv_cache", torch.bfloat16, (P, ps, _DIM_CKV))
+    k = _dev(kpe_cache, "kpe_cache", torch.bfloat16, (P, ps, _DIM_KPE))
+    ip, ix = _paging(plan, kv_indptr, kv_indices)
+    out, lse, code = _outputs(q_nope, out, lse, out_dtype)
+    stream = torch.cuda.current_stream(q_nope.device).cuda_stream
+    _check(L.mla_decode_noalloc(plan.handle, qn, qp, c, k, ip, ix, float(sm_scale), out.data_ptr(), code,
+                                lse.data_ptr(), stream), "mla_decode_noalloc")
     return out, lse
 
 

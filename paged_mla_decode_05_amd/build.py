@@ -21,7 +21,7 @@ def build(verbose: bool = False) -> str:
     objs = []
     bdir = os.path.join(HERE, "_build")
     os.makedirs(bdir, exist_ok=True)
-    for src in ("mla_attn.hip", "mla_lists.hip", "mla_model1.hip", "mla_api.cpp"):
+    for src in ("mla_attn.hip", "mla_lists.hip", "mla_model1.hip", "mla_static.hip", "mla_api.cpp"):
         obj = os.path.join(bdir, src + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
         cmd = [HIPCC] + COMMON + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
