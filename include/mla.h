@@ -23,10 +23,13 @@
  *     the stream.  The library owns only the host-side plan object.
  *   - No call throws.  Every call returns an mla_status; on error nothing is
  *     launched and no output is written.
- *   - Run calls (mla_decode, mla_prefill, mla_decode_fp8) allocate nothing,
- *     never synchronise and never copy to or from the host: they only enqueue
- *     kernels on `stream`, so they can be captured into a HIP graph.  Calls
- *     that overlap in time must use different workspaces.
+ *   - Run calls (mla_decode, mla_prefill, mla_decode_fp8 and the others)
+ *     allocate nothing, never synchronise and never copy to or from the host:
+ *     they only enqueue kernels on `stream`, so they can be captured into a
+ *     HIP graph.  The one exception is a plan made with validate = 1, whose
+ *     run calls read the device index arrays' check result back (one
+ *     synchronisation of `stream`) before launching.  Calls that overlap in
+ *     time must use different workspaces.
  */
 #ifndef MLA_H_
 #define MLA_H_
@@ -82,6 +85,16 @@ typedef enum mla_tile_mode {
   MLA_TILE_QUAD = 3
 } mla_tile_mode;
 
+/* Layouts of the lse output.
+ *   MLA_LSE_ROWS:        [rows, H] fp32, row = query token (the layout of
+ *                        "MLA Paged", decode and prefill outputs).
+ *   MLA_LSE_HEADS_FIRST: [batch, H, s_q] fp32, every request holding the
+ *                        same number s_q of query tokens (the lse of FlashMLA's
+ *                        "flash_mla_with_kvcache (Dense Attention)", batch x
+ *                        num_heads_q x seq_len_q); decode has s_q = 1, where
+ *                        both layouts coincide.                            */
+typedef enum mla_lse_layout { MLA_LSE_ROWS = 0, MLA_LSE_HEADS_FIRST = 1 } mla_lse_layout;
+
 typedef struct mla_plan_desc {
   int32_t kind;          /* mla_kind                                                */
   int32_t batch;         /* number of requests, >= 0                                */
@@ -96,6 +109,15 @@ typedef struct mla_plan_desc {
   int32_t max_splits;    /* upper bound on key chunks per request; 0 = automatic    */
   int32_t force_splits;  /* > 0: cut every request into this many chunks (testing)  */
   int32_t tile_mode;     /* mla_tile_mode                                           */
+  int32_t validate;      /* 1: every run call first checks the device index arrays
+                            against the plan on the device, synchronises the stream
+                            and returns MLA_ERR_INVALID_ARGUMENT before any attention
+                            launch if one is wrong (not capture-safe); 0: no check */
+  int32_t lse_layout;    /* mla_lse_layout                                          */
+  int32_t max_kv_len;    /* > 0: a capacity plan for any live key counts in
+                            [0, max_kv_len] (runs take them on the device)         */
+  int32_t max_seq_len_q; /* capacity plans, prefill: query tokens per request,
+                            >= every live q_len (0: the largest qo_indptr delta)  */
 } mla_plan_desc;
 
 typedef struct mla_plan mla_plan; /* opaque, immutable after creation */
@@ -117,10 +139,29 @@ typedef struct mla_plan mla_plan; /* opaque, immutable after creation */
  *                  offsets, qo_indptr[0] = 0, non-decreasing; with causal=1
  *                  each request needs q_len <= kv_len.
  * The plan is valid for any call with the same lengths and descriptor.
- * Errors: MLA_ERR_INVALID_ARGUMENT (null pointers, inconsistent arrays),
- * MLA_ERR_UNSUPPORTED (head dims other than 512/64, page_size not a power of
- * two in range, fp8 prefill), MLA_ERR_DEVICE (num_cus = 0 and the device
- * query failed).  Makes no device allocation and launches nothing.       */
+ *
+ * Capacity plans (desc.max_kv_len > 0; "batch_mla_decode_with_paged_kv_cache",
+ * Parameters: max_kv_len, the static K/V length bound, and max_seq_len_q, the
+ * per-request packed-query capacity, which may exceed the live lengths): the
+ * schedule is made as if every request had max_kv_len keys and, for prefill,
+ * max_seq_len_q query tokens (0: the largest delta of qo_indptr_host), with no
+ * causal trimming, so one plan serves every step whose live lengths stay
+ * within those bounds.  kv_len_host and kv_indptr_host are then ignored (may
+ * be NULL), and so is qo_indptr_host when max_seq_len_q > 0.  The live
+ * lengths go to mla_decode_live / mla_prefill_live on the device; work past
+ * them is skipped in the kernels.  Other run calls refuse capacity plans
+ * (MLA_ERR_PLAN_MISMATCH), and capacity plans are bf16 only.
+ *
+ * lse_layout MLA_LSE_HEADS_FIRST needs every request to have the same number
+ * of query tokens (capacity prefill: max_seq_len_q of them, live counts may
+ * be smaller); rows past a request's live tokens are left unwritten.
+ *
+ * Errors: MLA_ERR_INVALID_ARGUMENT (null pointers, inconsistent arrays,
+ * max_kv_len or max_seq_len_q < 0, unequal query counts with
+ * MLA_LSE_HEADS_FIRST, validate not 0 or 1), MLA_ERR_UNSUPPORTED (head dims
+ * other than 512/64, page_size not a power of two in range, fp8 prefill, an
+ * fp8 capacity plan), MLA_ERR_DEVICE (num_cus = 0 and the device query
+ * failed).  Makes no device allocation and launches nothing.             */
 mla_status mla_plan_create(mla_plan** plan, const mla_plan_desc* desc,
                            const int32_t* kv_len_host, const int32_t* kv_indptr_host,
                            const int32_t* qo_indptr_host);
@@ -169,8 +210,10 @@ mla_status mla_plan_upload(const mla_plan* plan, void* workspace, size_t workspa
  * Slots past kv_len in a request's last page and pages no request lists
  * are never read into the result (they may hold any bits, NaN included).
  * Errors: MLA_ERR_INVALID_ARGUMENT (null pointer, non-finite sm_scale, bad
- * out_dtype), MLA_ERR_PLAN_MISMATCH (plan is not a bf16 decode plan),
- * MLA_ERR_WORKSPACE, MLA_ERR_DEVICE (launch failed).                     */
+ * out_dtype; with validate = 1 also kv_indptr unequal to the plan's or a page
+ * id outside [0, num_pages)), MLA_ERR_PLAN_MISMATCH (plan is not a bf16
+ * decode plan, or is a capacity plan), MLA_ERR_WORKSPACE, MLA_ERR_DEVICE
+ * (launch failed).                                                       */
 mla_status mla_decode(const mla_plan* plan, const void* q_nope, const void* q_pe,
                       const void* ckv_cache, const void* kpe_cache, const int32_t* kv_indptr,
                       const int32_t* kv_indices, float sm_scale, void* out, int32_t out_dtype,
@@ -189,6 +232,30 @@ mla_status mla_prefill(const mla_plan* plan, const void* q_nope, const void* q_p
                        const int32_t* kv_indptr, const int32_t* kv_indices, float sm_scale,
                        void* out, int32_t out_dtype, float* lse, void* workspace,
                        size_t workspace_bytes, hipStream_t stream);
+
+/* Run calls of capacity plans (desc.max_kv_len > 0): as mla_decode /
+ * mla_prefill, with the live key counts on the device.
+ *   kv_len [batch] int32 device: keys of each request this step, each in
+ *     [0, max_kv_len] (the pages' seq_lens / cache_seqlens);
+ *   kv_indptr [batch+1] int32 device: page offsets of this step, with
+ *     kv_indptr[b+1] - kv_indptr[b] >= ceil(kv_len[b] / page_size);
+ *   qo_indptr [batch+1] int32 device (prefill): query offsets of this step,
+ *     every delta <= max_seq_len_q, with delta <= kv_len[b] when causal.
+ * Rows of a request past its live query tokens are not written (their lse
+ * entries included); a request with kv_len 0 gets out 0 and lse -inf.
+ * Out-of-bound live lengths are caught by validate = 1; without it a live
+ * count above the plan's bound is treated as the bound.  Errors as for
+ * mla_decode, plus MLA_ERR_PLAN_MISMATCH for a plan that is not a capacity
+ * plan of the call's kind.                                               */
+mla_status mla_decode_live(const mla_plan* plan, const void* q_nope, const void* q_pe, const void* ckv_cache,
+                           const void* kpe_cache, const int32_t* kv_len, const int32_t* kv_indptr,
+                           const int32_t* kv_indices, float sm_scale, void* out, int32_t out_dtype, float* lse,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+mla_status mla_prefill_live(const mla_plan* plan, const void* q_nope, const void* q_pe, const void* ckv_cache,
+                            const void* kpe_cache, const int32_t* qo_indptr, const int32_t* kv_len,
+                            const int32_t* kv_indptr, const int32_t* kv_indices, float sm_scale, void* out,
+                            int32_t out_dtype, float* lse, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
 
 /* Decode over the fp8 record cache (MLA_KV_FP8_E4M3_T128 above):
  *   kv_cache [num_pages, page_size, 656] uint8; q_nope / q_pe bf16 as in

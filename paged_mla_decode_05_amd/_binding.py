@@ -23,6 +23,9 @@ MLA_TILE_AUTO = 0
 MLA_TILE_WIDE = 1
 MLA_TILE_NARROW = 2
 MLA_TILE_QUAD = 3
+MLA_LSE_ROWS = 0
+MLA_LSE_HEADS_FIRST = 1
+MLA_ERR_INVALID_ARGUMENT = -1
 
 _DIM_CKV = 512
 _DIM_KPE = 64
@@ -40,7 +43,8 @@ class MLAError(RuntimeError):
 class _Desc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "kind", "batch", "num_qo_heads", "head_dim_ckv", "head_dim_kpe", "page_size", "num_pages",
-        "kv_format", "causal", "num_cus", "max_splits", "force_splits", "tile_mode")]
+        "kv_format", "causal", "num_cus", "max_splits", "force_splits", "tile_mode", "validate", "lse_layout",
+        "max_kv_len", "max_seq_len_q")]
 
 
 _lib = None
@@ -87,6 +91,10 @@ def load_library():
         L.mla_decode.restype = i32
         L.mla_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, i32, vp, vp, sz, vp]
         L.mla_prefill.restype = i32
+        L.mla_decode_live.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, i32, vp, vp, sz, vp]
+        L.mla_decode_live.restype = i32
+        L.mla_prefill_live.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, i32, vp, vp, sz, vp]
+        L.mla_prefill_live.restype = i32
         L.mla_decode_fp8.argtypes = [vp, vp, vp, vp, vp, vp, f32, vp, i32, vp, vp, sz, vp]
         L.mla_decode_fp8.restype = i32
         L.mla_decode_fp8_q8.argtypes = [vp, vp, vp, vp, vp, f32, vp, i32, vp, vp, sz, vp]
@@ -134,6 +142,8 @@ def _host_i32(x, n: Optional[int] = None):
 
 class Plan:
     """A host plan (split-KV schedule) plus its device workspace."""
+
+    s_q = 1  # query tokens per request (prefill plans: set at creation)
 
     def __init__(self, handle, desc: _Desc, kv_len, kv_indptr, qo_indptr):
         self._h = handle
@@ -212,22 +222,33 @@ class Plan:
 def mla_plan_create(kind: int, batch: int, num_heads: int, page_size: int, num_pages: int, kv_len,
                     kv_indptr, qo_indptr=None, kv_format: int = MLA_KV_BF16, causal: bool = True,
                     num_cus: int = 0, max_splits: int = 0, force_splits: int = 0,
-                    tile_mode: int = MLA_TILE_AUTO) -> Plan:
-    """Host plan for one set of request lengths (see include/mla.h)."""
+                    tile_mode: int = MLA_TILE_AUTO, validate: bool = False, lse_layout: int = MLA_LSE_ROWS,
+                    max_kv_len: int = 0, max_seq_len_q: int = 0) -> Plan:
+    """Host plan for one set of request lengths, or (max_kv_len > 0) a
+    capacity plan for any live lengths within the bounds (see include/mla.h)."""
     L = load_library()
     d = _Desc(kind=kind, batch=batch, num_qo_heads=num_heads, head_dim_ckv=_DIM_CKV,
               head_dim_kpe=_DIM_KPE, page_size=page_size, num_pages=num_pages, kv_format=kv_format,
               causal=int(bool(causal)), num_cus=num_cus, max_splits=max_splits,
-              force_splits=force_splits, tile_mode=tile_mode)
-    kl, kl_p = _host_i32(kv_len, batch)
-    ki, ki_p = _host_i32(kv_indptr, batch + 1)
+              force_splits=force_splits, tile_mode=tile_mode, validate=int(validate),
+              lse_layout=lse_layout, max_kv_len=max_kv_len, max_seq_len_q=max_seq_len_q)
+    kl, kl_p = _host_i32(kv_len, batch) if kv_len is not None else (None, None)
+    ki, ki_p = _host_i32(kv_indptr, batch + 1) if kv_indptr is not None else (None, None)
     qo, qo_p = _host_i32(qo_indptr, batch + 1) if qo_indptr is not None else (None, None)
     h = ctypes.c_void_p()
     P = ctypes.POINTER(ctypes.c_int32)
     cast = lambda p: ctypes.cast(p, P) if p is not None else None
     _check(L.mla_plan_create(ctypes.byref(h), ctypes.byref(d), cast(kl_p), cast(ki_p), cast(qo_p)),
            "mla_plan_create")
-    return Plan(h, d, kl, ki, qo)
+    plan = Plan(h, d, kl, ki, qo)
+    # query tokens per request: the lse layout [batch, H, s_q] is sized by it
+    if kind == MLA_KIND_PREFILL:
+        if max_kv_len > 0 and max_seq_len_q > 0:
+            plan.s_q = max_seq_len_q
+        else:
+            deltas = (qo[1:] - qo[:-1]) if qo is not None and batch > 0 else torch.ones(1, dtype=torch.int32)
+            plan.s_q = int(deltas.max()) if deltas.numel() else 1
+    return plan
 
 
 def mla_sparse_plan_create(num_tokens: int, num_heads: int, num_slots: int, topk: int,
@@ -275,7 +296,7 @@ def _sparse_extras(plan, q, indices, topk_length, attn_sink, out, lse, max_logit
     ix = _dev(indices, "indices", torch.int32, (T, topk))
     tl = _dev(topk_length, "topk_length", torch.int32, (T,)) if topk_length is not None else None
     sk = _dev(attn_sink, "attn_sink", torch.float32, (H,)) if attn_sink is not None else None
-    out, lse, code = _packed_outputs(q, out, lse, out_dtype)
+    out, lse, code = _packed_outputs(q, out, lse, out_dtype, plan)
     if max_logits is None:
         max_logits = torch.empty((T, H), dtype=torch.float32, device=q.device)
     mx = _dev(max_logits, "max_logits", torch.float32, (T, H))
@@ -322,16 +343,22 @@ def _dev(t: torch.Tensor, name: str, dtype, shape=None):
     return t.data_ptr()
 
 
-def _outputs(q_nope: torch.Tensor, out, lse, out_dtype):
+def _lse_shape(plan, rows: int, H: int):
+    if plan is not None and plan.desc.lse_layout == MLA_LSE_HEADS_FIRST:
+        return (plan.desc.batch, H, plan.s_q)
+    return (rows, H)
+
+
+def _outputs(q_nope: torch.Tensor, out, lse, out_dtype, plan=None):
     rows, H = q_nope.shape[0], q_nope.shape[1]
     if out is None:
         out = torch.empty((rows, H, _DIM_CKV), dtype=out_dtype, device=q_nope.device)
     if lse is None:
-        lse = torch.empty((rows, H), dtype=torch.float32, device=q_nope.device)
+        lse = torch.empty(_lse_shape(plan, rows, H), dtype=torch.float32, device=q_nope.device)
     if out.dtype not in (torch.bfloat16, torch.float32):
         raise ValueError("out must be bf16 or fp32")
     _dev(out, "out", out.dtype, (rows, H, _DIM_CKV))
-    _dev(lse, "lse", torch.float32, (rows, H))
+    _dev(lse, "lse", torch.float32, _lse_shape(plan, rows, H))
     code = MLA_DTYPE_BF16 if out.dtype == torch.bfloat16 else MLA_DTYPE_FP32
     return out, lse, code
 
@@ -342,10 +369,17 @@ def _q(plan: Plan, q_nope, q_pe, rows: int):
             _dev(q_pe, "q_pe", torch.bfloat16, (rows, H, _DIM_KPE)))
 
 
+def _nonempty(t: torch.Tensor) -> torch.Tensor:
+    """An empty index tensor has no storage (a null pointer, which the C ABI
+    refuses): hand over one padding entry instead; it is never read."""
+    return t if t.numel() > 0 else torch.zeros(1, dtype=t.dtype, device=t.device)
+
+
 def _paging(plan: Plan, kv_indptr, kv_indices):
+    kv_indices = _nonempty(kv_indices)
     a = _dev(kv_indptr, "kv_indptr", torch.int32, (plan.desc.batch + 1,))
     b = _dev(kv_indices, "kv_indices", torch.int32)
-    if plan.desc.batch > 0 and kv_indices.numel() < int(plan.kv_indptr[-1]):
+    if plan.desc.batch > 0 and plan.kv_indptr is not None and kv_indices.numel() < int(plan.kv_indptr[-1]):
         raise ValueError("kv_indices is shorter than kv_indptr[-1]")
     return a, b
 
@@ -359,7 +393,7 @@ def mla_decode(plan: Plan, q_nope, q_pe, ckv_cache, kpe_cache, kv_indptr, kv_ind
     c = _dev(ckv_cache, "ckv_cache", torch.bfloat16, (P, ps, _DIM_CKV))
     k = _dev(kpe_cache, "kpe_cache", torch.bfloat16, (P, ps, _DIM_KPE))
     ip, ix = _paging(plan, kv_indptr, kv_indices)
-    out, lse, code = _outputs(q_nope, out, lse, out_dtype)
+    out, lse, code = _outputs(q_nope, out, lse, out_dtype, plan)
     ws = plan.workspace(q_nope.device) if workspace is None else workspace
     stream = torch.cuda.current_stream(q_nope.device).cuda_stream
     _check(L.mla_decode(plan.handle, qn, qp, c, k, ip, ix, float(sm_scale), out.data_ptr(), code,
@@ -381,7 +415,7 @@ def mla_decode_noalloc(plan: Plan, q_nope, q_pe, ckv_cache, kpe_cache, kv_indptr
     c = _dev(ckv_cache, "ckv_cache", torch.bfloat16, (P, ps, _DIM_CKV))
     k = _dev(kpe_cache, "kpe_cache", torch.bfloat16, (P, ps, _DIM_KPE))
     ip, ix = _paging(plan, kv_indptr, kv_indices)
-    out, lse, code = _outputs(q_nope, out, lse, out_dtype)
+    out, lse, code = _outputs(q_nope, out, lse, out_dtype, plan)
     stream = torch.cuda.current_stream(q_nope.device).cuda_stream
     _check(L.mla_decode_noalloc(plan.handle, qn, qp, c, k, ip, ix, float(sm_scale), out.data_ptr(), code,
                                 lse.data_ptr(), stream), "mla_decode_noalloc")
@@ -399,11 +433,56 @@ def mla_prefill(plan: Plan, q_nope, q_pe, ckv_cache, kpe_cache, qo_indptr, kv_in
     k = _dev(kpe_cache, "kpe_cache", torch.bfloat16, (P, ps, _DIM_KPE))
     qo = _dev(qo_indptr, "qo_indptr", torch.int32, (B + 1,))
     ip, ix = _paging(plan, kv_indptr, kv_indices)
-    out, lse, code = _outputs(q_nope, out, lse, out_dtype)
+    out, lse, code = _outputs(q_nope, out, lse, out_dtype, plan)
     ws = plan.workspace(q_nope.device) if workspace is None else workspace
     stream = torch.cuda.current_stream(q_nope.device).cuda_stream
     _check(L.mla_prefill(plan.handle, qn, qp, c, k, qo, ip, ix, float(sm_scale), out.data_ptr(), code,
                          lse.data_ptr(), ws.data_ptr(), ws.numel(), stream), "mla_prefill")
+    return out, lse
+
+
+def mla_decode_live(plan: Plan, q_nope, q_pe, ckv_cache, kpe_cache, kv_len, kv_indptr, kv_indices, sm_scale: float,
+                    out=None, lse=None, out_dtype=torch.bfloat16, workspace=None):
+    """Decode with a capacity plan: kv_len [B] int32 on the device holds this
+    call's live key counts (each <= the plan's max_kv_len)."""
+    L = load_library()
+    B, P, ps = plan.desc.batch, plan.desc.num_pages, plan.desc.page_size
+    qn, qp = _q(plan, q_nope, q_pe, B)
+    c = _dev(ckv_cache, "ckv_cache", torch.bfloat16, (P, ps, _DIM_CKV))
+    k = _dev(kpe_cache, "kpe_cache", torch.bfloat16, (P, ps, _DIM_KPE))
+    kl = _dev(kv_len, "kv_len", torch.int32, (B,))
+    ip = _dev(kv_indptr, "kv_indptr", torch.int32, (B + 1,))
+    kv_indices = _nonempty(kv_indices)
+    ix = _dev(kv_indices, "kv_indices", torch.int32)
+    out, lse, code = _outputs(q_nope, out, lse, out_dtype, plan)
+    ws = plan.workspace(q_nope.device) if workspace is None else workspace
+    stream = torch.cuda.current_stream(q_nope.device).cuda_stream
+    _check(L.mla_decode_live(plan.handle, qn, qp, c, k, kl, ip, ix, float(sm_scale), out.data_ptr(), code,
+                             lse.data_ptr(), ws.data_ptr(), ws.numel(), stream), "mla_decode_live")
+    return out, lse
+
+
+def mla_prefill_live(plan: Plan, q_nope, q_pe, ckv_cache, kpe_cache, qo_indptr, kv_len, kv_indptr, kv_indices,
+                     sm_scale: float, out=None, lse=None, out_dtype=torch.bfloat16, workspace=None):
+    """Prefill with a capacity plan: qo_indptr [B+1], kv_len [B] and kv_indptr
+    [B+1] on the device hold this call's live query offsets, key counts and
+    page offsets.  q_nope / q_pe hold qo_indptr[B] query tokens (rows)."""
+    L = load_library()
+    B, P, ps = plan.desc.batch, plan.desc.num_pages, plan.desc.page_size
+    rows = q_nope.shape[0]
+    qn, qp = _q(plan, q_nope, q_pe, rows)
+    c = _dev(ckv_cache, "ckv_cache", torch.bfloat16, (P, ps, _DIM_CKV))
+    k = _dev(kpe_cache, "kpe_cache", torch.bfloat16, (P, ps, _DIM_KPE))
+    qo = _dev(qo_indptr, "qo_indptr", torch.int32, (B + 1,))
+    kl = _dev(kv_len, "kv_len", torch.int32, (B,))
+    ip = _dev(kv_indptr, "kv_indptr", torch.int32, (B + 1,))
+    kv_indices = _nonempty(kv_indices)
+    ix = _dev(kv_indices, "kv_indices", torch.int32)
+    out, lse, code = _outputs(q_nope, out, lse, out_dtype, plan)
+    ws = plan.workspace(q_nope.device) if workspace is None else workspace
+    stream = torch.cuda.current_stream(q_nope.device).cuda_stream
+    _check(L.mla_prefill_live(plan.handle, qn, qp, c, k, qo, kl, ip, ix, float(sm_scale), out.data_ptr(), code,
+                              lse.data_ptr(), ws.data_ptr(), ws.numel(), stream), "mla_prefill_live")
     return out, lse
 
 
@@ -415,7 +494,7 @@ def mla_decode_fp8(plan: Plan, q_nope, q_pe, kv_cache, kv_indptr, kv_indices, sm
     qn, qp = _q(plan, q_nope, q_pe, B)
     kv = _dev(kv_cache, "kv_cache", torch.uint8, (P, ps, _FP8_RECORD))
     ip, ix = _paging(plan, kv_indptr, kv_indices)
-    out, lse, code = _outputs(q_nope, out, lse, out_dtype)
+    out, lse, code = _outputs(q_nope, out, lse, out_dtype, plan)
     ws = plan.workspace(q_nope.device) if workspace is None else workspace
     stream = torch.cuda.current_stream(q_nope.device).cuda_stream
     _check(L.mla_decode_fp8(plan.handle, qn, qp, kv, ip, ix, float(sm_scale), out.data_ptr(), code,
@@ -427,11 +506,11 @@ def _packed_q(plan: Plan, q, rows: int):
     return _dev(q, "q", torch.bfloat16, (rows, plan.num_heads, _DIM_CKV + _DIM_KPE))
 
 
-def _packed_outputs(q: torch.Tensor, out, lse, out_dtype):
+def _packed_outputs(q: torch.Tensor, out, lse, out_dtype, plan=None):
     rows, H = q.shape[0], q.shape[1]
     if out is None:
         out = torch.empty((rows, H, _DIM_CKV), dtype=out_dtype, device=q.device)
-    return _outputs(out, out, lse, out.dtype)
+    return _outputs(out, out, lse, out.dtype, plan)
 
 
 def mla_decode_fp8_q8(plan: Plan, q, kv_cache, kv_indptr, kv_indices, sm_scale: float, out=None, lse=None,
@@ -443,7 +522,7 @@ def mla_decode_fp8_q8(plan: Plan, q, kv_cache, kv_indptr, kv_indices, sm_scale: 
     qq = _dev(q, "q", torch.uint8, (B, plan.num_heads, _DIM_CKV + _DIM_KPE))
     kv = _dev(kv_cache, "kv_cache", torch.uint8, (P, ps, _FP8_RECORD))
     ip, ix = _paging(plan, kv_indptr, kv_indices)
-    out, lse, code = _packed_outputs(q, out, lse, out_dtype)
+    out, lse, code = _packed_outputs(q, out, lse, out_dtype, plan)
     ws = plan.workspace(q.device) if workspace is None else workspace
     stream = torch.cuda.current_stream(q.device).cuda_stream
     _check(L.mla_decode_fp8_q8(plan.handle, qq, kv, ip, ix, float(sm_scale), out.data_ptr(), code, lse.data_ptr(),
@@ -461,7 +540,7 @@ def mla_decode_packed(plan: Plan, q, kv_cache, kv_indptr, kv_indices, sm_scale: 
     qq = _packed_q(plan, q, B)
     kv = _dev(kv_cache, "kv_cache", torch.bfloat16, (P, ps, _DIM_CKV + _DIM_KPE))
     ip, ix = _paging(plan, kv_indptr, kv_indices)
-    out, lse, code = _packed_outputs(q, out, lse, out_dtype)
+    out, lse, code = _packed_outputs(q, out, lse, out_dtype, plan)
     ws = plan.workspace(q.device) if workspace is None else workspace
     stream = torch.cuda.current_stream(q.device).cuda_stream
     _check(L.mla_decode_packed(plan.handle, qq, kv, ip, ix, float(sm_scale), float(out_scale), out.data_ptr(), code,
@@ -480,7 +559,7 @@ def mla_prefill_packed(plan: Plan, q, kv_cache, qo_indptr, kv_indptr, kv_indices
     kv = _dev(kv_cache, "kv_cache", torch.bfloat16, (P, ps, _DIM_CKV + _DIM_KPE))
     qo = _dev(qo_indptr, "qo_indptr", torch.int32, (B + 1,))
     ip, ix = _paging(plan, kv_indptr, kv_indices)
-    out, lse, code = _packed_outputs(q, out, lse, out_dtype)
+    out, lse, code = _packed_outputs(q, out, lse, out_dtype, plan)
     ws = plan.workspace(q.device) if workspace is None else workspace
     stream = torch.cuda.current_stream(q.device).cuda_stream
     _check(L.mla_prefill_packed(plan.handle, qq, kv, qo, ip, ix, float(sm_scale), float(out_scale), out.data_ptr(),

@@ -35,11 +35,18 @@ struct mla_plan {
   int32_t xcd_map = 0;         // quad mode: siblings share blockIdx.x mod 8
   int32_t num_slots = 0;       // partial-result slots
   std::vector<int32_t> kv_indptr;  // [batch + 1] host copy of the page offsets the plan was made for
+  std::vector<int32_t> qo_indptr;  // [batch + 1] prefill: host copy of the query offsets (empty for capacity plans)
+  int32_t capacity = 0;            // a capacity plan (desc.max_kv_len > 0): runs take live lengths
+  int32_t max_q = 1;               // query tokens per request a capacity plan allows
+  int32_t lse_sq = 0;              // > 0: lse laid out [batch, H, lse_sq]
   std::vector<int32_t> wg_ptr;  // [num_wgs + 1] item range of each workgroup
   std::vector<WorkItem> items;
   std::vector<SplitGroup> groups;
   std::vector<int32_t> blob;    // uploaded image: wg_ptr | items | groups
   size_t off_items = 0, off_groups = 0, off_part_lse = 0, off_part_o = 0, ws_bytes = 0;
+  // uploaded copies of the plan's kv_indptr / qo_indptr and the status word of
+  // the validate checks
+  size_t off_plan_kv = 0, off_plan_qo = 0, off_status = 0;
   // token-sparse plans: entries per list, and the workspace regions of the
   // compacted lists [batch][topk], their counts [batch], page offsets
   // [batch + 1] and the partial maxima [slots][rows_per_block]
@@ -128,7 +135,7 @@ void pack_units(mla_plan* p, const std::vector<Unit>& units, int64_t budget) {
     }
     const int32_t n = (int32_t)(p->items.size() - first);
     if (n > 1) {
-      SplitGroup g{u.b, u.row0, u.nrows, n, p->num_slots, {0, 0, 0}};
+      SplitGroup g{u.b, u.row0, u.nrows, n, p->num_slots, u.q_len, {0, 0}};
       for (int32_t k = 0; k < n; ++k) p->items[first + k].slot = p->num_slots + k;
       p->num_slots += n;
       p->groups.push_back(g);
@@ -177,7 +184,8 @@ mla_status build_schedule(mla_plan* p, const std::vector<int32_t>& kv_len,
     for (int64_t r0 = 0; r0 < rows; r0 += RB) {
       const int32_t nr = (int32_t)std::min<int64_t>(RB, rows - r0);
       int32_t vis = kv_len[b];
-      if (d.kind == MLA_KIND_PREFILL && d.causal) {
+      // capacity plans are not trimmed: the live counts move the causal bound
+      if (d.kind == MLA_KIND_PREFILL && d.causal && !p->capacity) {
         const int32_t last_q = (int32_t)((r0 + nr - 1) / H);  // query token of the block's last row
         vis = kv_len[b] - q_len[b] + last_q + 1;
       }
@@ -205,12 +213,16 @@ mla_status build_schedule(mla_plan* p, const std::vector<int32_t>& kv_len,
     p->grid = p->xcd_map ? (int32_t)cus * p->group_size : p->num_wgs * p->group_size;
   }
 
-  // Workspace layout: [wg_ptr | items | groups] [part_lse] [part_o]
+  // Workspace layout: [wg_ptr | items | groups | plan kv_indptr | plan
+  // qo_indptr] [status] [part_lse] [part_o]
   const size_t n_ptr = align_up((size_t)(p->num_wgs + 1) * 4, 32);
   p->off_items = n_ptr;
   p->off_groups = p->off_items + p->items.size() * sizeof(WorkItem);
-  const size_t blob_bytes = p->off_groups + p->groups.size() * sizeof(SplitGroup);
-  p->off_part_lse = align_up(blob_bytes, mla::kWsAlign);
+  p->off_plan_kv = p->off_groups + p->groups.size() * sizeof(SplitGroup);
+  p->off_plan_qo = p->off_plan_kv + p->kv_indptr.size() * 4;
+  const size_t blob_bytes = p->off_plan_qo + p->qo_indptr.size() * 4;
+  p->off_status = align_up(blob_bytes, mla::kWsAlign);
+  p->off_part_lse = align_up(p->off_status + 4, mla::kWsAlign);
   p->off_part_o = align_up(p->off_part_lse + (size_t)p->num_slots * RB * 4, mla::kWsAlign);
   p->ws_bytes = align_up(p->off_part_o + (size_t)p->num_slots * RB * mla::kDimCkv * 2, mla::kWsAlign);
   if (d.kind == MLA_KIND_SPARSE_DECODE) {
@@ -224,6 +236,63 @@ mla_status build_schedule(mla_plan* p, const std::vector<int32_t>& kv_len,
   std::memcpy(p->blob.data(), p->wg_ptr.data(), p->wg_ptr.size() * 4);
   std::memcpy((char*)p->blob.data() + p->off_items, p->items.data(), p->items.size() * sizeof(WorkItem));
   std::memcpy((char*)p->blob.data() + p->off_groups, p->groups.data(), p->groups.size() * sizeof(SplitGroup));
+  std::memcpy((char*)p->blob.data() + p->off_plan_kv, p->kv_indptr.data(), p->kv_indptr.size() * 4);
+  if (!p->qo_indptr.empty())
+    std::memcpy((char*)p->blob.data() + p->off_plan_qo, p->qo_indptr.data(), p->qo_indptr.size() * 4);
+  return MLA_OK;
+}
+
+mla_status device_cus(int32_t* num_cus) {
+  if (*num_cus != 0) return MLA_OK;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_DEVICE;
+  if (hipDeviceGetAttribute(num_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return MLA_ERR_DEVICE;
+  return MLA_OK;
+}
+
+// A capacity plan ("batch_mla_decode_with_paged_kv_cache": max_kv_len, the
+// static K/V length bound; max_seq_len_q, the per-request packed-query
+// capacity): every request planned at max_kv_len keys and max_q query
+// tokens, with no causal trimming; run calls clip the work to the live
+// counts they are given on the device.
+mla_status create_capacity_plan(mla_plan** out, const mla_plan_desc* d, const int32_t* qo_indptr_host) {
+  int32_t max_q = 1;
+  if (d->kind == MLA_KIND_PREFILL) {
+    max_q = d->max_seq_len_q;
+    if (max_q == 0) {
+      if (d->batch > 0 && !qo_indptr_host) return MLA_ERR_INVALID_ARGUMENT;
+      for (int32_t b = 0; b < d->batch; ++b) {
+        const int64_t n = (int64_t)qo_indptr_host[b + 1] - qo_indptr_host[b];
+        if (n < 0 || (b == 0 && qo_indptr_host[0] != 0)) return MLA_ERR_INVALID_ARGUMENT;
+        max_q = (int32_t)std::max<int64_t>(max_q, n);
+      }
+      max_q = std::max(max_q, 1);
+    }
+    if (d->causal && max_q > d->max_kv_len) return MLA_ERR_INVALID_ARGUMENT;
+  } else if (d->max_seq_len_q > 1) {
+    return MLA_ERR_INVALID_ARGUMENT;  // decode has one query token per request
+  }
+  if ((int64_t)max_q * d->num_qo_heads > ((int64_t)1 << 30)) return MLA_ERR_INVALID_ARGUMENT;
+  int32_t num_cus = d->num_cus;
+  mla_status st = device_cus(&num_cus);
+  if (st != MLA_OK) return st;
+  mla_plan* p = new (std::nothrow) mla_plan();
+  if (!p) return MLA_ERR_INVALID_ARGUMENT;
+  p->d = *d;
+  p->capacity = 1;
+  p->max_q = max_q;
+  // the bound's page layout (used by the block-table adapter's width check)
+  const int32_t pages = (d->max_kv_len + d->page_size - 1) / d->page_size;
+  p->kv_indptr.resize((size_t)d->batch + 1);
+  for (int32_t b = 0; b <= d->batch; ++b) p->kv_indptr[b] = b * pages;
+  if (d->lse_layout == MLA_LSE_HEADS_FIRST) p->lse_sq = max_q;
+  std::vector<int32_t> kv_len(d->batch, d->max_kv_len), q_len(d->batch, max_q);
+  st = build_schedule(p, kv_len, q_len, num_cus);
+  if (st != MLA_OK) {
+    delete p;
+    return st;
+  }
+  *out = p;
   return MLA_OK;
 }
 
@@ -256,9 +325,16 @@ mla_status mla_plan_create(mla_plan** out, const mla_plan_desc* d, const int32_t
   if (d->tile_mode < MLA_TILE_AUTO || d->tile_mode > MLA_TILE_QUAD) return MLA_ERR_INVALID_ARGUMENT;
   if (d->kv_format == MLA_KV_FP8_E4M3_T128 && d->tile_mode == MLA_TILE_QUAD) return MLA_ERR_UNSUPPORTED;
   if (d->max_splits < 0 || d->force_splits < 0 || d->num_cus < 0) return MLA_ERR_INVALID_ARGUMENT;
+  if (d->validate != 0 && d->validate != 1) return MLA_ERR_INVALID_ARGUMENT;
+  if (d->lse_layout != MLA_LSE_ROWS && d->lse_layout != MLA_LSE_HEADS_FIRST) return MLA_ERR_INVALID_ARGUMENT;
+  if (d->max_kv_len < 0 || d->max_seq_len_q < 0 || d->max_kv_len > (1 << 30)) return MLA_ERR_INVALID_ARGUMENT;
+  const bool cap = d->max_kv_len > 0;
+  if (!cap && d->max_seq_len_q > 0) return MLA_ERR_INVALID_ARGUMENT;
+  if (cap && d->kv_format != MLA_KV_BF16) return MLA_ERR_UNSUPPORTED;
+  if (d->kind == MLA_KIND_DECODE && qo_indptr_host) return MLA_ERR_INVALID_ARGUMENT;
+  if (cap) return create_capacity_plan(out, d, qo_indptr_host);
   if (d->batch > 0 && !kv_indptr_host) return MLA_ERR_INVALID_ARGUMENT;
   if (d->kind == MLA_KIND_PREFILL && d->batch > 0 && !qo_indptr_host) return MLA_ERR_INVALID_ARGUMENT;
-  if (d->kind == MLA_KIND_DECODE && qo_indptr_host) return MLA_ERR_INVALID_ARGUMENT;
 
   std::vector<int32_t> kv_len(d->batch), q_len(d->batch, 1);
   if (d->batch > 0 && kv_indptr_host[0] != 0) return MLA_ERR_INVALID_ARGUMENT;
@@ -277,20 +353,21 @@ mla_status mla_plan_create(mla_plan** out, const mla_plan_desc* d, const int32_t
       q_len[b] = (int32_t)n;
     }
   }
+  if (d->lse_layout == MLA_LSE_HEADS_FIRST)
+    for (int32_t b = 1; b < d->batch; ++b)
+      if (q_len[b] != q_len[0]) return MLA_ERR_INVALID_ARGUMENT;
 
   int32_t num_cus = d->num_cus;
-  if (num_cus == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_DEVICE;
-    if (hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return MLA_ERR_DEVICE;
-  }
+  const mla_status cus_st = device_cus(&num_cus);
+  if (cus_st != MLA_OK) return cus_st;
 
   mla_plan* p = new (std::nothrow) mla_plan();
   if (!p) return MLA_ERR_INVALID_ARGUMENT;
   p->d = *d;
   p->kv_indptr.assign(kv_indptr_host ? kv_indptr_host : nullptr, kv_indptr_host ? kv_indptr_host + d->batch + 1 : nullptr);
   if (p->kv_indptr.empty()) p->kv_indptr.assign(1, 0);
+  if (d->kind == MLA_KIND_PREFILL && qo_indptr_host) p->qo_indptr.assign(qo_indptr_host, qo_indptr_host + d->batch + 1);
+  if (d->lse_layout == MLA_LSE_HEADS_FIRST) p->lse_sq = d->batch > 0 ? q_len[0] : 1;
   mla_status st = build_schedule(p, kv_len, q_len, num_cus);
   if (st != MLA_OK) {
     delete p;
@@ -398,14 +475,43 @@ struct Sparse {
   float* max_logits = nullptr;
 };
 
+// The opt-in device-array checks (desc.validate = 1): one small kernel, then
+// the stream is synchronised and its verdict read back, before anything
+// reads through the arrays.
+mla_status validate_arrays(const mla_plan* p, char* w, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                           const int32_t* kv_indices, const int32_t* live_kv_len, hipStream_t stream) {
+  mla::ValidateArgs v{};
+  v.kv_indptr = kv_indptr;
+  v.kv_indices = kv_indices;
+  v.qo_indptr = p->d.kind == MLA_KIND_PREFILL ? qo_indptr : nullptr;
+  v.live_kv_len = live_kv_len;
+  v.plan_kv_indptr = (const int32_t*)(w + p->off_plan_kv);
+  v.plan_qo_indptr = p->qo_indptr.empty() ? nullptr : (const int32_t*)(w + p->off_plan_qo);
+  v.batch = p->d.batch;
+  v.page_size = p->d.page_size;
+  v.num_pages = p->d.num_pages;
+  v.max_kv_len = p->d.max_kv_len;
+  v.max_q = p->max_q;
+  v.causal = p->d.kind == MLA_KIND_PREFILL ? p->d.causal : 0;
+  v.status = (int32_t*)(w + p->off_status);
+  if (mla::launch_validate(v, stream) != hipSuccess) return MLA_ERR_DEVICE;
+  int32_t flags = -1;
+  if (hipMemcpyAsync(&flags, v.status, 4, hipMemcpyDeviceToHost, stream) != hipSuccess) return MLA_ERR_DEVICE;
+  if (hipStreamSynchronize(stream) != hipSuccess) return MLA_ERR_DEVICE;
+  return flags == 0 ? MLA_OK : MLA_ERR_INVALID_ARGUMENT;
+}
+
 mla_status run(const mla_plan* p, int32_t want_kind, int32_t want_format, const void* q_nope,
                const void* q_pe, const void* ckv, const void* kpe, const void* kv_fp8,
                const int32_t* qo_indptr, const int32_t* kv_indptr, const int32_t* kv_indices,
                float sm_scale, void* out, int32_t out_dtype, float* lse, void* ws, size_t ws_bytes,
                hipStream_t stream, const Layout& lay = kSplit, float out_scale = 1.f,
-               const Sparse* sparse = nullptr, bool q8 = false) {
+               const Sparse* sparse = nullptr, bool q8 = false, const int32_t* live_kv_len = nullptr,
+               bool live = false) {
   if (!p) return MLA_ERR_INVALID_ARGUMENT;
   if (p->d.kind != want_kind || p->d.kv_format != want_format) return MLA_ERR_PLAN_MISMATCH;
+  if ((p->capacity != 0) != live) return MLA_ERR_PLAN_MISMATCH;
+  if (live && !live_kv_len) return MLA_ERR_INVALID_ARGUMENT;
   if (out_dtype != MLA_DTYPE_BF16 && out_dtype != MLA_DTYPE_FP32) return MLA_ERR_INVALID_ARGUMENT;
   if (!std::isfinite(sm_scale) || !std::isfinite(out_scale)) return MLA_ERR_INVALID_ARGUMENT;
   if (p->items.empty()) return MLA_OK;  // nothing to compute (batch 0 or no rows)
@@ -417,6 +523,10 @@ mla_status run(const mla_plan* p, int32_t want_kind, int32_t want_format, const 
   if (!ws || ws_bytes < p->ws_bytes || ((uintptr_t)ws % mla::kWsAlign) != 0) return MLA_ERR_WORKSPACE;
   if (q8 && p->tile_mode != MLA_TILE_WIDE) return MLA_ERR_UNSUPPORTED;
   char* w = (char*)ws;
+  if (p->d.validate && !sparse) {
+    const mla_status vs = validate_arrays(p, w, qo_indptr, kv_indptr, kv_indices, live_kv_len, stream);
+    if (vs != MLA_OK) return vs;
+  }
   if (sparse) {
     // the lists are compacted into the workspace first; the attention kernel
     // then reads them as page lists of page size 1
@@ -464,6 +574,9 @@ mla_status run(const mla_plan* p, int32_t want_kind, int32_t want_format, const 
   a.q_stride = lay.q_stride;
   a.qpe_stride = lay.qpe_stride;
   a.out_scale = out_scale;
+  a.live_kv_len = live_kv_len;
+  a.live_q = (live && want_kind == MLA_KIND_PREFILL) ? 1 : 0;
+  a.lse_sq = p->lse_sq;
   if (sparse) {
     a.sparse_len = (const int32_t*)(w + p->off_sp_count);
     a.attn_sink = sparse->attn_sink;
@@ -509,6 +622,22 @@ mla_status mla_prefill(const mla_plan* p, const void* q_nope, const void* q_pe, 
                        float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
   return run(p, MLA_KIND_PREFILL, MLA_KV_BF16, q_nope, q_pe, ckv, kpe, nullptr, qo_indptr, kv_indptr,
              kv_indices, sm_scale, out, out_dtype, lse, ws, ws_bytes, stream);
+}
+
+mla_status mla_decode_live(const mla_plan* p, const void* q_nope, const void* q_pe, const void* ckv,
+                           const void* kpe, const int32_t* kv_len, const int32_t* kv_indptr,
+                           const int32_t* kv_indices, float sm_scale, void* out, int32_t out_dtype, float* lse,
+                           void* ws, size_t ws_bytes, hipStream_t stream) {
+  return run(p, MLA_KIND_DECODE, MLA_KV_BF16, q_nope, q_pe, ckv, kpe, nullptr, nullptr, kv_indptr, kv_indices,
+             sm_scale, out, out_dtype, lse, ws, ws_bytes, stream, kSplit, 1.f, nullptr, false, kv_len, true);
+}
+
+mla_status mla_prefill_live(const mla_plan* p, const void* q_nope, const void* q_pe, const void* ckv,
+                            const void* kpe, const int32_t* qo_indptr, const int32_t* kv_len,
+                            const int32_t* kv_indptr, const int32_t* kv_indices, float sm_scale, void* out,
+                            int32_t out_dtype, float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return run(p, MLA_KIND_PREFILL, MLA_KV_BF16, q_nope, q_pe, ckv, kpe, nullptr, qo_indptr, kv_indptr, kv_indices,
+             sm_scale, out, out_dtype, lse, ws, ws_bytes, stream, kSplit, 1.f, nullptr, false, kv_len, true);
 }
 
 mla_status mla_decode_fp8(const mla_plan* p, const void* q_nope, const void* q_pe, const void* kv,

@@ -583,10 +583,37 @@ __device__ __forceinline__ void store4(const AttnArgs& a, const WorkItem& it, co
   }
 }
 
+// Index of a final lse value: row qrow of [rows, H], or, for the layout
+// [requests, H, s_q] (FlashMLA's batch x heads x seq_len_q), request b, head
+// r % H, query token r / H (r counts the request's rows as token * H + head).
+__device__ __forceinline__ size_t lse_index(const AttnArgs& a, int b, int r, size_t qrow) {
+  if (a.lse_sq == 0) return qrow;
+  const int qi = r / a.num_heads;
+  return ((size_t)b * a.num_heads + (r - qi * a.num_heads)) * a.lse_sq + qi;
+}
+
+// Capacity plans: the item's rows and key range clipped to this call's live
+// counts (a live count above the plan's bound is taken as the bound).  False
+// when none of the item's rows exist this call: nothing is computed or
+// written for it (the combine skips those rows too).
+__device__ __forceinline__ bool clip_live(const AttnArgs& a, WorkItem& it) {
+  if (a.live_kv_len == nullptr) return true;
+  const int L = min(max(ld_const(a.live_kv_len, it.b), 0), it.kv_len);
+  int n = it.q_len;
+  if (a.live_q) n = min(max(ld_const(a.qo_indptr, it.b + 1) - ld_const(a.qo_indptr, it.b), 0), it.q_len);
+  it.nrows = min(it.nrows, n * a.num_heads - it.row0);
+  if (it.nrows <= 0) return false;
+  const int vis = a.causal ? L - n + (it.row0 + it.nrows - 1) / a.num_heads + 1 : L;
+  it.kv_len = L;
+  it.q_len = n;
+  it.tok1 = max(it.tok0, min(it.tok1, vis));
+  return true;
+}
+
 __device__ __forceinline__ void store_lse(const AttnArgs& a, const WorkItem& it, const RowInfo& ri,
                                           int r_in_block, float lse_nat) {
   if (it.slot < 0) {
-    a.lse[ri.qrow] = lse_nat;
+    a.lse[lse_index(a, it.b, it.row0 + r_in_block, ri.qrow)] = lse_nat;
   } else {
     a.part_lse[(size_t)it.slot * a.rows_per_block + r_in_block] = lse_nat;
   }
@@ -2078,6 +2105,7 @@ void mla_attn_quad_kernel(AttnArgs a) {
     it.kv_len = ld_const(ip, 5);
     it.q_len = ld_const(ip, 6);
     it.slot = ld_const(ip, 7);
+    if (!clip_live(a, it)) continue;
     if (kQuadRows * role >= it.nrows) continue;  // this slice of the row group is empty
     quad_item<kPC, false>(a, it, role, smem, wave, lane);
   }
@@ -2105,6 +2133,11 @@ __device__ __forceinline__ void combine_row(const AttnArgs& a, int gi, int r, in
   const int g_b = ld_const(gp, 0), g_row0 = ld_const(gp, 1), g_nrows = ld_const(gp, 2);
   const int nsplit = ld_const(gp, 3), slot0 = ld_const(gp, 4);
   if (r >= g_nrows) return;
+  if (a.live_kv_len != nullptr && a.live_q) {
+    // capacity prefill: rows past the request's live query tokens were not computed
+    const int n = min(max(ld_const(a.qo_indptr, g_b + 1) - ld_const(a.qo_indptr, g_b), 0), ld_const(gp, 5));
+    if (g_row0 + r >= n * a.num_heads) return;
+  }
   const int q_start = a.qo_indptr ? ld_const(a.qo_indptr, g_b) : g_b;
   const size_t row0 = (size_t)slot0 * a.rows_per_block + r;  // row r of the group's first slot
   const size_t stride = (size_t)a.rows_per_block;             // rows between consecutive slots
@@ -2172,7 +2205,7 @@ __device__ __forceinline__ void combine_row(const AttnArgs& a, int gi, int r, in
     dst[0] = f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
     dst[1] = f32x4{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
   }
-  if (lane == 0) a.lse[qrow] = (W > 0.f) ? M + __logf(W) : kNegInf;
+  if (lane == 0) a.lse[lse_index(a, g_b, rr, qrow)] = (W > 0.f) ? M + __logf(W) : kNegInf;
 }
 
 __global__ __launch_bounds__(256) void mla_combine_kernel(AttnArgs a) {
@@ -2224,6 +2257,8 @@ void mla_attn_kernel(AttnArgs a) {
       const int L = ld_const(a.sparse_len, it.b);
       it.kv_len = L;
       it.tok1 = max(it.tok0, min(it.tok1, L));
+    } else if (!clip_live(a, it)) {
+      continue;
     }
     if (kMode == 1 && kFp8) {
       wide8_item<kPC, kSparse, kQ8>(a, it, smem, wave, lane);

@@ -31,13 +31,15 @@ struct WorkItem {
 static_assert(sizeof(WorkItem) == 32, "work item is 8 int32");
 
 // One split (request, row block): its nsplit partial slots are consecutive.
+// q_len: query tokens of the request as planned (a capacity plan's bound).
 struct SplitGroup {
   int32_t b;
   int32_t row0;
   int32_t nrows;
   int32_t nsplit;
   int32_t slot0;
-  int32_t pad[3];
+  int32_t q_len;
+  int32_t pad[2];
 };
 static_assert(sizeof(SplitGroup) == 32, "split group is 8 int32");
 
@@ -80,7 +82,25 @@ struct AttnArgs {
   const float* attn_sink;     // [H] sink logit per head (natural-log units), or null
   float* max_logits;          // [rows_total, H] largest logit per row (natural units), or null
   float* part_max;            // [slots][rows_per_block] largest logit of each partial row
+  // capacity plans: live key counts [requests] (null otherwise); the plan's
+  // items and groups carry the bounds, the kernels clip them to these
+  const int32_t* live_kv_len;
+  int32_t live_q;             // capacity prefill: live query counts from qo_indptr
+  int32_t lse_sq;             // > 0: lse laid out [requests, H, lse_sq]; 0: [rows, H]
 };
+
+// Device-array checks of a run call with validate = 1 (mla_lists.hip).
+struct ValidateArgs {
+  const int32_t* kv_indptr;       // the call's [batch + 1]
+  const int32_t* kv_indices;
+  const int32_t* qo_indptr;       // prefill; null for decode
+  const int32_t* live_kv_len;     // capacity plans; null otherwise
+  const int32_t* plan_kv_indptr;  // the plan's copies (in the workspace); null for capacity plans
+  const int32_t* plan_qo_indptr;
+  int32_t batch, page_size, num_pages, max_kv_len, max_q, causal;
+  int32_t* status;                // written: 0 or a set of kValidate* flags
+};
+constexpr int32_t kValidateIndptr = 1, kValidateIndices = 2, kValidateQo = 4, kValidateLengths = 8;
 
 // Launchers (mla_attn.hip).  They only enqueue on `stream`; return hipError_t.
 // t0 / t1: optional events recorded by the attention kernel's own dispatch
@@ -101,6 +121,7 @@ hipError_t launch_sparse_lists(const int32_t* indices, int32_t num_tokens, int32
                                const int32_t* topk_length, int64_t num_slots, int32_t* list, int32_t* count,
                                int32_t* indptr, hipStream_t stream);
 hipError_t launch_combine(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_validate(const ValidateArgs& v, hipStream_t stream);
 // MODEL1 records [n, 604] -> bf16 rows [n, 576]; query rows [n, 512] -> [n, 576].
 hipError_t launch_model1_records(const uint8_t* records, int64_t n, __bf16* rows, hipStream_t stream);
 hipError_t launch_model1_q(const __bf16* q, int64_t n, __bf16* q576, hipStream_t stream);

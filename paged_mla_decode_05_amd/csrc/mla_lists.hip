@@ -4,7 +4,10 @@
 //    end is invalid) are compacted per query token, in order, so that the
 //    attention kernel can walk them as page lists of page size 1;
 //  * dense block tables ("batch_mla_decode_with_paged_kv_cache" block_tables,
-//    FlashMLA block_table) are copied into the CSR page lists of the run calls.
+//    FlashMLA block_table) are copied into the CSR page lists of the run calls;
+//  * the opt-in checks of a run call's device index arrays (the validate flag
+//    of "batch_mla_decode_with_paged_kv_cache": pre-planned runs may skip
+//    them) before any attention kernel reads through them.
 #include <hip/hip_runtime.h>
 
 #include "mla_internal.h"
@@ -82,7 +85,66 @@ __global__ __launch_bounds__(256) void mla_block_table_kernel(const int32_t* __r
   for (int j = threadIdx.x; j < n; j += 256) kv_indices[p0 + j] = row[j];
 }
 
+// One workgroup checks a run call's index arrays against the plan: page
+// offsets (start at 0, never decrease, equal to the plan's, or, for capacity
+// plans, enough pages for the live key count), query offsets likewise, live
+// counts within the plan's bounds, and then, only if all of that holds (so
+// the ranges below are the ones the attention kernel would read), every page
+// id the run would read lies in [0, num_pages).  Writes the flags found.
+__global__ __launch_bounds__(1024) void mla_validate_kernel(ValidateArgs v) {
+  __shared__ int flags;
+  if (threadIdx.x == 0) flags = 0;
+  __syncthreads();
+  const bool cap = v.live_kv_len != nullptr;
+  int f = 0;
+  for (int b = threadIdx.x; b <= v.batch; b += blockDim.x) {
+    const int p = v.kv_indptr[b];
+    if ((b == 0 && p != 0) || (!cap && p != v.plan_kv_indptr[b])) f |= kValidateIndptr;
+    if (v.qo_indptr != nullptr) {
+      const int q = v.qo_indptr[b];
+      if ((b == 0 && q != 0) || (!cap && q != v.plan_qo_indptr[b])) f |= kValidateQo;
+    }
+    if (b == v.batch) continue;
+    const int pages = v.kv_indptr[b + 1] - p;
+    if (pages < 0) f |= kValidateIndptr;
+    int n = 1;
+    if (v.qo_indptr != nullptr) {
+      n = v.qo_indptr[b + 1] - v.qo_indptr[b];
+      if (n < 0 || (cap && n > v.max_q)) f |= kValidateQo;
+    }
+    if (cap) {
+      const int L = v.live_kv_len[b];
+      if (L < 0 || L > v.max_kv_len) {
+        f |= kValidateLengths;
+      } else {
+        if ((int64_t)pages * v.page_size < L) f |= kValidateIndptr;
+        if (v.causal && v.qo_indptr != nullptr && n > L) f |= kValidateLengths;
+      }
+    }
+  }
+  if (f) atomicOr(&flags, f);
+  __syncthreads();
+  if (flags == 0) {
+    for (int b = 0; b < v.batch; ++b) {
+      const int p0 = v.kv_indptr[b];
+      const int need = cap ? (v.live_kv_len[b] + v.page_size - 1) / v.page_size : v.kv_indptr[b + 1] - p0;
+      for (int j = threadIdx.x; j < need; j += blockDim.x) {
+        const int pg = v.kv_indices[p0 + j];
+        if (pg < 0 || pg >= v.num_pages) f |= kValidateIndices;
+      }
+    }
+    if (f) atomicOr(&flags, f);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) *v.status = flags;
+}
+
 }  // namespace
+
+hipError_t launch_validate(const ValidateArgs& v, hipStream_t stream) {
+  hipLaunchKernelGGL(mla_validate_kernel, dim3(1), dim3(1024), 0, stream, v);
+  return hipGetLastError();
+}
 
 hipError_t launch_sparse_lists(const int32_t* indices, int32_t num_tokens, int32_t topk, const int32_t* topk_length,
                                int64_t num_slots, int32_t* list, int32_t* count, int32_t* indptr,

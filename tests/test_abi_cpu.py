@@ -333,3 +333,35 @@ def test_model1_expand_argument_checks(mla):
     assert L.mla_model1_expand_q(None, 0, None, None) == ok
     assert L.mla_model1_expand_q(None, -3, None, None) == bad
     assert L.mla_model1_expand_q(16, 3, 8, None) == bad
+
+
+def test_boundary_option_errors(mla):
+    ip = [0, 2, 3]
+    kw = dict(kind=0, batch=2, num_heads=16, page_size=64, num_pages=8, kv_len=[100, 30], kv_indptr=ip, num_cus=4)
+    for bad in (dict(validate=2), dict(lse_layout=2), dict(max_kv_len=-1), dict(max_seq_len_q=3),
+                dict(max_kv_len=100, max_seq_len_q=2)):
+        with pytest.raises(mla.MLAError) as e:
+            mla.mla_plan_create(**kw, **bad)
+        assert e.value.status == -1, bad
+    with pytest.raises(mla.MLAError) as e:  # capacity plans are bf16 only
+        mla.mla_plan_create(**dict(kw, kv_len=None, kv_indptr=None), kv_format=1, max_kv_len=100)
+    assert e.value.status == -2
+    qo = [0, 2, 5]
+    with pytest.raises(mla.MLAError) as e:  # [batch, H, s_q] needs one query count for all requests
+        mla.mla_plan_create(1, 2, 16, 64, 8, [100, 30], ip, qo_indptr=qo, lse_layout=1, num_cus=4)
+    assert e.value.status == -1
+    with pytest.raises(mla.MLAError) as e:  # causal capacity: more queries than keys
+        mla.mla_plan_create(1, 2, 16, 64, 8, None, None, max_kv_len=4, max_seq_len_q=5, num_cus=4)
+    assert e.value.status == -1
+    mla.mla_plan_create(1, 2, 16, 64, 8, [100, 30], ip, qo_indptr=[0, 3, 6], lse_layout=1, num_cus=4)
+
+
+@pytest.mark.parametrize("kind,mode", [(0, 1), (0, 2), (1, 1), (1, 3)])
+def test_capacity_plan_covers_the_bound(mla, kind, mode):
+    # every request planned at max_kv_len keys (and max_seq_len_q queries),
+    # with no causal trimming: the kernels clip to the live counts
+    B, H, max_kv, max_q = 5, 32, 1000, (3 if kind == 1 else 1)
+    plan = mla.mla_plan_create(kind, B, H, 16, 500, None, None, tile_mode=mode, max_kv_len=max_kv,
+                               max_seq_len_q=max_q if kind == 1 else 0, num_cus=64)
+    _check_cover(plan, [max_kv] * B, [max_q] * B, H)
+    assert all(it["t1"] <= max_kv for it in _items(plan))
