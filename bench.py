@@ -346,35 +346,32 @@ def setup_dense(args, mla, dev):
 
 def setup_model1(args, mla, dev):
     """Decode over MODEL1 records (448 NoPE dims in 7 tiles of 64 + 64 RoPE
-    dims, 604 bytes per token): one step expands the record pool to bf16
-    576-wide rows, widens q, and runs the concatenated-layout decode.
+    dims, 604 bytes per token), dequantised in the attention kernel
+    (mla_decode_model1): one step is that call.
 
     Algorithmic units of the MODEL1 attention: 2*512 + 2*448 = 1920 flops per
     visible (row, key); bytes = live records (604 B per token) + q (1024 B per
-    row) + out (896 B per row, 448 bf16 dims) + lse + page indices.  The
-    roofline object covers the attention kernel; the expansion kernel's time
-    is in the kernel trace of the same command."""
+    row) + out (896 B per row, 448 bf16 dims) + lse + page indices."""
     import numpy as np
     import torch
 
     from workloads import make_model1_workload
 
     log(f"bench: generating {args.config} on {dev}")
-    w = make_model1_workload(name=args.config, device=dev)
+    w = make_model1_workload(name=args.config, device=dev, poison=False)
     L = w.kv_len.numpy().astype(np.int64)
     H = w.num_heads
     flops = int(L.sum()) * H * (2 * 512 + 2 * 448)
     live = int(L.sum()) * 604
     bytes_alg = live + w.batch * H * (1024 + 896 + 4) + int(w.kv_indptr[-1]) * 4
     t_plan = time.perf_counter()
-    plan = mla.mla_plan_create(mla.MLA_KIND_DECODE, w.batch, H, w.page_size, w.num_pages, w.kv_len, w.kv_indptr)
+    plan = mla.mla_plan_create(mla.MLA_KIND_DECODE, w.batch, H, w.page_size, w.num_pages, w.kv_len, w.kv_indptr,
+                               kv_format=mla.MLA_KV_FP8_MODEL1, tile_mode=args.tile_mode)
     plan_ms = (time.perf_counter() - t_plan) * 1e3
     kv_indptr = w.kv_indptr.to(dev)
     kv_indices = w.kv_indices.to(dev)
     reps = max(1, min(16, math.ceil(args.rotate_bytes / max(w.records.numel(), 1))))
     pools = [w.records] + [w.records.clone() for _ in range(reps - 1)]
-    rows = torch.empty((w.num_pages, w.page_size, 576), dtype=torch.bfloat16, device=dev)
-    q576 = torch.empty((w.batch, H, 576), dtype=torch.bfloat16, device=dev)
     out = torch.empty((w.batch, H, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((w.batch, H), dtype=torch.float32, device=dev)
     ws = plan.workspace(dev)
@@ -382,9 +379,8 @@ def setup_model1(args, mla, dev):
         f"{plan.num_split_groups} split groups, {reps} record pool replicas of {w.records.numel() / 1e6:.0f} MB")
 
     def step(i):
-        mla.mla_model1_expand_records(pools[i % reps], rows)
-        mla.mla_model1_expand_q(w.q, q576)
-        mla.mla_decode_packed(plan, q576, rows, kv_indptr, kv_indices, w.sm_scale, out=out, lse=lse, workspace=ws)
+        mla.mla_decode_model1(plan, w.q, pools[i % reps], kv_indptr, kv_indices, w.sm_scale, out=out, lse=lse,
+                              workspace=ws)
 
     def cpu(secs):
         import oracle
@@ -407,7 +403,7 @@ def setup_model1(args, mla, dev):
               "rows": w.batch, "parallelism": "single GPU"}
     return {"step": step, "flops": flops, "live_kv": live, "bytes_alg": bytes_alg, "plan_ms": plan_ms,
             "config": config, "kernel": "mla_attn_kernel",
-            "dtype": "MODEL1 e4m3 records expanded to bf16 rows, bf16 math", "cpu_baseline": cpu}
+            "dtype": "MODEL1 e4m3 records read in the kernel, bf16 math", "cpu_baseline": cpu}
 
 
 def setup_sparse(args, mla, dev):

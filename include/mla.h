@@ -61,8 +61,21 @@ typedef enum mla_dtype { MLA_DTYPE_BF16 = 0, MLA_DTYPE_FP32 = 1 } mla_dtype;
  *     and Dequantization", V32_FP8Sparse): bytes 0..511 = 512 OCP e4m3
  *     codes of the latent dims, bytes 512..527 = four little-endian fp32
  *     scales (scale t applies to dims 128t..128t+127), bytes 528..655 = the
- *     64 rope dims as bf16.  Key value = code * scale; rope as stored.   */
-typedef enum mla_kv_format { MLA_KV_BF16 = 0, MLA_KV_FP8_E4M3_T128 = 1 } mla_kv_format;
+ *     64 rope dims as bf16.  Key value = code * scale; rope as stored.
+ *   MLA_KV_FP8_MODEL1: one cache [num_pages, page_size, 604] uint8, one
+ *     604-byte MODEL1 record per token (same page, MODEL1_FP8Sparse: d = 512
+ *     for q.k, 448 NoPE dims in 7 tiles of 64, 64 RoPE dims; the page gives
+ *     sizes only, the byte order read here is the printed one, packed):
+ *     bytes 0..447 = e4m3 codes (tile t = dims 64t..64t+63), bytes 448..475
+ *     = seven little-endian fp32 scales, bytes 476..603 = the 64 RoPE dims
+ *     as bf16.  Key value = code * scale, exactly as for the 656-byte
+ *     records; V = the 448 NoPE dims.  Decode only (mla_decode_model1,
+ *     mla_sparse_decode_model1); no quad tile.                            */
+typedef enum mla_kv_format {
+  MLA_KV_BF16 = 0,
+  MLA_KV_FP8_E4M3_T128 = 1,
+  MLA_KV_FP8_MODEL1 = 2
+} mla_kv_format;
 
 /* MLA_KIND_SPARSE_DECODE: plans made by mla_sparse_plan_create only. */
 typedef enum mla_kind { MLA_KIND_DECODE = 0, MLA_KIND_PREFILL = 1, MLA_KIND_SPARSE_DECODE = 2 } mla_kind;
@@ -322,13 +335,36 @@ mla_status mla_prefill_packed(const mla_plan* plan, const void* q, const void* k
 mla_status mla_block_table_to_indices(const mla_plan* plan, const int32_t* block_table, int32_t max_blocks,
                                       const int32_t* kv_indptr, int32_t* kv_indices, hipStream_t stream);
 
-/* MODEL1 records (FlashMLA digest, "FP8 KV Cache Quantization and
- * Dequantization": MODEL1_FP8Sparse, d = 512 for q.k, 448 NoPE dims in 7
- * tiles of 64 e4m3 codes with one fp32 scale each, 64 bf16 RoPE dims).  The
- * page gives sizes only; the byte order read here follows its printed
- * 656-byte layout: [448 codes][7 x fp32 scale][64 x bf16 RoPE], 604 bytes
- * per token, tile t = NoPE dims [64t, 64t+64).  The page dequantises to
- * BF16: value = bf16(fp32(code) * scale), both steps round to nearest even.
+/* Decode over MODEL1 records (MLA_KV_FP8_MODEL1 above), dequantised in the
+ * kernel as the 656-byte records are: codes converted exactly, each 64-dim
+ * tile's partial dot product scaled by the key's fp32 tile scale, P scaled
+ * per key by the output tile's scale before P.V.
+ *   q [batch, H, 512] bf16: 448 NoPE dims, then 64 RoPE dims
+ *   kv_cache [num_pages, page_size, 604] uint8
+ *   out [batch, H, 512] of out_dtype: dims 0..447 the attention output
+ *     (V = the 448 NoPE dims), dims 448..511 written as 0; lse [batch, H].
+ * Plan: a decode plan with kv_format MLA_KV_FP8_MODEL1.  Everything else,
+ * errors included, as for mla_decode_fp8.
+ *
+ * mla_sparse_decode_model1: token-sparse decode over MODEL1 records, as
+ * mla_sparse_decode_fp8 with q [num_tokens, H, 512] (448 NoPE + 64 RoPE),
+ * kv_cache [num_slots, 604] records and out [num_tokens, H, 512] (dims
+ * 448..511 written as 0); plan: mla_sparse_plan_create with
+ * MLA_KV_FP8_MODEL1.                                                      */
+mla_status mla_decode_model1(const mla_plan* plan, const void* q, const void* kv_cache, const int32_t* kv_indptr,
+                             const int32_t* kv_indices, float sm_scale, void* out, int32_t out_dtype, float* lse,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+mla_status mla_sparse_decode_model1(const mla_plan* plan, const void* q, const void* kv_cache,
+                                    const int32_t* indices, const int32_t* topk_length, const float* attn_sink,
+                                    float sm_scale, void* out, int32_t out_dtype, float* lse, float* max_logits,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The page's BF16 dequantisation of MODEL1 records ("FP8 KV Cache
+ * Quantization Utilities", dequantize_k_cache returns the BF16 cache), as a
+ * layout utility: value = bf16(fp32(code) * scale), both steps round to
+ * nearest even.  These rows are not what mla_decode_model1 attends over
+ * (it uses the exact products); attention over them is attention over the
+ * BF16-rounded keys.
  *
  * mla_model1_expand_records: records [num_tokens, 604] (u8, device, 4-byte
  * aligned) -> rows [num_tokens, 576] (bf16, device, 16-byte aligned) in the

@@ -54,6 +54,8 @@ from .mla_oracle import (  # noqa: F401
     M1_RECORD_BYTES,
     f32_to_bf16_rne,
     model1_record_decode,
+    model1_dequantize_bf16,
     model1_record_encode,
     mla_decode_model1_ref,
+    mla_sparse_decode_model1_ref,
 )

@@ -242,8 +242,9 @@ def f32_to_bf16_rne(x) -> np.ndarray:
     return u.astype(np.uint32).view(np.float32).astype(np.float64)
 
 
-def model1_record_decode(records) -> tuple[np.ndarray, np.ndarray]:
-    """604-byte MODEL1 token records -> (NoPE [..., 448], RoPE [..., 64]) float64.
+def _model1_fields(records):
+    """604-byte MODEL1 records -> (codes [n, 448] uint8, scales [n, 7] fp32,
+    RoPE float64 [n, 64], leading shape).
 
     "FP8 KV Cache Quantization and Dequantization" names the MODEL1_FP8Sparse
     layout by its sizes only (d = 512, d_nope = 448, d_rope = 64, tile 64,
@@ -251,9 +252,6 @@ def model1_record_decode(records) -> tuple[np.ndarray, np.ndarray]:
     the same order as the printed one, packed: bytes 0..447 are the e4m3
     codes (tile t = dims [64t, 64t+64)), bytes 448..475 seven little-endian
     fp32 scales, bytes 476..603 the 64 RoPE values as little-endian bf16.
-    The page's dequantize_k_cache returns BF16, so a NoPE value is
-    bf16(fp32(code) * scale): the product in fp32, then rounded to bf16
-    (both round to nearest even).
     """
     r = _as_u8(records)
     assert r.shape[-1] == M1_RECORD_BYTES
@@ -262,10 +260,36 @@ def model1_record_decode(records) -> tuple[np.ndarray, np.ndarray]:
     codes = flat[:, :M1_NOPE]
     scales = np.ascontiguousarray(flat[:, M1_NOPE:M1_NOPE + 4 * M1_NUM_TILES]).view("<f4")
     rope_bits = np.ascontiguousarray(flat[:, M1_NOPE + 4 * M1_NUM_TILES:]).view("<u2")
+    return codes, scales, bf16_bits_to_f64(rope_bits), lead
+
+
+def model1_record_decode(records) -> tuple[np.ndarray, np.ndarray]:
+    """604-byte MODEL1 token records -> (NoPE [..., 448], RoPE [..., 64]) float64.
+
+    The key the attention uses, read as for the 656-byte records: NoPE value
+    = code value * its tile's fp32 scale, exactly (an e4m3 value has 4
+    significant bits and the scale 24, so the float64 product is exact).
+    One reading serves both record formats; the page's dequantize_k_cache,
+    which rounds these values to BF16, is :func:`model1_dequantize_bf16`.
+    """
+    codes, scales, rope, lead = _model1_fields(records)
+    vals = e4m3_decode(codes).reshape(-1, M1_NUM_TILES, M1_TILE)
+    nope = (vals * scales.astype(np.float64)[:, :, None]).reshape(-1, M1_NOPE)
+    return nope.reshape(*lead, M1_NOPE), rope.reshape(*lead, HEAD_DIM_KPE)
+
+
+def model1_dequantize_bf16(records) -> tuple[np.ndarray, np.ndarray]:
+    """The page's dequantize_k_cache for MODEL1 records ("FP8 KV Cache
+    Quantization Utilities": it returns the BF16 dequantised cache): NoPE
+    value = bf16(fp32(code) * scale), the product rounded to fp32, then to
+    bf16, both to nearest even.  (NoPE [..., 448], RoPE [..., 64]) as the
+    float64 values of those bf16 numbers.  Not the attention's keys: those
+    are the exact products of :func:`model1_record_decode`.
+    """
+    codes, scales, rope, lead = _model1_fields(records)
     vals = e4m3_decode(codes).astype(np.float32).reshape(-1, M1_NUM_TILES, M1_TILE)
     prod = (vals * scales[:, :, None]).astype(np.float32)  # fp32 multiply
     nope = f32_to_bf16_rne(prod).reshape(-1, M1_NOPE)
-    rope = bf16_bits_to_f64(rope_bits)
     return nope.reshape(*lead, M1_NOPE), rope.reshape(*lead, HEAD_DIM_KPE)
 
 
@@ -302,7 +326,8 @@ def mla_decode_model1_ref(q, kv_records, kv_indptr, kv_indices, kv_len, sm_scale
     Definition as for the 656-byte records ("MLA Paged" decode; slot
     mapping and sizes from the FlashMLA FP8 section), with d = 512 for
     q . k and, reading, V = the 448 NoPE dims (as V = the 512 NoPE dims
-    of the 656-byte layout).
+    of the 656-byte layout).  Keys are the exact products code * scale of
+    :func:`model1_record_decode`.
     """
     qf = as_f64(q)
     B, H, D = qf.shape
@@ -625,7 +650,7 @@ def sparse_attend(qn, qp, kn, kp, sm_scale: float, attn_sink=None):
     qp = np.asarray(qp, dtype=np.float64)
     H = qn.shape[0]
     if kn.shape[0] == 0:
-        return np.zeros((H, HEAD_DIM_CKV)), np.full(H, -np.inf), np.full(H, -np.inf)
+        return np.zeros((H, kn.shape[1])), np.full(H, -np.inf), np.full(H, -np.inf)
     s = sm_scale * (qn @ kn.T + qp @ kp.T)  # [H, n]
     mx = s.max(axis=1)
     lse = mx + np.log(np.exp(s - mx[:, None]).sum(axis=1))
@@ -637,25 +662,24 @@ def sparse_attend(qn, qp, kn, kp, sm_scale: float, attn_sink=None):
     return out, lse, mx
 
 
-def _sparse_run(q, indices, num_slots, gather, sm_scale, topk_length, attn_sink, tokens):
+def _sparse_run(q, indices, num_slots, gather, sm_scale, topk_length, attn_sink, tokens, nope=HEAD_DIM_CKV):
     qq = as_f64(q)
-    if qq.shape[-1] != HEAD_DIM_CKV + HEAD_DIM_KPE:
-        raise ValueError("q must hold 576 dims per head (latent, then rope)")
+    if qq.shape[-1] != nope + HEAD_DIM_KPE:
+        raise ValueError(f"q must hold {nope + HEAD_DIM_KPE} dims per head (latent, then rope)")
     H = qq.shape[-2]
-    qq = qq.reshape(-1, H, HEAD_DIM_CKV + HEAD_DIM_KPE)
+    qq = qq.reshape(-1, H, nope + HEAD_DIM_KPE)
     T = qq.shape[0]
     idx = _as_int(indices)
     idx = idx.reshape(T, -1)
     lens = None if topk_length is None else _as_int(topk_length).reshape(T)
     sink = None if attn_sink is None else as_f64(attn_sink).reshape(H)
-    out = np.full((T, H, HEAD_DIM_CKV), np.nan)
+    out = np.full((T, H, nope), np.nan)
     lse = np.full((T, H), np.nan)
     mx = np.full((T, H), np.nan)
     for t in (range(T) if tokens is None else tokens):
         sel = sparse_valid_indices(idx[t], num_slots, None if lens is None else lens[t])
         kn, kp = gather(sel)
-        out[t], lse[t], mx[t] = sparse_attend(qq[t, :, :HEAD_DIM_CKV], qq[t, :, HEAD_DIM_CKV:], kn, kp,
-                                              sm_scale, sink)
+        out[t], lse[t], mx[t] = sparse_attend(qq[t, :, :nope], qq[t, :, nope:], kn, kp, sm_scale, sink)
     return out, lse, mx
 
 
@@ -715,3 +739,22 @@ def mla_sparse_prefill_ref(q, kv, indices, sm_scale: float, topk_length=None, at
         return rows[:, :HEAD_DIM_CKV], rows[:, HEAD_DIM_CKV:]
 
     return _sparse_run(q, indices, num_slots, gather, sm_scale, topk_length, attn_sink, tokens)
+
+
+def mla_sparse_decode_model1_ref(q, kv_records, indices, sm_scale: float, topk_length=None, attn_sink=None,
+                                 tokens=None):
+    """Token-sparse decode over MODEL1 records ("FP8 KV Cache Quantization and
+    Dequantization", MODEL1_FP8Sparse; the sparse decoding passages as for
+    :func:`mla_sparse_decode_fp8_ref`): q [..., H, 512] (448 NoPE + 64 RoPE
+    dims), kv_records [num_blocks, block_size, (1,) 604], indices [..., topk]
+    flat slots.  Keys are the exact products of :func:`model1_record_decode`,
+    V = the 448 NoPE dims.  Returns out [T, H, 448], lse [T, H],
+    max_logits [T, H] in float64.
+    """
+    num_slots = int(np.prod(kv_records.shape[:-1]))
+    if kv_records.shape[-1] != M1_RECORD_BYTES:
+        raise ValueError("MODEL1 records must be 604 bytes")
+    kv_records = _host(kv_records)
+    return _sparse_run(q, indices, num_slots,
+                       lambda sel: model1_record_decode(_flat_rows(kv_records, M1_RECORD_BYTES, sel)),
+                       sm_scale, topk_length, attn_sink, tokens, nope=M1_NOPE)

@@ -26,6 +26,7 @@ from ._binding import (  # noqa: F401
     mla_decode_fp8,
     mla_decode_fp8_q8,
     mla_decode_live,
+    mla_decode_model1,
     mla_decode_noalloc,
     mla_decode_packed,
     mla_model1_expand_q,
@@ -36,6 +37,7 @@ from ._binding import (  # noqa: F401
     mla_prefill_packed,
     mla_record_attention_events,
     mla_sparse_decode_fp8,
+    mla_sparse_decode_model1,
     mla_sparse_plan_create,
     mla_sparse_prefill,
     MLA_KIND_DECODE,
@@ -43,6 +45,7 @@ from ._binding import (  # noqa: F401
     MLA_KIND_SPARSE_DECODE,
     MLA_KV_BF16,
     MLA_KV_FP8_E4M3_T128,
+    MLA_KV_FP8_MODEL1,
     MLA_LSE_ROWS,
     MLA_LSE_HEADS_FIRST,
     MLA_ERR_INVALID_ARGUMENT,

@@ -17,6 +17,7 @@ MLA_KIND_PREFILL = 1
 MLA_KIND_SPARSE_DECODE = 2
 MLA_KV_BF16 = 0
 MLA_KV_FP8_E4M3_T128 = 1
+MLA_KV_FP8_MODEL1 = 2
 MLA_DTYPE_BF16 = 0
 MLA_DTYPE_FP32 = 1
 MLA_TILE_AUTO = 0
@@ -110,6 +111,10 @@ def load_library():
         L.mla_sparse_decode_fp8.argtypes = [vp, vp, vp, vp, vp, vp, f32, vp, i32, vp, vp, vp, sz, vp]
         L.mla_sparse_decode_fp8.restype = i32
         L.mla_sparse_prefill.argtypes = [vp, vp, vp, vp, vp, vp, f32, vp, i32, vp, vp, vp, sz, vp]
+        L.mla_decode_model1.argtypes = [vp, vp, vp, vp, vp, f32, vp, i32, vp, vp, sz, vp]
+        L.mla_decode_model1.restype = i32
+        L.mla_sparse_decode_model1.argtypes = [vp, vp, vp, vp, vp, vp, f32, vp, i32, vp, vp, vp, sz, vp]
+        L.mla_sparse_decode_model1.restype = i32
         L.mla_sparse_prefill.restype = i32
         L.mla_model1_expand_records.argtypes = [vp, ctypes.c_int64, vp, vp]
         L.mla_model1_expand_records.restype = i32
@@ -290,9 +295,9 @@ def mla_sparse_decode_fp8(plan: Plan, q, kv_cache, indices, sm_scale: float, top
     return out, lse, max_logits
 
 
-def _sparse_extras(plan, q, indices, topk_length, attn_sink, out, lse, max_logits, out_dtype):
+def _sparse_extras(plan, q, indices, topk_length, attn_sink, out, lse, max_logits, out_dtype, q_dims=_DIM_CKV + _DIM_KPE):
     T, H, topk = plan.desc.batch, plan.desc.num_qo_heads, plan.topk
-    qq = _dev(q, "q", torch.bfloat16, (T, H, _DIM_CKV + _DIM_KPE))
+    qq = _dev(q, "q", torch.bfloat16, (T, H, q_dims))
     ix = _dev(indices, "indices", torch.int32, (T, topk))
     tl = _dev(topk_length, "topk_length", torch.int32, (T,)) if topk_length is not None else None
     sk = _dev(attn_sink, "attn_sink", torch.float32, (H,)) if attn_sink is not None else None
@@ -622,3 +627,50 @@ def mla_model1_expand_q(q, q576=None):
     stream = torch.cuda.current_stream(q.device).cuda_stream
     _check(L.mla_model1_expand_q(q.data_ptr(), n, q576.data_ptr(), stream), "mla_model1_expand_q")
     return q576
+
+
+def mla_decode_model1(plan: Plan, q, kv_cache, kv_indptr, kv_indices, sm_scale: float, out=None, lse=None,
+                      out_dtype=torch.bfloat16, workspace=None):
+    """Paged decode over MODEL1 records, dequantised in the kernel: q [B, H, 512]
+    bf16 (448 NoPE + 64 RoPE), kv_cache [num_pages, page_size, 604] uint8.
+    Returns (out [B, H, 512] with dims 448..511 zero, lse [B, H])."""
+    L = load_library()
+    if plan.desc.kv_format != MLA_KV_FP8_MODEL1:
+        raise ValueError("mla_decode_model1 needs a plan made with kv_format=MLA_KV_FP8_MODEL1")
+    B, P, ps = plan.desc.batch, plan.desc.num_pages, plan.desc.page_size
+    qq = _dev(q, "q", torch.bfloat16, (B, plan.num_heads, MODEL1_NOPE + _DIM_KPE))
+    kv = _dev(kv_cache, "kv_cache", torch.uint8, (P, ps, MODEL1_RECORD))
+    ip, ix = _paging(plan, kv_indptr, kv_indices)
+    if out is None:
+        out = torch.empty((B, plan.num_heads, _DIM_CKV), dtype=out_dtype, device=q.device)
+    out, lse, code = _outputs(out, out, lse, out.dtype, plan)
+    ws = plan.workspace(q.device) if workspace is None else workspace
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(L.mla_decode_model1(plan.handle, qq, kv, ip, ix, float(sm_scale), out.data_ptr(), code, lse.data_ptr(),
+                               ws.data_ptr(), ws.numel(), stream), "mla_decode_model1")
+    return out, lse
+
+
+def mla_sparse_decode_model1(plan: Plan, q, kv_cache, indices, sm_scale: float, topk_length=None, attn_sink=None,
+                             out=None, lse=None, max_logits=None, out_dtype=torch.bfloat16, workspace=None):
+    """Token-sparse decode over MODEL1 records: q [T, H, 512] bf16, kv_cache
+    [..., 604] uint8 (num_slots records), indices [T, topk] int32 flat slots.
+    Returns (out [T, H, 512] with dims 448..511 zero, lse [T, H], max_logits [T, H])."""
+    L = load_library()
+    if plan.desc.kv_format != MLA_KV_FP8_MODEL1:
+        raise ValueError("mla_sparse_decode_model1 needs a plan made with kv_format=MLA_KV_FP8_MODEL1")
+    if not isinstance(kv_cache, torch.Tensor) or kv_cache.shape[-1] != MODEL1_RECORD or \
+            kv_cache.numel() // MODEL1_RECORD != plan.desc.num_pages:
+        raise ValueError(f"kv_cache must hold {plan.desc.num_pages} records of {MODEL1_RECORD} bytes")
+    kv = _dev(kv_cache, "kv_cache", torch.uint8)
+    if out is None:
+        out = torch.empty((plan.desc.batch, plan.num_heads, _DIM_CKV), dtype=out_dtype, device=q.device)
+    qq, ix, tl, sk, out, lse, code, max_logits, mx = _sparse_extras(plan, q, indices, topk_length, attn_sink, out,
+                                                                     lse, max_logits, out_dtype,
+                                                                     q_dims=MODEL1_NOPE + _DIM_KPE)
+    ws = plan.workspace(q.device) if workspace is None else workspace
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(L.mla_sparse_decode_model1(plan.handle, qq, kv, ix, tl, sk, float(sm_scale), out.data_ptr(), code,
+                                      lse.data_ptr(), mx, ws.data_ptr(), ws.numel(), stream),
+           "mla_sparse_decode_model1")
+    return out, lse, max_logits

@@ -320,10 +320,11 @@ mla_status mla_plan_create(mla_plan** out, const mla_plan_desc* d, const int32_t
   if (d->batch < 0 || d->num_qo_heads < 1 || d->num_pages < 1) return MLA_ERR_INVALID_ARGUMENT;
   if (d->head_dim_ckv != mla::kDimCkv || d->head_dim_kpe != mla::kDimKpe) return MLA_ERR_UNSUPPORTED;
   if (!is_pow2(d->page_size) || d->page_size > 4096) return MLA_ERR_UNSUPPORTED;
-  if (d->kv_format != MLA_KV_BF16 && d->kv_format != MLA_KV_FP8_E4M3_T128) return MLA_ERR_UNSUPPORTED;
-  if (d->kv_format == MLA_KV_FP8_E4M3_T128 && d->kind != MLA_KIND_DECODE) return MLA_ERR_UNSUPPORTED;
+  if (d->kv_format != MLA_KV_BF16 && d->kv_format != MLA_KV_FP8_E4M3_T128 && d->kv_format != MLA_KV_FP8_MODEL1)
+    return MLA_ERR_UNSUPPORTED;
+  if (d->kv_format != MLA_KV_BF16 && d->kind != MLA_KIND_DECODE) return MLA_ERR_UNSUPPORTED;
   if (d->tile_mode < MLA_TILE_AUTO || d->tile_mode > MLA_TILE_QUAD) return MLA_ERR_INVALID_ARGUMENT;
-  if (d->kv_format == MLA_KV_FP8_E4M3_T128 && d->tile_mode == MLA_TILE_QUAD) return MLA_ERR_UNSUPPORTED;
+  if (d->kv_format != MLA_KV_BF16 && d->tile_mode == MLA_TILE_QUAD) return MLA_ERR_UNSUPPORTED;
   if (d->max_splits < 0 || d->force_splits < 0 || d->num_cus < 0) return MLA_ERR_INVALID_ARGUMENT;
   if (d->validate != 0 && d->validate != 1) return MLA_ERR_INVALID_ARGUMENT;
   if (d->lse_layout != MLA_LSE_ROWS && d->lse_layout != MLA_LSE_HEADS_FIRST) return MLA_ERR_INVALID_ARGUMENT;
@@ -383,7 +384,8 @@ mla_status mla_sparse_plan_create(mla_plan** out, int32_t num_tokens, int32_t nu
   *out = nullptr;
   if (num_tokens < 0 || num_heads < 1 || num_slots < 1 || topk < 1 || num_cus < 0 || force_splits < 0)
     return MLA_ERR_INVALID_ARGUMENT;
-  if (kv_format != MLA_KV_BF16 && kv_format != MLA_KV_FP8_E4M3_T128) return MLA_ERR_UNSUPPORTED;
+  if (kv_format != MLA_KV_BF16 && kv_format != MLA_KV_FP8_E4M3_T128 && kv_format != MLA_KV_FP8_MODEL1)
+    return MLA_ERR_UNSUPPORTED;
   if ((int64_t)num_tokens * topk > ((int64_t)1 << 31) - 1) return MLA_ERR_INVALID_ARGUMENT;
   if (num_cus == 0) {
     int dev = 0;
@@ -466,6 +468,9 @@ struct Layout {
 constexpr Layout kSplit{mla::kDimCkv * 2, mla::kDimKpe * 2, mla::kDimCkv, mla::kDimKpe};
 constexpr Layout kPacked{(mla::kDimCkv + mla::kDimKpe) * 2, (mla::kDimCkv + mla::kDimKpe) * 2,
                          mla::kDimCkv + mla::kDimKpe, mla::kDimCkv + mla::kDimKpe};
+// MODEL1 queries: one 512-wide row per (token, head), 448 NoPE dims then 64 RoPE dims.
+constexpr int kM1Nope = 448;
+constexpr Layout kModel1Q{0, 0, kM1Nope + mla::kDimKpe, kM1Nope + mla::kDimKpe};
 
 // Inputs of the token-sparse decode beyond the dense ones.
 struct Sparse {
@@ -518,7 +523,7 @@ mla_status run(const mla_plan* p, int32_t want_kind, int32_t want_format, const 
   if (!q_nope || !q_pe || !out || !lse) return MLA_ERR_INVALID_ARGUMENT;
   if (sparse ? !sparse->indices : (!kv_indptr || !kv_indices)) return MLA_ERR_INVALID_ARGUMENT;
   if (want_format == MLA_KV_BF16 && (!ckv || !kpe)) return MLA_ERR_INVALID_ARGUMENT;
-  if (want_format == MLA_KV_FP8_E4M3_T128 && !kv_fp8) return MLA_ERR_INVALID_ARGUMENT;
+  if (want_format != MLA_KV_BF16 && !kv_fp8) return MLA_ERR_INVALID_ARGUMENT;
   if (want_kind == MLA_KIND_PREFILL && !qo_indptr) return MLA_ERR_INVALID_ARGUMENT;
   if (!ws || ws_bytes < p->ws_bytes || ((uintptr_t)ws % mla::kWsAlign) != 0) return MLA_ERR_WORKSPACE;
   if (q8 && p->tile_mode != MLA_TILE_WIDE) return MLA_ERR_UNSUPPORTED;
@@ -585,10 +590,9 @@ mla_status run(const mla_plan* p, int32_t want_kind, int32_t want_format, const 
   }
   hipEvent_t ev0 = t_ev_before, ev1 = t_ev_after;
   t_ev_before = t_ev_after = nullptr;
-  hipError_t e = sparse ? mla::launch_sparse_attention(a, stream, ev0, ev1)
+  hipError_t e = sparse ? mla::launch_sparse_attention(a, stream, ev0, ev1, want_format == MLA_KV_FP8_MODEL1)
                  : q8     ? mla::launch_attention_q8(a, stream, ev0, ev1)
-                          : mla::launch_attention(a, p->tile_mode, want_format == MLA_KV_FP8_E4M3_T128, stream, ev0,
-                                                  ev1);
+                          : mla::launch_attention(a, p->tile_mode, want_format, stream, ev0, ev1);
   if (e != hipSuccess) return MLA_ERR_DEVICE;
   if (!p->groups.empty()) {
     e = mla::launch_combine(a, stream);
@@ -691,6 +695,29 @@ mla_status mla_sparse_decode_fp8(const mla_plan* p, const void* q, const void* k
   const char* qb = (const char*)q;
   return run(p, MLA_KIND_SPARSE_DECODE, MLA_KV_FP8_E4M3_T128, q, q ? qb + mla::kDimCkv * 2 : nullptr, nullptr, nullptr,
              kv_cache, nullptr, nullptr, nullptr, sm_scale, out, out_dtype, lse, ws, ws_bytes, stream, kPacked, 1.f,
+             &sp);
+}
+
+mla_status mla_decode_model1(const mla_plan* p, const void* q, const void* kv_cache, const int32_t* kv_indptr,
+                             const int32_t* kv_indices, float sm_scale, void* out, int32_t out_dtype, float* lse,
+                             void* ws, size_t ws_bytes, hipStream_t stream) {
+  const char* qb = (const char*)q;
+  return run(p, MLA_KIND_DECODE, MLA_KV_FP8_MODEL1, q, q ? qb + kM1Nope * 2 : nullptr, nullptr, nullptr, kv_cache,
+             nullptr, kv_indptr, kv_indices, sm_scale, out, out_dtype, lse, ws, ws_bytes, stream, kModel1Q);
+}
+
+mla_status mla_sparse_decode_model1(const mla_plan* p, const void* q, const void* kv_cache, const int32_t* indices,
+                                    const int32_t* topk_length, const float* attn_sink, float sm_scale, void* out,
+                                    int32_t out_dtype, float* lse, float* max_logits, void* ws, size_t ws_bytes,
+                                    hipStream_t stream) {
+  Sparse sp;
+  sp.indices = indices;
+  sp.topk_length = topk_length;
+  sp.attn_sink = attn_sink;
+  sp.max_logits = max_logits;
+  const char* qb = (const char*)q;
+  return run(p, MLA_KIND_SPARSE_DECODE, MLA_KV_FP8_MODEL1, q, q ? qb + kM1Nope * 2 : nullptr, nullptr, nullptr,
+             kv_cache, nullptr, nullptr, nullptr, sm_scale, out, out_dtype, lse, ws, ws_bytes, stream, kModel1Q, 1.f,
              &sp);
 }
 

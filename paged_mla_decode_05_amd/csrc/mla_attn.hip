@@ -43,6 +43,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "mla_internal.h"
 
 namespace mla {
@@ -388,24 +390,68 @@ __device__ __forceinline__ void issue_stage_bf16(const AttnArgs& a, LDS_AS char*
 }
 
 // ---------------------------------------------------------------------------
-// fp8 record caches (FlashMLA, "Quantization and Dequantization": per token
-// 512 e4m3 codes, four fp32 scales of 128 dims each, the 64 rope dims as
-// bf16; 656 bytes).  A stage's records move raw into LDS with 16-byte direct
-// loads; the workgroup then dequantises them into the bf16 stage layout the
-// attention bodies read, so the compute path is the one of the bf16 cache.
-// Wave w moves the 16 records of keys [16w, 16w+16): 16 x 41 chunks of 16
-// bytes, lane l of issue i taking chunk 64i + l, so the raw stage is the 64
-// records back to back.  Keys past tok_end re-read the chunk's last key.
+// fp8 record caches (FlashMLA, "FP8 KV Cache Quantization and
+// Dequantization"): per token, e4m3 codes of the NoPE dims, one fp32 scale
+// per tile of them, and the 64 RoPE dims as bf16.  Two record formats:
+//  * FmtV32 (V32_FP8Sparse, 656 bytes): 512 codes, 4 scales of 128-dim
+//    tiles, RoPE at byte 528; moved to LDS as it is (41 chunks of 16 bytes).
+//  * FmtM1 (MODEL1_FP8Sparse, 604 bytes, packed in the printed order):
+//    448 codes, 7 scales of 64-dim tiles at byte 448, RoPE at byte 476.  Its
+//    records are 4-byte aligned only, so each one moves as 39 chunks picked
+//    per lane that re-lay it in LDS with every field 16-byte aligned:
+//    codes at 0..447, RoPE at 448..575, scales 0..3 at 576..591 and 3..6 at
+//    592..607 (two overlapping 16-byte reads of the 28 scale bytes), and one
+//    pad chunk.  The 624-byte stride (156 dwords, 4 x odd) puts the 16 keys
+//    of a K read on distinct LDS banks, as the 164-dword V32 stride does.
+// A stage's 64 records sit back to back in LDS at the format's stride.
+// Wave w moves the records of keys [16w, 16w+16): lane l of issue i takes
+// chunk 64i + l of them.  Keys past tok_end re-read the chunk's last key.
 // ---------------------------------------------------------------------------
-constexpr int kRecChunks = kFp8RecordBytes / 16;                 // 41
-constexpr int kFp8RawBytes = kStageTokens * kFp8RecordBytes;     // 41984
-constexpr int kFp8DmaPerWave = (16 * kRecChunks + 63) / 64;      // 11
-constexpr int kFp8RawOff = kStageBytes;                          // [bf16 stage][raw 0][raw 1][scales]
-constexpr int kFp8ScaleOff = kStageBytes + 2 * kFp8RawBytes;     // float [4 tiles][64 keys]
-constexpr int kFp8LdsBytes = kFp8ScaleOff + 4 * kStageTokens * 4;  // 158720
-static_assert(kFp8LdsBytes <= 160 * 1024, "fp8 LDS budget");
+struct FmtV32 {
+  static constexpr bool kM1 = false;
+  static constexpr int kRecBytes = kFp8RecordBytes;  // 656 in HBM
+  static constexpr int kStride = 656;                // in LDS
+  static constexpr int kChunks = 41;
+  static constexpr int kNope = 512, kTileDims = 128, kTiles = 4;
+  static constexpr int kRopeOff = 528;
+  static constexpr bool kPairedDims = true;          // P.V output tiles pair dims D and D + 64
+  __device__ static int goff(int c) { return 16 * c; }
+  __device__ static int div_chunks(int c) { return (int)(__umul24((uint32_t)c, 200u) >> 13); }  // c / 41, c < 704
+  __device__ static int scale_off(int t) { return 512 + 4 * t; }
+};
+struct FmtM1 {
+  static constexpr bool kM1 = true;
+  static constexpr int kRecBytes = 604;
+  static constexpr int kStride = 624;
+  static constexpr int kChunks = 39;
+  static constexpr int kNope = 448, kTileDims = 64, kTiles = 7;
+  static constexpr int kRopeOff = 448;
+  static constexpr bool kPairedDims = false;
+  __device__ static int goff(int c) {
+    return c < 28 ? 16 * c : (c < 36 ? 476 + 16 * (c - 28) : (c == 36 ? 448 : (c == 37 ? 460 : 0)));
+  }
+  __device__ static int div_chunks(int c) { return (int)(__umul24((uint32_t)c, 1681u) >> 16); }  // c / 39, c < 640
+  __device__ static int scale_off(int t) { return t < 4 ? 576 + 4 * t : 580 + 4 * t; }
+  static constexpr int kScaleHiOff = 592;            // the 16-byte chunk holding scales 3 .. 6
+};
 
-template <int kPageClass>
+template <class Fmt>
+struct RecLayout {
+  static constexpr int kRawBytes = kStageTokens * Fmt::kStride;               // one stage in LDS
+  static constexpr int kDmaPerWave = (16 * Fmt::kChunks + 63) / 64;          // 11 (V32), 10 (M1)
+  static constexpr int kTail = 16 * Fmt::kChunks - 64 * (kDmaPerWave - 1);   // lanes of the last slice
+  static constexpr int kRawOff = kStageBytes;                                 // [bf16 stage][raw 0][raw 1][scales]
+  static constexpr int kScaleOff = kStageBytes + 2 * kRawBytes;               // float [tiles][64 keys]
+  static constexpr int kNarrowLds = kScaleOff + Fmt::kTiles * kStageTokens * 4;
+};
+constexpr int kFp8RawBytes = RecLayout<FmtV32>::kRawBytes;                    // 41984
+constexpr int kFp8DmaPerWave = RecLayout<FmtV32>::kDmaPerWave;                // 11
+constexpr int kFp8LdsBytes = RecLayout<FmtV32>::kNarrowLds;                   // 158720
+static_assert(kFp8LdsBytes <= 160 * 1024, "fp8 LDS budget");
+static_assert(RecLayout<FmtM1>::kNarrowLds <= kFp8LdsBytes, "MODEL1 records fit the fp8 kernels' LDS");
+static_assert(RecLayout<FmtV32>::kTail == 16 && RecLayout<FmtM1>::kTail == 48, "tail slices");
+
+template <int kPageClass, class Fmt = FmtV32>
 struct RecordLoader {
   const char* base;  // kPageBig: record of the stage's first key
   int page;          // other classes: lane j < 16 holds the page of key 16w + j (clamped)
@@ -413,7 +459,7 @@ struct RecordLoader {
   int s_tok0;
   LDS_AS char* raw;
   uint32_t on = ~0u;  // EXEC mask (both halves) of the slices: zero turns issue() into no-ops
-  static constexpr int kSlices = kFp8DmaPerWave;
+  static constexpr int kSlices = RecLayout<Fmt>::kDmaPerWave;
 
   __device__ __forceinline__ void begin(const AttnArgs& a, LDS_AS char* raw_stage, int page_base, int tok0,
                                         int tok_end, int wave) {
@@ -424,7 +470,7 @@ struct RecordLoader {
     last = tok_end - 1 - tok0;
     if (kPageClass == kPageBig) {
       const int pg = ld_const(a.kv_indices, page_base + (tok0 >> sh));
-      base = (const char*)a.kv_fp8 + (((size_t)pg << sh) + (tok0 & mask)) * kFp8RecordBytes;
+      base = (const char*)a.kv_fp8 + (((size_t)pg << sh) + (tok0 & mask)) * Fmt::kRecBytes;
       return;
     }
     const int lane = lane_here();
@@ -441,37 +487,43 @@ struct RecordLoader {
   __device__ __forceinline__ void issue(const AttnArgs& a, int i, int wave) {
     const int lane = lane_here();
     const int c = 64 * i + lane;
-    const int cc = min(c, 16 * kRecChunks - 1);
-    const int tr = (int)(__umul24((uint32_t)cc, 200u) >> 13);  // cc / 41 for cc < 704 (24-bit multiply: full rate)
-    const int k = cc - kRecChunks * tr;
+    const int cc = min(c, 16 * Fmt::kChunks - 1);
+    const int tr = Fmt::div_chunks(cc);
+    const int k = cc - Fmt::kChunks * tr;
     const int tc = min(wave * 16 + tr, last);
-    LDS_AS char* dst = raw + (wave * 16 * kRecChunks + 64 * i) * 16;
-    // the last slice holds the 16 chunks 640..655: lanes 0..15 only
-    constexpr int kTail = 16 * kRecChunks - 64 * (kFp8DmaPerWave - 1);
-    static_assert(kTail == 16, "tail slice is lanes 0..15");
+    LDS_AS char* dst = raw + (wave * 16 * Fmt::kChunks + 64 * i) * 16;
+    constexpr int kTail = RecLayout<Fmt>::kTail;
     const uint32_t onu = __builtin_amdgcn_readfirstlane(on);  // wave-uniform; keep it scalar for the asm
-    const uint32_t lo = (i == kFp8DmaPerWave - 1) ? (onu & 0xFFFFu) : onu;
-    const uint32_t hi = (i == kFp8DmaPerWave - 1) ? 0u : onu;
+    const bool tail = i == kSlices - 1;
+    uint32_t lo = onu, hi = onu;
+    if constexpr (kTail < 32) {
+      if (tail) {
+        lo = onu & ((1u << kTail) - 1u);
+        hi = 0u;
+      }
+    } else if constexpr (kTail < 64) {
+      if (tail) hi = onu & ((1u << (kTail - 32)) - 1u);
+    }
     if (kPageClass == kPageBig) {
-      dma16_x(base, __umul24((uint32_t)tc, (uint32_t)kFp8RecordBytes) + 16u * k, lds_addr(dst), lo, hi);
+      dma16_x(base, __umul24((uint32_t)tc, (uint32_t)Fmt::kRecBytes) + (uint32_t)Fmt::goff(k), lds_addr(dst), lo, hi);
     } else {
       const int p = __shfl(page, tr);
       const int sh = a.page_shift;
       const int T = s_tok0 + tc;
-      const char* src = (const char*)a.kv_fp8 + (((size_t)p << sh) + (T & ((1 << sh) - 1))) * kFp8RecordBytes +
-                        16 * k;
+      const char* src = (const char*)a.kv_fp8 + (((size_t)p << sh) + (T & ((1 << sh) - 1))) * Fmt::kRecBytes +
+                        Fmt::goff(k);
       dma16_vx(src, lds_addr(dst), lo, hi);
     }
   }
 };
 
-template <int kPageClass>
+template <int kPC, class Fmt = FmtV32>
 __device__ __forceinline__ void issue_stage_fp8(const AttnArgs& a, LDS_AS char* raw, int page_base, int s_tok0,
                                                 int tok_end, int wave) {
-  RecordLoader<kPageClass> ld;
+  RecordLoader<kPC, Fmt> ld;
   ld.begin(a, raw, page_base, s_tok0, tok_end, wave);
 #pragma unroll
-  for (int i = 0; i < kFp8DmaPerWave; ++i) ld.issue(a, i, wave);
+  for (int i = 0; i < RecordLoader<kPC, Fmt>::kSlices; ++i) ld.issue(a, i, wave);
 }
 
 // Four e4m3 codes (one per byte of x) as bf16, exactly: gfx950's scaled
@@ -488,28 +540,39 @@ __device__ __forceinline__ void codes_to_bf16(uint32_t x, bf16x8& h, int at) {
 }
 
 // Wave w unpacks the records of keys [16w, 16w+16) from the raw stage: the
-// ckv codes go to the bf16 stage as exact bf16 values (code, not code *
-// scale), the rope dims are copied, and the four tile scales go to the
-// scale table sct[tile][key].  The scale is applied in fp32 by the consumer:
-// to each tile's partial dot product in Q.K^T, and to P for the tile's
-// output dims in P.V, so no dequantised key is ever rounded.  Lane l
-// handles ckv chunk l (dims 8l..8l+7) of every key, then two rope chunks;
-// all reads are issued before the first conversion.
+// codes go to the bf16 stage as exact bf16 values (code, not code * scale),
+// the rope dims are copied, and the tile scales go to the scale table
+// sct[tile][key].  The scale is applied in fp32 by the consumer: to each
+// tile's partial dot product in Q.K^T, and to P for the tile's output dims
+// in P.V, so no dequantised key is ever rounded.  Lane l handles ckv chunk l
+// (dims 8l..8l+7) of every key (MODEL1: lanes 56..63, the dims past the 448
+// NoPE dims, write zeros), then two rope chunks; all reads are issued before
+// the first conversion.
+template <class Fmt = FmtV32>
 __device__ __forceinline__ void dequant_stage(const LDS_AS char* __restrict__ raw, LDS_AS char* __restrict__ st,
                                               LDS_AS float* __restrict__ sct, int wave, int lane) {
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  constexpr int S = Fmt::kStride;
+  const bool has = 8 * lane < Fmt::kNope;
   u32x2 codes[16];
   u32x4 rope[2];
-  float sc = 0.f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) codes[i] = *(const LDS_AS u32x2*)(raw + (wave * 16 + i) * kFp8RecordBytes + 8 * lane);
+  for (int i = 0; i < 16; ++i)
+    codes[i] = has ? *(const LDS_AS u32x2*)(raw + (wave * 16 + i) * S + 8 * lane) : u32x2{0u, 0u};
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int t = wave * 16 + 8 * i + (lane >> 3);
-    rope[i] = *(const LDS_AS u32x4*)(raw + t * kFp8RecordBytes + kDimCkv + 16 + 16 * (lane & 7));
+    rope[i] = *(const LDS_AS u32x4*)(raw + t * S + Fmt::kRopeOff + 16 * (lane & 7));
   }
-  // scales: lane l < 64 holds scale (l & 3) of key 16w + (l >> 2)
-  sc = *(const LDS_AS float*)(raw + (wave * 16 + (lane >> 2)) * kFp8RecordBytes + kDimCkv + 4 * (lane & 3));
+  // scales: entry e = 64 j + lane < 16 * tiles holds scale e % tiles of key 16w + e / tiles
+  constexpr int kScales = 16 * Fmt::kTiles;
+  float sc[(kScales + 63) / 64];
+#pragma unroll
+  for (int j = 0; j < (kScales + 63) / 64; ++j) {
+    const int e = min(64 * j + lane, kScales - 1);
+    const int key = e / Fmt::kTiles, t = e - Fmt::kTiles * key;
+    sc[j] = *(const LDS_AS float*)(raw + (wave * 16 + key) * S + Fmt::scale_off(t));
+  }
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     bf16x8 h;
@@ -522,7 +585,12 @@ __device__ __forceinline__ void dequant_stage(const LDS_AS char* __restrict__ ra
     const int t = wave * 16 + 8 * i + (lane >> 3);
     *(LDS_AS u32x4*)(st + kpe_off(t, lane & 7)) = rope[i];
   }
-  sct[(lane & 3) * kStageTokens + wave * 16 + (lane >> 2)] = sc;
+#pragma unroll
+  for (int j = 0; j < (kScales + 63) / 64; ++j) {
+    const int e = 64 * j + lane;
+    const int key = e / Fmt::kTiles, t = e - Fmt::kTiles * key;
+    if (e < kScales) sct[t * kStageTokens + wave * 16 + key] = sc[j];
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1307,10 +1375,14 @@ __device__ void ds_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* smem
 // MFMAs.
 // ---------------------------------------------------------------------------
 constexpr int kW8Bufs = 3;
-constexpr int kW8TabOff = kW8Bufs * kFp8RawBytes;                   // per-wave scale tables
-constexpr int kW8LdsBytes = kW8TabOff + 4 * 4 * kStageTokens * 4;   // [4 waves][4 tiles][64 keys] f32
-static_assert(kW8LdsBytes <= 160 * 1024, "fp8 wide LDS budget");
-static_assert(kW8LdsBytes <= kFp8LdsBytes && 4 * 32 * kCkvRowBytes <= kFp8LdsBytes, "fits the fp8 kernels' LDS");
+template <class Fmt>
+struct W8Layout {
+  static constexpr int kTabOff = kW8Bufs * RecLayout<Fmt>::kRawBytes;                 // per-wave scale tables
+  static constexpr int kLdsBytes = kTabOff + 4 * Fmt::kTiles * kStageTokens * 4;      // [4 waves][tiles][64 keys] f32
+};
+static_assert(W8Layout<FmtV32>::kLdsBytes <= kFp8LdsBytes && W8Layout<FmtM1>::kLdsBytes <= kFp8LdsBytes &&
+                  4 * 32 * kCkvRowBytes <= kFp8LdsBytes,
+              "fits the fp8 kernels' LDS");
 
 __device__ __forceinline__ bf16x8 codes8(uint32_t lo, uint32_t hi) {
   bf16x8 h;
@@ -1324,8 +1396,21 @@ __device__ __forceinline__ bf16x8 codes8(uint32_t lo, uint32_t hi) {
 // latent dims then runs on the fp8 x fp8 MFMA (32x32x64), 64 dims per step,
 // straight from the key codes in LDS (no conversion); the 64 rope dims are
 // converted to bf16 once (exactly) and stay on the bf16 MFMA, as does P.V.
-template <int kPC, bool kSparse = false, bool kQ8 = false>
+// Fmt: the record format (FmtV32 or FmtM1; kQ8 with FmtV32 only).  MODEL1
+// records have 448 NoPE dims in 7 tiles of 64: 14 code steps of 32 dims in
+// Q.K^T, folded every 2 steps, and 14 output tiles of 32 dims in P.V (tiles
+// 14 and 15, dims 448..511, stay 0); their output tiles hold 32 consecutive
+// dims, so each one lies inside one scale tile.
+template <int kPC, bool kSparse = false, bool kQ8 = false, class Fmt = FmtV32>
 __device__ void wide8_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* smem, int wave, int) {
+  static_assert(!kQ8 || !Fmt::kM1, "the e4m3 query runs over the 656-byte records");
+  constexpr int S = Fmt::kStride;                 // record stride in LDS
+  constexpr int kRaw = RecLayout<Fmt>::kRawBytes; // one stage
+  constexpr int kDma = RecLayout<Fmt>::kDmaPerWave;
+  constexpr int kM = Fmt::kNope / 32;             // 32-dim code steps of Q.K^T
+  constexpr int kMT = Fmt::kTileDims / 32;        // code steps per scale tile
+  constexpr int kT = Fmt::kTiles;
+  constexpr int kJ = 2 * kM;                      // P.V steps (32 output dims x 16 keys each)
   const int lane = lane_here();  // lane-derived values recomputed per item (kept across items they get spilled)
   const int g = lane >> 5;
   const int n = lane & 31;
@@ -1339,12 +1424,12 @@ __device__ void wide8_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* s
   // row and is masked by its key bound of 0), so no wait splits them.
   const int page_base = ld_const(a.kv_indptr, it.b);
   const int nstage = (it.tok1 - it.tok0 + kStageTokens - 1) / kStageTokens;
-  if (nstage > 0) issue_stage_fp8<kPC>(a, smem, page_base, it.tok0, it.tok1, wave);
+  if (nstage > 0) issue_stage_fp8<kPC, Fmt>(a, smem, page_base, it.tok0, it.tok1, wave);
 
   // Query fragments in the codes' dim order: nope k-step 2m+s, half g holds
   // dims 32m + 16g + 8s .. +7; rope k-steps as in the bf16 path.  kQ8: step
   // c of the fp8 MFMA, half g holds the codes of dims 64c + 32g .. +31.
-  bf16x8 qf[kQ8 ? 1 : 32];
+  bf16x8 qf[kQ8 ? 1 : 2 * kM];
   bf16x8 qr[4];
   i32x8 q8[kQ8 ? 8 : 1];
   if constexpr (kQ8) {
@@ -1365,25 +1450,26 @@ __device__ void wide8_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* s
     const __bf16* qn = (const __bf16*)a.q_nope + ri.qrow * a.q_stride + 16 * g;
     const __bf16* qp = (const __bf16*)a.q_pe + ri.qrow * a.qpe_stride + 8 * g;
 #pragma unroll
-    for (int m = 0; m < 16; ++m)
+    for (int m = 0; m < kM; ++m)
 #pragma unroll
       for (int sh = 0; sh < 2; ++sh) qf[2 * m + sh] = *(const bf16x8*)(qn + 32 * m + 8 * sh);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qr[ks] = *(const bf16x8*)(qp + 16 * ks);
   }
   // byte offsets inside a raw stage
-  const int kaddr = n * kFp8RecordBytes + (kQ8 ? 32 : 16) * g;           // + tb*656 + 32m (kQ8: + 64c)
-  const int raddr = n * kFp8RecordBytes + kDimCkv + 16 + 16 * g;        // rope: + tb*656 + 32kr
+  const int kaddr = n * S + (kQ8 ? 32 : 16) * g;           // + tb*S + 32m (kQ8: + 64c)
+  const int raddr = n * S + Fmt::kRopeOff + 16 * g;        // rope: + tb*S + 32kr
   int vaddr;
   {
     // tr_b8: in each 16-lane group, lane pair j supplies key 8(j/4) + 4h + j%4
-    // of the 16-key step (h = lane / 32), dims 64((lane/16)%2) + 8(lane%2) ..
-    // of the tile's paired dims (see wide_dim)
+    // of the 16-key step (h = lane / 32), dims P((lane/16)%2) + 8(lane%2) ..
+    // of the output tile: P = 64 for V32's paired dims, 16 for MODEL1's
+    // consecutive ones (see wide_dim)
     const int p = lane & 15, j = p >> 1;
     const int vkey = 8 * (j >> 2) + 4 * g + (j & 3);
-    vaddr = vkey * kFp8RecordBytes + 64 * ((lane >> 4) & 1) + 8 * (p & 1);  // + (tb + 16kk)*656 + D(cb)
+    vaddr = vkey * S + (Fmt::kPairedDims ? 64 : 16) * ((lane >> 4) & 1) + 8 * (p & 1);  // + (tb + 16kk)*S + D(cb)
   }
-  LDS_AS float* tab = (LDS_AS float*)(smem + kW8TabOff) + wave * 4 * kStageTokens;
+  LDS_AS float* tab = (LDS_AS float*)(smem + W8Layout<Fmt>::kTabOff) + wave * kT * kStageTokens;
 
   WideState st;
 #pragma unroll
@@ -1393,17 +1479,17 @@ __device__ void wide8_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* s
   st.o_live = false;
   float m_top = kNegInf;  // token-sparse: the row's largest logit (log2 units)
 
-  if (nstage > 1) issue_stage_fp8<kPC>(a, smem + kFp8RawBytes, page_base, it.tok0 + kStageTokens, it.tok1, wave);
+  if (nstage > 1) issue_stage_fp8<kPC, Fmt>(a, smem + kRaw, page_base, it.tok0 + kStageTokens, it.tok1, wave);
   for (int s = 0; s < nstage; ++s) {
     // stage s must have landed; stage s+1's records may still be in flight
     if (s + 1 < nstage) {
-      wait_vmcnt<kFp8DmaPerWave>();
+      wait_vmcnt<kDma>();
     } else {
       wait_vmcnt<0>();
     }
     __syncthreads();  // stage s visible; every wave is done with stage s-1 (its buffer is refilled below)
     const int buf = s % kW8Bufs;
-    const LDS_AS char* __restrict__ raw = smem + buf * kFp8RawBytes;
+    const LDS_AS char* __restrict__ raw = smem + buf * kRaw;
     // this lane's K codes and V^T rows: the sums are kept in registers (the
     // empty asm makes them opaque), so every read below is base + immediate
     uint32_t kb_u = lds_addr(raw) + kaddr, vb_u = lds_addr(raw) + vaddr, rb_u = lds_addr(raw) + raddr;
@@ -1412,15 +1498,20 @@ __device__ void wide8_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* s
     const LDS_AS char* __restrict__ vbase = (const LDS_AS char*)(uintptr_t)vb_u;
     const LDS_AS char* __restrict__ rbase = (const LDS_AS char*)(uintptr_t)rb_u;  // rope dims
     const bool more = s + 2 < nstage;
-    RecordLoader<kPC> ld;
-    ld.begin(a, smem + ((s + 2) % kW8Bufs) * kFp8RawBytes, page_base, it.tok0 + (more ? s + 2 : s) * kStageTokens,
+    RecordLoader<kPC, Fmt> ld;
+    ld.begin(a, smem + ((s + 2) % kW8Bufs) * kRaw, page_base, it.tok0 + (more ? s + 2 : s) * kStageTokens,
              it.tok1, wave);
     ld.on = __builtin_amdgcn_readfirstlane(more ? ~0u : 0u);
     {
       // this wave's copy of the stage's tile scales: tab[t][key]
-      const f32x4 sc = *(const LDS_AS f32x4*)(raw + lane * kFp8RecordBytes + kDimCkv);
+      const f32x4 sc = *(const LDS_AS f32x4*)(raw + lane * S + Fmt::scale_off(0));
 #pragma unroll
       for (int t = 0; t < 4; ++t) tab[t * kStageTokens + lane] = sc[t];
+      if constexpr (kT > 4) {
+        const f32x4 sc2 = *(const LDS_AS f32x4*)(raw + lane * S + FmtM1::kScaleHiOff);  // scales 3 .. 6
+#pragma unroll
+        for (int t = 4; t < kT; ++t) tab[t * kStageTokens + lane] = sc2[t - 3];
+      }
     }
     const int stage_tok = it.tok0 + s * kStageTokens;
 #pragma unroll
@@ -1437,7 +1528,7 @@ __device__ void wide8_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* s
       {
         bf16x8 rp[4];  // all four rope fragments in flight before the chain starts
 #pragma unroll
-        for (int kr2 = 0; kr2 < 4; ++kr2) rp[kr2] = *(const LDS_AS bf16x8*)(rbase + tb * kFp8RecordBytes + 32 * kr2);
+        for (int kr2 = 0; kr2 < 4; ++kr2) rp[kr2] = *(const LDS_AS bf16x8*)(rbase + tb * S + 32 * kr2);
         pin_loads();
 #pragma unroll
         for (int kr2 = 0; kr2 < 4; ++kr2) {
@@ -1460,8 +1551,8 @@ __device__ void wide8_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* s
         // two 64-deep fp8 steps per 128-dim tile
         constexpr int KD8 = 2;  // 32-code reads in flight
         auto kread8 = [&](int c) -> i32x8 {
-          const u32x4 lo = *(const LDS_AS u32x4*)(kbase + tb * kFp8RecordBytes + 64 * c);
-          const u32x4 hi = *(const LDS_AS u32x4*)(kbase + tb * kFp8RecordBytes + 64 * c + 16);
+          const u32x4 lo = *(const LDS_AS u32x4*)(kbase + tb * S + 64 * c);
+          const u32x4 hi = *(const LDS_AS u32x4*)(kbase + tb * S + 64 * c + 16);
           return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
         };
         i32x8 kr8[KD8];
@@ -1487,33 +1578,33 @@ __device__ void wide8_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* s
       } else {
       constexpr int KD = 3;  // 16-code reads in flight
       u32x4 kr[KD];
-      auto kread = [&](int m) -> u32x4 { return *(const LDS_AS u32x4*)(kbase + tb * kFp8RecordBytes + 32 * m); };
+      auto kread = [&](int m) -> u32x4 { return *(const LDS_AS u32x4*)(kbase + tb * S + 32 * m); };
 #pragma unroll
       for (int i = 0; i < KD; ++i) kr[i] = kread(i);
 #pragma unroll
-      for (int m = 0; m < 16; ++m) {
+      for (int m = 0; m < kM; ++m) {
         pin_loads();
         const u32x4 c = kr[m % KD];
-        if (m + KD < 16) kr[m % KD] = kread(m + KD);
+        if (m + KD < kM) kr[m % KD] = kread(m + KD);
         const bf16x8 a0 = codes8(c[0], c[1]), a1 = codes8(c[2], c[3]);
-        f32x16& pa = part[(m >> 2) & 1];
-        if ((m & 3) == 0) {
+        f32x16& pa = part[(m / kMT) & 1];
+        if (m % kMT == 0) {
           mfma32_first(pa, a0, qf[2 * m]);
         } else {
           mfma32_acc(pa, a0, qf[2 * m]);
         }
         mfma32_acc(pa, a1, qf[2 * m + 1]);
-        if ((m & 3) == 0 && m > 0) {
+        if (m % kMT == 0 && m > 0) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) tsc[q] = scales((m >> 2) - 1, q);
+          for (int q = 0; q < 4; ++q) tsc[q] = scales(m / kMT - 1, q);
         }
-        if ((m & 3) == 1 && m > 1) fold((m >> 2) - 1);
+        if (m % kMT == 1 && m > 1) fold(m / kMT - 1);
       }
       }
       pin_loads();
 #pragma unroll
-      for (int q = 0; q < 4; ++q) tsc[q] = scales(3, q);
-      fold(3);
+      for (int q = 0; q < 4; ++q) tsc[q] = scales(kT - 1, q);
+      fold(kT - 1);
       // ---- online softmax (base 2); lane holds keys 8(r/4) + 4g + r%4 of the sub-tile
       float sv[16];
       float mx = kNegInf;
@@ -1549,7 +1640,8 @@ __device__ void wide8_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* s
       typedef int i32x2 __attribute__((ext_vector_type(2)));
       auto vread = [&](int j) -> u32x2 {  // j = 2*cb + kk
         const int cb = j >> 1, kk = j & 1;
-        const LDS_AS char* src = vbase + (tb + 16 * kk) * kFp8RecordBytes + 128 * (cb >> 2) + 16 * (cb & 3);
+        const int dcol = Fmt::kPairedDims ? 128 * (cb >> 2) + 16 * (cb & 3) : 32 * cb;
+        const LDS_AS char* src = vbase + (tb + 16 * kk) * S + dcol;
         return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS i32x2*)src));
       };
       u32x2 vr[VD];
@@ -1559,25 +1651,27 @@ __device__ void wide8_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* s
       f32x4 nsc[4];  // scales of the next tile, read half a tile ahead
 #pragma unroll
       for (int q = 0; q < 4; ++q) nsc[q] = scales(0, q);
+      constexpr int kJT = 2 * kMT;  // P.V steps per scale tile
 #pragma unroll
-      for (int j = 0; j < 32; ++j) {
+      for (int j = 0; j < kJ; ++j) {
         pin_loads();
-        if ((j & 7) == 0) {
-          // output dims of tile j/8: P scaled by each key's tile scale
+        if (j % kJT == 0) {
+          // output dims of tile j / kJT: P scaled by each key's tile scale
 #pragma unroll
           for (int q = 0; q < 4; ++q)
 #pragma unroll
             for (int r = 0; r < 4; ++r) pt[q >> 1][4 * (q & 1) + r] = (__bf16)(pf[4 * q + r] * nsc[q][r]);
         }
-        if ((j & 7) == 4 && j < 24) {
+        if (j % kJT == kJT / 2 && j < kJ - kJT) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) nsc[q] = scales((j >> 3) + 1, q);
+          for (int q = 0; q < 4; ++q) nsc[q] = scales(j / kJT + 1, q);
         }
         const u32x2 v = vr[j % VD];
-        if (j + VD < 32) vr[j % VD] = vread(j + VD);
+        if (j + VD < kJ) vr[j % VD] = vread(j + VD);
         st.o[j >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(codes8(v[0], v[1]), pt[j & 1], st.o[j >> 1], 0, 0, 0);
         // the records of the stage after next ride along P.V (Q.K^T waits on its own LDS reads)
-        if ((j & 3) == 0 && sub * 8 + (j >> 2) < RecordLoader<kPC>::kSlices) ld.issue(a, sub * 8 + (j >> 2), wave);
+        if ((j & 3) == 0 && sub * (kJ / 4) + (j >> 2) < RecordLoader<kPC, Fmt>::kSlices)
+          ld.issue(a, sub * (kJ / 4) + (j >> 2), wave);
       }
       pin_loads();
     }
@@ -1585,7 +1679,7 @@ __device__ void wide8_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* s
   __syncthreads();  // every wave is done with the stage buffers before the epilogue stages rows there
   {
     const int rib_e = wave * 32 + (lane_here() & 31);  // row info recomputed rather than kept across the loop
-    wide_epilogue<true, kSparse>(a, it, st, row_info(a, it, rib_e), rib_e, smem, wave, lane, m_top);
+    wide_epilogue<Fmt::kPairedDims, kSparse>(a, it, st, row_info(a, it, rib_e), rib_e, smem, wave, lane, m_top);
   }
 }
 
@@ -1601,7 +1695,9 @@ struct NarrowState {
   float l_run;
 };
 
-template <int kPC, bool kFp8>
+// kM1 (fp8 only): MODEL1 records, 448 NoPE dims in 64-dim scale tiles; the
+// k-steps and output tiles past dim 448 are skipped (their keys are zero).
+template <int kPC, bool kFp8, bool kM1 = false>
 __device__ __forceinline__ void narrow_body(const AttnArgs& a, const bf16x8 (&qf)[18], NarrowState& st,
                                             const LDS_AS char* __restrict__ cur, LDS_AS char* __restrict__ nxt,
                                             bool prefetch, int page_base, int next_tok, int tok_end,
@@ -1620,11 +1716,13 @@ __device__ __forceinline__ void narrow_body(const AttnArgs& a, const bf16x8 (&qf
 #pragma unroll
   for (int ks = 0; ks < 18; ++ks) {
     if (prefetch) ld.issue(a, ks, wave);  // one prefetch slice per k-step
+    if (kM1 && (ks == 14 || ks == 15)) continue;  // dims 448..511
     const bf16x8 kf = ks < 16 ? lds_read_b128(cur, kb[ks & 3] + 256 * (ks >> 2)) : lds_read_b128(cur, pb[ks - 16]);
     if (kFp8 && ks < 16) {
+      constexpr int kKsPerTile = kM1 ? 2 : 4;  // 32-dim k-steps per scale tile
       part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], part, 0, 0, 0);
-      if ((ks & 3) == 3) {
-        sacc += part * scales(ks >> 2);
+      if (ks % kKsPerTile == kKsPerTile - 1) {
+        sacc += part * scales(ks / kKsPerTile);
         part = f32x4{};
       }
     } else {
@@ -1668,10 +1766,11 @@ __device__ __forceinline__ void narrow_body(const AttnArgs& a, const bf16x8 (&qf
   }
   // O^T[16 dims x 16 rows] += V^T[16 dims x 16 keys] . P^T[16 keys x 16 rows]
 #pragma unroll
-  for (int cb = 0; cb < 32; ++cb) {
-    if (kFp8 && (cb & 7) == 0) {
-      // output dims of tile cb/8: P scaled by each key's tile scale
-      const f32x4 ps = pf * scales(cb >> 3);
+  for (int cb = 0; cb < (kM1 ? 28 : 32); ++cb) {
+    constexpr int kCbPerTile = kM1 ? 4 : 8;  // 16-dim output tiles per scale tile
+    if (kFp8 && cb % kCbPerTile == 0) {
+      // output dims of tile cb / kCbPerTile: P scaled by each key's tile scale
+      const f32x4 ps = pf * scales(cb / kCbPerTile);
 #pragma unroll
       for (int r = 0; r < 4; ++r) pt[r] = __builtin_bit_cast(short, (__bf16)ps[r]);
     }
@@ -1680,8 +1779,10 @@ __device__ __forceinline__ void narrow_body(const AttnArgs& a, const bf16x8 (&qf
   }
 }
 
-template <int kPC, bool kFp8>
+template <int kPC, bool kFp8, bool kM1 = false>
 __device__ void narrow_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* smem, int wave, int lane) {
+  using Fmt = typename std::conditional<kM1, FmtM1, FmtV32>::type;
+  using RL = RecLayout<Fmt>;
   const int g4 = lane >> 4;  // lane quarter
   const int n = lane & 15;   // row within the block
   const RowInfo ri = row_info(a, it, n);
@@ -1693,7 +1794,7 @@ __device__ void narrow_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* 
     const __bf16* qn = (const __bf16*)a.q_nope + ri.qrow * a.q_stride + 8 * g4;
     const __bf16* qp = (const __bf16*)a.q_pe + ri.qrow * a.qpe_stride + 8 * g4;
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) qf[ks] = ri.ok ? *(const bf16x8*)(qn + 32 * ks) : z;
+    for (int ks = 0; ks < 16; ++ks) qf[ks] = ri.ok && 32 * ks < (kM1 ? FmtM1::kNope : kDimCkv) ? *(const bf16x8*)(qn + 32 * ks) : z;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) qf[16 + ks] = ri.ok ? *(const bf16x8*)(qp + 32 * ks) : z;
   }
@@ -1720,24 +1821,24 @@ __device__ void narrow_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* 
   const int page_base = ld_const(a.kv_indptr, it.b);
   const int nstage = (it.tok1 - it.tok0 + kStageTokens - 1) / kStageTokens;
   if (kFp8) {
-    LDS_AS char* raw = smem + kFp8RawOff;
-    LDS_AS float* sct = (LDS_AS float*)(smem + kFp8ScaleOff);
-    if (nstage > 0) issue_stage_fp8<kPC>(a, raw, page_base, it.tok0, it.tok1, wave);
-    if (nstage > 1) issue_stage_fp8<kPC>(a, raw + kFp8RawBytes, page_base, it.tok0 + kStageTokens, it.tok1, wave);
+    LDS_AS char* raw = smem + RL::kRawOff;
+    LDS_AS float* sct = (LDS_AS float*)(smem + RL::kScaleOff);
+    if (nstage > 0) issue_stage_fp8<kPC, Fmt>(a, raw, page_base, it.tok0, it.tok1, wave);
+    if (nstage > 1) issue_stage_fp8<kPC, Fmt>(a, raw + RL::kRawBytes, page_base, it.tok0 + kStageTokens, it.tok1, wave);
     for (int s = 0; s < nstage; ++s) {
       if (s + 1 < nstage) {
-        wait_vmcnt<kFp8DmaPerWave>();
+        wait_vmcnt<RL::kDmaPerWave>();
       } else {
         wait_vmcnt<0>();
       }
       __syncthreads();
-      dequant_stage(raw + (s & 1) * kFp8RawBytes, smem, sct, wave, lane);
+      dequant_stage<Fmt>(raw + (s & 1) * RL::kRawBytes, smem, sct, wave, lane);
       __syncthreads();
       if (s + 2 < nstage)
-        issue_stage_fp8<kPC>(a, raw + (s & 1) * kFp8RawBytes, page_base, it.tok0 + (s + 2) * kStageTokens, it.tok1,
-                             wave);
-      narrow_body<kPC, true>(a, qf, st, smem, smem, false, page_base, 0, it.tok1, it.tok0 + s * kStageTokens, bound,
-                             kb, pb, vb, wave, lane, sct);
+        issue_stage_fp8<kPC, Fmt>(a, raw + (s & 1) * RL::kRawBytes, page_base, it.tok0 + (s + 2) * kStageTokens,
+                                  it.tok1, wave);
+      narrow_body<kPC, true, kM1>(a, qf, st, smem, smem, false, page_base, 0, it.tok1, it.tok0 + s * kStageTokens,
+                                  bound, kb, pb, vb, wave, lane, sct);
     }
     __syncthreads();
   } else {
@@ -2230,7 +2331,7 @@ __device__ __forceinline__ int xcd_list(int b, int n) {
   return base + (b >> 3);
 }
 
-template <int kMode, int kPC, bool kFp8, bool kSparse = false, bool kQ8 = false>
+template <int kMode, int kPC, bool kFp8, bool kSparse = false, bool kQ8 = false, bool kM1 = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_attn_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char
@@ -2261,13 +2362,13 @@ void mla_attn_kernel(AttnArgs a) {
       continue;
     }
     if (kMode == 1 && kFp8) {
-      wide8_item<kPC, kSparse, kQ8>(a, it, smem, wave, lane);
+      wide8_item<kPC, kSparse, kQ8, typename std::conditional<kM1, FmtM1, FmtV32>::type>(a, it, smem, wave, lane);
     } else if (kMode == 1 && !kSparse) {
       ds_item<kPC>(a, it, smem, wave);
     } else if (kMode == 1) {
       wide_item<kPC, kSparse>(a, it, smem, wave, lane);
     } else {
-      narrow_item<kPC, kFp8>(a, it, smem, wave, lane);
+      narrow_item<kPC, kFp8, kM1>(a, it, smem, wave, lane);
     }
   }
 }
@@ -2280,7 +2381,10 @@ void mla_attn_kernel(AttnArgs a) {
 // its execution, no queue gaps); with null events it is a plain launch.
 template <int kMode, int kPC>
 hipError_t launch_mode(const AttnArgs& a, int kv_fp8, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
-  if (kv_fp8) {
+  if (kv_fp8 == 2) {
+    hipExtLaunchKernelGGL((mla_attn_kernel<kMode, kPC, true, false, false, true>), dim3(a.num_wgs), dim3(256), 0,
+                          stream, t0, t1, 0, a);
+  } else if (kv_fp8) {
     hipExtLaunchKernelGGL((mla_attn_kernel<kMode, kPC, true>), dim3(a.num_wgs), dim3(256), 0, stream, t0, t1, 0, a);
   } else {
     hipExtLaunchKernelGGL((mla_attn_kernel<kMode, kPC, false>), dim3(a.num_wgs), dim3(256), 0, stream, t0, t1, 0, a);
@@ -2330,10 +2434,13 @@ hipError_t launch_attention_q8(const AttnArgs& a, hipStream_t stream, hipEvent_t
   return hipGetLastError();
 }
 
-hipError_t launch_sparse_attention(const AttnArgs& a, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
+hipError_t launch_sparse_attention(const AttnArgs& a, hipStream_t stream, hipEvent_t t0, hipEvent_t t1, bool m1) {
   if (a.num_wgs <= 0) return hipSuccess;
   if (a.page_shift != 0 || a.sparse_len == nullptr) return hipErrorInvalidValue;
-  if (a.kv_fp8 != nullptr) {
+  if (a.kv_fp8 != nullptr && m1) {
+    hipExtLaunchKernelGGL((mla_attn_kernel<1, kPageSmall, true, true, false, true>), dim3(a.num_wgs), dim3(256), 0,
+                          stream, t0, t1, 0, a);
+  } else if (a.kv_fp8 != nullptr) {
     hipExtLaunchKernelGGL((mla_attn_kernel<1, kPageSmall, true, true>), dim3(a.num_wgs), dim3(256), 0, stream, t0,
                           t1, 0, a);
   } else {

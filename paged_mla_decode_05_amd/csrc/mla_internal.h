@@ -105,14 +105,15 @@ constexpr int32_t kValidateIndptr = 1, kValidateIndices = 2, kValidateQo = 4, kV
 // Launchers (mla_attn.hip).  They only enqueue on `stream`; return hipError_t.
 // t0 / t1: optional events recorded by the attention kernel's own dispatch
 // at the start and end of its execution (null: none).
+// kv_fp8: 0 bf16 caches, 1 656-byte records, 2 MODEL1 records (604 bytes).
 hipError_t launch_attention(const AttnArgs& a, int tile_mode, int kv_fp8, hipStream_t stream, hipEvent_t t0,
                             hipEvent_t t1);
 // Decode over fp8 records with an fp8 (e4m3) query: WIDE tile, q_nope =
 // the [rows, H, 576] codes with q_stride 576.
 hipError_t launch_attention_q8(const AttnArgs& a, hipStream_t stream, hipEvent_t t0, hipEvent_t t1);
 // Token-sparse attention (WIDE tile, page size 1, key lists bounded by
-// a.sparse_len) over fp8 records (a.kv_fp8 set) or bf16 rows.
-hipError_t launch_sparse_attention(const AttnArgs& a, hipStream_t stream, hipEvent_t t0, hipEvent_t t1);
+// a.sparse_len) over fp8 records (a.kv_fp8 set; m1: MODEL1 records) or bf16 rows.
+hipError_t launch_sparse_attention(const AttnArgs& a, hipStream_t stream, hipEvent_t t0, hipEvent_t t1, bool m1);
 // Stable compaction of each query token's key list: entries k < n_t (n_t =
 // min(topk_length[t], topk), or topk when topk_length is null) with
 // 0 <= idx < num_slots are copied, in order, to list[t * topk ...];

@@ -1,10 +1,20 @@
-"""GPU parity of the MODEL1 record path (FlashMLA FP8 section,
-MODEL1_FP8Sparse): the record expansion is byte work and must equal the
-oracle's dequantisation bit for bit (bf16 bits, signed zeros included);
-decode over the expanded rows and queries, through the concatenated-layout
-entry point, is checked against the MODEL1 oracle (q.k over 512 dims,
-V = the 448 NoPE dims) with the bf16 tolerances, since both sides attend
-over the same bf16 keys.  Output dims 448..511 must be exactly 0."""
+"""GPU parity of the MODEL1 record path (FlashMLA "FP8 KV Cache Quantization
+and Dequantization", MODEL1_FP8Sparse: 448 NoPE dims in 7 tiles of 64, 604
+bytes per token).
+
+* mla_decode_model1 / mla_sparse_decode_model1 read the records in the
+  attention kernel and use the exact keys code * scale, the reading taken
+  for both record formats; they are checked against the oracle on those
+  exact keys with the fp8-cache tolerances (output max |err| <= 6e-2,
+  relative L2 <= 3e-2, lse and max_logits within 1e-3), short contexts
+  (L = 1) included.  Unused records are NaN bytes.  Output dims 448..511
+  must be exactly 0.
+* The BF16 dequantisation utility (the page's dequantize_k_cache) is byte
+  work and must equal the oracle's BF16 dequantisation bit for bit; decode
+  over its rows, through the concatenated-layout call, is attention over
+  BF16 keys and is checked against the plain attention oracle on the same
+  BF16 values with the bf16 tolerances.
+"""
 
 import sys
 
@@ -13,12 +23,14 @@ import pytest
 import torch
 
 import oracle
-from workloads import make_model1_workload
+from workloads import make_model1_workload, quantize_model1_records
 
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
-TOL = dict(max_abs=2e-2, rel_l2=1e-2, lse=1e-3)
+TOL_BF16 = dict(max_abs=2e-2, rel_l2=1e-2, lse=1e-3)
+TOL_FP8 = dict(max_abs=6e-2, rel_l2=3e-2, lse=1e-3)
+M1 = 448
 
 
 def say(*a):
@@ -34,13 +46,142 @@ def mla():
     return m
 
 
+def compare(out, lse, ref_o, ref_l, tol, mx=None, ref_m=None):
+    o = out.double().cpu().numpy()
+    l = lse.double().cpu().numpy()
+    assert np.all(np.isfinite(o)) and not np.any(np.isnan(l)) and not np.any(np.isposinf(l))
+    assert (o[..., M1:] == 0).all(), "dims 448..511 must be written as 0"
+    o = o[..., :M1]
+    empty = np.isneginf(ref_l)
+    assert np.array_equal(np.isneginf(l), empty) and np.all(o[empty] == 0)
+    err = np.abs(o - ref_o).max()
+    den = np.linalg.norm(ref_o)
+    rel = np.linalg.norm(o - ref_o) / den if den > 0 else 0.0
+    lerr = np.abs(l[~empty] - ref_l[~empty]).max() if (~empty).any() else 0.0
+    merr = 0.0
+    if mx is not None:
+        m = mx.double().cpu().numpy()
+        assert np.array_equal(np.isneginf(m), empty)
+        merr = np.abs(m[~empty] - ref_m[~empty]).max() if (~empty).any() else 0.0
+    say(f"    max|dout|={err:.3e} relL2={rel:.3e} max|dlse|={lerr:.3e} max|dmax|={merr:.3e}")
+    assert err <= tol["max_abs"] and rel <= tol["rel_l2"] and lerr <= tol["lse"] and merr <= tol["lse"]
+
+
 def bf16_bits(x64):
     return torch.from_numpy(np.ascontiguousarray(x64)).to(torch.bfloat16).view(torch.int16).numpy()
 
 
+# ---------------------------------------------------------------------------
+# decode over the records, dequantised in the kernel
+# ---------------------------------------------------------------------------
+
+CASES = [
+    # (heads, page_size, kv_lens, tile_mode, force_splits, out fp32)
+    (16, 64, [1, 37, 64, 200], 0, 0, False),
+    (16, 16, [5, 300, 0, 1], 2, 3, True),
+    (16, 1, [3, 70, 129], 2, 2, False),
+    (40, 4, [100, 400, 0, 33], 0, 2, False),
+    (128, 64, [1, 37, 64, 200], 1, 0, False),
+    (128, 16, [700, 3, 65], 1, 3, True),
+    (128, 1, [2, 130], 1, 2, False),
+    (128, 256, [1000, 1, 257], 0, 4, False),
+    (64, 64, [300, 5000], 1, 0, False),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"H{c[0]}-ps{c[1]}-m{c[3]}-s{c[4]}" for c in CASES])
+def test_decode_model1(mla, case):
+    H, ps, lens, mode, fs, f32 = case
+    say(f"model1 decode (in-kernel records) H={H} page_size={ps} lens={lens} tile_mode={mode} force_splits={fs}")
+    w = make_model1_workload(lens, heads=H, page_size=ps, seed=40 + H + ps)
+    plan = mla.mla_plan_create(mla.MLA_KIND_DECODE, w.batch, H, ps, w.num_pages, w.kv_len, w.kv_indptr,
+                               kv_format=mla.MLA_KV_FP8_MODEL1, tile_mode=mode, force_splits=fs)
+    out, lse = mla.mla_decode_model1(plan, w.q.to(DEV), w.records.to(DEV), w.kv_indptr.to(DEV),
+                                     w.kv_indices.to(DEV), w.sm_scale,
+                                     out_dtype=torch.float32 if f32 else torch.bfloat16)
+    torch.cuda.synchronize()
+    ref = oracle.mla_decode_model1_ref(w.q, w.records, w.kv_indptr, w.kv_indices, w.kv_len, w.sm_scale)
+    compare(out, lse, *ref, TOL_FP8)
+
+
+@pytest.mark.parametrize("H,mode", [(16, 2), (128, 1)])
+def test_model1_page_permutation_is_bitwise_invariant(mla, H, mode):
+    w = make_model1_workload([130, 64, 1, 900], heads=H, page_size=16, seed=61)
+    res = []
+    for permute in (False, True):
+        if permute:
+            perm = torch.randperm(w.num_pages, generator=torch.Generator().manual_seed(11))
+            rec2 = torch.empty_like(w.records)
+            rec2[perm] = w.records
+            w.records, w.kv_indices = rec2, perm.to(torch.int32)[w.kv_indices.long()]
+        plan = mla.mla_plan_create(mla.MLA_KIND_DECODE, w.batch, H, 16, w.num_pages, w.kv_len, w.kv_indptr,
+                                   kv_format=mla.MLA_KV_FP8_MODEL1, tile_mode=mode, force_splits=2)
+        res.append(mla.mla_decode_model1(plan, w.q.to(DEV), w.records.to(DEV), w.kv_indptr.to(DEV),
+                                         w.kv_indices.to(DEV), w.sm_scale))
+    torch.cuda.synchronize()
+    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+
+
+def test_decode_model1_full_size(mla):
+    say("decode_model1_b64_h128 (bench launch configuration), every request")
+    w = make_model1_workload(name="decode_model1_b64_h128", device=DEV)
+    plan = mla.mla_plan_create(mla.MLA_KIND_DECODE, w.batch, w.num_heads, w.page_size, w.num_pages, w.kv_len,
+                               w.kv_indptr, kv_format=mla.MLA_KV_FP8_MODEL1)
+    out, lse = mla.mla_decode_model1(plan, w.q, w.records, w.kv_indptr.to(DEV), w.kv_indices.to(DEV), w.sm_scale)
+    torch.cuda.synchronize()
+    ref = oracle.mla_decode_model1_ref(w.q, w.records, w.kv_indptr, w.kv_indices, w.kv_len, w.sm_scale)
+    compare(out, lse, *ref, TOL_FP8)
+
+
+# ---------------------------------------------------------------------------
+# token-sparse decode over the records (MODEL1_FP8Sparse)
+# ---------------------------------------------------------------------------
+
+SPARSE_CASES = [
+    # (tokens, heads, slots, topk, invalid every, topk_length, sink, force_splits)
+    (6, 32, 700, 96, 7, False, True, 2),
+    (4, 128, 3000, 2048, 0, True, False, 0),
+    (5, 64, 50, 130, 3, True, True, 3),      # more entries than rows: repeats
+    (3, 128, 900, 64, 1, False, False, 0),   # every entry invalid: empty lists
+]
+
+
+@pytest.mark.parametrize("case", SPARSE_CASES, ids=[f"T{c[0]}-H{c[1]}-n{c[2]}-k{c[3]}-s{c[7]}" for c in SPARSE_CASES])
+def test_sparse_decode_model1(mla, case):
+    T, H, n_slots, topk, inv, use_len, use_sink, fs = case
+    say(f"model1 sparse: T={T} H={H} slots={n_slots} topk={topk} invalid every {inv} lengths={use_len} "
+        f"sink={use_sink} splits={fs}")
+    g = torch.Generator().manual_seed(77 + T + H)
+    src = torch.randn((n_slots, 512), generator=g).to(torch.bfloat16)
+    rec = quantize_model1_records(src)
+    q = torch.randn((T, H, 512), generator=g).to(torch.bfloat16)
+    idx = torch.randint(0, n_slots, (T, topk), generator=g, dtype=torch.int64).to(torch.int32)
+    if inv == 1:
+        idx[:] = -1
+    elif inv:
+        idx[:, ::inv] = -1
+        idx[:, 1::2 * inv] = n_slots  # past the pool end: invalid too
+    tl = torch.randint(0, topk + 1, (T,), generator=g, dtype=torch.int64).to(torch.int32) if use_len else None
+    sink = (torch.randn(H, generator=g) + 4.0).to(torch.float32) if use_sink else None
+    scale = 0.07
+    plan = mla.mla_sparse_plan_create(T, H, n_slots, topk, kv_format=mla.MLA_KV_FP8_MODEL1, force_splits=fs)
+    out, lse, mx = mla.mla_sparse_decode_model1(plan, q.to(DEV), rec.to(DEV), idx.to(DEV), scale,
+                                                topk_length=None if tl is None else tl.to(DEV),
+                                                attn_sink=None if sink is None else sink.to(DEV))
+    torch.cuda.synchronize()
+    ref_o, ref_l, ref_m = oracle.mla_sparse_decode_model1_ref(q, rec, idx.numpy(), scale,
+                                                              topk_length=None if tl is None else tl.numpy(),
+                                                              attn_sink=None if sink is None else sink.numpy())
+    compare(out, lse, ref_o, ref_l, TOL_FP8, mx=mx, ref_m=ref_m)
+
+
+# ---------------------------------------------------------------------------
+# the BF16 dequantisation utility (dequantize_k_cache) and attention over it
+# ---------------------------------------------------------------------------
+
 def test_expand_records_bit_exact(mla):
-    say("model1: record expansion, 2 requests, page size 16")
-    w = make_model1_workload([300, 5], heads=2, page_size=16, seed=21)
+    say("model1: BF16 record expansion, 2 requests, page size 16")
+    w = make_model1_workload([300, 5], heads=2, page_size=16, seed=21, poison=False)
     rec = w.records.clone()
     # hand-placed codes: subnormals, the largest code, signed zeros, a zero tile
     rec[0, 0, :8] = torch.tensor([0x01, 0x81, 0x07, 0x7E, 0xFE, 0x00, 0x80, 0x38], dtype=torch.uint8)
@@ -49,7 +190,7 @@ def test_expand_records_bit_exact(mla):
     rows = mla.mla_model1_expand_records(rec.to(DEV))
     torch.cuda.synchronize()
     got = rows.cpu().view(torch.int16).numpy()
-    nope, rope = oracle.model1_record_decode(rec)
+    nope, rope = oracle.model1_dequantize_bf16(rec)
     assert np.array_equal(got[..., :448], bf16_bits(nope))
     assert (got[..., 448:512] == 0).all()
     assert np.array_equal(got[..., 512:], rec[..., 476:].contiguous().view(torch.int16).numpy())
@@ -64,19 +205,9 @@ def test_expand_q_bit_exact(mla):
     assert torch.equal(q576[..., 512:].view(torch.int16), q[..., 448:].view(torch.int16))
 
 
-CASES = [
-    # (heads, page_size, kv_lens, tile_mode, force_splits)
-    (16, 64, [1, 37, 64, 200], 0, 0),
-    (16, 16, [5, 300, 0, 1], 2, 3),
-    (128, 16, [700, 3, 65], 1, 3),
-    (128, 64, [1000, 1, 257], 0, 0),
-]
-
-
-@pytest.mark.parametrize("case", CASES, ids=[f"H{c[0]}-ps{c[1]}-m{c[3]}-s{c[4]}" for c in CASES])
-def test_decode_over_expanded_records(mla, case):
-    H, ps, lens, mode, fs = case
-    say(f"model1 decode H={H} page_size={ps} lens={lens} tile_mode={mode} force_splits={fs}")
+@pytest.mark.parametrize("H,ps,lens,mode,fs", [(16, 16, [5, 300, 0, 1], 2, 3), (128, 64, [1000, 1, 257], 0, 0)])
+def test_decode_over_bf16_dequantised_rows(mla, H, ps, lens, mode, fs):
+    say(f"model1 decode over BF16-dequantised rows H={H} page_size={ps} lens={lens}")
     w = make_model1_workload(lens, heads=H, page_size=ps, seed=40 + H + ps)
     rows = mla.mla_model1_expand_records(w.records.to(DEV))
     q576 = mla.mla_model1_expand_q(w.q.to(DEV))
@@ -84,54 +215,12 @@ def test_decode_over_expanded_records(mla, case):
                                tile_mode=mode, force_splits=fs)
     out, lse = mla.mla_decode_packed(plan, q576, rows, w.kv_indptr.to(DEV), w.kv_indices.to(DEV), w.sm_scale)
     torch.cuda.synchronize()
-    ref_o, ref_l = oracle.mla_decode_model1_ref(w.q, w.records, w.kv_indptr, w.kv_indices, w.kv_len, w.sm_scale)
-    o = out.double().cpu().numpy()
-    l = lse.double().cpu().numpy()
-    assert (o[..., 448:] == 0).all()
-    o = o[..., :448]
-    empty = np.isneginf(ref_l)
-    assert np.array_equal(np.isneginf(l), empty) and np.all(o[empty] == 0)
-    err = np.abs(o - ref_o).max()
-    rel = np.linalg.norm(o - ref_o) / np.linalg.norm(ref_o)
-    lerr = np.abs(l[~empty] - ref_l[~empty]).max()
-    say(f"    max|dout|={err:.3e} relL2={rel:.3e} max|dlse|={lerr:.3e}")
-    assert err <= TOL["max_abs"] and rel <= TOL["rel_l2"] and lerr <= TOL["lse"]
-
-
-def test_sparse_attention_over_expanded_records(mla):
-    """The token-sparse form (MODEL1_FP8Sparse): per-query key lists with
-    invalid entries, an attention sink and forced splits, over rows expanded
-    from MODEL1 records, against the oracle's sparse attention over its own
-    dequantised keys (widened with zeros in dims 448..511, the form the
-    dense MODEL1 oracle test pins as the same attention)."""
-    from workloads import quantize_model1_records
-
-    say("model1 sparse: s_q=6 H=32 s_kv=700 topk=96, sink, 2 splits")
-    g = torch.Generator().manual_seed(77)
-    s_q, H, s_kv, topk = 6, 32, 700, 96
-    src = torch.randn((s_kv, 512), generator=g).to(torch.bfloat16)
-    rec = quantize_model1_records(src)
-    q = torch.randn((s_q, H, 512), generator=g).to(torch.bfloat16)
-    idx = torch.randint(0, s_kv, (s_q, topk), generator=g, dtype=torch.int64).to(torch.int32)
-    idx[:, ::7] = -1
-    sink = (torch.randn(H, generator=g) + 4.0).to(torch.float32)
-    scale = 0.07
-    rows = mla.mla_model1_expand_records(rec.to(DEV))
-    q576 = mla.mla_model1_expand_q(q.to(DEV))
-    plan = mla.mla_sparse_plan_create(s_q, H, s_kv, topk, kv_format=mla.MLA_KV_BF16, force_splits=2)
-    out, lse, mx = mla.mla_sparse_prefill(plan, q576, rows, idx.to(DEV), scale, attn_sink=sink.to(DEV))
-    torch.cuda.synchronize()
-    nope, rope = oracle.model1_record_decode(rec)
-    kv = np.zeros((s_kv, 576))
-    kv[:, :448], kv[:, 512:] = nope, rope
-    qq = np.zeros((s_q, H, 576))
-    qq[..., :448], qq[..., 512:] = q[..., :448].double().numpy(), q[..., 448:].double().numpy()
-    ref_o, ref_l, ref_m = oracle.mla_sparse_prefill_ref(qq, kv, idx.numpy(), scale, attn_sink=sink.numpy())
-    o = out.double().cpu().numpy()
-    assert (o[..., 448:] == 0).all()
-    err = np.abs(o[..., :448] - ref_o[..., :448]).max()
-    rel = np.linalg.norm(o[..., :448] - ref_o[..., :448]) / np.linalg.norm(ref_o[..., :448])
-    lerr = np.abs(lse.double().cpu().numpy() - ref_l).max()
-    merr = np.abs(mx.double().cpu().numpy() - ref_m).max()
-    say(f"    max|dout|={err:.3e} relL2={rel:.3e} max|dlse|={lerr:.3e} max|dmax|={merr:.3e}")
-    assert err <= TOL["max_abs"] and rel <= TOL["rel_l2"] and lerr <= TOL["lse"] and merr <= TOL["lse"]
+    # the plain attention oracle over the BF16 keys, widened with zeros in dims 448..511
+    nope, rope = oracle.model1_dequantize_bf16(w.records)
+    ckv = np.zeros(w.records.shape[:2] + (512,))
+    ckv[..., :M1] = np.nan_to_num(nope)
+    qn = np.zeros((w.batch, H, 512))
+    qn[..., :M1] = w.q[..., :M1].double().numpy()
+    ref_o, ref_l = oracle.mla_decode_ref(qn, w.q[..., M1:].double().numpy(), ckv, np.nan_to_num(rope), w.kv_indptr,
+                                         w.kv_indices, w.kv_len, w.sm_scale)
+    compare(out, lse, ref_o[..., :M1], ref_l, TOL_BF16)

@@ -223,7 +223,9 @@ def _model1_pin_suite():
 
     checks = [
         m1.test_hand_built_record,
+        m1.test_hand_built_record_bf16_dequantisation,
         m1.test_round_trip_within_the_quantisation_bound,
+        m1.test_sparse_decode_matches_brute_force,
         m1.test_decode_matches_torch_sdpa_on_the_dequantised_keys,
         m1.test_input_quantiser_matches_the_oracle_encoder,
         m1.test_bf16_rounding_matches_torch_and_ties_go_to_even,
@@ -253,30 +255,53 @@ def _model1_decode_variant(mistake):
         rope_bytes = np.ascontiguousarray(flat[:, r0:r0 + 128]) if mistake != "rope_offset" else \
             np.ascontiguousarray(np.concatenate([flat[:, r0:REC], flat[:, M1 + 28:M1 + 30]], axis=1))
         rope = om.bf16_bits_to_f64(rope_bytes.view("<u2"))
-        vals = om.e4m3_decode(codes).astype(np.float32)
+        vals = om.e4m3_decode(codes)
         if mistake == "tile_128":
             tiles = np.repeat(scales[:, :4], 2, axis=1)[:, :7]  # each scale covering 128 dims
         else:
             tiles = scales
-        prod = (vals.reshape(-1, 7, 64) * tiles[:, :, None]).astype(np.float32)
-        if mistake == "no_bf16_rounding":
-            nope = prod.astype(np.float64).reshape(-1, M1)
-        elif mistake == "truncate":
-            u = prod.view(np.uint32) & np.uint32(0xFFFF0000)
-            nope = u.view(np.float32).astype(np.float64).reshape(-1, M1)
-        else:
-            nope = om.f32_to_bf16_rne(prod).reshape(-1, M1)
+        prod = vals.reshape(-1, 7, 64) * tiles.astype(np.float64)[:, :, None]
+        if mistake == "bf16_keys":  # the keys rounded as the page's BF16 utility returns them
+            prod = om.f32_to_bf16_rne(prod.astype(np.float32))
+        elif mistake == "fp32_product":
+            prod = prod.astype(np.float32).astype(np.float64)
+        nope = prod.reshape(-1, M1)
         return nope.reshape(*lead, M1), rope.reshape(*lead, 64)
 
     return decode
 
 
-@pytest.mark.parametrize("mistake", ["scale_offset", "rope_offset", "tile_128", "no_bf16_rounding", "truncate"])
+def _model1_bf16_variant(mistake):
+    exact = om.model1_record_decode
+
+    def dequant(records):
+        nope, rope = exact(records)
+        prod = nope.astype(np.float32)
+        if mistake == "no_bf16_rounding":
+            out = prod.astype(np.float64)
+        else:  # truncate instead of rounding
+            u = prod.view(np.uint32) & np.uint32(0xFFFF0000)
+            out = u.view(np.float32).astype(np.float64)
+        return out, rope
+
+    return dequant
+
+
+@pytest.mark.parametrize("mistake", ["scale_offset", "rope_offset", "tile_128", "bf16_keys", "fp32_product"])
 def test_model1_record_mistakes_are_caught(monkeypatch, mistake):
     assert _model1_pin_suite() == 0  # the real decoder passes every pin
     bad = _model1_decode_variant(mistake)
     monkeypatch.setattr(om, "model1_record_decode", bad)
     monkeypatch.setattr(oracle, "model1_record_decode", bad)
+    assert _model1_pin_suite() > 0
+
+
+@pytest.mark.parametrize("mistake", ["no_bf16_rounding", "truncate"])
+def test_model1_bf16_dequantisation_mistakes_are_caught(monkeypatch, mistake):
+    assert _model1_pin_suite() == 0
+    bad = _model1_bf16_variant(mistake)
+    monkeypatch.setattr(om, "model1_dequantize_bf16", bad)
+    monkeypatch.setattr(oracle, "model1_dequantize_bf16", bad)
     assert _model1_pin_suite() > 0
 
 

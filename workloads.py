@@ -462,9 +462,12 @@ class Model1Workload:
 
 def make_model1_workload(kv_lens=None, *, batch: Optional[int] = None, heads: int = 16, page_size: int = 64, seed: int = 0,
                          device: Union[str, torch.device] = "cpu", pool_factor: int = 2,
-                         sm_scale: float = SM_SCALE_DEFAULT, name: str = "custom_model1") -> Model1Workload:
+                         sm_scale: float = SM_SCALE_DEFAULT, name: str = "custom_model1",
+                         poison: bool = True) -> Model1Workload:
     """Decode over MODEL1 records: lengths -> page permutation -> q -> source
-    pool (bf16 N(0,1), 512 dims per token) -> records, in that draw order."""
+    pool (bf16 N(0,1), 512 dims per token) -> records, in that draw order.
+    With ``poison`` every record no request reads (unused pages, tail slots)
+    is all 0xFF bytes: NaN codes, NaN scales and NaN RoPE values."""
     if kv_lens is None:
         spec = dict(MODEL1_CONFIGS[name])
         seed, batch, heads = spec["seed"], spec["batch"], spec["heads"]
@@ -485,6 +488,17 @@ def make_model1_workload(kv_lens=None, *, batch: Optional[int] = None, heads: in
     src = _randn_bf16((pool_pages, page_size, MODEL1_NOPE + HEAD_DIM_KPE), gv, device,
                       chunk_rows=max(1, 65536 // page_size))
     records = quantize_model1_records(src)
+    del src
+    kv_indices = perm[:needed].clone()
+    if poison:
+        live = torch.zeros(pool_pages * page_size, dtype=torch.bool)
+        for b in range(batch):
+            L = int(lens[b])
+            pg = kv_indices[int(kv_indptr[b]):int(kv_indptr[b + 1])].to(torch.int64)
+            slots = (pg[:, None] * page_size + torch.arange(page_size)[None, :]).reshape(-1)[:L]
+            live[slots] = True
+        dead = (~live).nonzero().reshape(-1).to(device)
+        records.view(-1, MODEL1_RECORD_BYTES)[dead] = 0xFF
     return Model1Workload(name=name, batch=batch, num_heads=heads, page_size=page_size, num_pages=pool_pages,
-                          q=q, records=records, kv_indptr=kv_indptr, kv_indices=perm[:needed].clone(),
+                          q=q, records=records, kv_indptr=kv_indptr, kv_indices=kv_indices,
                           kv_len=lens.to(torch.int32), sm_scale=sm_scale, seed=seed)
