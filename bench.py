@@ -138,9 +138,10 @@ def write_counters(config_name, pmc_dir, copy_bytes, commands):
     wv = _pmc_values(os.path.join(pmc_dir, "write"), "mla_attn")
     fetch_b = statistics.median(fv) * 1024 * f_fetch
     write_b = statistics.median(wv) * 1024 * f_write
+    activity = _activity_lines(os.path.join(pmc_dir, "sq"))
     path = os.path.join(ROOT, "profiles", f"attention_{config_name}_counters.txt")
     with open(path, "w") as fo:
-        fo.write(f"# HBM traffic of the attention kernel, workload {config_name}\n")
+        fo.write(f"# HBM traffic and matrix-core / LDS activity of the attention kernel, workload {config_name}\n")
         fo.write("# rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (KiB per dispatch), median over dispatches,\n")
         fo.write(f"# scaled by the same counters on a plain copy kernel of {copy_bytes} bytes read + written\n")
         for c in commands:
@@ -153,7 +154,48 @@ def write_counters(config_name, pmc_dir, copy_bytes, commands):
         fo.write(f"hbm_fetch_bytes_per_launch: {fetch_b:.0f}\n")
         fo.write(f"hbm_write_bytes_per_launch: {write_b:.0f}\n")
         fo.write(f"hbm_bytes_per_launch: {fetch_b + write_b:.0f}\n")
+        for line in activity:
+            fo.write(line + "\n")
     return path
+
+
+def _activity_lines(sq_dir):
+    """Matrix-core and LDS activity of the attention kernel from one
+    rocprofv3 --pmc run of SQ counters (medians over dispatches):
+    SQ_VALU_MFMA_BUSY_CYCLES (cycles, summed over SIMDs), SQ_WAVE_CYCLES
+    (quad-cycles, summed over waves; one wave per SIMD here, so 4x it is the
+    SIMD-cycles the waves were resident), SQ_LDS_IDX_ACTIVE and
+    SQ_LDS_BANK_CONFLICT (LDS cycles, summed over CUs), instruction counts.
+    Empty when the run is absent."""
+    import csv
+    import glob
+    import statistics
+
+    per = {}
+    for f in glob.glob(os.path.join(sq_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if "mla_attn" not in r.get("Kernel_Name", ""):
+                continue
+            key = (r["Dispatch_Id"], r["Counter_Name"])
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    if not per:
+        return []
+    names = sorted({k[1] for k in per})
+    med = {n: statistics.median([v for (d, c), v in per.items() if c == n]) for n in names}
+    out = ["# activity: rocprofv3 --pmc SQ counters of the same kernel (median per dispatch)"]
+    out += [f"{n}: {med[n]:.0f}" for n in names]
+    busy, waves = med.get("SQ_VALU_MFMA_BUSY_CYCLES"), med.get("SQ_WAVE_CYCLES")
+    if busy is not None and waves:
+        out.append(f"mfma_busy_per_resident_simd_cycle: {busy / (4.0 * waves):.4f}")
+    conf, act = med.get("SQ_LDS_BANK_CONFLICT"), med.get("SQ_LDS_IDX_ACTIVE")
+    if conf is not None and act:
+        out.append(f"lds_bank_conflict_share_of_lds_active_cycles: {conf / act:.4f}")
+    if act is not None and waves:
+        out.append(f"lds_active_cycles_per_resident_cu_cycle: {act / waves:.4f}")
+    vi, mi = med.get("SQ_INSTS_VALU"), med.get("SQ_INSTS_MFMA")
+    if vi is not None and mi:
+        out.append(f"valu_instructions_per_mfma: {(vi - mi) / mi:.2f}")
+    return out
 
 
 def copy_calibration(nbytes):
