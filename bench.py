@@ -614,11 +614,15 @@ def main():
             mla.mla_record_attention_events(kb[i], ke[i])
         step(args.warmup + i)
     t_end.record()
+    issued = time.perf_counter() - wall0
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t_start.elapsed_time(t_end) / args.steps
     attn_ms = sorted(ev.elapsed_ms(kb[i], ke[i]) for i in sampled)
     attn_avg = sum(attn_ms) / len(attn_ms)
+    # host time to issue a step: when it approaches the step time, the
+    # launches (not the GPU) set the pace
+    log(f"bench: host issue {issued / args.steps * 1e6:.1f} us/step")
     log(f"bench: {ms_step * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us), attention kernel avg "
         f"{attn_avg * 1e3:.1f} us (p10 {attn_ms[len(attn_ms) // 10] * 1e3:.1f}, "
         f"p90 {attn_ms[(9 * len(attn_ms)) // 10] * 1e3:.1f})")

@@ -18,6 +18,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <new>
+#include <utility>
 #include <vector>
 
 #include "mla_internal.h"
@@ -146,6 +147,53 @@ void pack_units(mla_plan* p, const std::vector<Unit>& units, int64_t budget) {
   p->grid = p->num_wgs;
 }
 
+// Modeled cost of the longest list of a packing, in key-token units: each
+// item costs its stages plus the fixed per-item cost.
+int64_t max_list_cost(const mla_plan* p) {
+  int64_t worst = 0;
+  for (size_t w = 0; w + 1 < p->wg_ptr.size(); ++w) {
+    int64_t c = 0;
+    for (int32_t i = p->wg_ptr[w]; i < p->wg_ptr[w + 1]; ++i) {
+      const WorkItem& it = p->items[i];
+      c += kItemOverhead + (it.tok1 - it.tok0 + mla::kStageTokens - 1) / mla::kStageTokens * mla::kStageTokens;
+    }
+    worst = std::max(worst, c);
+  }
+  return worst;
+}
+
+// One item per list: every unit is cut into the fewest pieces of at most
+// `k` stages, its stages spread evenly over them, and each piece is a list of
+// its own (units in order, so a unit's pieces sit on neighbouring lists).
+// All lists then start at once and no list pays two item costs; the units of
+// one request that see the same keys (its query tokens) walk them at the
+// same time on neighbouring lists, which share an XCD and its L2.
+void pack_even(mla_plan* p, const std::vector<Unit>& units, int64_t k) {
+  const int64_t stage = mla::kStageTokens;
+  p->items.clear();
+  p->groups.clear();
+  p->wg_ptr.assign(1, 0);
+  p->num_slots = 0;
+  for (const Unit& u : units) {
+    const int64_t ns = std::max<int64_t>(1, (u.vis + stage - 1) / stage);
+    const int64_t n = (ns + k - 1) / k;
+    int64_t t = 0;
+    for (int64_t j = 0; j < n; ++j) {
+      const int64_t e = std::min<int64_t>(u.vis, t + (ns / n + (j < ns % n ? 1 : 0)) * stage);
+      p->items.push_back({u.b, u.row0, u.nrows, (int32_t)t, (int32_t)e, u.kv_len, u.q_len,
+                          n > 1 ? p->num_slots + (int32_t)j : -1});
+      p->wg_ptr.push_back((int32_t)p->items.size());
+      t = e;
+    }
+    if (n > 1) {
+      p->groups.push_back({u.b, u.row0, u.nrows, (int32_t)n, p->num_slots, u.q_len, {0, 0}});
+      p->num_slots += (int32_t)n;
+    }
+  }
+  p->num_wgs = (int32_t)p->wg_ptr.size() - 1;
+  p->grid = p->num_wgs;
+}
+
 mla_status build_schedule(mla_plan* p, const std::vector<int32_t>& kv_len,
                           const std::vector<int32_t>& q_len, int32_t num_cus) {
   const mla_plan_desc& d = p->d;
@@ -209,6 +257,31 @@ mla_status build_schedule(mla_plan* p, const std::vector<int32_t>& kv_len,
     budget += iter < 400 ? std::max<int64_t>(16, budget / 256) : budget;
   }
   if (p->num_wgs > cus) return MLA_ERR_INVALID_ARGUMENT;  // unreachable: the loop exits only when they fit
+  // The one-item-per-list packing with the smallest piece bound that fits,
+  // when its longest list is modeled no longer than the greedy packing's.
+  if (d.force_splits == 0) {
+    int64_t k = 1;
+    for (const Unit& u : units) k = std::max<int64_t>(k, (u.vis + mla::kStageTokens - 1) / mla::kStageTokens);
+    auto pieces = [&](int64_t kk) {
+      int64_t n = 0, most = 0;
+      for (const Unit& u : units) {
+        const int64_t ns = std::max<int64_t>(1, (u.vis + mla::kStageTokens - 1) / mla::kStageTokens);
+        n += (ns + kk - 1) / kk;
+        most = std::max<int64_t>(most, (ns + kk - 1) / kk);
+      }
+      return std::make_pair(n, most);
+    };
+    if (pieces(k).first <= cus) {
+      // pieces(kk).first only grows as kk shrinks: bisect for the smallest kk that fits
+      int64_t lo = 0, hi = k;  // pieces(hi) fits; lo does not (or is 0)
+      while (hi - lo > 1) {
+        const int64_t mid = (lo + hi) / 2;
+        if (pieces(mid).first <= cus) hi = mid; else lo = mid;
+      }
+      const bool splits_ok = d.max_splits <= 0 || pieces(hi).second <= d.max_splits;
+      if (splits_ok && kItemOverhead + hi * mla::kStageTokens < max_list_cost(p)) pack_even(p, units, hi);
+    }
+  }
   if (p->tile_mode == MLA_TILE_QUAD) {
     p->grid = p->xcd_map ? (int32_t)cus * p->group_size : p->num_wgs * p->group_size;
   }
