@@ -241,10 +241,16 @@ __device__ __forceinline__ void dma16_vx(const void* vaddr, uint32_t lds, uint32
       : "=&s"(save), "=&s"(save_exec)
       : "v"(vaddr), "s"(lds), "s"(lo), "s"(hi));
 }
+// `on` is wave-uniform; readfirstlane keeps it in an SGPR for the asm operand
+// wherever the compiler had moved it to a VGPR.
 __device__ __forceinline__ void dma16_on(const void* sbase, uint32_t voff, uint32_t lds, uint32_t on) {
+  on = __builtin_amdgcn_readfirstlane(on);
   dma16_x(sbase, voff, lds, on, on);
 }
-__device__ __forceinline__ void dma16_v_on(const void* vaddr, uint32_t lds, uint32_t on) { dma16_vx(vaddr, lds, on, on); }
+__device__ __forceinline__ void dma16_v_on(const void* vaddr, uint32_t lds, uint32_t on) {
+  on = __builtin_amdgcn_readfirstlane(on);
+  dma16_vx(vaddr, lds, on, on);
+}
 
 // The lane id, re-materialised where it is used: values derived from it are
 // cheap to recompute, and keeping them live across the stage loop only
@@ -933,17 +939,16 @@ __device__ __forceinline__ void wide_epilogue(const AttnArgs& a, const WorkItem&
         *(LDS_AS bf16x4*)(ob + n * kCkvRowBytes + ((chunk ^ (n & 7)) << 4) + 8 * g) = h;
       }
     }
-    const size_t out_row0 = row_base(a, it) + it.row0 + wave * 32;  // output row of rr = 0
-#pragma unroll 4
-    for (int rr = 0; rr < 32; ++rr) {
-      const u32x4 v = *(const LDS_AS u32x4*)(ob + rr * kCkvRowBytes + ((lane ^ (rr & 7)) << 4));
-      if (wave * 32 + rr < it.nrows) {
-        __bf16* dst = (it.slot < 0)
-                          ? (__bf16*)a.out + (out_row0 + rr) * kDimCkv
-                          : a.part_o + ((size_t)it.slot * a.rows_per_block + wave * 32 + rr) * kDimCkv;
-        *(u32x4*)(dst + 8 * lane) = v;
-      }
-    }
+    // all reads first, then the stores (see ds_epilogue)
+    u32x4 v[32];
+#pragma unroll
+    for (int rr = 0; rr < 32; ++rr) v[rr] = *(const LDS_AS u32x4*)(ob + rr * kCkvRowBytes + ((lane ^ (rr & 7)) << 4));
+    __bf16* dst = (it.slot < 0 ? (__bf16*)a.out + (row_base(a, it) + it.row0) * kDimCkv
+                               : a.part_o + (size_t)it.slot * a.rows_per_block * kDimCkv) +
+                  (size_t)wave * 32 * kDimCkv + 8 * lane;
+#pragma unroll
+    for (int rr = 0; rr < 32; ++rr)
+      if (wave * 32 + rr < it.nrows) *(u32x4*)(dst + rr * kDimCkv) = v[rr];
     __syncthreads();  // the staging rows overlap the next item's first stage
     return;
   }
@@ -1119,7 +1124,9 @@ __device__ __forceinline__ void ds_stage(const AttnArgs& a, const bf16x8 (&qf)[3
     done(st.l_run);
   };
 
-  auto qk = [&](f32x16& sacc, int tb, int dma0, auto&& side) {
+  // The next stage's 18 direct-load slices: one every `dstep` k-steps from
+  // slice dma0 up to (not including) dend.
+  auto qk = [&](f32x16& sacc, int tb, int dma0, int dstep, int dend, auto&& side) {
     constexpr int KD = 3;  // K fragments in flight
     bf16x8 kr[KD];
 #pragma unroll
@@ -1127,8 +1134,7 @@ __device__ __forceinline__ void ds_stage(const AttnArgs& a, const bf16x8 (&qf)[3
 #pragma unroll
     for (int ks = 0; ks < 36; ++ks) {
       pin_loads();
-      if ((ks & 3) == 0 && dma0 + (ks >> 2) < StageLoader<kPC>::kSlices)
-        ld.issue(a, dma0 + (ks >> 2), wave);  // the next stage, 9 slices per sub-tile
+      if (ks % dstep == 0 && dma0 + ks / dstep < dend) ld.issue(a, dma0 + ks / dstep, wave);
       const bf16x8 k0 = kr[ks % KD];
       if (ks == 0) {
         mfma32_first<false>(sacc, k0, qf[0]);
@@ -1194,10 +1200,14 @@ __device__ __forceinline__ void ds_stage(const AttnArgs& a, const bf16x8 (&qf)[3
   bf16x8 pt0[2], pt1[2];
   LDS_AS char* p0 = smem + kDsPOff;
   LDS_AS char* p1 = cur + kStageCkvBytes;
-  qk(sa0, 0, 0, [&](int) {});
+  // Slices 0-8 ride along Q.K^T of sub-tile 0, 9-13 along sub-tile 1 and
+  // 14-17 along the first P.V: issued denser, the loads fill the CU's
+  // queue of outstanding misses and the issuing wave stalls in the middle
+  // of its MFMA chain; issued during the last P.V they land too late.
+  qk(sa0, 0, 0, 4, 9, [&](int) {});
 #pragma unroll
   for (int r = 0; r < 16; ++r) s0[r] = sa0[r];
-  qk(sa1, 32, 9, [&](int ks) {
+  qk(sa1, 32, 9, 8, 14, [&](int ks) {
     if (ks < 16) sm_scale_mask(s0, sm0, 0, ks);
     if (ks == 16) sm_decide(sm0);
     if (ks >= 17 && ks < 33) sm_exp(s0, sm0, pt0, ks - 17);
@@ -1208,6 +1218,7 @@ __device__ __forceinline__ void ds_stage(const AttnArgs& a, const bf16x8 (&qf)[3
   __syncthreads();  // A: P0 and its factors visible; every wave's Q.K^T of the stage is done
   rescale(0, false);
   pv(0, p0, [&](int i) {
+    if (i % 8 == 0) ld.issue(a, 14 + i / 8, wave);
     if (i < 16) sm_scale_mask(s1, sm1, 32, i);
     if (i == 16) sm_decide(sm1);
     if (i >= 17) sm_exp(s1, sm1, pt1, i - 17);
@@ -1256,17 +1267,22 @@ __device__ __forceinline__ void ds_epilogue(const AttnArgs& a, const WorkItem& i
         }
       }
     }
-    const size_t out_row0 = row_base(a, it) + it.row0;
+    // every read is issued before the first store: with one wave per SIMD
+    // nothing else hides the LDS latency of reads waited for one by one
     const int c = lane & 15;
-#pragma unroll 4
+    u32x4 v[32];
+#pragma unroll
     for (int i = 0; i < 32; ++i) {
       const int R = 4 * i + (lane >> 4);
-      const u32x4 v = *(const LDS_AS u32x4*)(ob + R * 256 + ((c ^ (R & 15)) << 4));
-      if (R < it.nrows) {
-        __bf16* dst = (it.slot < 0) ? (__bf16*)a.out + (out_row0 + R) * kDimCkv
-                                    : a.part_o + ((size_t)it.slot * a.rows_per_block + R) * kDimCkv;
-        *(u32x4*)(dst + 128 * wave + 8 * c) = v;
-      }
+      v[i] = *(const LDS_AS u32x4*)(ob + R * 256 + ((c ^ (R & 15)) << 4));
+    }
+    __bf16* dst = (it.slot < 0 ? (__bf16*)a.out + (row_base(a, it) + it.row0) * kDimCkv
+                               : a.part_o + (size_t)it.slot * a.rows_per_block * kDimCkv) +
+                  128 * wave + 8 * c;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const int R = 4 * i + (lane >> 4);
+      if (R < it.nrows) *(u32x4*)(dst + R * kDimCkv) = v[i];
     }
   } else {
 #pragma unroll
