@@ -939,16 +939,17 @@ __device__ __forceinline__ void wide_epilogue(const AttnArgs& a, const WorkItem&
         *(LDS_AS bf16x4*)(ob + n * kCkvRowBytes + ((chunk ^ (n & 7)) << 4) + 8 * g) = h;
       }
     }
-    // all reads first, then the stores (see ds_epilogue)
-    u32x4 v[32];
-#pragma unroll
-    for (int rr = 0; rr < 32; ++rr) v[rr] = *(const LDS_AS u32x4*)(ob + rr * kCkvRowBytes + ((lane ^ (rr & 7)) << 4));
-    __bf16* dst = (it.slot < 0 ? (__bf16*)a.out + (row_base(a, it) + it.row0) * kDimCkv
-                               : a.part_o + (size_t)it.slot * a.rows_per_block * kDimCkv) +
-                  (size_t)wave * 32 * kDimCkv + 8 * lane;
-#pragma unroll
-    for (int rr = 0; rr < 32; ++rr)
-      if (wave * 32 + rr < it.nrows) *(u32x4*)(dst + rr * kDimCkv) = v[rr];
+    const size_t out_row0 = row_base(a, it) + it.row0 + wave * 32;  // output row of rr = 0
+#pragma unroll 4
+    for (int rr = 0; rr < 32; ++rr) {
+      const u32x4 v = *(const LDS_AS u32x4*)(ob + rr * kCkvRowBytes + ((lane ^ (rr & 7)) << 4));
+      if (wave * 32 + rr < it.nrows) {
+        __bf16* dst = (it.slot < 0)
+                          ? (__bf16*)a.out + (out_row0 + rr) * kDimCkv
+                          : a.part_o + ((size_t)it.slot * a.rows_per_block + wave * 32 + rr) * kDimCkv;
+        *(u32x4*)(dst + 8 * lane) = v;
+      }
+    }
     __syncthreads();  // the staging rows overlap the next item's first stage
     return;
   }
