@@ -109,6 +109,32 @@ def test_prefill_schedule_covers_visible_keys(mla, causal):
     _check_cover(plan, lens, qlens, 128, causal=causal, prefill=True)
 
 
+def test_prefill_gangs_walk_keys_together(mla):
+    """The query tokens of a prefill request (one 128-row block each) get the
+    same key pieces, at the same position of neighbouring lists."""
+    rng = np.random.default_rng(11)
+    B = 32
+    qlens = rng.integers(1, 9, B)
+    lens = rng.integers(1024, 4097, B)
+    qo = np.concatenate([[0], np.cumsum(qlens)])
+    indptr = np.concatenate([[0], np.cumsum(-(-lens // 64))])
+    plan = mla.mla_plan_create(1, B, 128, 64, int(indptr[-1]), lens, indptr, qo_indptr=qo, causal=True,
+                               num_cus=256)
+    items, ptr = _check_cover(plan, lens, qlens, 128, causal=True, prefill=True)
+    where = {}  # (b, row0) -> [(list, position, t0)]
+    for w in range(len(ptr) - 1):
+        for pos, it in enumerate(items[ptr[w]:ptr[w + 1]]):
+            where.setdefault((it["b"], it["row0"]), []).append((w, pos, it["t0"]))
+    ganged = 0
+    for b in range(B):
+        seqs = [sorted(where[(b, 128 * j)]) for j in range(qlens[b])]
+        for j in range(1, qlens[b]):
+            assert [(pos, t0) for _, pos, t0 in seqs[j]] == [(pos, t0) for _, pos, t0 in seqs[0]]
+            assert [w for w, _, _ in seqs[j]] == [w + j for w, _, _ in seqs[0]]
+            ganged += 1
+    assert ganged == int(np.sum(qlens - 1))
+
+
 def test_forced_splits(mla):
     lens = np.array([1, 37, 64, 200, 1000])
     indptr = np.concatenate([[0], np.cumsum(-(-lens // 64))])
