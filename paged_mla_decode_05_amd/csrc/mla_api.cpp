@@ -203,9 +203,11 @@ void pack_even(mla_plan* p, const std::vector<Unit>& units, int64_t k) {
 // becomes w real lists, one per row block, with the same pieces.  The w
 // lists of a request then walk the same key ranges at the same time on
 // neighbouring workgroups, which share an XCD: its L2 serves the keys to w
-// workgroups from one HBM read.  Returns false (p untouched) when no request
-// has two row blocks with visible key counts within one stage of each other.
-bool pack_gangs(mla_plan* p, const std::vector<Unit>& units, int64_t cus) {
+// workgroups from one HBM read.  Gangs wider than `cap` are cut into
+// sub-gangs of at most `cap` blocks (fewer widths pack with less waste).
+// Returns false (p untouched) when no request has two row blocks with
+// visible key counts within one stage of each other.
+bool pack_gangs(mla_plan* p, const std::vector<Unit>& units, int64_t cus, int32_t cap) {
   const int64_t stage = mla::kStageTokens;
   // gangs: runs of units of one request whose visible key counts differ by
   // less than a stage; anything else is a gang of one
@@ -219,8 +221,15 @@ bool pack_gangs(mla_plan* p, const std::vector<Unit>& units, int64_t cus) {
       if (h2 - l2 >= stage) break;
       lo = l2, hi = h2, ++j;
     }
-    gangs.push_back({i, j - i, hi});
-    widest = std::max(widest, j - i);
+    const int32_t n = (j - i + cap - 1) / cap;  // sub-gangs of near-equal width
+    for (int32_t k = 0, f = i; k < n; ++k) {
+      const int32_t w = (j - i) / n + (k < (j - i) % n ? 1 : 0);
+      int32_t v = 0;
+      for (int32_t m = f; m < f + w; ++m) v = std::max(v, units[m].vis);
+      gangs.push_back({f, w, v});
+      widest = std::max(widest, w);
+      f += w;
+    }
     i = j;
   }
   if (widest < 2) return false;
@@ -378,22 +387,30 @@ mla_status build_schedule(mla_plan* p, const std::vector<int32_t>& kv_len,
       if (splits_ok && kItemOverhead + hi * mla::kStageTokens < max_list_cost(p)) pack_even(p, units, hi);
     }
   }
-  // Gang packing (prefill): preferred unless its longest list is modeled
+  // Gang packing (prefill): the gang width cap with the shortest modeled
+  // longest list (the widest on ties), preferred unless that list is modeled
   // kGangSlack longer than the packing chosen so far.  Lists that share their
   // keys through L2 ran their stages about 14% faster on the 128-head causal
   // prefill than the model, which counts HBM-fed stages, assumes.
   if (d.kind == MLA_KIND_PREFILL && d.force_splits == 0 && d.max_splits == 0 && mode == MLA_TILE_WIDE) {
     const int64_t before = max_list_cost(p);
-    mla_plan alt;
-    alt.d = p->d;
-    alt.rows_per_block = p->rows_per_block;
-    if (pack_gangs(&alt, units, cus) && (double)max_list_cost(&alt) <= kGangSlack * (double)before) {
-      p->items.swap(alt.items);
-      p->groups.swap(alt.groups);
-      p->wg_ptr.swap(alt.wg_ptr);
-      p->num_slots = alt.num_slots;
-      p->num_wgs = alt.num_wgs;
-      p->grid = alt.grid;
+    mla_plan best;
+    int64_t best_cost = -1;
+    for (int32_t cap = 8; cap >= 2; --cap) {
+      mla_plan alt;
+      alt.d = p->d;
+      alt.rows_per_block = p->rows_per_block;
+      if (!pack_gangs(&alt, units, cus, cap)) break;
+      const int64_t c = max_list_cost(&alt);
+      if (best_cost < 0 || c < best_cost) best = std::move(alt), best_cost = c;
+    }
+    if (best_cost >= 0 && (double)best_cost <= kGangSlack * (double)before) {
+      p->items.swap(best.items);
+      p->groups.swap(best.groups);
+      p->wg_ptr.swap(best.wg_ptr);
+      p->num_slots = best.num_slots;
+      p->num_wgs = best.num_wgs;
+      p->grid = best.grid;
     }
   }
   if (p->tile_mode == MLA_TILE_QUAD) {
