@@ -1235,7 +1235,12 @@ __device__ __forceinline__ void ds_stage(const AttnArgs& a, const bf16x8 (&qf)[3
 // Dim-split WIDE epilogue: the row owners share 1 / l (and the output scale
 // of final rows) through LDS; each wave then writes its 128 dims of every
 // row.  bf16 rows are staged in LDS (256 bytes per row slice, 16-byte
-// chunks XOR-swizzled by row) and stored 4 rows per instruction.
+// chunks XOR-swizzled by row) and stored 4 rows per instruction.  A lane
+// writes 8 bytes (half a chunk); rows R with stage_half(R) = 1 keep their
+// two halves swapped, so that the 32 lanes of a write (rows n, n + 8,
+// n + 16, n + 24 on the same chunk position) fall on distinct banks; the
+// swap is undone on the way out, where it is known at compile time.
+__device__ __forceinline__ int stage_half(int R) { return ((R >> 3) ^ (R >> 4)) & 1; }
 __device__ __forceinline__ void ds_epilogue(const AttnArgs& a, const WorkItem& it, WideState& st,
                                             LDS_AS char* smem, int wave) {
   const int lane = lane_here();
@@ -1264,7 +1269,7 @@ __device__ __forceinline__ void ds_epilogue(const AttnArgs& a, const WorkItem& i
 #pragma unroll
           for (int e = 0; e < 4; ++e) h[e] = (__bf16)(st.o[4 * d + r][4 * q + e] * inv4[r]);
           const int c = 4 * d + q;  // 16-byte chunk of the 256-byte row slice
-          *(LDS_AS bf16x4*)(ob + R * 256 + ((c ^ (R & 15)) << 4) + 8 * g) = h;
+          *(LDS_AS bf16x4*)(ob + R * 256 + ((c ^ (R & 15)) << 4) + 8 * (g ^ stage_half(R))) = h;
         }
       }
     }
@@ -1276,6 +1281,7 @@ __device__ __forceinline__ void ds_epilogue(const AttnArgs& a, const WorkItem& i
     for (int i = 0; i < 32; ++i) {
       const int R = 4 * i + (lane >> 4);
       v[i] = *(const LDS_AS u32x4*)(ob + R * 256 + ((c ^ (R & 15)) << 4));
+      if (stage_half(4 * i)) v[i] = u32x4{v[i][2], v[i][3], v[i][0], v[i][1]};  // same for the 4 rows 4i..4i+3
     }
     __bf16* dst = (it.slot < 0 ? (__bf16*)a.out + (row_base(a, it) + it.row0) * kDimCkv
                                : a.part_o + (size_t)it.slot * a.rows_per_block * kDimCkv) +
