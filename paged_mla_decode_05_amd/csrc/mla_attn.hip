@@ -1318,11 +1318,12 @@ __device__ void ds_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* smem
   const RowInfo ri = row_info(a, it, wave * 32 + n);
   const int bound = row_key_bound(a, it, ri);
 
-  // Stage 0's direct loads first, then the query rows (unconditional: a
-  // missing row reads the item's first row and is masked by its bound of 0).
+  // The query rows first (unconditional: a missing row reads the item's
+  // first row and is masked by its bound of 0), then stage 0's direct loads,
+  // whose page lookups (two dependent scalar loads) the query loads need not
+  // wait for.  The first stage waits for both.
   const int page_base = ld_const(a.kv_indptr, it.b);
   const int nstage = (it.tok1 - it.tok0 + kStageTokens - 1) / kStageTokens;
-  if (nstage > 0) issue_stage_bf16<kPC>(a, smem, page_base, it.tok0, it.tok1, wave, lane);
   bf16x8 qf[36];
   {
     const __bf16* qn = (const __bf16*)a.q_nope + ri.qrow * a.q_stride + 8 * g;
@@ -1332,6 +1333,7 @@ __device__ void ds_item(const AttnArgs& a, const WorkItem& it, LDS_AS char* smem
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qf[32 + ks] = *(const bf16x8*)(qp + 16 * ks);
   }
+  if (nstage > 0) issue_stage_bf16<kPC>(a, smem, page_base, it.tok0, it.tok1, wave, lane);
   int kb[8], pb[4], vb[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) kb[k] = ckv_off(n, 2 * k + g);
