@@ -387,30 +387,26 @@ mla_status build_schedule(mla_plan* p, const std::vector<int32_t>& kv_len,
       if (splits_ok && kItemOverhead + hi * mla::kStageTokens < max_list_cost(p)) pack_even(p, units, hi);
     }
   }
-  // Gang packing (prefill): the gang width cap with the shortest modeled
-  // longest list (the widest on ties), preferred unless that list is modeled
-  // kGangSlack longer than the packing chosen so far.  Lists that share their
-  // keys through L2 ran their stages about 14% faster on the 128-head causal
+  // Gang packing (prefill): the widest gang width cap (the most query tokens
+  // sharing each key stage through L2) whose modeled longest list is within
+  // kGangSlack of the packing chosen so far.  Lists that share their keys
+  // through L2 ran their stages about 14% faster on the 128-head causal
   // prefill than the model, which counts HBM-fed stages, assumes.
   if (d.kind == MLA_KIND_PREFILL && d.force_splits == 0 && d.max_splits == 0 && mode == MLA_TILE_WIDE) {
-    const int64_t before = max_list_cost(p);
-    mla_plan best;
-    int64_t best_cost = -1;
+    const double limit = kGangSlack * (double)max_list_cost(p);
     for (int32_t cap = 8; cap >= 2; --cap) {
       mla_plan alt;
       alt.d = p->d;
       alt.rows_per_block = p->rows_per_block;
       if (!pack_gangs(&alt, units, cus, cap)) break;
-      const int64_t c = max_list_cost(&alt);
-      if (best_cost < 0 || c < best_cost) best = std::move(alt), best_cost = c;
-    }
-    if (best_cost >= 0 && (double)best_cost <= kGangSlack * (double)before) {
-      p->items.swap(best.items);
-      p->groups.swap(best.groups);
-      p->wg_ptr.swap(best.wg_ptr);
-      p->num_slots = best.num_slots;
-      p->num_wgs = best.num_wgs;
-      p->grid = best.grid;
+      if ((double)max_list_cost(&alt) > limit) continue;
+      p->items.swap(alt.items);
+      p->groups.swap(alt.groups);
+      p->wg_ptr.swap(alt.wg_ptr);
+      p->num_slots = alt.num_slots;
+      p->num_wgs = alt.num_wgs;
+      p->grid = alt.grid;
+      break;
     }
   }
   if (p->tile_mode == MLA_TILE_QUAD) {
