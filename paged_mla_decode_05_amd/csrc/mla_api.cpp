@@ -245,8 +245,14 @@ bool pack_gangs(mla_plan* p, const std::vector<Unit>& units, int64_t cus, int32_
   mla_plan tmp;
   tmp.d = p->d;
   std::vector<std::vector<std::vector<WorkItem>>> packed(widest + 1);  // [w][gang list] -> pieces
-  for (int64_t budget = std::max<int64_t>((total + cus - 1) / cus, kItemOverhead + kMinChunk);;) {
+  // Smallest budget whose packing fits in `cus` lists.  With one gang list
+  // per width class the count is the sum of the widths present; if even that
+  // does not fit, there is no gang packing.  Small steps first, then
+  // doubling ones, as in build_schedule, so the search always ends.
+  int64_t budget = std::max<int64_t>((total + cus - 1) / cus, kItemOverhead + kMinChunk);
+  for (int iter = 0;; ++iter) {
     int64_t lists = 0;
+    bool single = true;  // every class packed into one gang list
     for (int32_t w = 1; w <= widest; ++w) {
       packed[w].clear();
       if (cls[w].empty()) continue;
@@ -254,9 +260,11 @@ bool pack_gangs(mla_plan* p, const std::vector<Unit>& units, int64_t cus, int32_
       for (int32_t l = 0; l < tmp.num_wgs; ++l)
         packed[w].emplace_back(tmp.items.begin() + tmp.wg_ptr[l], tmp.items.begin() + tmp.wg_ptr[l + 1]);
       lists += (int64_t)w * tmp.num_wgs;
+      single = single && tmp.num_wgs == 1;
     }
     if (lists <= cus) break;
-    budget += std::max<int64_t>(16, budget / 256);
+    if (single) return false;
+    budget += iter < 400 ? std::max<int64_t>(16, budget / 256) : budget;
   }
   // expand: gang list -> w real lists; item.b holds the gang index until here
   p->items.clear();

@@ -138,6 +138,40 @@ def test_prefill_gangs_walk_keys_together(mla):
     assert ganged >= 0.6 * int(np.sum(qlens - 1))
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_prefill_schedules_cover_random_shapes(mla, seed):
+    """Random prefill shapes (every tile mode, causal or not, CU counts from 1
+    to 300): whichever packing the planner keeps (greedy, one item per list,
+    gangs), every visible key of every row block is covered exactly once."""
+    rng = np.random.default_rng(100 + seed)
+    B = int(rng.integers(1, 24))
+    H = int(rng.choice([16, 40, 64, 128, 256]))
+    qlens = rng.integers(0, 17, B)
+    lens = qlens + rng.integers(0, 3000, B)
+    qo = np.concatenate([[0], np.cumsum(qlens)])
+    ps = int(rng.choice([1, 16, 64]))
+    indptr = np.concatenate([[0], np.cumsum(-(-lens // ps))])
+    causal = bool(rng.integers(0, 2))
+    plan = mla.mla_plan_create(1, B, H, ps, int(max(1, indptr[-1])), lens, indptr, qo_indptr=qo, causal=causal,
+                               num_cus=int(rng.integers(1, 301)), tile_mode=int(rng.integers(0, 4)))
+    _check_cover(plan, lens, qlens, H, causal=causal, prefill=True)
+
+
+@pytest.mark.timeout(60)
+@pytest.mark.parametrize("num_cus", [1, 3, 7, 8, 9])
+def test_prefill_gangs_wider_than_the_machine(mla, num_cus):
+    """Requests with more query tokens (gang width) than there are lists: the
+    gang search gives up and the greedy plan is kept (this once looped)."""
+    qlens = np.array([16, 9, 1, 12])
+    lens = qlens + np.array([3000, 500, 70, 1200])
+    qo = np.concatenate([[0], np.cumsum(qlens)])
+    indptr = np.concatenate([[0], np.cumsum(-(-lens // 64))])
+    plan = mla.mla_plan_create(1, 4, 128, 64, int(indptr[-1]), lens, indptr, qo_indptr=qo, causal=True,
+                               num_cus=num_cus, tile_mode=1)
+    _, ptr = _check_cover(plan, lens, qlens, 128, causal=True, prefill=True)
+    assert len(ptr) - 1 <= num_cus
+
+
 def test_forced_splits(mla):
     lens = np.array([1, 37, 64, 200, 1000])
     indptr = np.concatenate([[0], np.cumsum(-(-lens // 64))])
