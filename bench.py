@@ -566,7 +566,7 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: this library has no multi-GPU path "
               "(one MI355X share of the workload is what it measures).", file=sys.stderr)
         sys.exit(2)
 

@@ -45,7 +45,7 @@ extern "C" {
 typedef enum mla_status {
   MLA_OK = 0,
   MLA_ERR_INVALID_ARGUMENT = -1, /* null pointer, bad size, inconsistent host arrays */
-  MLA_ERR_UNSUPPORTED = -2,      /* a shape or mode this build does not implement     */
+  MLA_ERR_UNSUPPORTED = -2,      /* a shape or mode this library does not implement   */
   MLA_ERR_WORKSPACE = -3,        /* workspace missing, misaligned or too small        */
   MLA_ERR_PLAN_MISMATCH = -4,    /* run call does not match the plan's kind / format  */
   MLA_ERR_DEVICE = -5            /* a HIP runtime call or kernel launch failed        */

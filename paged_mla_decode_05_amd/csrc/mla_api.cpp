@@ -689,7 +689,7 @@ struct Sparse {
 };
 
 // The opt-in device-array checks (desc.validate = 1): one small kernel, then
-// the stream is synchronised and its verdict read back, before anything
+// the stream is synchronised and its result read back, before anything
 // reads through the arrays.
 mla_status validate_arrays(const mla_plan* p, char* w, const int32_t* qo_indptr, const int32_t* kv_indptr,
                            const int32_t* kv_indices, const int32_t* live_kv_len, hipStream_t stream) {
