@@ -268,3 +268,53 @@ def test_capacity_live_lengths_are_validated(mla):
     # a capacity plan cannot run through the exact-length calls, nor an exact plan through the live ones
     with pytest.raises(mla.MLAError):
         mla.mla_decode(plan, x["q_nope"], x["q_pe"], x["ckv"], x["kpe"], x["kv_indptr"], x["kv_indices"], w.sm_scale)
+
+
+# ---------------------------------------------------------------------------
+# gang-packed prefill plans (128 heads, several query tokens per request:
+# each token's 128-row block gets the same key pieces on neighbouring lists)
+# ---------------------------------------------------------------------------
+
+def _is_ganged(plan, H):
+    items = plan.work_items().numpy()
+    ptr = plan.workgroup_ptr().numpy()
+    first = {}
+    for w in range(len(ptr) - 1):
+        for pos, it in enumerate(items[ptr[w]:ptr[w + 1]]):
+            first.setdefault((int(it[0]), int(it[1])), (w, pos, int(it[3])))
+    return any(first.get((b, r0 + H)) == (w + 1, pos, t0) for (b, r0), (w, pos, t0) in first.items())
+
+
+@pytest.mark.parametrize("layout", [0, 1])
+def test_gang_prefill(mla, layout):
+    H, s_q = 128, 4
+    w = make_workload(kind="prefill", kv_lens=[700, 2100, 64, 1500], q_lens=[s_q] * 4, heads=H, page_size=64,
+                      seed=540 + layout)
+    x = _dev_inputs(w)
+    plan = mla.mla_plan_create(mla.MLA_KIND_PREFILL, w.batch, H, w.page_size, w.num_pages, w.kv_len, w.kv_indptr,
+                               qo_indptr=w.qo_indptr, lse_layout=layout)
+    assert _is_ganged(plan, H)
+    out, lse = mla.mla_prefill(plan, x["q_nope"], x["q_pe"], x["ckv"], x["kpe"], x["qo_indptr"], x["kv_indptr"],
+                               x["kv_indices"], w.sm_scale)
+    torch.cuda.synchronize()
+    if layout == mla.MLA_LSE_HEADS_FIRST:
+        lse = lse.permute(0, 2, 1).reshape(-1, H)
+    compare(out, lse, *oracle.mla_prefill_ref(w.q_nope, w.q_pe, w.ckv, w.kpe, w.qo_indptr, w.kv_indptr,
+                                              w.kv_indices, w.kv_len, w.sm_scale))
+
+
+def test_gang_capacity_prefill(mla):
+    H, max_kv, max_q = 128, 4096, 4
+    plan = mla.mla_plan_create(mla.MLA_KIND_PREFILL, 3, H, 64, 200, None, None, max_kv_len=max_kv,
+                               max_seq_len_q=max_q, validate=True)
+    assert _is_ganged(plan, H)
+    for step, (qlens, lens) in enumerate([([4, 2, 4], [4096, 900, 4]), ([1, 4, 3], [64, 4000, 1500])]):
+        say(f"gang capacity prefill step {step}: q {qlens} kv {lens}")
+        w = make_workload(kind="prefill", kv_lens=lens, q_lens=qlens, heads=H, page_size=64, seed=545 + step,
+                          pool_pages=200)
+        x = _dev_inputs(w)
+        out, lse = mla.mla_prefill_live(plan, x["q_nope"], x["q_pe"], x["ckv"], x["kpe"], x["qo_indptr"],
+                                        w.kv_len.to(DEV), x["kv_indptr"], x["kv_indices"], w.sm_scale)
+        torch.cuda.synchronize()
+        compare(out, lse, *oracle.mla_prefill_ref(w.q_nope, w.q_pe, w.ckv, w.kpe, w.qo_indptr, w.kv_indptr,
+                                                  w.kv_indices, w.kv_len, w.sm_scale))
